@@ -1,0 +1,174 @@
+"""fp64 CPU oracle for split-KV decode attention -- TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, the smoke check and the benchmark's CPU-baseline leg may
+import this package.  The GPU library and its Python binding never import it.
+
+The arithmetic lives in ``fd_oracle.c`` (plain C, double precision, one
+thread per independent (batch, head, query-position) row).  This module only
+builds that file with gcc, loads it with ctypes and marshals numpy arrays.
+
+Inputs are numpy arrays holding the exact values the GPU reads:
+  * fp32 tensors as ``np.float32``;
+  * bf16 tensors as their raw bit patterns, ``np.uint16``.
+Outputs are ``np.float64``.
+
+Layouts: q/out ``[B, Hq, q_len, D]``, k/v ``[B, Hkv, Lmax, D]``,
+cache_lens ``[B]`` int32, lse ``[B, Hq, q_len]``, partials
+``[B, Hq, q_len, S, D]`` and ``[B, Hq, q_len, S]``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "fd_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+_lib = None
+
+
+def build(out_path: str = _LIB, src_path: str = _SRC, extra_flags=()) -> str:
+    """Compile the oracle with gcc into a shared library; return its path."""
+    cmd = ["gcc", "-O2", "-std=c11", "-Wall", "-fPIC", "-shared", "-pthread",
+           *extra_flags, "-o", out_path, src_path, "-lm"]
+    subprocess.run(cmd, check=True)
+    return out_path
+
+
+def _declare(lib):
+    i32, dbl, vp = ctypes.c_int, ctypes.c_double, ctypes.c_void_p
+    lib.orc_attention.argtypes = [i32] * 7 + [vp, vp, vp, vp, dbl, vp, vp, i32]
+    lib.orc_attention.restype = i32
+    lib.orc_attention_split.argtypes = ([i32] * 7 + [vp, vp, vp, vp, dbl, i32, i32, i32]
+                                        + [vp] * 5 + [i32])
+    lib.orc_attention_split.restype = i32
+    lib.orc_attention_sequential.argtypes = [i32] * 7 + [vp, vp, vp, vp, dbl, i32, vp, vp, i32]
+    lib.orc_attention_sequential.restype = i32
+    lib.orc_merge_lse.argtypes = [ctypes.c_long, i32, i32, vp, vp, vp, vp]
+    lib.orc_merge_lse.restype = i32
+    return lib
+
+
+def load(path: str | None = None):
+    """Load (building first if needed) the oracle library."""
+    global _lib
+    if path is not None:
+        return _declare(ctypes.CDLL(path))
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build()
+        _lib = _declare(ctypes.CDLL(_LIB))
+    return _lib
+
+
+def _ptr(a: np.ndarray):
+    return ctypes.c_void_p(a.ctypes.data)
+
+
+def _prep(q, k, v, cache_lens):
+    q = np.ascontiguousarray(q)
+    k = np.ascontiguousarray(k)
+    v = np.ascontiguousarray(v)
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share one dtype")
+    if q.dtype == np.float32:
+        code = 0
+    elif q.dtype == np.uint16:
+        code = 1
+    else:
+        raise TypeError("inputs must be float32 values or uint16 bf16 bit patterns")
+    if q.ndim != 4 or k.ndim != 4 or v.shape != k.shape:
+        raise ValueError("q must be [B,Hq,q_len,D]; k and v [B,Hkv,Lmax,D]")
+    B, Hq, q_len, D = q.shape
+    Bk, Hkv, Lmax, Dk = k.shape
+    if Bk != B or Dk != D:
+        raise ValueError("q and k/v disagree on batch or head_dim")
+    lens = np.ascontiguousarray(np.asarray(cache_lens, dtype=np.int32))
+    if lens.shape != (B,):
+        raise ValueError("cache_lens must have shape [B]")
+    return q, k, v, lens, (B, Hq, Hkv, D, q_len, Lmax, code)
+
+
+def _check(rc, name):
+    if rc != 0:
+        raise ValueError(f"{name}: oracle rejected its arguments (rc={rc})")
+
+
+def attention(q, k, v, cache_lens, scale, nthreads: int = 0, lib=None):
+    """Plain definition: returns (out [B,Hq,q_len,D], lse [B,Hq,q_len]) in fp64."""
+    lib = lib or load()
+    q, k, v, lens, dims = _prep(q, k, v, cache_lens)
+    B, Hq, Hkv, D, q_len, Lmax, code = dims
+    out = np.empty((B, Hq, q_len, D), np.float64)
+    lse = np.empty((B, Hq, q_len), np.float64)
+    rc = lib.orc_attention(*dims, _ptr(q), _ptr(k), _ptr(v), _ptr(lens),
+                           float(np.float32(scale)), _ptr(out), _ptr(lse), nthreads)
+    _check(rc, "attention")
+    return out, lse
+
+
+def attention_split(q, k, v, cache_lens, scale, num_splits: int = 0, tile_len: int = 0,
+                    slots: int | None = None, nthreads: int = 0, lib=None):
+    """Split form.  Returns (out, lse, o_part, m_part, lse_part).
+
+    ``num_splits > 0``: tile = ceil(L_b / num_splits) for each sequence.
+    ``num_splits == 0``: fixed tile ``tile_len``.
+    ``slots``: partial slots per row (default: the largest tile count).
+    """
+    lib = lib or load()
+    q, k, v, lens, dims = _prep(q, k, v, cache_lens)
+    B, Hq, Hkv, D, q_len, Lmax, code = dims
+    if slots is None:
+        counts = []
+        for L in lens.tolist():
+            T = -(-L // num_splits) if num_splits > 0 else tile_len
+            T = max(T, 1)
+            counts.append(-(-L // T))
+        slots = max([1] + counts)
+    out = np.empty((B, Hq, q_len, D), np.float64)
+    lse = np.empty((B, Hq, q_len), np.float64)
+    o_part = np.empty((B, Hq, q_len, slots, D), np.float64)
+    m_part = np.empty((B, Hq, q_len, slots), np.float64)
+    lse_part = np.empty((B, Hq, q_len, slots), np.float64)
+    rc = lib.orc_attention_split(*dims, _ptr(q), _ptr(k), _ptr(v), _ptr(lens),
+                                 float(np.float32(scale)), int(num_splits), int(tile_len),
+                                 int(slots), _ptr(o_part), _ptr(m_part), _ptr(lse_part),
+                                 _ptr(out), _ptr(lse), nthreads)
+    _check(rc, "attention_split")
+    return out, lse, o_part, m_part, lse_part
+
+
+def attention_sequential(q, k, v, cache_lens, scale, block: int = 256, nthreads: int = 0,
+                         lib=None):
+    """Running-rescaling form over fixed blocks of ``block`` keys."""
+    lib = lib or load()
+    q, k, v, lens, dims = _prep(q, k, v, cache_lens)
+    B, Hq, Hkv, D, q_len, Lmax, code = dims
+    out = np.empty((B, Hq, q_len, D), np.float64)
+    lse = np.empty((B, Hq, q_len), np.float64)
+    rc = lib.orc_attention_sequential(*dims, _ptr(q), _ptr(k), _ptr(v), _ptr(lens),
+                                      float(np.float32(scale)), int(block), _ptr(out),
+                                      _ptr(lse), nthreads)
+    _check(rc, "attention_sequential")
+    return out, lse
+
+
+def merge_lse(o_part, lse_part, lib=None):
+    """Merge partials o_part [..., S, D] with lse_part [..., S] into (out, lse)."""
+    lib = lib or load()
+    o_part = np.ascontiguousarray(o_part, dtype=np.float64)
+    lse_part = np.ascontiguousarray(lse_part, dtype=np.float64)
+    S, D = o_part.shape[-2], o_part.shape[-1]
+    lead = o_part.shape[:-2]
+    if lse_part.shape != lead + (S,):
+        raise ValueError("lse_part must be o_part's shape without the last axis")
+    rows = int(np.prod(lead)) if lead else 1
+    out = np.empty(lead + (D,), np.float64)
+    lse = np.empty(lead, np.float64)
+    rc = lib.orc_merge_lse(rows, S, D, _ptr(o_part), _ptr(lse_part), _ptr(out), _ptr(lse))
+    _check(rc, "merge_lse")
+    return out, lse
