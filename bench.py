@@ -1,0 +1,244 @@
+#!/usr/bin/env python3
+"""Benchmark of split-KV decode attention on one MI355X.
+
+One step = one whole pass of the method over one batch: the per-tile partial
+kernel and the merge kernel (``fd_decode_attention``), on inputs already
+resident in HBM.  The default workload is the 32k-context GQA decode layer
+(batch 1, 32 query heads, 8 KV heads, head_dim 128, bf16, planner splits).
+
+Timing: W untimed warm-up steps, then K timed steps between two
+synchronisations, measured with events on the stream the kernels run on.  The
+K/V caches rotate over several identical copies (>= 1 GiB in total) so that
+the 256 MB last-level cache cannot hold them and every step reads HBM.
+
+Printed: one JSON line with the metric (algorithmic GB/s per step, i.e. the
+bytes any implementation must move -- K, V, q, out, lse -- over the step
+time), the roofline of the dominant kernel (the partial kernel, timed per
+launch with events), and the fp64 CPU oracle's rate on a bounded sample of the
+same workload as a reference point.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode-attention HBM GB/s (% of MI355X peak) and µs/step at 32k ctx"
+HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "decode_attention_14_amd", "csrc", f)
+                  for f in ("fd_decode.hip", "fd_internal.h")]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def parse_args():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="gqa_32k")
+    ap.add_argument("--num-splits", type=int, default=0, help="force a split count (0: planner)")
+    ap.add_argument("--tile-len", type=int, default=0, help="override the planner's tile length")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target oracle time")
+    ap.add_argument("--calibrate-copy", type=int, default=0,
+                    help="also run N plain 512 MiB device copies (counter calibration)")
+    return ap.parse_args()
+
+
+def algorithmic_bytes(w, lens):
+    """Bytes any implementation must move: visible K and V rows, q, out, lse."""
+    el = 2 if w.dtype == "bf16" else 4
+    kv = 2 * sum(lens) * w.num_kv_heads * w.head_dim * el
+    q = w.batch * w.num_q_heads * w.q_len * w.head_dim * el
+    return kv, q, q, w.batch * w.num_q_heads * w.q_len * 4
+
+
+def cpu_baseline(w, q, k, v, cl, alg_bytes, seconds):
+    import oracle
+    from decode_attention_14_amd.inputs import as_oracle_array
+
+    threads = max(1, min(16, os.cpu_count() or 1))
+    qa, ka, va, la = as_oracle_array(q), as_oracle_array(k), as_oracle_array(v), cl.numpy()
+    oracle.load()
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.attention(qa, ka, va, la, w.scale, nthreads=threads)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or reps >= 1000:
+            break
+    return {
+        "value": round(alg_bytes * reps / el / 1e9, 4),
+        "unit": "GB/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{reps} full step(s) of {w.name} in fp64 ({el:.1f} s)",
+    }
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the multi-GPU sequence split is a design, not part of this build)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from decode_attention_14_amd import binding as fd
+    from decode_attention_14_amd.inputs import WORKLOADS, workload_inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    fd.load_library()
+    w = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"[bench] generating {w.name}", file=sys.stderr, flush=True)
+    q, k, v, cl = workload_inputs(w)
+    lens = cl.tolist()
+    kv_b, q_b, out_b, lse_b = algorithmic_bytes(w, lens)
+    step_bytes = kv_b + q_b + out_b + lse_b
+    partial_bytes = kv_b + q_b
+
+    plan = fd.plan_for(q, k, cl, num_splits=args.num_splits)
+    if args.tile_len:
+        plan = fd.Plan(fd.FdPlan(args.tile_len, max(1, -(-max(lens) // args.tile_len))), [])
+    num_splits = args.num_splits
+    slots = num_splits if num_splits else plan.max_splits
+
+    copies = int(min(8, max(2, math.ceil((1 << 30) / max(1, 2 * k.numel() * k.element_size())))))
+    qd, cld = q.to(dev), cl.to(dev)
+    kd0, vd0 = k.to(dev), v.to(dev)
+    kvs = [(kd0, vd0)] + [(kd0.clone(), vd0.clone()) for _ in range(copies - 1)]
+    del q, k, v
+    out = torch.empty_like(qd)
+    lse = torch.empty(qd.shape[:3], dtype=torch.float32, device=dev)
+    dims = fd.dims_of(qd, kd0)
+    ws_bytes = fd.workspace_bytes(dims, slots) if slots > 1 else 0
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    o_part = torch.empty(*qd.shape[:3], slots, w.head_dim, dtype=torch.float32, device=dev)
+    m_part = torch.empty(*qd.shape[:3], slots, dtype=torch.float32, device=dev)
+    l_part = torch.empty_like(m_part)
+    fplan = plan.plan if not num_splits else None
+
+    def step(i):
+        kd, vd = kvs[i % copies]
+        fd.decode_attention(qd, kd, vd, cld, scale=w.scale, num_splits=num_splits, plan=fplan,
+                            out=out, lse=lse, workspace=ws if ws_bytes else None)
+
+    print(f"[bench] plan {plan.plan} copies={copies} warmup={args.warmup} steps={args.steps}",
+          file=sys.stderr, flush=True)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+    print(f"[bench] timed {args.steps} steps: {ms_per_step * 1e3:.2f} us/step (wall {wall:.3f} s)",
+          file=sys.stderr, flush=True)
+
+    # Dominant kernel alone: the partial pass, timed per launch with events.
+    n_k = max(20, min(args.steps, 200))
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(n_k)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(n_k)]
+    cstarts = [torch.cuda.Event(enable_timing=True) for _ in range(n_k)]
+    cends = [torch.cuda.Event(enable_timing=True) for _ in range(n_k)]
+    for i in range(n_k):
+        kd, vd = kvs[i % copies]
+        starts[i].record(stream)
+        if slots > 1:
+            fd.decode_partials(qd, kd, vd, cld, scale=w.scale, num_splits=num_splits, plan=fplan,
+                               o_part=o_part, m_part=m_part, lse_part=l_part)
+        else:
+            fd.decode_attention(qd, kd, vd, cld, scale=w.scale, out=out, lse=lse)
+        ends[i].record(stream)
+        cstarts[i].record(stream)
+        if slots > 1:
+            fd.combine(o_part, l_part, out_dtype=out.dtype, out=out, lse=lse)
+        cends[i].record(stream)
+    torch.cuda.synchronize()
+    part_ms = sum(s.elapsed_time(e) for s, e in zip(starts, ends)) / n_k
+    comb_ms = sum(s.elapsed_time(e) for s, e in zip(cstarts, cends)) / n_k if slots > 1 else 0.0
+    achieved = partial_bytes / (part_ms * 1e-3) / 1e9
+
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        try:
+            t = json.load(open(TRAFFIC_FILE)).get(w.name)
+            if t and t.get("kernel_hash") == kernel_source_hash() and t.get("tile_len") == plan.tile_len:
+                traffic = t.get("bytes_per_launch")
+        except (OSError, ValueError):
+            traffic = None
+
+    for i in range(args.calibrate_copy):
+        a = torch.empty(1 << 29, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+
+    result = {
+        "metric": METRIC,
+        "value": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "us_per_step": round(ms_per_step * 1e3, 3),
+        "pct_of_hbm_peak": round(100 * step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": w.name, "batch": w.batch, "q_heads": w.num_q_heads,
+            "kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "q_len": w.q_len,
+            "cache_lens": "fixed %d" % lens[0] if len(set(lens)) == 1 else "U%s sum %d" % (
+                list(w.len_range), sum(lens)),
+            "tile_len": plan.tile_len, "splits": slots, "kv_copies": copies,
+            "step_bytes": step_bytes,
+        },
+        "kernels": {"partial_us": round(part_ms * 1e3, 3), "combine_us": round(comb_ms * 1e3, 3)},
+        "roofline": {
+            "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+            "kernel": "fd_partial_kernel", "bytes_per_launch": partial_bytes,
+        },
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the fp64 oracle on host cores", file=sys.stderr, flush=True)
+        qh, kh, vh, clh = workload_inputs(w)
+        result["cpu_baseline"] = cpu_baseline(w, qh, kh, vh, clh, step_bytes, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,276 @@
+"""Python binding of the C ABI in ``include/fd.h`` (ctypes; argument marshalling only).
+
+torch supplies device memory and the stream: tensors are passed as raw device
+pointers, and work is enqueued on ``torch.cuda.current_stream()`` of the input
+device.  Every computation runs in the HIP kernels of ``libfd.so``; if the
+library is missing this module raises instead of computing anything itself.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from dataclasses import dataclass
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.environ.get("FD_LIBRARY", os.path.join(_PKG, "libfd.so"))
+
+FD_OK, FD_ERR_INVALID, FD_ERR_UNSUPPORTED, FD_ERR_WORKSPACE, FD_ERR_DEVICE = 0, -1, -2, -3, -4
+FD_F32, FD_BF16 = 0, 1
+FD_MAX_SPLITS = 256
+
+EXPORTS = ("fd_plan_splits", "fd_workspace_bytes", "fd_decode_partials", "fd_combine_splits",
+           "fd_decode_attention", "fd_status_string", "fd_last_error", "fd_version")
+
+
+class FdDims(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("q_len", ctypes.c_int32), ("max_cache_len", ctypes.c_int32),
+                ("dtype", ctypes.c_int32)]
+
+
+class FdPlan(ctypes.Structure):
+    _fields_ = [("tile_len", ctypes.c_int32), ("max_splits", ctypes.c_int32),
+                ("workspace_bytes", ctypes.c_uint64), ("work_units", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
+
+    def __repr__(self):
+        return (f"FdPlan(tile_len={self.tile_len}, max_splits={self.max_splits}, "
+                f"workspace_bytes={self.workspace_bytes}, work_units={self.work_units})")
+
+
+class FdError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{status_string(status)}: {message}")
+        self.status = status
+
+
+_lib = None
+
+
+def load_library(path: str | None = None):
+    """Load ``libfd.so`` (raises if it is not built)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"HIP library {p} is not built; run __graft_entry__.build() first")
+    lib = ctypes.CDLL(p)
+    vp, i32, u64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint64
+    dims_p, plan_p = ctypes.POINTER(FdDims), ctypes.POINTER(FdPlan)
+    lib.fd_plan_splits.argtypes = [dims_p, vp, i32, i32, plan_p, vp]
+    lib.fd_plan_splits.restype = i32
+    lib.fd_workspace_bytes.argtypes = [dims_p, i32]
+    lib.fd_workspace_bytes.restype = u64
+    lib.fd_decode_partials.argtypes = [dims_p, vp, vp, vp, vp, ctypes.c_float, i32, plan_p,
+                                       vp, vp, vp, vp]
+    lib.fd_decode_partials.restype = i32
+    lib.fd_combine_splits.argtypes = [i32, i32, i32, i32, i32, vp, vp, i32, vp, vp, vp]
+    lib.fd_combine_splits.restype = i32
+    lib.fd_decode_attention.argtypes = [dims_p, vp, vp, vp, vp, ctypes.c_float, i32, plan_p,
+                                        vp, u64, vp, vp, vp]
+    lib.fd_decode_attention.restype = i32
+    lib.fd_status_string.argtypes = [i32]
+    lib.fd_status_string.restype = ctypes.c_char_p
+    lib.fd_last_error.argtypes = []
+    lib.fd_last_error.restype = ctypes.c_char_p
+    lib.fd_version.argtypes = []
+    lib.fd_version.restype = i32
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().fd_status_string(status).decode()
+
+
+def _check(status: int):
+    if status != FD_OK:
+        raise FdError(status, load_library().fd_last_error().decode())
+
+
+def _dtype_code(t: torch.dtype) -> int:
+    if t == torch.bfloat16:
+        return FD_BF16
+    if t == torch.float32:
+        return FD_F32
+    raise FdError(FD_ERR_UNSUPPORTED, f"dtype {t} not supported (bfloat16 or float32)")
+
+
+def make_dims(batch, num_q_heads, num_kv_heads, head_dim, q_len, max_cache_len, dtype) -> FdDims:
+    code = dtype if isinstance(dtype, int) else _dtype_code(dtype)
+    return FdDims(batch, num_q_heads, num_kv_heads, head_dim, q_len, max_cache_len, code)
+
+
+def dims_of(q: torch.Tensor, k: torch.Tensor) -> FdDims:
+    if q.dim() != 4 or k.dim() != 4:
+        raise FdError(FD_ERR_INVALID, "q must be [B,Hq,q_len,D] and k_cache [B,Hkv,Lmax,D]")
+    B, Hq, q_len, D = q.shape
+    Bk, Hkv, Lmax, Dk = k.shape
+    if Bk != B or Dk != D:
+        raise FdError(FD_ERR_INVALID, f"q {tuple(q.shape)} and k_cache {tuple(k.shape)} disagree")
+    return make_dims(B, Hq, Hkv, D, q_len, Lmax, q.dtype)
+
+
+@dataclass
+class Plan:
+    plan: FdPlan
+    splits_per_seq: list
+
+    @property
+    def tile_len(self):
+        return self.plan.tile_len
+
+    @property
+    def max_splits(self):
+        return self.plan.max_splits
+
+    @property
+    def workspace_bytes(self):
+        return self.plan.workspace_bytes
+
+
+def plan_splits(dims: FdDims, cache_lens_host, num_splits: int = 0, num_cus: int = 0) -> Plan:
+    """Host-side split plan from host lengths (list, numpy array or CPU tensor)."""
+    lib = load_library()
+    lens = torch.as_tensor(cache_lens_host, dtype=torch.int32).cpu().contiguous()
+    if lens.numel() != dims.batch:
+        raise FdError(FD_ERR_INVALID, "cache_lens must have batch entries")
+    splits = torch.zeros(max(dims.batch, 1), dtype=torch.int32)
+    p = FdPlan()
+    _check(lib.fd_plan_splits(ctypes.byref(dims), ctypes.c_void_p(lens.data_ptr()),
+                              int(num_splits), int(num_cus), ctypes.byref(p),
+                              ctypes.c_void_p(splits.data_ptr())))
+    return Plan(p, splits[:dims.batch].tolist())
+
+
+def plan_for(q: torch.Tensor, k: torch.Tensor, cache_lens_host, num_splits: int = 0,
+             num_cus: int = 0) -> Plan:
+    return plan_splits(dims_of(q, k), cache_lens_host, num_splits, num_cus)
+
+
+def workspace_bytes(dims: FdDims, max_splits: int) -> int:
+    return int(load_library().fd_workspace_bytes(ctypes.byref(dims), int(max_splits)))
+
+
+def _ptr(t):
+    return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _check_inputs(q, k_cache, v_cache, cache_lens):
+    if v_cache.shape != k_cache.shape:
+        raise FdError(FD_ERR_INVALID, f"v_cache {tuple(v_cache.shape)} != k_cache {tuple(k_cache.shape)}")
+    if not (q.dtype == k_cache.dtype == v_cache.dtype):
+        raise FdError(FD_ERR_INVALID, "q, k_cache and v_cache must share one dtype")
+    if cache_lens.dtype != torch.int32 or cache_lens.shape != (q.shape[0],):
+        raise FdError(FD_ERR_INVALID, "cache_lens must be int32 of shape [B]")
+    devs = {t.device for t in (q, k_cache, v_cache, cache_lens)}
+    if len(devs) != 1:
+        raise FdError(FD_ERR_INVALID, "all tensors must be on one device")
+
+
+def _check_buffer(t, shape, dtype, name):
+    if t is not None and (tuple(t.shape) != tuple(shape) or t.dtype != dtype):
+        raise FdError(FD_ERR_INVALID, f"{name} must be {dtype} of shape {tuple(shape)}")
+
+
+def _default_scale(D, scale):
+    return float(1.0 / math.sqrt(D)) if scale is None else float(scale)
+
+
+def _require_cuda(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise FdError(FD_ERR_INVALID, "tensors must be on the GPU")
+        if t is not None and not t.is_contiguous():
+            raise FdError(FD_ERR_INVALID, "tensors must be contiguous")
+
+
+def decode_attention(q, k_cache, v_cache, cache_lens, scale=None, num_splits: int = 0,
+                     plan: Plan | FdPlan | None = None, out=None, lse=None, workspace=None):
+    """Split-KV attention.  Returns (out, lse); allocates what is not given.
+
+    q [B,Hq,q_len,D]; k_cache, v_cache [B,Hkv,Lmax,D]; cache_lens [B] int32 on
+    the device.  ``num_splits > 0`` forces the split count; otherwise ``plan``
+    (None: a single tile per sequence).
+    """
+    lib = load_library()
+    _require_cuda(q, k_cache, v_cache, cache_lens, out, lse, workspace)
+    dims = dims_of(q, k_cache)
+    _check_inputs(q, k_cache, v_cache, cache_lens)
+    _check_buffer(out, q.shape, q.dtype, "out")
+    _check_buffer(lse, q.shape[:3], torch.float32, "lse")
+    fp = plan.plan if isinstance(plan, Plan) else plan
+    slots = num_splits if num_splits > 0 else (fp.max_splits if fp is not None else 1)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    ws_bytes = workspace_bytes(dims, slots) if slots > 1 else 0
+    if workspace is None and ws_bytes:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    given = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib.fd_decode_attention(ctypes.byref(dims), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                   _ptr(cache_lens), ctypes.c_float(_default_scale(q.shape[-1], scale)),
+                                   int(num_splits), ctypes.byref(fp) if fp is not None else None,
+                                   _ptr(workspace), given, _ptr(out), _ptr(lse),
+                                   _stream(q.device)))
+    return out, lse
+
+
+def decode_partials(q, k_cache, v_cache, cache_lens, scale=None, num_splits: int = 0,
+                    plan: Plan | FdPlan | None = None, o_part=None, m_part=None, lse_part=None):
+    """First pass only.  Returns (o_part [B,Hq,q_len,S,D], m_part, lse_part [B,Hq,q_len,S])."""
+    lib = load_library()
+    _require_cuda(q, k_cache, v_cache, cache_lens, o_part, m_part, lse_part)
+    dims = dims_of(q, k_cache)
+    _check_inputs(q, k_cache, v_cache, cache_lens)
+    fp = plan.plan if isinstance(plan, Plan) else plan
+    slots = num_splits if num_splits > 0 else (fp.max_splits if fp is not None else 0)
+    if slots < 1:
+        raise FdError(FD_ERR_INVALID, "decode_partials needs num_splits > 0 or a plan")
+    B, Hq, T, D = q.shape
+    _check_buffer(o_part, (B, Hq, T, slots, D), torch.float32, "o_part")
+    _check_buffer(m_part, (B, Hq, T, slots), torch.float32, "m_part")
+    _check_buffer(lse_part, (B, Hq, T, slots), torch.float32, "lse_part")
+    if o_part is None:
+        o_part = torch.empty(B, Hq, T, slots, D, dtype=torch.float32, device=q.device)
+    if m_part is None:
+        m_part = torch.empty(B, Hq, T, slots, dtype=torch.float32, device=q.device)
+    if lse_part is None:
+        lse_part = torch.empty(B, Hq, T, slots, dtype=torch.float32, device=q.device)
+    _check(lib.fd_decode_partials(ctypes.byref(dims), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                  _ptr(cache_lens), ctypes.c_float(_default_scale(D, scale)),
+                                  int(num_splits), ctypes.byref(fp) if fp is not None else None,
+                                  _ptr(o_part), _ptr(m_part), _ptr(lse_part), _stream(q.device)))
+    return o_part, m_part, lse_part
+
+
+def combine(o_part, lse_part, out_dtype=torch.float32, out=None, lse=None):
+    """Second pass only: o_part [B,H,T,S,D], lse_part [B,H,T,S] fp32 -> (out, lse)."""
+    lib = load_library()
+    _require_cuda(o_part, lse_part, out, lse)
+    if o_part.dim() != 5 or lse_part.shape != o_part.shape[:4]:
+        raise FdError(FD_ERR_INVALID, "o_part must be [B,H,T,S,D] and lse_part [B,H,T,S]")
+    if o_part.dtype != torch.float32 or lse_part.dtype != torch.float32:
+        raise FdError(FD_ERR_INVALID, "partials must be float32")
+    B, H, T, S, D = o_part.shape
+    _check_buffer(out, (B, H, T, D), out.dtype if out is not None else out_dtype, "out")
+    _check_buffer(lse, (B, H, T), torch.float32, "lse")
+    if out is None:
+        out = torch.empty(B, H, T, D, dtype=out_dtype, device=o_part.device)
+    if lse is None:
+        lse = torch.empty(B, H, T, dtype=torch.float32, device=o_part.device)
+    _check(lib.fd_combine_splits(B, H, T, D, S, _ptr(o_part), _ptr(lse_part),
+                                 _dtype_code(out.dtype), _ptr(out), _ptr(lse),
+                                 _stream(o_part.device)))
+    return out, lse

@@ -1,0 +1,334 @@
+// fd_api.cpp -- the C ABI declared in include/fd.h: argument validation, the
+// split planner, workspace layout and kernel dispatch.  No device memory is
+// allocated here and nothing is synchronised; kernels are enqueued on the
+// caller's stream.
+#include "fd.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+
+#include "fd_internal.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+fd_status fail(fd_status st, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+void clear_error() { g_last_error[0] = '\0'; }
+
+constexpr int64_t kAlign = 256;
+constexpr float kLog2e = 1.44269504088896340736f;
+
+// Planner constants.  Tiles of 256..1024 keys (page "ChunkedPrefill与
+// FlashDecoding技术解析" §3.1); fewer than about 256 keys per chunk loses to
+// launch and merge overhead (page "FlashDecoding算法原理与多GPU并行解码实战",
+// benchmark section).  Tiles are multiples of 64 keys, the partial kernel's
+// step for bf16 at D = 128.
+constexpr int kMinTile = 256;
+constexpr int kMaxTile = 1024;
+constexpr int kTileGranule = 64;
+constexpr int kUnitsPerCU = 4;
+
+int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+bool misaligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) != 0; }
+
+fd_status check_dims(const fd_dims* d) {
+    if (!d) return fail(FD_ERR_INVALID, "dims is NULL");
+    if (d->batch < 0) return fail(FD_ERR_INVALID, "batch %d < 0", d->batch);
+    if (d->num_q_heads < 1 || d->num_kv_heads < 1)
+        return fail(FD_ERR_INVALID, "head counts must be >= 1 (Hq=%d, Hkv=%d)", d->num_q_heads,
+                    d->num_kv_heads);
+    if (d->num_q_heads % d->num_kv_heads != 0)
+        return fail(FD_ERR_INVALID, "num_q_heads %d is not a multiple of num_kv_heads %d",
+                    d->num_q_heads, d->num_kv_heads);
+    if (d->q_len < 1) return fail(FD_ERR_INVALID, "q_len %d < 1", d->q_len);
+    if (d->max_cache_len < 0) return fail(FD_ERR_INVALID, "max_cache_len %d < 0", d->max_cache_len);
+    if (d->head_dim != 64 && d->head_dim != 128)
+        return fail(FD_ERR_UNSUPPORTED, "head_dim %d not supported (64 or 128)", d->head_dim);
+    if (d->dtype != FD_F32 && d->dtype != FD_BF16)
+        return fail(FD_ERR_UNSUPPORTED, "dtype %d not supported (FD_F32 or FD_BF16)", d->dtype);
+    if (d->batch > 65535) return fail(FD_ERR_UNSUPPORTED, "batch %d above 65535", d->batch);
+    const int64_t rows = (int64_t)d->num_q_heads / d->num_kv_heads * d->q_len;
+    const int64_t blocks = ceil_div(rows, fdk::partial_rows_per_block((int)std::min<int64_t>(rows, 8)));
+    if (blocks * d->num_kv_heads > 65535)
+        return fail(FD_ERR_UNSUPPORTED, "num_kv_heads x row blocks (%lld) above 65535",
+                    (long long)(blocks * d->num_kv_heads));
+    const int64_t total_rows = (int64_t)d->batch * d->num_q_heads * d->q_len;
+    if (total_rows > INT32_MAX) return fail(FD_ERR_UNSUPPORTED, "batch x heads x q_len too large");
+    return FD_OK;
+}
+
+int64_t total_rows(const fd_dims* d) { return (int64_t)d->batch * d->num_q_heads * d->q_len; }
+
+struct Layout {
+    int64_t o_off, m_off, lse_off, bytes;
+};
+
+Layout workspace_layout(const fd_dims* d, int slots) {
+    const int64_t rows = total_rows(d);
+    Layout l;
+    l.o_off = 0;
+    l.m_off = align_up(rows * slots * d->head_dim * 4, kAlign);
+    l.lse_off = l.m_off + align_up(rows * slots * 4, kAlign);
+    l.bytes = l.lse_off + align_up(rows * slots * 4, kAlign);
+    return l;
+}
+
+// Resolve the split rule of a call.  Returns FD_OK and fills *rule.
+fd_status resolve_rule(int32_t num_splits, const fd_plan* plan, fdk::SplitRule* rule) {
+    if (num_splits < 0 || num_splits > FD_MAX_SPLITS)
+        return fail(FD_ERR_INVALID, "num_splits %d outside [0, %d]", num_splits, FD_MAX_SPLITS);
+    if (num_splits > 0) {
+        *rule = {0, num_splits, num_splits};
+        return FD_OK;
+    }
+    if (!plan) {
+        *rule = {0, 1, 1};  // one tile holding every key
+        return FD_OK;
+    }
+    if (plan->max_splits < 1 || plan->max_splits > FD_MAX_SPLITS)
+        return fail(FD_ERR_INVALID, "plan max_splits %d outside [1, %d]", plan->max_splits, FD_MAX_SPLITS);
+    if (plan->tile_len < 1)
+        return fail(FD_ERR_INVALID, "plan tile_len %d < 1 (a forced-count plan needs num_splits)",
+                    plan->tile_len);
+    *rule = {plan->tile_len, 1, plan->max_splits};
+    return FD_OK;
+}
+
+fd_status check_tensors(const fd_dims* d, const void* q, const void* k, const void* v,
+                        const int32_t* lens) {
+    if (!q || !k || !v || !lens) return fail(FD_ERR_INVALID, "q, k_cache, v_cache and cache_lens must be non-NULL");
+    if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16))
+        return fail(FD_ERR_INVALID, "q, k_cache and v_cache must be 16-byte aligned");
+    if (misaligned(lens, 4)) return fail(FD_ERR_INVALID, "cache_lens must be 4-byte aligned");
+    (void)d;
+    return FD_OK;
+}
+
+fdk::PartialArgs make_args(const fd_dims* d, const void* q, const void* k, const void* v,
+                           const int32_t* lens, float scale, const fdk::SplitRule& rule) {
+    fdk::PartialArgs a{};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.cache_lens = lens;
+    a.Hq = d->num_q_heads;
+    a.Hkv = d->num_kv_heads;
+    a.q_len = d->q_len;
+    a.Lmax = d->max_cache_len;
+    a.n_rep = d->num_q_heads / d->num_kv_heads;
+    a.rows = a.n_rep * d->q_len;
+    a.row_blocks = (int32_t)ceil_div(a.rows, fdk::partial_rows_per_block(a.rows));
+    a.rule = rule;
+    a.qk_scale = scale * kLog2e;
+    return a;
+}
+
+fd_status device_status(hipError_t e, const char* what) {
+    if (e != hipSuccess) return fail(FD_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+    return FD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fd_status_string(int32_t status) {
+    switch (status) {
+        case FD_OK: return "FD_OK";
+        case FD_ERR_INVALID: return "FD_ERR_INVALID";
+        case FD_ERR_UNSUPPORTED: return "FD_ERR_UNSUPPORTED";
+        case FD_ERR_WORKSPACE: return "FD_ERR_WORKSPACE";
+        case FD_ERR_DEVICE: return "FD_ERR_DEVICE";
+        default: return "FD_STATUS_UNKNOWN";
+    }
+}
+
+const char* fd_last_error(void) { return g_last_error; }
+
+int32_t fd_version(void) { return 100; }
+
+uint64_t fd_workspace_bytes(const fd_dims* dims, int32_t max_splits) {
+    if (max_splits <= 1 || max_splits > FD_MAX_SPLITS) return 0;
+    char saved[sizeof g_last_error];
+    std::memcpy(saved, g_last_error, sizeof saved);
+    const bool ok = check_dims(dims) == FD_OK;
+    std::memcpy(g_last_error, saved, sizeof saved);
+    if (!ok) return 0;
+    return (uint64_t)workspace_layout(dims, max_splits).bytes;
+}
+
+fd_status fd_plan_splits(const fd_dims* dims, const int32_t* cache_lens_host, int32_t num_splits,
+                         int32_t num_cus, fd_plan* plan, int32_t* splits_per_seq) {
+    clear_error();
+    fd_status st = check_dims(dims);
+    if (st != FD_OK) return st;
+    if (!plan) return fail(FD_ERR_INVALID, "plan is NULL");
+    if (dims->batch > 0 && !cache_lens_host) return fail(FD_ERR_INVALID, "cache_lens_host is NULL");
+    if (num_splits < 0 || num_splits > FD_MAX_SPLITS)
+        return fail(FD_ERR_INVALID, "num_splits %d outside [0, %d]", num_splits, FD_MAX_SPLITS);
+    if (num_cus < 0) return fail(FD_ERR_INVALID, "num_cus %d < 0", num_cus);
+    int64_t sum_len = 0;
+    int32_t max_len = 0;
+    for (int b = 0; b < dims->batch; ++b) {
+        const int32_t L = cache_lens_host[b];
+        if (L < 0 || L > dims->max_cache_len)
+            return fail(FD_ERR_INVALID, "cache_lens[%d] = %d outside [0, %d]", b, L, dims->max_cache_len);
+        sum_len += L;
+        max_len = std::max(max_len, L);
+    }
+    const int rows = dims->num_q_heads / dims->num_kv_heads * dims->q_len;
+    const int64_t row_blocks = ceil_div(rows, fdk::partial_rows_per_block(rows));
+    const int64_t lanes = (int64_t)dims->num_kv_heads * row_blocks;  // units per tile position
+
+    fd_plan p{};
+    if (num_splits > 0) {
+        p.tile_len = 0;
+        p.max_splits = num_splits;
+        int64_t units = 0;
+        for (int b = 0; b < dims->batch; ++b) {
+            const int32_t L = cache_lens_host[b];
+            const int64_t T = std::max<int64_t>(1, ceil_div(L, num_splits));
+            const int64_t S = ceil_div(L, T);
+            units += S * lanes;
+            if (splits_per_seq) splits_per_seq[b] = (int32_t)S;
+        }
+        p.work_units = (int32_t)std::min<int64_t>(units, INT32_MAX);
+    } else {
+        if (num_cus == 0) {
+            int dev = 0;
+            hipDeviceProp_t prop;
+            if (hipGetDevice(&dev) != hipSuccess || hipGetDeviceProperties(&prop, dev) != hipSuccess)
+                return fail(FD_ERR_DEVICE, "cannot query the compute-unit count; pass num_cus");
+            num_cus = prop.multiProcessorCount;
+        }
+        // Spread the batch's key rows over kUnitsPerCU units per CU.
+        const int64_t key_rows = sum_len * lanes;
+        int64_t T = ceil_div(std::max<int64_t>(key_rows, 1), (int64_t)num_cus * kUnitsPerCU);
+        T = align_up(T, kTileGranule);
+        T = std::min<int64_t>(std::max<int64_t>(T, kMinTile), kMaxTile);
+        if (ceil_div(max_len, T) > FD_MAX_SPLITS) T = align_up(ceil_div(max_len, FD_MAX_SPLITS), kTileGranule);
+        int64_t smax = 1, units = 0;
+        for (int b = 0; b < dims->batch; ++b) {
+            const int64_t S = ceil_div(cache_lens_host[b], T);
+            smax = std::max(smax, S);
+            units += S * lanes;
+            if (splits_per_seq) splits_per_seq[b] = (int32_t)S;
+        }
+        p.tile_len = (int32_t)T;
+        p.max_splits = (int32_t)smax;
+        p.work_units = (int32_t)std::min<int64_t>(units, INT32_MAX);
+    }
+    p.workspace_bytes = p.max_splits > 1 ? (uint64_t)workspace_layout(dims, p.max_splits).bytes : 0;
+    *plan = p;
+    return FD_OK;
+}
+
+fd_status fd_decode_partials(const fd_dims* dims, const void* q, const void* k_cache,
+                             const void* v_cache, const int32_t* cache_lens, float scale,
+                             int32_t num_splits, const fd_plan* plan, float* o_part,
+                             float* m_part, float* lse_part, void* stream) {
+    clear_error();
+    fd_status st = check_dims(dims);
+    if (st != FD_OK) return st;
+    if (num_splits == 0 && !plan)
+        return fail(FD_ERR_INVALID, "fd_decode_partials needs num_splits > 0 or a plan");
+    fdk::SplitRule rule;
+    if ((st = resolve_rule(num_splits, plan, &rule)) != FD_OK) return st;
+    if (dims->batch == 0) return FD_OK;
+    if ((st = check_tensors(dims, q, k_cache, v_cache, cache_lens)) != FD_OK) return st;
+    if (!o_part || !m_part || !lse_part)
+        return fail(FD_ERR_INVALID, "o_part, m_part and lse_part must be non-NULL");
+    if (misaligned(o_part, 16) || misaligned(m_part, 4) || misaligned(lse_part, 4))
+        return fail(FD_ERR_INVALID, "o_part must be 16-byte aligned, m_part and lse_part 4-byte aligned");
+    fdk::PartialArgs a = make_args(dims, q, k_cache, v_cache, cache_lens, scale, rule);
+    a.o_part = o_part;
+    a.m_part = m_part;
+    a.lse_part = lse_part;
+    a.direct = 0;
+    return device_status(fdk::launch_partials(dims->dtype, dims->head_dim, dims->batch, a,
+                                              static_cast<hipStream_t>(stream)),
+                         "partial kernel launch");
+}
+
+fd_status fd_combine_splits(int32_t batch, int32_t num_heads, int32_t q_len, int32_t head_dim,
+                            int32_t max_splits, const float* o_part, const float* lse_part,
+                            int32_t out_dtype, void* out, float* lse, void* stream) {
+    clear_error();
+    if (batch < 0 || num_heads < 1 || q_len < 1)
+        return fail(FD_ERR_INVALID, "bad sizes (batch=%d, num_heads=%d, q_len=%d)", batch, num_heads, q_len);
+    if (max_splits < 1 || max_splits > FD_MAX_SPLITS)
+        return fail(FD_ERR_INVALID, "max_splits %d outside [1, %d]", max_splits, FD_MAX_SPLITS);
+    if (head_dim != 64 && head_dim != 128)
+        return fail(FD_ERR_UNSUPPORTED, "head_dim %d not supported (64 or 128)", head_dim);
+    if (out_dtype != FD_F32 && out_dtype != FD_BF16)
+        return fail(FD_ERR_UNSUPPORTED, "out_dtype %d not supported", out_dtype);
+    const int64_t rows = (int64_t)batch * num_heads * q_len;
+    if (rows > INT32_MAX) return fail(FD_ERR_UNSUPPORTED, "too many rows");
+    if (rows == 0) return FD_OK;
+    if (!o_part || !lse_part || !out) return fail(FD_ERR_INVALID, "o_part, lse_part and out must be non-NULL");
+    if (misaligned(o_part, 16) || misaligned(out, out_dtype == FD_BF16 ? 8 : 16) || misaligned(lse_part, 4) ||
+        (lse && misaligned(lse, 4)))
+        return fail(FD_ERR_INVALID, "misaligned buffer (o_part and out need 16 bytes, bf16 out 8)");
+    return device_status(fdk::launch_combine(head_dim, out_dtype, rows, max_splits, o_part, lse_part,
+                                             out, lse, static_cast<hipStream_t>(stream)),
+                         "combine kernel launch");
+}
+
+fd_status fd_decode_attention(const fd_dims* dims, const void* q, const void* k_cache,
+                              const void* v_cache, const int32_t* cache_lens, float scale,
+                              int32_t num_splits, const fd_plan* plan, void* workspace,
+                              uint64_t workspace_bytes, void* out, float* lse, void* stream) {
+    clear_error();
+    fd_status st = check_dims(dims);
+    if (st != FD_OK) return st;
+    fdk::SplitRule rule;
+    if ((st = resolve_rule(num_splits, plan, &rule)) != FD_OK) return st;
+    if (dims->batch == 0) return FD_OK;
+    if ((st = check_tensors(dims, q, k_cache, v_cache, cache_lens)) != FD_OK) return st;
+    if (!out) return fail(FD_ERR_INVALID, "out is NULL");
+    if (misaligned(out, 16)) return fail(FD_ERR_INVALID, "out must be 16-byte aligned");
+    if (lse && misaligned(lse, 4)) return fail(FD_ERR_INVALID, "lse must be 4-byte aligned");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    fdk::PartialArgs a = make_args(dims, q, k_cache, v_cache, cache_lens, scale, rule);
+    if (rule.slots == 1) {
+        a.out = out;
+        a.lse = lse;
+        a.direct = 1;
+        return device_status(fdk::launch_partials(dims->dtype, dims->head_dim, dims->batch, a, s),
+                             "partial kernel launch");
+    }
+    const Layout lay = workspace_layout(dims, rule.slots);
+    if (!workspace || workspace_bytes < (uint64_t)lay.bytes)
+        return fail(FD_ERR_WORKSPACE, "workspace of %llu bytes needed, %llu given%s",
+                    (unsigned long long)lay.bytes, (unsigned long long)workspace_bytes,
+                    workspace ? "" : " (NULL)");
+    if (misaligned(workspace, kAlign)) return fail(FD_ERR_INVALID, "workspace must be 256-byte aligned");
+    char* ws = static_cast<char*>(workspace);
+    a.o_part = reinterpret_cast<float*>(ws + lay.o_off);
+    a.m_part = reinterpret_cast<float*>(ws + lay.m_off);
+    a.lse_part = reinterpret_cast<float*>(ws + lay.lse_off);
+    a.direct = 0;
+    if ((st = device_status(fdk::launch_partials(dims->dtype, dims->head_dim, dims->batch, a, s),
+                            "partial kernel launch")) != FD_OK)
+        return st;
+    return device_status(fdk::launch_combine(dims->head_dim, dims->dtype, total_rows(dims), rule.slots,
+                                             a.o_part, a.lse_part, out, lse, s),
+                         "combine kernel launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,48 @@
+// fd_internal.h -- launch interface between the C-ABI layer (fd_api.cpp) and
+// the HIP kernels (fd_decode.hip).  Not installed; not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fdk {
+
+// How the keys [0, L_b) of sequence b are cut into tiles.
+//   tile_len > 0 : tiles of tile_len keys;
+//   tile_len == 0: num_splits tiles of ceil(L_b / num_splits) keys.
+// At most `slots` tiles; if more would be needed the last tile takes the rest.
+struct SplitRule {
+    int32_t tile_len;
+    int32_t num_splits;
+    int32_t slots;
+};
+
+struct PartialArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const int32_t* cache_lens;
+    float* o_part;   // [rows_total, slots, D]      (partials mode)
+    float* m_part;   // [rows_total, slots]
+    float* lse_part; // [rows_total, slots]
+    void* out;       // [rows_total, D]             (direct mode)
+    float* lse;      // [rows_total] or nullptr
+    int32_t Hq, Hkv, q_len, Lmax, n_rep;
+    int32_t rows;       // query rows per (sequence, KV head): n_rep * q_len
+    int32_t row_blocks; // workgroups per (sequence, KV head, tile) along rows
+    SplitRule rule;
+    float qk_scale;     // scale * log2(e): scores are kept in base 2
+    int32_t direct;     // 1: single slot, write out/lse instead of partials
+};
+
+// Rows handled by one workgroup of the vector partial kernel.
+int partial_rows_per_block(int rows);
+
+hipError_t launch_partials(int dtype, int head_dim, int batch, const PartialArgs& a,
+                           hipStream_t stream);
+
+hipError_t launch_combine(int head_dim, int out_dtype, int64_t rows, int slots,
+                          const float* o_part, const float* lse_part, void* out, float* lse,
+                          hipStream_t stream);
+
+}  // namespace fdk

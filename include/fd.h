@@ -1,0 +1,179 @@
+/*
+ * fd.h -- C ABI of the split-KV ("FlashDecoding") attention library for
+ * AMD MI355X (gfx950).
+ *
+ * The operation.  For every sequence b, query head h and query position t,
+ *
+ *     out[b,h,t,:] = softmax_j( scale * <q[b,h,t,:], k[b,g,j,:]> ) . v[b,g,j,:]
+ *     lse[b,h,t]   = ln sum_j exp( scale * <q[b,h,t,:], k[b,g,j,:]> )
+ *
+ * over the keys j the row may see, with g = h / (Hq / Hkv) (consecutive query
+ * heads share one KV head; page "FlashDecoding算法原理与多GPU并行解码实战",
+ * engineering details item 3).  For decode (q_len = 1) the row sees keys
+ * 0 .. L_b-1, L_b = cache_lens[b] (the length mask of that page's multi-GPU
+ * section).  For a chunk of q_len > 1 new tokens whose K/V are already the
+ * last q_len entries of the cache, position t sees keys 0 .. L_b-q_len+t
+ * (page "ChunkedPrefill与FlashDecoding技术解析" §2.1: causal within the chunk,
+ * full view of the cached prefix).  A row with no visible key gets out = 0
+ * and lse = -inf.
+ *
+ * The method.  The keys of each sequence are cut along the sequence axis into
+ * tiles ("splits"); each tile yields a normalised partial output o_s, its row
+ * max m_s and its log-sum-exp lse_s (page "ChunkedPrefill与FlashDecoding技术
+ * 解析" §3.1, tiles of typically 256-1024 tokens); a second pass merges the
+ * partials by rescaling with the global maximum (same page §3.1 and §3.2; the
+ * merge of page "FlashDecoding算法原理..." multi-GPU step 3):
+ *     LSE = ln sum_s exp(lse_s),   out = sum_s exp(lse_s - LSE) o_s.
+ *
+ * Conventions shared by every call:
+ *   - Tensors are dense, row-major, in device memory owned by the caller.
+ *     The library never allocates, frees or synchronises: work is enqueued
+ *     on `stream` (a hipStream_t; NULL = the default stream) and the call
+ *     returns at once.
+ *   - q, out   [B, Hq, q_len, D]     dtype of fd_dims.dtype
+ *     k_cache, v_cache [B, Hkv, Lmax, D]   same dtype
+ *     cache_lens [B] int32 on the device, each in [0, Lmax] (values outside
+ *     are clamped into that range on the device; they are never read past)
+ *     lse [B, Hq, q_len] fp32, natural log, may be NULL
+ *   - q, k_cache, v_cache, out, o_part must be 16-byte aligned.
+ *   - Every call validates its arguments first.  On any error it returns a
+ *     negative fd_status, records a message for fd_last_error(), and enqueues
+ *     nothing.  A device-side launch failure returns FD_ERR_DEVICE.
+ *   - Supported: dtype FD_F32 or FD_BF16; D = 64 or 128; any Hq/Hkv ratio;
+ *     any q_len >= 1.  Arithmetic is fp32 throughout (scores, softmax,
+ *     accumulation); out is rounded to its dtype with round-to-nearest-even.
+ */
+#ifndef FD_H
+#define FD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fd_status {
+    FD_OK = 0,
+    FD_ERR_INVALID = -1,     /* malformed arguments */
+    FD_ERR_UNSUPPORTED = -2, /* well-formed but not implemented (dtype, D) */
+    FD_ERR_WORKSPACE = -3,   /* workspace missing or too small */
+    FD_ERR_DEVICE = -4       /* HIP runtime error */
+} fd_status;
+
+typedef enum fd_dtype { FD_F32 = 0, FD_BF16 = 1 } fd_dtype;
+
+/* Most partial slots a row may have. */
+#define FD_MAX_SPLITS 256
+
+typedef struct fd_dims {
+    int32_t batch;         /* B >= 0 (0: nothing to do) */
+    int32_t num_q_heads;   /* Hq >= 1 */
+    int32_t num_kv_heads;  /* Hkv >= 1, Hq % Hkv == 0 */
+    int32_t head_dim;      /* D: 64 or 128 */
+    int32_t q_len;         /* query rows per sequence, >= 1 (1 = decode) */
+    int32_t max_cache_len; /* Lmax >= 0: capacity (row stride) of the caches */
+    int32_t dtype;         /* fd_dtype of q, k_cache, v_cache, out */
+} fd_dims;
+
+/* A split plan.  Sequence b is cut into tiles of `tile_len` keys,
+ * S_b = min(ceil(L_b / tile_len), max_splits) of them; when the ceiling
+ * exceeds max_splits the last tile also takes the remaining keys.  Callers
+ * may fill a plan by hand (tile_len >= 1, 1 <= max_splits <= FD_MAX_SPLITS)
+ * or get one from fd_plan_splits. */
+typedef struct fd_plan {
+    int32_t tile_len;         /* keys per tile */
+    int32_t max_splits;       /* partial slots per row */
+    uint64_t workspace_bytes; /* bytes fd_decode_attention needs (0 if max_splits == 1) */
+    int32_t work_units;       /* (sequence, KV head, row block, tile) units holding keys */
+    int32_t reserved;
+} fd_plan;
+
+/* fd_plan_splits -- choose tile length and split counts from host lengths.
+ *
+ * Host-only and pure: reads `cache_lens_host` [B] (host memory), writes
+ * `*plan` and, if non-NULL, `splits_per_seq` [B] (host memory, S_b per
+ * sequence).  With `num_splits` > 0 the count is forced: sequence b uses
+ * tiles of ceil(L_b / num_splits) keys (the chunk size of the algorithm
+ * section of page "FlashDecoding算法原理..."), which may give fewer than
+ * num_splits tiles; plan->tile_len is then 0 and plan->max_splits =
+ * num_splits (<= FD_MAX_SPLITS).  With num_splits == 0 the planner picks one
+ * tile length for the batch: enough (sequence, KV head, tile) work units to
+ * give every compute unit several, tiles between 256 and 1024 keys (page
+ * "ChunkedPrefill与FlashDecoding技术解析" §3.1; below about 256 keys per chunk
+ * launch overhead eats the gain, page "FlashDecoding算法原理..." benchmark
+ * section), raised if needed so no sequence needs more than FD_MAX_SPLITS.
+ * `num_cus` is the compute-unit count to plan for; 0 queries the current
+ * HIP device (the only device call this function may make).
+ * Errors: FD_ERR_INVALID for bad dims, negative lengths, lengths above
+ * max_cache_len, num_splits outside [0, FD_MAX_SPLITS] or num_cus < 0. */
+fd_status fd_plan_splits(const fd_dims* dims, const int32_t* cache_lens_host, int32_t num_splits,
+                         int32_t num_cus, fd_plan* plan, int32_t* splits_per_seq);
+
+/* fd_workspace_bytes -- bytes of workspace fd_decode_attention needs for
+ * `max_splits` partial slots per row (0 when max_splits <= 1 or dims are
+ * invalid).  The workspace holds o_part, m_part and lse_part as laid out for
+ * fd_decode_partials, each starting on a 256-byte boundary. */
+uint64_t fd_workspace_bytes(const fd_dims* dims, int32_t max_splits);
+
+/* fd_decode_partials -- the first pass only: per-tile partials.
+ *
+ * Slots per row S = num_splits if num_splits > 0, else plan->max_splits
+ * (plan must then be non-NULL).  Writes, for every row (b,h,t) and slot s:
+ *   o_part  [B, Hq, q_len, S, D] fp32  tile output normalised by its own sum
+ *   m_part  [B, Hq, q_len, S]    fp32  tile max of the scaled scores
+ *   lse_part[B, Hq, q_len, S]    fp32  tile log-sum-exp (natural log)
+ * A slot whose tile holds no key visible to the row gets m = lse = -inf and
+ * its o_part entry is left unwritten.  This is the "local O and S" step of
+ * page "ChunkedPrefill与FlashDecoding技术解析" §3.2; the partials of several
+ * devices can be merged with fd_combine_splits.
+ * Errors as listed under the conventions; FD_ERR_INVALID if o_part, m_part
+ * or lse_part is NULL. */
+fd_status fd_decode_partials(const fd_dims* dims, const void* q, const void* k_cache,
+                             const void* v_cache, const int32_t* cache_lens, float scale,
+                             int32_t num_splits, const fd_plan* plan, float* o_part,
+                             float* m_part, float* lse_part, void* stream);
+
+/* fd_combine_splits -- the second pass only: merge partials.
+ *
+ * rows = batch * num_heads * q_len; o_part [rows, max_splits, head_dim] and
+ * lse_part [rows, max_splits] fp32 in device memory.  Slots with
+ * lse = -inf are empty: their o_part entries do not affect the result and
+ * may hold anything, NaN included.  Writes
+ * out [rows, head_dim] in out_dtype (FD_F32 or FD_BF16, RNE) and, if
+ * non-NULL, lse [rows] fp32.  A row without a finite slot gets out = 0 and
+ * lse = -inf.  Errors: FD_ERR_INVALID for negative sizes, max_splits outside
+ * [1, FD_MAX_SPLITS], NULL or misaligned buffers; FD_ERR_UNSUPPORTED for
+ * other head_dim or out_dtype values. */
+fd_status fd_combine_splits(int32_t batch, int32_t num_heads, int32_t q_len, int32_t head_dim,
+                            int32_t max_splits, const float* o_part, const float* lse_part,
+                            int32_t out_dtype, void* out, float* lse, void* stream);
+
+/* fd_decode_attention -- the whole operation: partials, then merge.
+ *
+ * Split choice: num_splits > 0 forces that many tiles per sequence (as in
+ * fd_plan_splits); else `plan` (may be NULL: one tile per sequence).  With a
+ * single slot the partial kernel writes out and lse directly and no
+ * workspace is needed (`workspace` may be NULL).  Otherwise `workspace`
+ * (device memory, 256-byte aligned, caller-owned, contents irrelevant on
+ * entry and clobbered on return) must hold at least
+ * fd_workspace_bytes(dims, slots) bytes, else FD_ERR_WORKSPACE. */
+fd_status fd_decode_attention(const fd_dims* dims, const void* q, const void* k_cache,
+                              const void* v_cache, const int32_t* cache_lens, float scale,
+                              int32_t num_splits, const fd_plan* plan, void* workspace,
+                              uint64_t workspace_bytes, void* out, float* lse, void* stream);
+
+/* Diagnostics.  fd_status_string returns a static name for a status.
+ * fd_last_error returns the message of the last failed call on this thread
+ * ("" if none); the pointer stays valid until the next call on the thread. */
+const char* fd_status_string(int32_t status);
+const char* fd_last_error(void);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int32_t fd_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FD_H */

@@ -1,0 +1,248 @@
+"""Host-side checks of the C ABI: the library loads, exports what the header
+declares, the planner's properties hold, and malformed calls are rejected
+before anything is enqueued.  No GPU is needed: every call here either is
+host-only (the planner) or fails validation before any HIP call.
+"""
+import ctypes
+import math
+import os
+import re
+
+import numpy as np
+import pytest
+
+from decode_attention_14_amd import binding as fd
+from decode_attention_14_amd.inputs import WORKLOADS
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fd.h")
+
+# Non-null, 256-byte aligned fake addresses.  Used only in calls that must fail
+# validation; nothing ever dereferences them.
+FAKE = [ctypes.c_void_p(0x100000 * (i + 1)) for i in range(8)]
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return fd.load_library()
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fd_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = header_functions()
+    assert set(names) == set(fd.EXPORTS), names
+    for n in names:
+        assert hasattr(lib, n), f"{n} not exported"
+
+
+def test_version_and_status_strings(lib):
+    assert lib.fd_version() >= 100
+    assert fd.status_string(fd.FD_OK) == "FD_OK"
+    assert fd.status_string(fd.FD_ERR_WORKSPACE) == "FD_ERR_WORKSPACE"
+    assert fd.status_string(-99) == "FD_STATUS_UNKNOWN"
+
+
+def dims(B=1, Hq=32, Hkv=8, D=128, T=1, Lmax=32768, dt=fd.FD_BF16):
+    return fd.make_dims(B, Hq, Hkv, D, T, Lmax, dt)
+
+
+def tiles_of(L, tile_len, num_splits, slots):
+    """The tile boundaries the ABI documents for one sequence."""
+    T = tile_len if tile_len > 0 else -(-L // num_splits)
+    T = max(T, 1)
+    S = min(-(-L // T), slots)
+    return [(s * T, L if s == S - 1 else min(L, (s + 1) * T)) for s in range(S)]
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_planner_on_workloads(name):
+    w = WORKLOADS[name]
+    rng = np.random.Generator(np.random.PCG64(w.seed))
+    if w.len_range:
+        lens = rng.integers(w.len_range[0], w.len_range[1] + 1, size=w.batch).tolist()
+    else:
+        lens = [w.cache_len] * w.batch
+    d = fd.make_dims(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.q_len, w.max_cache_len,
+                     fd.FD_BF16 if w.dtype == "bf16" else fd.FD_F32)
+    p = fd.plan_splits(d, lens, num_splits=w.num_splits, num_cus=256)
+    assert 1 <= p.max_splits <= fd.FD_MAX_SPLITS
+    if w.num_splits:
+        assert p.tile_len == 0 and p.max_splits == w.num_splits
+    else:
+        assert p.tile_len % 64 == 0
+        assert 256 <= p.tile_len <= 1024 or max(lens) > 1024 * 256
+    for L, S in zip(lens, p.splits_per_seq):
+        t = tiles_of(L, p.tile_len, w.num_splits, p.max_splits)
+        assert len(t) == S
+        # exact, ordered partition of [0, L)
+        assert t[0][0] == 0 and t[-1][1] == L
+        assert all(a[1] == b[0] for a, b in zip(t, t[1:]))
+        assert all(hi > lo for lo, hi in t)
+    if p.max_splits > 1:
+        assert p.workspace_bytes == fd.workspace_bytes(d, p.max_splits) > 0
+    else:
+        assert p.workspace_bytes == 0
+
+
+def test_planner_headline_fills_the_chip():
+    p = fd.plan_splits(dims(), [32768], num_cus=256)
+    assert p.tile_len == 256 and p.max_splits == 128
+    assert p.plan.work_units == 8 * 128  # KV heads x tiles, at least 4 per CU
+
+
+def test_planner_short_and_empty_sequences():
+    p = fd.plan_splits(dims(B=4), [0, 1, 255, 256], num_cus=256)
+    assert p.splits_per_seq == [0, 1, 1, 1]
+    assert p.max_splits == 1 and p.workspace_bytes == 0
+
+
+def test_planner_caps_splits_for_long_contexts():
+    d = dims(B=1, Lmax=1 << 20)
+    p = fd.plan_splits(d, [1 << 20], num_cus=256)
+    assert p.max_splits <= fd.FD_MAX_SPLITS
+    assert p.tile_len * p.max_splits >= 1 << 20
+
+
+def test_planner_forced_counts_follow_ceil_rule():
+    d = dims(B=5, Lmax=100)
+    p = fd.plan_splits(d, [9, 0, 1, 100, 7], num_splits=4, num_cus=256)
+    # ceil(L / ceil(L / 4)): 9 keys in chunks of 3 -> 3 tiles; 7 in chunks of 2 -> 4
+    assert p.splits_per_seq == [3, 0, 1, 4, 4]
+    assert p.max_splits == 4 and p.tile_len == 0
+
+
+def test_planner_varlen_balances_units():
+    w = WORKLOADS["varlen_b32"]
+    rng = np.random.Generator(np.random.PCG64(3))
+    lens = rng.integers(512, 8193, size=32).tolist()
+    d = fd.make_dims(32, 64, 8, 128, 1, 8192, fd.FD_BF16)
+    p = fd.plan_splits(d, lens, num_cus=256)
+    tiles = [hi - lo for L in lens for lo, hi in tiles_of(L, p.tile_len, 0, p.max_splits)]
+    assert max(tiles) <= p.tile_len
+    assert p.plan.work_units == 8 * len(tiles)
+    assert p.plan.work_units >= 256
+
+
+@pytest.mark.parametrize("bad,status", [
+    (dict(Hq=30, Hkv=8), fd.FD_ERR_INVALID),
+    (dict(D=96), fd.FD_ERR_UNSUPPORTED),
+    (dict(T=0), fd.FD_ERR_INVALID),
+    (dict(dt=7), fd.FD_ERR_UNSUPPORTED),
+    (dict(B=-1), fd.FD_ERR_INVALID),
+    (dict(Lmax=-5), fd.FD_ERR_INVALID),
+])
+def test_planner_rejects_bad_dims(lib, bad, status):
+    args = dict(B=1, Hq=32, Hkv=8, D=128, T=1, Lmax=64, dt=fd.FD_BF16)
+    args.update(bad)
+    d = dims(**args)
+    lens = (ctypes.c_int32 * 1)(16)
+    p = fd.FdPlan()
+    assert lib.fd_plan_splits(ctypes.byref(d), lens, 0, 256, ctypes.byref(p), None) == status
+    assert lib.fd_last_error().decode()
+
+
+def test_planner_rejects_bad_lengths_and_counts(lib):
+    d = dims(B=2, Lmax=64)
+    p = fd.FdPlan()
+    for lens, ns, cus in [((5, 65), 0, 256), ((-1, 3), 0, 256), ((5, 5), 257, 256),
+                          ((5, 5), -1, 256), ((5, 5), 0, -1)]:
+        arr = (ctypes.c_int32 * 2)(*lens)
+        rc = lib.fd_plan_splits(ctypes.byref(d), arr, ns, cus, ctypes.byref(p), None)
+        assert rc == fd.FD_ERR_INVALID, (lens, ns, cus)
+
+
+def call_decode(lib, d, ptrs=None, num_splits=0, plan=None, ws=None, ws_bytes=0, out=None):
+    q, k, v, lens, o, lse = ptrs or FAKE[:6]
+    return lib.fd_decode_attention(ctypes.byref(d), q, k, v, lens, ctypes.c_float(0.1), num_splits,
+                                   ctypes.byref(plan) if plan is not None else None, ws, ws_bytes,
+                                   o if out is None else out, lse, None)
+
+
+@pytest.mark.parametrize("bad,status", [
+    (dict(Hq=12, Hkv=8), fd.FD_ERR_INVALID),
+    (dict(D=256), fd.FD_ERR_UNSUPPORTED),
+    (dict(T=0), fd.FD_ERR_INVALID),
+    (dict(dt=3), fd.FD_ERR_UNSUPPORTED),
+    (dict(B=70000), fd.FD_ERR_UNSUPPORTED),
+])
+def test_decode_rejects_bad_dims(lib, bad, status):
+    args = dict(B=1, Hq=32, Hkv=8, D=128, T=1, Lmax=64, dt=fd.FD_BF16)
+    args.update(bad)
+    assert call_decode(lib, dims(**args)) == status
+
+
+def test_decode_rejects_null_and_misaligned(lib):
+    d = dims(Lmax=64)
+    q, k, v, lens, o, lse = FAKE[:6]
+    assert call_decode(lib, d, (None, k, v, lens, o, lse)) == fd.FD_ERR_INVALID
+    assert call_decode(lib, d, (q, k, v, None, o, lse)) == fd.FD_ERR_INVALID
+    assert call_decode(lib, d, (q, k, v, lens, None, lse)) == fd.FD_ERR_INVALID
+    odd = ctypes.c_void_p(0x100008)
+    assert call_decode(lib, d, (odd, k, v, lens, o, lse)) == fd.FD_ERR_INVALID
+    assert call_decode(lib, d, (q, k, v, lens, odd, lse)) == fd.FD_ERR_INVALID
+    assert call_decode(lib, d, (q, k, v, lens, o, ctypes.c_void_p(0x100002))) == fd.FD_ERR_INVALID
+    assert "aligned" in lib.fd_last_error().decode()
+
+
+def test_decode_rejects_missing_or_small_workspace(lib):
+    d = dims(Lmax=64)
+    assert call_decode(lib, d, num_splits=4) == fd.FD_ERR_WORKSPACE
+    need = lib.fd_workspace_bytes(ctypes.byref(d), 4)
+    assert need > 0
+    assert call_decode(lib, d, num_splits=4, ws=FAKE[6], ws_bytes=need - 1) == fd.FD_ERR_WORKSPACE
+    assert "workspace" in lib.fd_last_error().decode()
+    # a misaligned workspace of the right size is rejected too
+    assert call_decode(lib, d, num_splits=4, ws=ctypes.c_void_p(0x100010),
+                       ws_bytes=need) == fd.FD_ERR_INVALID
+
+
+def test_decode_rejects_bad_split_arguments(lib):
+    d = dims(Lmax=64)
+    assert call_decode(lib, d, num_splits=257) == fd.FD_ERR_INVALID
+    assert call_decode(lib, d, num_splits=-2) == fd.FD_ERR_INVALID
+    bad = fd.FdPlan(tile_len=0, max_splits=4)
+    assert call_decode(lib, d, plan=bad) == fd.FD_ERR_INVALID
+    bad = fd.FdPlan(tile_len=256, max_splits=300)
+    assert call_decode(lib, d, plan=bad) == fd.FD_ERR_INVALID
+
+
+def test_partials_and_combine_reject_bad_arguments(lib):
+    d = dims(Lmax=64)
+    q, k, v, lens, o, m = FAKE[:6]
+    # neither a split count nor a plan
+    assert lib.fd_decode_partials(ctypes.byref(d), q, k, v, lens, ctypes.c_float(1.0), 0, None,
+                                  o, m, FAKE[6], None) == fd.FD_ERR_INVALID
+    assert lib.fd_decode_partials(ctypes.byref(d), q, k, v, lens, ctypes.c_float(1.0), 4, None,
+                                  None, m, FAKE[6], None) == fd.FD_ERR_INVALID
+    assert lib.fd_combine_splits(1, 32, 1, 128, 0, FAKE[0], FAKE[1], fd.FD_BF16, FAKE[2], None,
+                                 None) == fd.FD_ERR_INVALID
+    assert lib.fd_combine_splits(1, 32, 1, 128, 257, FAKE[0], FAKE[1], fd.FD_BF16, FAKE[2], None,
+                                 None) == fd.FD_ERR_INVALID
+    assert lib.fd_combine_splits(1, 32, 1, 96, 4, FAKE[0], FAKE[1], fd.FD_BF16, FAKE[2], None,
+                                 None) == fd.FD_ERR_UNSUPPORTED
+    assert lib.fd_combine_splits(1, 32, 1, 128, 4, None, FAKE[1], fd.FD_BF16, FAKE[2], None,
+                                 None) == fd.FD_ERR_INVALID
+    assert lib.fd_combine_splits(1, 32, 1, 128, 4, FAKE[0], FAKE[1], 5, FAKE[2], None,
+                                 None) == fd.FD_ERR_UNSUPPORTED
+
+
+def test_empty_batch_is_a_no_op(lib):
+    d = dims(B=0)
+    # nothing to do: OK without touching any pointer
+    assert lib.fd_decode_attention(ctypes.byref(d), None, None, None, None, ctypes.c_float(1.0), 0,
+                                   None, None, 0, None, None, None) == fd.FD_OK
+    assert lib.fd_combine_splits(0, 4, 1, 64, 2, None, None, fd.FD_F32, None, None, None) == fd.FD_OK
+
+
+def test_workspace_layout_size():
+    d = dims(B=2, Hq=8, Hkv=2, D=64, T=3, Lmax=100, dt=fd.FD_F32)
+    rows = 2 * 8 * 3
+    S = 5
+    expect = (math.ceil(rows * S * 64 * 4 / 256) * 256 + 2 * math.ceil(rows * S * 4 / 256) * 256)
+    assert fd.workspace_bytes(d, S) == expect
+    assert fd.workspace_bytes(d, 1) == 0
