@@ -39,9 +39,29 @@
 namespace fdk {
 namespace {
 
+// Tuning constants of the partial kernel: 16-byte load instructions per
+// tensor per step for row blocks of up to 4 rows and of 8 rows, and an
+// optional occupancy target (waves per SIMD; 0 lets the compiler choose).
+#ifndef FD_STEP_LOADS_R4
+#define FD_STEP_LOADS_R4 4
+#endif
+#ifndef FD_STEP_LOADS_R8
+#define FD_STEP_LOADS_R8 2
+#endif
+#ifndef FD_WAVES_PER_SIMD
+#define FD_WAVES_PER_SIMD 0
+#endif
+#if FD_WAVES_PER_SIMD > 0
+#define FD_OCCUPANCY __attribute__((amdgpu_waves_per_eu(FD_WAVES_PER_SIMD)))
+#else
+#define FD_OCCUPANCY
+#endif
+
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
+#define FD_COMBINE_MAX_SLOTS 256
+static_assert(FD_COMBINE_MAX_SLOTS == kThreads, "one lse slot per combine thread");
 
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
 
@@ -146,15 +166,53 @@ __device__ __forceinline__ float slice_dot(const Slice<BF16>& q, const Slice<BF1
     }
 }
 
-template <bool BF16, int D, int ROWS>
-__global__ __launch_bounds__(kThreads) void fd_partial_kernel(PartialArgs a) {
+// Wave-uniform copies (scalar registers) of values the compiler cannot prove
+// uniform by itself.
+__device__ __forceinline__ uint32_t uniform(uint32_t x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ const char* uniform(const char* p) {
+    const uint64_t u = reinterpret_cast<uint64_t>(p);
+    const uint64_t lo = uniform((uint32_t)u), hi = uniform((uint32_t)(u >> 32));
+    return reinterpret_cast<const char*>(lo | (hi << 32));
+}
+
+// Buffer resource over [base, base + bytes): loads at or past `bytes` return 0
+// and touch no memory, so tail lanes need no address clamping.  Base and
+// range must be wave-uniform.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const char* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(uniform(base)), (short)0,
+                                             (int)uniform(bytes), 0x00020000);
+}
+
+template <bool BF16>
+__device__ __forceinline__ void buffer_slice(Slice<BF16>& s, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+    typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+    const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+    if constexpr (BF16) {
+        s.w[0] = x[0]; s.w[1] = x[1]; s.w[2] = x[2]; s.w[3] = x[3];
+    } else {
+        s.w[0] = __uint_as_float(x[0]); s.w[1] = __uint_as_float(x[1]);
+        s.w[2] = __uint_as_float(x[2]); s.w[3] = __uint_as_float(x[3]);
+    }
+}
+
+template <bool BF16, int U>
+struct StepBuf {
+    Slice<BF16> k[U];
+    Slice<BF16> v[U];
+};
+
+template <bool BF16, int D, int ROWS, bool CAUSAL>
+__global__ __launch_bounds__(kThreads) FD_OCCUPANCY void fd_partial_kernel(PartialArgs a) {
     using S16 = Slice<BF16>;
-    constexpr int E = S16::E;         // elements per lane per row slice
-    constexpr int LPR = D / E;        // lanes per key row
-    constexpr int KPI = 64 / LPR;     // key rows per wave load instruction
-    constexpr int U = ROWS >= 8 ? 2 : 4;  // load instructions per tensor per step
-    constexpr int WKEYS = U * KPI;    // keys per wave per step
-    constexpr int KSTEP = kWaves * WKEYS;
+    constexpr int E = S16::E;             // elements per lane per row slice
+    constexpr int LPR = D / E;            // lanes per key row
+    constexpr int KPI = 64 / LPR;         // key rows per wave load instruction
+    constexpr int U = ROWS >= 8 ? FD_STEP_LOADS_R8 : FD_STEP_LOADS_R4;  // loads per tensor per step
+    constexpr int WKEYS = U * KPI;        // keys per wave per step
+    constexpr int KSTEP = kWaves * WKEYS; // keys per workgroup step
+    constexpr int ROWB = D * (BF16 ? 2 : 4);  // bytes per key row
+    constexpr uint32_t UBYTES = KPI * ROWB;   // bytes per wave load instruction
+    constexpr uint32_t SBYTES = KSTEP * ROWB; // bytes per workgroup step
     static_assert(LPR >= 1 && LPR <= 64 && 64 % LPR == 0, "lane layout");
 
     __shared__ float sm_m[kWaves][ROWS];
@@ -201,33 +259,35 @@ __global__ __launch_bounds__(kThreads) void fd_partial_kernel(PartialArgs a) {
         return;
     }
 
-    // Visible-key end of each row inside this tile: position t of a chunk of
-    // q_len rows sees keys < L - q_len + t + 1 (decode: < L).
+    // Visible-key end of each row inside this tile.  Position t of a chunk
+    // of q_len rows sees keys < L - q_len + t + 1; decode rows see < L.
+    // Keys at or past mask_from need per-row masking; below it all are live.
     int rend[ROWS];
+    int mask_from = hi;
 #pragma unroll
     for (int r = 0; r < ROWS; ++r) {
-        int t = (r0 + r) % a.q_len;
-        int nv = L - a.q_len + t + 1;
-        rend[r] = (r < nrows) ? min(hi, nv) : lo;
+        rend[r] = hi;
+        if constexpr (CAUSAL) {
+            const int t = (r0 + r) % a.q_len;
+            const int nv = L - a.q_len + t + 1;
+            if (r < nrows) rend[r] = max(lo, min(hi, nv));
+            mask_from = min(mask_from, rend[r]);
+        }
     }
 
-    // This lane's slice of every query row.
+    // This lane's slice of every query row (inactive rows are zero).
     S16 qs[ROWS];
     const size_t elem = BF16 ? 2 : 4;
 #pragma unroll
     for (int r = 0; r < ROWS; ++r) {
         if (r < nrows) {
             load_slice<BF16>(qs[r], static_cast<const char*>(a.q) + ((row0 + r) * D + pos * E) * elem);
-            if constexpr (!BF16) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) qs[r].w[i] *= a.qk_scale;
-            }
         } else {
 #pragma unroll
             for (int i = 0; i < 4; ++i) qs[r].w[i] = 0;
         }
     }
-    const float dot_scale = BF16 ? a.qk_scale : 1.0f;
+    const float c = a.qk_scale;  // scale * log2(e): scores live in base 2
 
     float m[ROWS], l[ROWS], acc[ROWS][E];
 #pragma unroll
@@ -238,73 +298,100 @@ __global__ __launch_bounds__(kThreads) void fd_partial_kernel(PartialArgs a) {
         for (int e = 0; e < E; ++e) acc[r][e] = 0.f;
     }
 
-    const int64_t head_off = ((int64_t)b * a.Hkv + g) * a.Lmax * D + pos * E;
-    const char* kbase = static_cast<const char*>(a.k) + head_off * elem;
-    const char* vbase = static_cast<const char*>(a.v) + head_off * elem;
+    // Each step reads through a buffer resource covering the rest of the
+    // tile from that step on: the base and range are scalars, the lane
+    // offset is fixed, and the per-instruction offsets are immediates.
+    const int64_t tile_row = ((int64_t)b * a.Hkv + g) * a.Lmax + lo;
+    const char* kt = uniform(static_cast<const char*>(a.k) + tile_row * ROWB);
+    const char* vt = uniform(static_cast<const char*>(a.v) + tile_row * ROWB);
+    const uint32_t tile_bytes = uniform((uint32_t)(hi - lo) * (uint32_t)ROWB);
+    const uint32_t lane_off = (uint32_t)((w * WKEYS + grp) * ROWB + pos * 16);
+    const int lane_key = lo + w * WKEYS + grp;  // key of (step 0, u 0) for this lane
     const int nsteps = (hi - lo + KSTEP - 1) / KSTEP;
-    const int wfirst = lo + w * WKEYS + grp;  // key of (step 0, u 0) for this lane
 
-    S16 kc[U], vc[U], kn[U], vn[U];
-    auto load_step = [&](int step, S16 (&kr)[U], S16 (&vr)[U]) {
+    using Buf = StepBuf<BF16, U>;
+    auto load = [&](Buf& x, int step) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            int j = wfirst + step * KSTEP + u * KPI;
-            j = j < hi ? j : hi - 1;  // tail rows re-read a valid row; masked below
-            load_slice<BF16>(kr[u], kbase + (int64_t)j * D * elem);
-            load_slice<BF16>(vr[u], vbase + (int64_t)j * D * elem);
+            // Scalar arithmetic only (tile_bytes < 2^31): bytes of the tile
+            // left from this instruction's first row on, or 0 past its end.
+            const int done = (int)uniform((uint32_t)step) * (int)SBYTES + u * (int)UBYTES;
+            const int left = max((int)tile_bytes - done, 0);
+            buffer_slice<BF16>(x.k[u], tile_rsrc(kt + done, (uint32_t)left), lane_off);
+            buffer_slice<BF16>(x.v[u], tile_rsrc(vt + done, (uint32_t)left), lane_off);
         }
     };
 
-    load_step(0, kc, vc);
-    for (int step = 0; step < nsteps; ++step) {
-        if (step + 1 < nsteps) load_step(step + 1, kn, vn);
-
+    auto compute = [&](const Buf& x, int step) {
         float sc[U][ROWS];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int j = wfirst + step * KSTEP + u * KPI;
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int r = 0; r < ROWS; ++r) sc[u][r] = group_sum<LPR>(slice_dot<BF16>(qs[r], x.k[u])) * c;
+        // Only a step reaching mask_from has dead keys (tile tail, causal
+        // limit); the test is uniform over the workgroup.
+        if (lo + (step + 1) * KSTEP > mask_from) {
+            const int j0 = lane_key + step * KSTEP;
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int r = 0; r < ROWS; ++r)
+                    if (j0 + u * KPI >= rend[r]) sc[u][r] = -INFINITY;
+        }
+        // Running max; rescale the state only when some max moved.
+        float mx[ROWS];
+        bool moved = false;
+#pragma unroll
+        for (int r = 0; r < ROWS; ++r) {
+            mx[r] = m[r];
+#pragma unroll
+            for (int u = 0; u < U; ++u) mx[r] = fmaxf(mx[r], sc[u][r]);
+            moved |= mx[r] > m[r];
+        }
+        if (__any(moved)) {
 #pragma unroll
             for (int r = 0; r < ROWS; ++r) {
-                float d = group_sum<LPR>(slice_dot<BF16>(qs[r], kc[u])) * dot_scale;
-                sc[u][r] = j < rend[r] ? d : -INFINITY;
+                const float mref = mx[r] == -INFINITY ? 0.f : mx[r];
+                const float alpha = fast_exp2(m[r] - mref);
+                l[r] *= alpha;
+#pragma unroll
+                for (int e = 0; e < E; ++e) acc[r][e] *= alpha;
+                m[r] = mx[r];
             }
         }
-
         float p[U][ROWS];
 #pragma unroll
         for (int r = 0; r < ROWS; ++r) {
-            float mx = m[r];
-#pragma unroll
-            for (int u = 0; u < U; ++u) mx = fmaxf(mx, sc[u][r]);
-            const float mref = mx == -INFINITY ? 0.f : mx;
-            const float alpha = fast_exp2(m[r] - mref);
-            float ps = 0.f;
+            const float mref = m[r] == -INFINITY ? 0.f : m[r];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 p[u][r] = fast_exp2(sc[u][r] - mref);
-                ps += p[u][r];
+                l[r] += p[u][r];
             }
-            l[r] = l[r] * alpha + ps;
-#pragma unroll
-            for (int e = 0; e < E; ++e) acc[r][e] *= alpha;
-            m[r] = mx;
         }
-
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             float vf[E];
-            to_float<BF16>(vc[u], vf);
+            to_float<BF16>(x.v[u], vf);
 #pragma unroll
             for (int r = 0; r < ROWS; ++r)
 #pragma unroll
                 for (int e = 0; e < E; ++e) acc[r][e] = fmaf(p[u][r], vf[e], acc[r][e]);
         }
+    };
 
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            kc[u] = kn[u];
-            vc[u] = vn[u];
-        }
+    // Two register buffers in turn: the loads of step i+1 are in flight while
+    // step i is computed.  The load past the last step falls outside the
+    // tile's buffer range and reads nothing.
+    Buf A, B;
+    load(A, 0);
+    for (int step = 0;;) {
+        load(B, step + 1);
+        compute(A, step);
+        if (++step >= nsteps) break;
+        load(A, step + 1);
+        compute(B, step);
+        if (++step >= nsteps) break;
     }
 
     // Merge the KPI key groups of this wave (lanes with equal pos).
@@ -387,57 +474,72 @@ __device__ __forceinline__ float wave_sum(float x) {
     return x;
 }
 
+// One workgroup per row.  Thread (sp, c) owns float4 column c of the slots
+// sp, sp + NSP, ...; all of its o_part loads are issued before the lse
+// reductions so that a single memory round trip covers the row.
 template <int D, bool OUT_BF16>
 __global__ __launch_bounds__(kThreads) void fd_combine_kernel(const float* __restrict__ o_part,
                                                               const float* __restrict__ lse_part,
                                                               int slots, void* out, float* lse) {
-    constexpr int TPS = D / 4;             // threads per slot, one float4 each
-    constexpr int NSP = kThreads / TPS;    // slots read in parallel
+    constexpr int TPS = D / 4;           // threads per slot, one float4 each
+    constexpr int NSP = kThreads / TPS;  // slots read in parallel
+    constexpr int CH = 16;               // slots per thread per batch of loads
     __shared__ float red[kWaves];
+    __shared__ float sm_lse[FD_COMBINE_MAX_SLOTS];
     __shared__ float4 sm_acc[NSP][TPS];
 
     const int64_t row = blockIdx.x;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int w = tid >> 6;
+    const int sp = tid / TPS;
+    const int c = tid - sp * TPS;
     const float* lp = lse_part + row * slots;
+    const float4* op = reinterpret_cast<const float4*>(o_part + row * slots * D) + c;
 
-    float mx = -INFINITY;
-    for (int s = tid; s < slots; s += kThreads) mx = fmaxf(mx, lp[s]);
-    mx = wave_max(mx);
+    float4 ov[CH];
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+        const int s = sp + i * NSP;
+        ov[i] = s < slots ? op[(int64_t)s * TPS] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    const float x = tid < slots ? lp[tid] : -INFINITY;
+    sm_lse[tid] = x;
+
+    float mx = wave_max(x);
     if (lane == 0) red[w] = mx;
     __syncthreads();
     mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
     __syncthreads();
-
     const bool empty = mx == -INFINITY;
-    float z = 0.f;
-    if (!empty)
-        for (int s = tid; s < slots; s += kThreads) {
-            const float x = lp[s];
-            z += x == -INFINITY ? 0.f : __expf(x - mx);
-        }
+    float z = (empty || x == -INFINITY) ? 0.f : __expf(x - mx);
     z = wave_sum(z);
     if (lane == 0) red[w] = z;
     __syncthreads();
     z = (red[0] + red[1]) + (red[2] + red[3]);
     const float LSE = empty ? -INFINITY : mx + __logf(z);
 
-    const int sp = tid / TPS;
-    const int c = tid - sp * TPS;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     if (!empty) {
-        const float4* op = reinterpret_cast<const float4*>(o_part + row * slots * D) + c;
-#pragma unroll 4
-        for (int s = sp; s < slots; s += NSP) {
-            const float x = lp[s];
-            const float4 o = op[(int64_t)s * TPS];
-            const float wgt = __expf(x - LSE);
-            const bool live = x != -INFINITY;
-            acc.x = live ? fmaf(wgt, o.x, acc.x) : acc.x;
-            acc.y = live ? fmaf(wgt, o.y, acc.y) : acc.y;
-            acc.z = live ? fmaf(wgt, o.z, acc.z) : acc.z;
-            acc.w = live ? fmaf(wgt, o.w, acc.w) : acc.w;
+        for (int base = 0; base < slots; base += CH * NSP) {
+            if (base > 0) {
+#pragma unroll
+                for (int i = 0; i < CH; ++i) {
+                    const int s = base + sp + i * NSP;
+                    ov[i] = s < slots ? op[(int64_t)s * TPS] : make_float4(0.f, 0.f, 0.f, 0.f);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < CH; ++i) {
+                const int s = base + sp + i * NSP;
+                const float xs = s < slots ? sm_lse[s] : -INFINITY;
+                const bool live = xs != -INFINITY;
+                const float wgt = live ? __expf(xs - LSE) : 0.f;
+                acc.x = live ? fmaf(wgt, ov[i].x, acc.x) : acc.x;
+                acc.y = live ? fmaf(wgt, ov[i].y, acc.y) : acc.y;
+                acc.z = live ? fmaf(wgt, ov[i].z, acc.z) : acc.z;
+                acc.w = live ? fmaf(wgt, ov[i].w, acc.w) : acc.w;
+            }
         }
     }
     sm_acc[sp][c] = acc;
@@ -445,8 +547,8 @@ __global__ __launch_bounds__(kThreads) void fd_combine_kernel(const float* __res
     if (tid < TPS) {
         float4 t = sm_acc[0][tid];
 #pragma unroll
-        for (int x = 1; x < NSP; ++x) {
-            const float4 y = sm_acc[x][tid];
+        for (int i = 1; i < NSP; ++i) {
+            const float4 y = sm_acc[i][tid];
             t.x += y.x; t.y += y.y; t.z += y.z; t.w += y.w;
         }
         if constexpr (OUT_BF16) {
@@ -462,17 +564,25 @@ __global__ __launch_bounds__(kThreads) void fd_combine_kernel(const float* __res
     }
 }
 
-template <bool BF16, int D>
-hipError_t launch_partials_d(int batch, const PartialArgs& a, hipStream_t stream) {
+template <bool BF16, int D, bool CAUSAL>
+void launch_partials_c(int batch, const PartialArgs& a, hipStream_t stream) {
     const int rpb = partial_rows_per_block(a.rows);
     dim3 grid(a.rule.slots, a.Hkv * a.row_blocks, batch);
     dim3 block(kThreads);
     switch (rpb) {
-        case 1: hipLaunchKernelGGL((fd_partial_kernel<BF16, D, 1>), grid, block, 0, stream, a); break;
-        case 2: hipLaunchKernelGGL((fd_partial_kernel<BF16, D, 2>), grid, block, 0, stream, a); break;
-        case 4: hipLaunchKernelGGL((fd_partial_kernel<BF16, D, 4>), grid, block, 0, stream, a); break;
-        default: hipLaunchKernelGGL((fd_partial_kernel<BF16, D, 8>), grid, block, 0, stream, a); break;
+        case 1: hipLaunchKernelGGL((fd_partial_kernel<BF16, D, 1, CAUSAL>), grid, block, 0, stream, a); break;
+        case 2: hipLaunchKernelGGL((fd_partial_kernel<BF16, D, 2, CAUSAL>), grid, block, 0, stream, a); break;
+        case 4: hipLaunchKernelGGL((fd_partial_kernel<BF16, D, 4, CAUSAL>), grid, block, 0, stream, a); break;
+        default: hipLaunchKernelGGL((fd_partial_kernel<BF16, D, 8, CAUSAL>), grid, block, 0, stream, a); break;
     }
+}
+
+template <bool BF16, int D>
+hipError_t launch_partials_d(int batch, const PartialArgs& a, hipStream_t stream) {
+    if (a.q_len > 1)
+        launch_partials_c<BF16, D, true>(batch, a, stream);
+    else
+        launch_partials_c<BF16, D, false>(batch, a, stream);
     return hipGetLastError();
 }
 
