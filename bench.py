@@ -6,16 +6,18 @@ kernel and the merge kernel (``fd_decode_attention``), on inputs already
 resident in HBM.  The default workload is the 32k-context GQA decode layer
 (batch 1, 32 query heads, 8 KV heads, head_dim 128, bf16, planner splits).
 
-Timing: W untimed warm-up steps, then K timed steps between two
-synchronisations, measured with events on the stream the kernels run on.  The
-K/V caches rotate over several identical copies (>= 1 GiB in total) so that
-the 256 MB last-level cache cannot hold them and every step reads HBM.
+Timing: W untimed eager warm-up steps; then the K steps are captured once in a
+HIP graph (so host launch overhead is not measured), the graph is replayed
+once untimed, and one timed replay of exactly K steps is bracketed by
+synchronisations and events on the stream the kernels run on.  The K/V caches
+rotate over several identical copies (>= 1 GiB in total) so that the 256 MB
+last-level cache cannot hold them and every step reads HBM.
 
-Printed: one JSON line with the metric (algorithmic GB/s per step, i.e. the
-bytes any implementation must move -- K, V, q, out, lse -- over the step
-time), the roofline of the dominant kernel (the partial kernel, timed per
-launch with events), and the fp64 CPU oracle's rate on a bounded sample of the
-same workload as a reference point.
+Printed: one JSON line with the metric (algorithmic GB/s per step: the bytes
+any implementation must move -- K, V, q, out, lse -- over the step time), the
+roofline of the dominant kernel (the partial pass, timed per launch over a
+graph of back-to-back launches), and the fp64 CPU oracle's rate on a bounded
+sample of the same workload as a reference point.
 """
 from __future__ import annotations
 
@@ -34,10 +36,12 @@ METRIC = "decode-attention HBM GB/s (% of MI355X peak) and µs/step at 32k ctx"
 HBM_PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "decode_attention_14_amd", "csrc", f)
-                  for f in ("fd_decode.hip", "fd_internal.h")]
+                  for f in ("fd_decode.hip", "fd_mfma.hip", "fd_device.h", "fd_internal.h")] + [
+                      os.path.join(ROOT, "decode_attention_14_amd", "build.py")]
 
 
 def kernel_source_hash() -> str:
+    """Hash of the kernel sources and build flags; counter data is tied to it."""
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
         with open(p, "rb") as f:
@@ -53,6 +57,7 @@ def parse_args():
     ap.add_argument("--workload", default="gqa_32k")
     ap.add_argument("--num-splits", type=int, default=0, help="force a split count (0: planner)")
     ap.add_argument("--tile-len", type=int, default=0, help="override the planner's tile length")
+    ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of a graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target oracle time")
     ap.add_argument("--calibrate-copy", type=int, default=0,
@@ -66,6 +71,13 @@ def algorithmic_bytes(w, lens):
     kv = 2 * sum(lens) * w.num_kv_heads * w.head_dim * el
     q = w.batch * w.num_q_heads * w.q_len * w.head_dim * el
     return kv, q, q, w.batch * w.num_q_heads * w.q_len * 4
+
+
+def partial_kernel_name(w) -> str:
+    """The partial-pass kernel the library dispatches to for this workload:
+    matrix cores for bf16 row groups of up to 32 rows, vector ALUs otherwise."""
+    rows = w.num_q_heads // w.num_kv_heads * w.q_len
+    return "fd_mfma_partial_kernel" if w.dtype == "bf16" and rows <= 32 else "fd_partial_kernel"
 
 
 def cpu_baseline(w, q, k, v, cl, alg_bytes, seconds):
@@ -98,7 +110,6 @@ def main():
               "(the multi-GPU sequence split is a design, not part of this build)", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
     from decode_attention_14_amd import binding as fd
@@ -133,7 +144,7 @@ def main():
     lse = torch.empty(qd.shape[:3], dtype=torch.float32, device=dev)
     dims = fd.dims_of(qd, kd0)
     ws_bytes = fd.workspace_bytes(dims, slots) if slots > 1 else 0
-    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    ws = fd.new_workspace(ws_bytes, dev)
     o_part = torch.empty(*qd.shape[:3], slots, w.head_dim, dtype=torch.float32, device=dev)
     m_part = torch.empty(*qd.shape[:3], slots, dtype=torch.float32, device=dev)
     l_part = torch.empty_like(m_part)
@@ -144,51 +155,54 @@ def main():
         fd.decode_attention(qd, kd, vd, cld, scale=w.scale, num_splits=num_splits, plan=fplan,
                             out=out, lse=lse, workspace=ws if ws_bytes else None)
 
-    print(f"[bench] plan {plan.plan} copies={copies} warmup={args.warmup} steps={args.steps}",
-          file=sys.stderr, flush=True)
+    def partial(i):
+        kd, vd = kvs[i % copies]
+        if slots > 1:
+            fd.decode_partials(qd, kd, vd, cld, scale=w.scale, num_splits=num_splits, plan=fplan,
+                               o_part=o_part, m_part=m_part, lse_part=l_part)
+        else:
+            fd.decode_attention(qd, kd, vd, cld, scale=w.scale, out=out, lse=lse)
+
+    def combine(i):
+        fd.combine(o_part, l_part, out_dtype=out.dtype, out=out, lse=lse)
+
+    stream = torch.cuda.current_stream(dev)
+
+    def timed(fn, n):
+        """Average ms per call of fn(0..n-1): one untimed pass, then one timed
+        pass, as a graph replay unless --no-graph."""
+        graph = None
+        if not args.no_graph:
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                for i in range(n):
+                    fn(i)
+        run = graph.replay if graph is not None else (lambda: [fn(i) for i in range(n)])
+        run()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        run()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    print(f"[bench] plan {plan.plan} copies={copies} warmup={args.warmup} steps={args.steps} "
+          f"graph={not args.no_graph}", file=sys.stderr, flush=True)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-
-    stream = torch.cuda.current_stream(dev)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     t0 = time.perf_counter()
-    e0.record(stream)
-    for i in range(args.steps):
-        step(i)
-    e1.record(stream)
-    torch.cuda.synchronize()
+    ms_per_step = timed(step, args.steps)
     wall = time.perf_counter() - t0
-    ms_per_step = e0.elapsed_time(e1) / args.steps
-    print(f"[bench] timed {args.steps} steps: {ms_per_step * 1e3:.2f} us/step (wall {wall:.3f} s)",
-          file=sys.stderr, flush=True)
+    print(f"[bench] timed {args.steps} steps: {ms_per_step * 1e3:.2f} us/step (wall incl. capture "
+          f"{wall:.3f} s)", file=sys.stderr, flush=True)
 
-    # Each kernel alone, launched back to back on the same stream between two
-    # events; the average per launch includes the short gap between
-    # consecutive kernels, so it slightly overstates the kernel's own time.
+    # The partial pass alone and the merge alone, back to back in a graph; the
+    # average per launch includes the short gap between consecutive kernels.
     n_k = max(20, min(args.steps, 200))
-
-    def timed(fn):
-        for i in range(3):
-            fn(i)
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        for i in range(n_k):
-            fn(i)
-        b.record(stream)
-        torch.cuda.synchronize()
-        return a.elapsed_time(b) / n_k
-
-    if slots > 1:
-        part_ms = timed(lambda i: fd.decode_partials(
-            qd, kvs[i % copies][0], kvs[i % copies][1], cld, scale=w.scale, num_splits=num_splits,
-            plan=fplan, o_part=o_part, m_part=m_part, lse_part=l_part))
-        comb_ms = timed(lambda i: fd.combine(o_part, l_part, out_dtype=out.dtype, out=out, lse=lse))
-    else:
-        part_ms = timed(lambda i: fd.decode_attention(qd, kvs[i % copies][0], kvs[i % copies][1], cld,
-                                                      scale=w.scale, out=out, lse=lse))
-        comb_ms = 0.0
+    part_ms = timed(partial, n_k)
+    comb_ms = timed(combine, n_k) if slots > 1 else 0.0
     achieved = partial_bytes / (part_ms * 1e-3) / 1e9
 
     traffic = None
@@ -227,13 +241,13 @@ def main():
             "cache_lens": "fixed %d" % lens[0] if len(set(lens)) == 1 else "U%s sum %d" % (
                 list(w.len_range), sum(lens)),
             "tile_len": plan.tile_len, "splits": slots, "kv_copies": copies,
-            "step_bytes": step_bytes,
+            "step_bytes": step_bytes, "timing": "eager" if args.no_graph else "graph",
         },
         "kernels": {"partial_us": round(part_ms * 1e3, 3), "combine_us": round(comb_ms * 1e3, 3)},
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-            "kernel": "fd_partial_kernel", "bytes_per_launch": partial_bytes,
+            "kernel": partial_kernel_name(w), "bytes_per_launch": partial_bytes,
         },
     }
     if not args.no_cpu_baseline:

@@ -158,6 +158,11 @@ def workspace_bytes(dims: FdDims, max_splits: int) -> int:
     return int(load_library().fd_workspace_bytes(ctypes.byref(dims), int(max_splits)))
 
 
+def new_workspace(nbytes: int, device) -> torch.Tensor:
+    """Device memory for a decode_attention workspace (contents irrelevant)."""
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
 def _ptr(t):
     return ctypes.c_void_p(0 if t is None else t.data_ptr())
 
@@ -217,7 +222,7 @@ def decode_attention(q, k_cache, v_cache, cache_lens, scale=None, num_splits: in
         lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
     ws_bytes = workspace_bytes(dims, slots) if slots > 1 else 0
     if workspace is None and ws_bytes:
-        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+        workspace = new_workspace(ws_bytes, q.device)
     given = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(lib.fd_decode_attention(ctypes.byref(dims), _ptr(q), _ptr(k_cache), _ptr(v_cache),
                                    _ptr(cache_lens), ctypes.c_float(_default_scale(q.shape[-1], scale)),

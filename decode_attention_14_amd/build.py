@@ -8,7 +8,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libfd.so")
-SOURCES = ["fd_api.cpp", "fd_decode.hip"]
+SOURCES = ["fd_api.cpp", "fd_decode.hip", "fd_mfma.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # Packed fp32 instructions are disabled for every HIP translation unit.
@@ -16,6 +16,9 @@ FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     "-Wall", "-Wno-unused-function",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # matrix-core results in ordinary VGPRs: the kernels rescale them with
+    # vector ops, which cannot read accumulation registers directly
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 

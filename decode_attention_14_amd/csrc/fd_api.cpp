@@ -34,12 +34,15 @@ constexpr float kLog2e = 1.44269504088896340736f;
 // Planner constants.  Tiles of 256..1024 keys (page "ChunkedPrefill与
 // FlashDecoding技术解析" §3.1); fewer than about 256 keys per chunk loses to
 // launch and merge overhead (page "FlashDecoding算法原理与多GPU并行解码实战",
-// benchmark section).  Tiles are multiples of 64 keys, the partial kernel's
-// step for bf16 at D = 128.
+// benchmark section).  Tiles are multiples of 64 keys.  The tile length
+// spreads the batch's key rows over one work unit per compute unit: measured
+// on MI355X, a 32k-context GQA layer streams fastest with one long tile per
+// CU (1024 keys, 256 units), and shorter tiles only add per-unit start-up
+// and merge work.
 constexpr int kMinTile = 256;
 constexpr int kMaxTile = 1024;
 constexpr int kTileGranule = 64;
-constexpr int kUnitsPerCU = 4;
+constexpr int kUnitsPerCU = 1;
 
 int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -63,7 +66,8 @@ fd_status check_dims(const fd_dims* d) {
         return fail(FD_ERR_UNSUPPORTED, "dtype %d not supported (FD_F32 or FD_BF16)", d->dtype);
     if (d->batch > 65535) return fail(FD_ERR_UNSUPPORTED, "batch %d above 65535", d->batch);
     const int64_t rows = (int64_t)d->num_q_heads / d->num_kv_heads * d->q_len;
-    const int64_t blocks = ceil_div(rows, fdk::partial_rows_per_block((int)std::min<int64_t>(rows, 8)));
+    if (rows > INT32_MAX) return fail(FD_ERR_UNSUPPORTED, "num_q_heads / num_kv_heads x q_len too large");
+    const int64_t blocks = ceil_div(rows, fdk::partial_block_rows(d->dtype, d->head_dim, (int)rows));
     if (blocks * d->num_kv_heads > 65535)
         return fail(FD_ERR_UNSUPPORTED, "num_kv_heads x row blocks (%lld) above 65535",
                     (long long)(blocks * d->num_kv_heads));
@@ -132,7 +136,7 @@ fdk::PartialArgs make_args(const fd_dims* d, const void* q, const void* k, const
     a.Lmax = d->max_cache_len;
     a.n_rep = d->num_q_heads / d->num_kv_heads;
     a.rows = a.n_rep * d->q_len;
-    a.row_blocks = (int32_t)ceil_div(a.rows, fdk::partial_rows_per_block(a.rows));
+    a.row_blocks = (int32_t)ceil_div(a.rows, fdk::partial_block_rows(d->dtype, d->head_dim, a.rows));
     a.rule = rule;
     a.qk_scale = scale * kLog2e;
     return a;
@@ -192,7 +196,7 @@ fd_status fd_plan_splits(const fd_dims* dims, const int32_t* cache_lens_host, in
         max_len = std::max(max_len, L);
     }
     const int rows = dims->num_q_heads / dims->num_kv_heads * dims->q_len;
-    const int64_t row_blocks = ceil_div(rows, fdk::partial_rows_per_block(rows));
+    const int64_t row_blocks = ceil_div(rows, fdk::partial_block_rows(dims->dtype, dims->head_dim, rows));
     const int64_t lanes = (int64_t)dims->num_kv_heads * row_blocks;  // units per tile position
 
     fd_plan p{};

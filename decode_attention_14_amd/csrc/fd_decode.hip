@@ -34,6 +34,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "fd_device.h"
 #include "fd_internal.h"
 
 namespace fdk {
@@ -51,64 +52,23 @@ namespace {
 #ifndef FD_WAVES_PER_SIMD
 #define FD_WAVES_PER_SIMD 0
 #endif
+// Cache-policy bits of the K/V buffer loads (2: non-temporal, the data is
+// read once and should not displace anything).
+#ifndef FD_LOAD_AUX
+#define FD_LOAD_AUX 2
+#endif
 #if FD_WAVES_PER_SIMD > 0
 #define FD_OCCUPANCY __attribute__((amdgpu_waves_per_eu(FD_WAVES_PER_SIMD)))
 #else
 #define FD_OCCUPANCY
 #endif
 
-constexpr float kLn2 = 0.69314718055994530942f;
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / 64;
-#define FD_COMBINE_MAX_SLOTS 256
-static_assert(FD_COMBINE_MAX_SLOTS == kThreads, "one lse slot per combine thread");
+#ifndef FD_PARTIAL_THREADS
+#define FD_PARTIAL_THREADS 256
+#endif
 
-typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
-
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-
-// fp32 -> bf16 with round-to-nearest-even; NaN stays a quiet NaN.
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
-}
-
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// DPP lane moves inside 16-lane rows (bound_ctrl: no lane reads outside).
-template <int CTRL>
-__device__ __forceinline__ float dpp(float x) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, true));
-}
-constexpr int kDppXor1 = 0xB1;           // quad_perm [1,0,3,2]
-constexpr int kDppXor2 = 0x4E;           // quad_perm [2,3,0,1]
-constexpr int kDppRowHalfMirror = 0x141; // lane i <- lane 7-i within 8
-constexpr int kDppRowMirror = 0x140;     // lane i <- lane 15-i within 16
-
-// Sum over aligned groups of N lanes; every lane of the group gets the sum.
-template <int N>
-__device__ __forceinline__ float group_sum(float x) {
-    static_assert(N == 1 || N == 2 || N == 4 || N == 8 || N == 16 || N == 32 || N == 64, "N");
-    if constexpr (N >= 2) x += dpp<kDppXor1>(x);
-    if constexpr (N >= 4) x += dpp<kDppXor2>(x);
-    if constexpr (N >= 8) x += dpp<kDppRowHalfMirror>(x);
-    if constexpr (N >= 16) x += dpp<kDppRowMirror>(x);
-    if constexpr (N >= 32) x += __shfl_xor(x, 16);
-    if constexpr (N >= 64) x += __shfl_xor(x, 32);
-    return x;
-}
-
-__device__ __forceinline__ void tile_of(const SplitRule& r, int L, int s, int& lo, int& hi, int& S) {
-    int T = r.tile_len > 0 ? r.tile_len : (L + r.num_splits - 1) / r.num_splits;
-    if (T < 1) T = 1;
-    S = (L + T - 1) / T;
-    if (S > r.slots) S = r.slots;
-    lo = s * T;
-    hi = (s == S - 1) ? L : min(L, lo + T);
-}
+constexpr int kPThreads = FD_PARTIAL_THREADS;     // partial kernel
+constexpr int kPWaves = kPThreads / 64;
 
 // One 16-byte slice of a row: E elements.
 template <bool BF16> struct Slice;
@@ -166,27 +126,10 @@ __device__ __forceinline__ float slice_dot(const Slice<BF16>& q, const Slice<BF1
     }
 }
 
-// Wave-uniform copies (scalar registers) of values the compiler cannot prove
-// uniform by itself.
-__device__ __forceinline__ uint32_t uniform(uint32_t x) { return __builtin_amdgcn_readfirstlane(x); }
-__device__ __forceinline__ const char* uniform(const char* p) {
-    const uint64_t u = reinterpret_cast<uint64_t>(p);
-    const uint64_t lo = uniform((uint32_t)u), hi = uniform((uint32_t)(u >> 32));
-    return reinterpret_cast<const char*>(lo | (hi << 32));
-}
-
-// Buffer resource over [base, base + bytes): loads at or past `bytes` return 0
-// and touch no memory, so tail lanes need no address clamping.  Base and
-// range must be wave-uniform.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const char* base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(uniform(base)), (short)0,
-                                             (int)uniform(bytes), 0x00020000);
-}
-
 template <bool BF16>
 __device__ __forceinline__ void buffer_slice(Slice<BF16>& s, __amdgpu_buffer_rsrc_t r, uint32_t off) {
     typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
-    const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+    const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, FD_LOAD_AUX);
     if constexpr (BF16) {
         s.w[0] = x[0]; s.w[1] = x[1]; s.w[2] = x[2]; s.w[3] = x[3];
     } else {
@@ -202,22 +145,22 @@ struct StepBuf {
 };
 
 template <bool BF16, int D, int ROWS, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) FD_OCCUPANCY void fd_partial_kernel(PartialArgs a) {
+__global__ __launch_bounds__(kPThreads) FD_OCCUPANCY void fd_partial_kernel(PartialArgs a) {
     using S16 = Slice<BF16>;
     constexpr int E = S16::E;             // elements per lane per row slice
     constexpr int LPR = D / E;            // lanes per key row
     constexpr int KPI = 64 / LPR;         // key rows per wave load instruction
     constexpr int U = ROWS >= 8 ? FD_STEP_LOADS_R8 : FD_STEP_LOADS_R4;  // loads per tensor per step
     constexpr int WKEYS = U * KPI;        // keys per wave per step
-    constexpr int KSTEP = kWaves * WKEYS; // keys per workgroup step
+    constexpr int KSTEP = kPWaves * WKEYS; // keys per workgroup step
     constexpr int ROWB = D * (BF16 ? 2 : 4);  // bytes per key row
     constexpr uint32_t UBYTES = KPI * ROWB;   // bytes per wave load instruction
     constexpr uint32_t SBYTES = KSTEP * ROWB; // bytes per workgroup step
     static_assert(LPR >= 1 && LPR <= 64 && 64 % LPR == 0, "lane layout");
 
-    __shared__ float sm_m[kWaves][ROWS];
-    __shared__ float sm_l[kWaves][ROWS];
-    __shared__ float sm_acc[kWaves][ROWS][D];
+    __shared__ float sm_m[kPWaves][ROWS];
+    __shared__ float sm_l[kPWaves][ROWS];
+    __shared__ float sm_acc[kPWaves][ROWS][D];
 
     const int s = blockIdx.x;
     const int g = blockIdx.y / a.row_blocks;
@@ -245,14 +188,16 @@ __global__ __launch_bounds__(kThreads) FD_OCCUPANCY void fd_partial_kernel(Parti
         // No keys in this slot.  Mark it empty for the merge (or, with a
         // single slot and an empty sequence, write the empty-row result).
         if (a.direct) {
-            for (int idx = tid; idx < nrows * D; idx += kThreads) {
+            for (int idx = tid; idx < nrows * D; idx += kPThreads) {
                 if constexpr (BF16)
                     reinterpret_cast<uint16_t*>(a.out)[row0 * D + idx] = 0;
                 else
                     reinterpret_cast<float*>(a.out)[row0 * D + idx] = 0.f;
             }
             if (a.lse && tid < nrows) a.lse[row0 + tid] = -INFINITY;
-        } else if (tid < nrows) {
+            return;
+        }
+        if (tid < nrows) {
             a.m_part[(row0 + tid) * slots + s] = -INFINITY;
             a.lse_part[(row0 + tid) * slots + s] = -INFINITY;
         }
@@ -426,16 +371,16 @@ __global__ __launch_bounds__(kThreads) FD_OCCUPANCY void fd_partial_kernel(Parti
     __syncthreads();
 
     // Merge the wave states; thread idx handles output (r, d).
-    for (int idx = tid; idx < nrows * D; idx += kThreads) {
+    for (int idx = tid; idx < nrows * D; idx += kPThreads) {
         const int r = idx / D;
         const int d = idx - r * D;
         float M = -INFINITY;
 #pragma unroll
-        for (int x = 0; x < kWaves; ++x) M = fmaxf(M, sm_m[x][r]);
+        for (int x = 0; x < kPWaves; ++x) M = fmaxf(M, sm_m[x][r]);
         const float Mr = M == -INFINITY ? 0.f : M;
         float num = 0.f, den = 0.f;
 #pragma unroll
-        for (int x = 0; x < kWaves; ++x) {
+        for (int x = 0; x < kPWaves; ++x) {
             const float f = fast_exp2(sm_m[x][r] - Mr);
             num = fmaf(f, sm_acc[x][r][d], num);
             den = fmaf(f, sm_l[x][r], den);
@@ -461,114 +406,56 @@ __global__ __launch_bounds__(kThreads) FD_OCCUPANCY void fd_partial_kernel(Parti
 }
 
 // ---------------------------------------------------------------------------
-// Merge pass.
+// Merge pass: one workgroup of kCThreads per query row.  Wave w accumulates
+// the slots w, w + kCWaves, ... (merge_slots_wave), then wave 0 merges the
+// wave states through LDS and writes the row.
 
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
-    return x;
-}
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
-    return x;
-}
+constexpr int kCThreads = 256;
+constexpr int kCWaves = kCThreads / 64;
 
-// One workgroup per row.  Thread (sp, c) owns float4 column c of the slots
-// sp, sp + NSP, ...; all of its o_part loads are issued before the lse
-// reductions so that a single memory round trip covers the row.
 template <int D, bool OUT_BF16>
-__global__ __launch_bounds__(kThreads) void fd_combine_kernel(const float* __restrict__ o_part,
-                                                              const float* __restrict__ lse_part,
-                                                              int slots, void* out, float* lse) {
-    constexpr int TPS = D / 4;           // threads per slot, one float4 each
-    constexpr int NSP = kThreads / TPS;  // slots read in parallel
-    constexpr int CH = 16;               // slots per thread per batch of loads
-    __shared__ float red[kWaves];
-    __shared__ float sm_lse[FD_COMBINE_MAX_SLOTS];
-    __shared__ float4 sm_acc[NSP][TPS];
-
+__global__ __launch_bounds__(kCThreads) void fd_combine_kernel(const float* __restrict__ o_part,
+                                                               const float* __restrict__ lse_part, int slots,
+                                                               void* out, float* lse) {
+    constexpr int C4 = D / 4;
+    __shared__ float sm_m[kCWaves], sm_z[kCWaves];
+    __shared__ float4 sm_acc[kCWaves][C4];
     const int64_t row = blockIdx.x;
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int w = tid >> 6;
-    const int sp = tid / TPS;
-    const int c = tid - sp * TPS;
-    const float* lp = lse_part + row * slots;
-    const float4* op = reinterpret_cast<const float4*>(o_part + row * slots * D) + c;
-
-    float4 ov[CH];
-#pragma unroll
-    for (int i = 0; i < CH; ++i) {
-        const int s = sp + i * NSP;
-        ov[i] = s < slots ? op[(int64_t)s * TPS] : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-    const float x = tid < slots ? lp[tid] : -INFINITY;
-    sm_lse[tid] = x;
-
-    float mx = wave_max(x);
-    if (lane == 0) red[w] = mx;
-    __syncthreads();
-    mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    __syncthreads();
-    const bool empty = mx == -INFINITY;
-    float z = (empty || x == -INFINITY) ? 0.f : __expf(x - mx);
-    z = wave_sum(z);
-    if (lane == 0) red[w] = z;
-    __syncthreads();
-    z = (red[0] + red[1]) + (red[2] + red[3]);
-    const float LSE = empty ? -INFINITY : mx + __logf(z);
-
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (!empty) {
-        for (int base = 0; base < slots; base += CH * NSP) {
-            if (base > 0) {
-#pragma unroll
-                for (int i = 0; i < CH; ++i) {
-                    const int s = base + sp + i * NSP;
-                    ov[i] = s < slots ? op[(int64_t)s * TPS] : make_float4(0.f, 0.f, 0.f, 0.f);
-                }
-            }
-#pragma unroll
-            for (int i = 0; i < CH; ++i) {
-                const int s = base + sp + i * NSP;
-                const float xs = s < slots ? sm_lse[s] : -INFINITY;
-                const bool live = xs != -INFINITY;
-                const float wgt = live ? __expf(xs - LSE) : 0.f;
-                acc.x = live ? fmaf(wgt, ov[i].x, acc.x) : acc.x;
-                acc.y = live ? fmaf(wgt, ov[i].y, acc.y) : acc.y;
-                acc.z = live ? fmaf(wgt, ov[i].z, acc.z) : acc.z;
-                acc.w = live ? fmaf(wgt, ov[i].w, acc.w) : acc.w;
-            }
+    const int w = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const MergeState st = merge_slots_wave<D>(o_part + row * slots * D, lse_part + row * slots, slots, w,
+                                              kCWaves, lane);
+    if (lane < C4) {
+        sm_acc[w][lane] = st.acc;
+        if (lane == 0) {
+            sm_m[w] = st.m;
+            sm_z[w] = st.z;
         }
     }
-    sm_acc[sp][c] = acc;
     __syncthreads();
-    if (tid < TPS) {
-        float4 t = sm_acc[0][tid];
+    if (w == 0 && lane < C4) {
+        MergeState t{sm_m[0], sm_z[0], sm_acc[0][lane]};
 #pragma unroll
-        for (int i = 1; i < NSP; ++i) {
-            const float4 y = sm_acc[i][tid];
-            t.x += y.x; t.y += y.y; t.z += y.z; t.w += y.w;
-        }
-        if constexpr (OUT_BF16) {
-            uint16_t* o = reinterpret_cast<uint16_t*>(out) + row * D + tid * 4;
-            uint2 packed;
-            packed.x = (uint32_t)f32_to_bf16(t.x) | ((uint32_t)f32_to_bf16(t.y) << 16);
-            packed.y = (uint32_t)f32_to_bf16(t.z) | ((uint32_t)f32_to_bf16(t.w) << 16);
-            *reinterpret_cast<uint2*>(o) = packed;
-        } else {
-            reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + row * D)[tid] = t;
-        }
-        if (tid == 0 && lse) lse[row] = LSE;
+        for (int x = 1; x < kCWaves; ++x) merge_into(t, MergeState{sm_m[x], sm_z[x], sm_acc[x][lane]});
+        void* orow = OUT_BF16 ? (void*)(reinterpret_cast<uint16_t*>(out) + row * D)
+                              : (void*)(reinterpret_cast<float*>(out) + row * D);
+        write_merged<OUT_BF16>(t, orow, lane, lse ? lse + row : nullptr);
     }
+}
+
+// Rows per workgroup of the vector kernel.
+int vector_block_rows(int rows) {
+    if (rows <= 1) return 1;
+    if (rows <= 2) return 2;
+    if (rows <= 4) return 4;
+    return 8;
 }
 
 template <bool BF16, int D, bool CAUSAL>
 void launch_partials_c(int batch, const PartialArgs& a, hipStream_t stream) {
-    const int rpb = partial_rows_per_block(a.rows);
+    const int rpb = vector_block_rows(a.rows);
     dim3 grid(a.rule.slots, a.Hkv * a.row_blocks, batch);
-    dim3 block(kThreads);
+    dim3 block(kPThreads);
     switch (rpb) {
         case 1: hipLaunchKernelGGL((fd_partial_kernel<BF16, D, 1, CAUSAL>), grid, block, 0, stream, a); break;
         case 2: hipLaunchKernelGGL((fd_partial_kernel<BF16, D, 2, CAUSAL>), grid, block, 0, stream, a); break;
@@ -588,15 +475,13 @@ hipError_t launch_partials_d(int batch, const PartialArgs& a, hipStream_t stream
 
 }  // namespace
 
-int partial_rows_per_block(int rows) {
-    if (rows <= 1) return 1;
-    if (rows <= 2) return 2;
-    if (rows <= 4) return 4;
-    return 8;
+int partial_block_rows(int dtype, int head_dim, int rows) {
+    return mfma_partials_supported(dtype, head_dim, rows) ? rows : vector_block_rows(rows);
 }
 
 hipError_t launch_partials(int dtype, int head_dim, int batch, const PartialArgs& a,
                            hipStream_t stream) {
+    if (mfma_partials_supported(dtype, head_dim, a.rows)) return launch_partials_mfma(head_dim, batch, a, stream);
     const bool bf16 = dtype == 1;
     if (bf16) {
         return head_dim == 64 ? launch_partials_d<true, 64>(batch, a, stream)
@@ -609,7 +494,7 @@ hipError_t launch_partials(int dtype, int head_dim, int batch, const PartialArgs
 hipError_t launch_combine(int head_dim, int out_dtype, int64_t rows, int slots,
                           const float* o_part, const float* lse_part, void* out, float* lse,
                           hipStream_t stream) {
-    dim3 grid((unsigned)rows), block(kThreads);
+    dim3 grid((unsigned)rows), block(kCThreads);
     const bool bf16 = out_dtype == 1;
     if (head_dim == 64) {
         if (bf16)

@@ -35,11 +35,19 @@ struct PartialArgs {
     int32_t direct;     // 1: single slot, write out/lse instead of partials
 };
 
-// Rows handled by one workgroup of the vector partial kernel.
-int partial_rows_per_block(int rows);
+// Query rows one workgroup of the partial pass serves, for calls with `rows`
+// = n_rep * q_len rows per (sequence, KV head).  The grid has
+// ceil(rows / partial_block_rows) row blocks per (sequence, KV head, tile).
+int partial_block_rows(int dtype, int head_dim, int rows);
 
+// The partial pass: picks the matrix-core kernel (bf16, up to 32 rows) or the
+// vector kernel (fp32, or more rows) and launches it on `stream`.
 hipError_t launch_partials(int dtype, int head_dim, int batch, const PartialArgs& a,
                            hipStream_t stream);
+
+// Matrix-core partial kernel (fd_mfma.hip) and its applicability.
+bool mfma_partials_supported(int dtype, int head_dim, int rows);
+hipError_t launch_partials_mfma(int head_dim, int batch, const PartialArgs& a, hipStream_t stream);
 
 hipError_t launch_combine(int head_dim, int out_dtype, int64_t rows, int slots,
                           const float* o_part, const float* lse_part, void* out, float* lse,

@@ -1,0 +1,423 @@
+// fd_mfma.hip -- split-KV partial kernel on the matrix cores, for bf16 caches
+// on gfx950 (CDNA4).
+//
+// Same operation as the vector kernel in fd_decode.hip: one workgroup per
+// (tile s, KV head g, sequence b) turns the tile's keys into a partial output
+// with its max and log-sum-exp (page "ChunkedPrefill与FlashDecoding技术解析"
+// §3.1: tile-local attention, then the online-softmax merge), with each K/V
+// row read once for all query rows of the GQA group (page "FlashDecoding算法
+// 原理与多GPU并行解码实战", engineering details item 3).  It serves row
+// groups of up to 32 query rows: the n_rep heads of a decode step, or the
+// rows of a short causal chunk.
+//
+// Why matrix cores for decode.  The method does 4 flop per byte of K/V at a
+// GQA ratio of 4, so the work is bound by HBM; on the vector ALUs, though,
+// the dot products, cross-lane sums and P.V FMAs cost about half of the
+// issue slots that streaming at full HBM speed leaves, and the waves then
+// stall on their own arithmetic instead of keeping loads in flight.  On the
+// matrix cores the same work takes a few percent of the SIMD, so each wave
+// mostly issues loads and waits on memory.
+//
+// Data path.  The tile is cut into blocks of 16 keys.  Wave w takes blocks
+// w, w + 4, w + 8, ... (the four waves stream adjacent memory) and keeps a
+// private ring of FD_MFMA_STAGES block buffers in LDS, filled by direct
+// buffer-to-LDS loads, so the loads in flight cost no registers.  Each row's
+// 16-byte chunks are stored XOR-swizzled by the row, which keeps both LDS
+// read patterns below free of bank conflicts.
+//
+//   S^T = K Q^T  v_mfma_f32_16x16x32_bf16: A = 16 keys x 32 dims of K (one
+//                ds_read_b128 per lane), B = the query rows, held in
+//                registers for the whole tile.  Lane (group G, column q)
+//                receives the scores of keys 4G..4G+3 for query row q.
+//   P V          v_mfma_f32_16x16x16bf16_1k per 16 output dims: A = V^T
+//                (ds_read_b64_tr_b16 turns row-major V into the transposed
+//                operand), B = P^T, which is exactly the score layout above,
+//                so P never moves between lanes.  P is split into a bf16
+//                high part and a bf16 remainder, two products, so the
+//                weights keep about 16 significant bits.
+//   softmax      per lane in base 2 with a lazily moved reference max: the
+//                state is rescaled only when a score exceeds the reference
+//                by more than 2^8 (an exact identity; p <= 256 stays
+//                representable), so most blocks need no cross-lane traffic.
+//                The exact tile max is tracked separately for m_part.
+//
+// The four waves' states are merged through LDS at the end, as in the vector
+// kernel.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fd_device.h"
+#include "fd_internal.h"
+
+namespace fdk {
+namespace {
+
+#ifndef FD_MFMA_STAGES
+#define FD_MFMA_STAGES 4
+#endif
+#ifndef FD_LOAD_AUX
+#define FD_LOAD_AUX 2
+#endif
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
+typedef __attribute__((ext_vector_type(4))) short s16x4_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+#ifndef FD_MFMA_THREADS
+#define FD_MFMA_THREADS 256
+#endif
+constexpr int kMT = FD_MFMA_THREADS;  // threads per workgroup
+constexpr int kMW = kMT / 64;     // waves per workgroup
+constexpr int kKB = 16;           // keys per block
+constexpr int kNS = FD_MFMA_STAGES;
+constexpr float kTau = 8.f;       // lazy rescale threshold, log2 units
+
+template <int D>
+struct Geo {
+    static constexpr int ROWB = 2 * D;          // bytes per key row
+    static constexpr int CH = ROWB / 16;        // 16-byte chunks per row
+    static constexpr int RPI = 64 / CH;         // rows per 1 KiB LDS-load instruction
+    static constexpr int IPB = kKB / RPI;       // instructions per block per tensor
+    static constexpr int BLKB = kKB * ROWB;     // bytes per block per tensor
+    static constexpr int STAGEB = 2 * BLKB;     // K then V
+    static constexpr int WAVEB = kNS * STAGEB;  // ring bytes per wave
+    static constexpr int KS = D / 32;           // k-steps of the score product
+    static constexpr int DB = D / 16;           // output blocks of the P.V product
+    static_assert(CH == 8 || CH == 16, "D = 64 or 128");
+};
+
+// Byte offset inside a block of global chunk c of row r (XOR swizzle).
+template <int D>
+__device__ __forceinline__ int swz(int r, int c) {
+    return r * Geo<D>::ROWB + ((c ^ (r & (Geo<D>::CH - 1))) << 4);
+}
+
+// s_waitcnt with only the vector-memory counter constrained: wait until at
+// most N vector loads of this wave are outstanding (gfx9 encoding: vmcnt in
+// bits [3:0] and [15:14]; expcnt and lgkmcnt left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_le() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xf) | ((N >> 4) << 14) | (0x7 << 4) | (0xf << 8));
+}
+
+// Transposing LDS read, ds_read_b64_tr_b16: in each 16-lane group, lane
+// 4j + q names 4 consecutive bf16 of a row; lane i receives element i % 4 of
+// lane 4j + i / 4 for j = 0..3.  Issued as inline assembly because the
+// compiler treats the builtin as possibly aliasing the LDS loads in flight and
+// would wait for all of them; the result is only valid after lds_settle().
+__device__ __forceinline__ bf16x4_t tr_read(const char* p) {
+    const auto p3 = (const __attribute__((address_space(3))) char*)p;
+    const uint32_t addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p3));
+    bf16x4_t r;
+    asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(addr));
+    return r;
+}
+
+// Wait for every LDS read of this wave, then make the transposed reads'
+// registers visible to the compiler as defined here.
+template <int N>
+__device__ __forceinline__ void lds_settle(bf16x4_t (&v)[N]) {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < N; ++i) asm volatile("" : "+v"(v[i]));
+}
+
+// Start the loads of one block (16 rows of K and of V, `left` bytes of the
+// tile from kp/vp on; none if left <= 0) into LDS at dst: K rows first, then
+// V rows.  Lane l of load instruction i reads its row's global chunk
+// dma_off[i]; the data lands at dst + i * 1024 + 16 * l.  Rows past `left`
+// read as zeros and cost no memory traffic.
+template <int D>
+__device__ __forceinline__ void load_block(const char* kp, const char* vp, int left, char* dst,
+                                           const uint32_t* dma_off) {
+    const uint32_t n = left > 0 ? (uint32_t)left : 0u;
+    const __amdgpu_buffer_rsrc_t rk = tile_rsrc(kp, n);
+    const __amdgpu_buffer_rsrc_t rv = tile_rsrc(vp, n);
+#pragma unroll
+    for (int i = 0; i < Geo<D>::IPB; ++i) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t*)(dst + i * 1024), 16, dma_off[i], 0, 0,
+                                                 FD_LOAD_AUX);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)(dst + Geo<D>::BLKB + i * 1024), 16,
+                                                 dma_off[i], 0, 0, FD_LOAD_AUX);
+    }
+}
+
+template <int D, int NB, bool CAUSAL>
+__global__ __launch_bounds__(kMT) void fd_mfma_partial_kernel(PartialArgs a) {
+    using G = Geo<D>;
+    constexpr int NR = 16 * NB;  // query rows per workgroup
+    constexpr int RS = D + 4;    // padded row stride of the merge area (floats)
+    constexpr int MERGEB = kMW * (NR * RS + 3 * NR) * 4;
+    constexpr int SMEMB = kMW * G::WAVEB > MERGEB ? kMW * G::WAVEB : MERGEB;
+    __shared__ __attribute__((aligned(16))) char smem[SMEMB];
+
+    const int s = blockIdx.x;
+    const int g = blockIdx.y;
+    const int b = blockIdx.z;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = (int)uniform((uint32_t)(tid >> 6));
+    const int grp = lane >> 4;
+    const int col = lane & 15;
+
+    int L = a.cache_lens[b];
+    L = L < 0 ? 0 : (L > a.Lmax ? a.Lmax : L);
+    int lo, hi, S;
+    tile_of(a.rule, L, s, lo, hi, S);
+    lo = (int)uniform((uint32_t)lo);
+    hi = (int)uniform((uint32_t)hi);
+
+    const int nrows = a.rows;
+    const int64_t row0 = ((int64_t)b * a.Hq + (int64_t)g * a.n_rep) * a.q_len;
+    const int slots = a.rule.slots;
+
+    if (s >= S) {
+        if (a.direct) {
+            for (int idx = tid; idx < nrows * D; idx += kMT)
+                reinterpret_cast<uint16_t*>(a.out)[row0 * D + idx] = 0;
+            if (a.lse && tid < nrows) a.lse[row0 + tid] = -INFINITY;
+            return;
+        }
+        if (tid < nrows) {
+            a.m_part[(row0 + tid) * slots + s] = -INFINITY;
+            a.lse_part[(row0 + tid) * slots + s] = -INFINITY;
+        }
+        return;
+    }
+
+    // Visible-key end of this lane's query row in each N block.  Causal rows
+    // t of a chunk see keys < L - q_len + t + 1; the smallest end (t = 0)
+    // bounds the keys every row sees.
+    int rend[NB];
+    int mask_from = hi;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+        rend[nb] = hi;
+        const int r = nb * 16 + col;
+        if constexpr (CAUSAL) {
+            if (r < nrows) rend[nb] = max(lo, min(hi, L - a.q_len + (r % a.q_len) + 1));
+        }
+    }
+    if constexpr (CAUSAL) mask_from = max(lo, min(hi, L - a.q_len + 1));
+
+    // Query rows: B operand of S^T = K Q^T (column = row, 8 dims per lane).
+    bf16x8_t qf[NB][G::KS];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+        const int r = nb * 16 + col;
+#pragma unroll
+        for (int ks = 0; ks < G::KS; ++ks) {
+            if (r < nrows) {
+                const uint4 x = *reinterpret_cast<const uint4*>(
+                    static_cast<const uint16_t*>(a.q) + (row0 + r) * D + 8 * grp + 32 * ks);
+                qf[nb][ks] = __builtin_bit_cast(bf16x8_t, x);
+            } else {
+                qf[nb][ks] = __builtin_bit_cast(bf16x8_t, make_uint4(0, 0, 0, 0));
+            }
+        }
+    }
+    const float c = a.qk_scale;  // scale * log2(e)
+
+    f32x4_t acc[NB][G::DB];
+    float m[NB], l[NB], mx[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+        m[nb] = -INFINITY;
+        l[nb] = 0.f;
+        mx[nb] = -INFINITY;
+#pragma unroll
+        for (int db = 0; db < G::DB; ++db) acc[nb][db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+
+    char* ring = smem + w * G::WAVEB;
+    const int64_t tile_row = ((int64_t)b * a.Hkv + g) * a.Lmax + lo;
+    const char* kt = static_cast<const char*>(a.k) + tile_row * G::ROWB;
+    const char* vt = static_cast<const char*>(a.v) + tile_row * G::ROWB;
+    const int tile_bytes = (hi - lo) * G::ROWB;
+    const int nblk = (hi - lo + kKB - 1) / kKB;
+    const int nw = w < nblk ? (nblk - w + kMW - 1) / kMW : 0;
+
+    // Lane l of load instruction i fills LDS slot (row i*RPI + l/CH, chunk
+    // l%CH) of the block with the row's global chunk (l%CH) ^ row.
+    uint32_t dma_off[G::IPB];
+#pragma unroll
+    for (int i = 0; i < G::IPB; ++i) {
+        const int r = i * G::RPI + lane / G::CH;
+        const int cg = (lane % G::CH) ^ (r & (G::CH - 1));
+        dma_off[i] = (uint32_t)(r * G::ROWB + cg * 16);
+    }
+
+    // Wave block j is tile block w + 4j and goes to ring slot j % kNS.
+#pragma unroll
+    for (int j = 0; j < kNS - 1; ++j) {
+        const int off = (w + j * kMW) * G::BLKB;
+        load_block<D>(kt + off, vt + off, tile_bytes - off, ring + j * G::STAGEB, dma_off);
+    }
+
+    for (int j = 0; j < nw; ++j) {
+        {
+            const int jn = j + kNS - 1;
+            const int off = (w + jn * kMW) * G::BLKB;
+            load_block<D>(kt + off, vt + off, tile_bytes - off, ring + (jn % kNS) * G::STAGEB, dma_off);
+        }
+        wait_vmcnt_le<(kNS - 1) * 2 * G::IPB>();  // block j has landed
+        const char* kb = ring + (j % kNS) * G::STAGEB;
+        const char* vb = kb + G::BLKB;
+
+        bf16x8_t kf[G::KS];
+#pragma unroll
+        for (int ks = 0; ks < G::KS; ++ks)
+            kf[ks] = *reinterpret_cast<const bf16x8_t*>(kb + swz<D>(col, grp + 4 * ks));
+        bf16x4_t vf[G::DB];
+        {
+            const int r = 4 * grp + (col >> 2);
+            const int q4 = col & 3;
+#pragma unroll
+            for (int db = 0; db < G::DB; ++db)
+                vf[db] = tr_read(vb + swz<D>(r, 2 * db + (q4 >> 1)) + 8 * (q4 & 1));
+        }
+        lds_settle(vf);
+
+        const int key0 = lo + (w + j * kMW) * kKB;  // first key of the block
+        const bool edge = key0 + kKB > mask_from;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            f32x4_t st = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < G::KS; ++ks)
+                st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks], qf[nb][ks], st, 0, 0, 0);
+            float x[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) x[i] = st[i] * c;
+            if (edge) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (key0 + 4 * grp + i >= rend[nb]) x[i] = -INFINITY;
+            }
+            const float bm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+            mx[nb] = fmaxf(mx[nb], bm);
+            if (__any(bm > m[nb] + kTau)) {
+                float bw = fmaxf(bm, __shfl_xor(bm, 16));
+                bw = fmaxf(bw, __shfl_xor(bw, 32));
+                const float mn = fmaxf(m[nb], bw);
+                const float alpha = m[nb] == -INFINITY ? 0.f : fast_exp2(m[nb] - mn);
+                l[nb] *= alpha;
+#pragma unroll
+                for (int db = 0; db < G::DB; ++db) acc[nb][db] *= alpha;
+                m[nb] = mn;
+            }
+            const float mref = m[nb] == -INFINITY ? 0.f : m[nb];
+            float p[4];
+            bf16x4_t ph, pl;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                p[i] = fast_exp2(x[i] - mref);
+                ph[i] = (__bf16)p[i];
+                pl[i] = (__bf16)(p[i] - (float)ph[i]);
+            }
+            l[nb] += (p[0] + p[1]) + (p[2] + p[3]);
+#pragma unroll
+            for (int db = 0; db < G::DB; ++db) {
+                acc[nb][db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+                    __builtin_bit_cast(s16x4_t, vf[db]), __builtin_bit_cast(s16x4_t, ph), acc[nb][db], 0, 0, 0);
+                acc[nb][db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+                    __builtin_bit_cast(s16x4_t, vf[db]), __builtin_bit_cast(s16x4_t, pl), acc[nb][db], 0, 0, 0);
+            }
+        }
+    }
+
+    // Merge: the four lane groups of a column, then the four waves via LDS.
+    wait_vmcnt_le<0>();
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+        l[nb] += __shfl_xor(l[nb], 16);
+        l[nb] += __shfl_xor(l[nb], 32);
+        mx[nb] = fmaxf(mx[nb], __shfl_xor(mx[nb], 16));
+        mx[nb] = fmaxf(mx[nb], __shfl_xor(mx[nb], 32));
+    }
+    __syncthreads();  // every wave is done with its ring
+    float* sm_acc = reinterpret_cast<float*>(smem);  // [kMW][NR][RS]
+    float* sm_m = sm_acc + kMW * NR * RS;            // [kMW][NR]
+    float* sm_l = sm_m + kMW * NR;
+    float* sm_x = sm_l + kMW * NR;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+        const int r = nb * 16 + col;
+#pragma unroll
+        for (int db = 0; db < G::DB; ++db)
+            *reinterpret_cast<f32x4_t*>(sm_acc + (w * NR + r) * RS + 16 * db + 4 * grp) = acc[nb][db];
+        if (grp == 0) {
+            sm_m[w * NR + r] = m[nb];
+            sm_l[w * NR + r] = l[nb];
+            sm_x[w * NR + r] = mx[nb];
+        }
+    }
+    __syncthreads();
+
+    for (int idx = tid; idx < nrows * D; idx += kMT) {
+        const int r = idx / D;
+        const int d = idx - r * D;
+        float M = -INFINITY, X = -INFINITY;
+#pragma unroll
+        for (int x = 0; x < kMW; ++x) {
+            M = fmaxf(M, sm_m[x * NR + r]);
+            X = fmaxf(X, sm_x[x * NR + r]);
+        }
+        float num = 0.f, den = 0.f;
+        if (M != -INFINITY) {
+#pragma unroll
+            for (int x = 0; x < kMW; ++x) {
+                const float mw = sm_m[x * NR + r];
+                const float f = mw == -INFINITY ? 0.f : fast_exp2(mw - M);
+                num = fmaf(f, sm_acc[(x * NR + r) * RS + d], num);
+                den = fmaf(f, sm_l[x * NR + r], den);
+            }
+        }
+        const bool empty = M == -INFINITY;
+        const float o = empty ? 0.f : num / den;
+        const float lse_v = empty ? -INFINITY : (M + log2f(den)) * kLn2;
+        const int64_t row = row0 + r;
+        if (a.direct) {
+            reinterpret_cast<uint16_t*>(a.out)[row * D + d] = f32_to_bf16(o);
+            if (d == 0 && a.lse) a.lse[row] = lse_v;
+        } else {
+            if (!empty) a.o_part[(row * slots + s) * D + d] = o;
+            if (d == 0) {
+                a.m_part[row * slots + s] = empty ? -INFINITY : X * kLn2;
+                a.lse_part[row * slots + s] = lse_v;
+            }
+        }
+    }
+}
+
+template <int D, int NB>
+void launch_nb(int batch, const PartialArgs& a, hipStream_t stream) {
+    dim3 grid(a.rule.slots, a.Hkv, batch), block(kMT);
+    if (a.q_len > 1)
+        hipLaunchKernelGGL((fd_mfma_partial_kernel<D, NB, true>), grid, block, 0, stream, a);
+    else
+        hipLaunchKernelGGL((fd_mfma_partial_kernel<D, NB, false>), grid, block, 0, stream, a);
+}
+
+}  // namespace
+
+bool mfma_partials_supported(int dtype, int head_dim, int rows) {
+    return dtype == 1 && (head_dim == 64 || head_dim == 128) && rows >= 1 && rows <= 32;
+}
+
+hipError_t launch_partials_mfma(int head_dim, int batch, const PartialArgs& a, hipStream_t stream) {
+    const bool two = a.rows > 16;
+    if (head_dim == 64) {
+        if (two) launch_nb<64, 2>(batch, a, stream);
+        else launch_nb<64, 1>(batch, a, stream);
+    } else {
+        if (two) launch_nb<128, 2>(batch, a, stream);
+        else launch_nb<128, 1>(batch, a, stream);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace fdk

@@ -157,7 +157,8 @@ fd_status fd_combine_splits(int32_t batch, int32_t num_heads, int32_t q_len, int
  * workspace is needed (`workspace` may be NULL).  Otherwise `workspace`
  * (device memory, 256-byte aligned, caller-owned, contents irrelevant on
  * entry and clobbered on return) must hold at least
- * fd_workspace_bytes(dims, slots) bytes, else FD_ERR_WORKSPACE. */
+ * fd_workspace_bytes(dims, slots) bytes, else FD_ERR_WORKSPACE.  Calls that
+ * share a workspace must not run concurrently. */
 fd_status fd_decode_attention(const fd_dims* dims, const void* q, const void* k_cache,
                               const void* v_cache, const int32_t* cache_lens, float scale,
                               int32_t num_splits, const fd_plan* plan, void* workspace,

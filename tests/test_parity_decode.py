@@ -223,3 +223,57 @@ def test_combine_matches_oracle_merge():
                                 out_dtype=out_dtype)
             torch.cuda.synchronize()
             compare(f"combine D={D} S={S} {out_dtype}", go, gl, ro, rl, tol)
+
+
+# ---------------------------------------------------------------------------
+# Workspace reuse and graph replays
+
+
+def test_workspace_reuse_with_garbage_and_changing_shapes():
+    say("[case] one garbage-filled workspace reused across shapes and split counts")
+    ws = torch.full((64 << 20,), 0xFF, dtype=torch.uint8, device="cuda")
+    cases = [
+        (2, 32, 8, 128, 1, 3000, "bf16", [3000, 1234], 7),
+        (1, 32, 8, 128, 1, 5000, "bf16", [5000], 40),
+        (4, 16, 2, 64, 1, 900, "bf16", [900, 1, 0, 450], 5),
+        (2, 8, 2, 128, 1, 700, "f32", [700, 333], 6),
+        (2, 32, 8, 128, 1, 3000, "bf16", [3000, 1234], 9),
+    ]
+    for i, (B, Hq, Hkv, D, T, Lmax, dt, lens, S) in enumerate(cases):
+        q, k, v, cl = inputs(B, Hq, Hkv, D, T, Lmax, dt, 1200 + i, lens)
+        sc = _scale(D)
+        ref = run_oracle(q, k, v, cl, sc)
+        for rep in range(2):
+            out, lse = fd.decode_attention(q.cuda(), k.cuda(), v.cuda(), cl.cuda(), scale=sc,
+                                           num_splits=S, workspace=ws)
+            torch.cuda.synchronize()
+            compare(f"reuse case {i} rep {rep}", out, lse, *ref, TOL[dt])
+
+
+def test_graph_replays_match_eager():
+    say("[case] graph replays of the split-KV step")
+    q, k, v, cl = inputs(1, 32, 8, 128, 1, 8192, "bf16", 1300, [8192])
+    sc = _scale(128)
+    qd, kd, vd, cld = q.cuda(), k.cuda(), v.cuda(), cl.cuda()
+    plan = fd.plan_for(q, k, cl)
+    out = torch.empty_like(qd)
+    lse = torch.empty(qd.shape[:3], dtype=torch.float32, device="cuda")
+    ws = fd.new_workspace(fd.workspace_bytes(fd.dims_of(qd, kd), plan.max_splits), "cuda")
+    fd.decode_attention(qd, kd, vd, cld, scale=sc, plan=plan, out=out, lse=lse, workspace=ws)
+    torch.cuda.synchronize()
+    eager_out, eager_lse = out.clone(), lse.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fd.decode_attention(qd, kd, vd, cld, scale=sc, plan=plan, out=out, lse=lse, workspace=ws)
+    for rep in range(4):
+        out.zero_()
+        lse.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager_out.view(torch.int16)), f"replay {rep}: out differs"
+        assert torch.equal(lse, eager_lse), f"replay {rep}: lse differs"
+        # eager work on the same workspace between replays
+        fd.decode_attention(qd, kd, vd, cld, scale=sc, num_splits=5, workspace=ws)
+        torch.cuda.synchronize()
+    compare("graph replay", out, lse, *run_oracle(q, k, v, cl, sc), TOL["bf16"])
