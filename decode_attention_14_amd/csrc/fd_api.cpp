@@ -220,11 +220,15 @@ fd_status fd_plan_splits(const fd_dims* dims, const int32_t* cache_lens_host, in
                 return fail(FD_ERR_DEVICE, "cannot query the compute-unit count; pass num_cus");
             num_cus = prop.multiProcessorCount;
         }
-        // Spread the batch's key rows over kUnitsPerCU units per CU.
+        // Spread the batch's key rows over kUnitsPerCU units per CU.  Row
+        // tiles of a long chunk (more than 32 rows per workgroup) are dense
+        // matrix work whose partials cost as much to write and merge as the
+        // K/V they read, so their tiles are not capped at kMaxTile.
         const int64_t key_rows = sum_len * lanes;
         int64_t T = ceil_div(std::max<int64_t>(key_rows, 1), (int64_t)num_cus * kUnitsPerCU);
         T = align_up(T, kTileGranule);
-        T = std::min<int64_t>(std::max<int64_t>(T, kMinTile), kMaxTile);
+        T = std::max<int64_t>(T, kMinTile);
+        if (fdk::partial_block_rows(dims->dtype, dims->head_dim, rows) <= 32) T = std::min<int64_t>(T, kMaxTile);
         if (ceil_div(max_len, T) > FD_MAX_SPLITS) T = align_up(ceil_div(max_len, FD_MAX_SPLITS), kTileGranule);
         int64_t smax = 1, units = 0;
         for (int b = 0; b < dims->batch; ++b) {

@@ -476,7 +476,7 @@ hipError_t launch_partials_d(int batch, const PartialArgs& a, hipStream_t stream
 }  // namespace
 
 int partial_block_rows(int dtype, int head_dim, int rows) {
-    return mfma_partials_supported(dtype, head_dim, rows) ? rows : vector_block_rows(rows);
+    return mfma_partials_supported(dtype, head_dim, rows) ? mfma_block_rows(rows) : vector_block_rows(rows);
 }
 
 hipError_t launch_partials(int dtype, int head_dim, int batch, const PartialArgs& a,

@@ -40,13 +40,15 @@ struct PartialArgs {
 // ceil(rows / partial_block_rows) row blocks per (sequence, KV head, tile).
 int partial_block_rows(int dtype, int head_dim, int rows);
 
-// The partial pass: picks the matrix-core kernel (bf16, up to 32 rows) or the
-// vector kernel (fp32, or more rows) and launches it on `stream`.
+// The partial pass: picks a matrix-core kernel (bf16) or the vector kernel
+// (fp32) and launches it on `stream`.
 hipError_t launch_partials(int dtype, int head_dim, int batch, const PartialArgs& a,
                            hipStream_t stream);
 
-// Matrix-core partial kernel (fd_mfma.hip) and its applicability.
+// Matrix-core partial kernels (fd_mfma.hip): their applicability and the
+// rows of a workgroup (all of a group of up to 32 rows; else a chunk tile).
 bool mfma_partials_supported(int dtype, int head_dim, int rows);
+int mfma_block_rows(int rows);
 hipError_t launch_partials_mfma(int head_dim, int batch, const PartialArgs& a, hipStream_t stream);
 
 hipError_t launch_combine(int head_dim, int out_dtype, int64_t rows, int slots,

@@ -145,6 +145,82 @@ __device__ __forceinline__ void load_block(const char* kp, const char* vp, int l
     }
 }
 
+// The math of one 16-key block for NB blocks of 16 query rows, given the
+// block's K fragments (A operand of S^T = K Q^T) and transposed V fragments
+// (A operand of O^T = V^T P^T) in registers.  Lane (group grp, column q)
+// holds, per row block nb: the running reference max m (equal in the four
+// groups), its share l of the running sum, the exact running max mx of its
+// own scores, and acc[nb][db] = O^T rows 16 db + 4 grp .. +3 of column q.
+// Keys at or past rend[nb] are masked when `edge` (the block reaches a row's
+// end); c = scale * log2(e).
+template <int D, int NB>
+__device__ __forceinline__ void block_math(const bf16x8_t (&kf)[Geo<D>::KS], const bf16x4_t (&vf)[Geo<D>::DB],
+                                           const bf16x8_t (&qf)[NB][Geo<D>::KS], f32x4_t (&acc)[NB][Geo<D>::DB],
+                                           float (&m)[NB], float (&l)[NB], float (&mx)[NB], int key0, bool edge,
+                                           const int (&rend)[NB], float c, int grp) {
+    using G = Geo<D>;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+        f32x4_t st = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < G::KS; ++ks)
+            st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks], qf[nb][ks], st, 0, 0, 0);
+        float x[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[i] = st[i] * c;
+        if (edge) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (key0 + 4 * grp + i >= rend[nb]) x[i] = -INFINITY;
+        }
+        const float bm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+        mx[nb] = fmaxf(mx[nb], bm);
+        if (__any(bm > m[nb] + kTau)) {
+            float bw = fmaxf(bm, __shfl_xor(bm, 16));
+            bw = fmaxf(bw, __shfl_xor(bw, 32));
+            const float mn = fmaxf(m[nb], bw);
+            const float alpha = m[nb] == -INFINITY ? 0.f : fast_exp2(m[nb] - mn);
+            l[nb] *= alpha;
+#pragma unroll
+            for (int db = 0; db < G::DB; ++db) acc[nb][db] *= alpha;
+            m[nb] = mn;
+        }
+        const float mref = m[nb] == -INFINITY ? 0.f : m[nb];
+        float p[4];
+        bf16x4_t ph, pl;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            p[i] = fast_exp2(x[i] - mref);
+            ph[i] = (__bf16)p[i];
+            pl[i] = (__bf16)(p[i] - (float)ph[i]);
+        }
+        l[nb] += (p[0] + p[1]) + (p[2] + p[3]);
+#pragma unroll
+        for (int db = 0; db < G::DB; ++db) {
+            acc[nb][db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+                __builtin_bit_cast(s16x4_t, vf[db]), __builtin_bit_cast(s16x4_t, ph), acc[nb][db], 0, 0, 0);
+            acc[nb][db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+                __builtin_bit_cast(s16x4_t, vf[db]), __builtin_bit_cast(s16x4_t, pl), acc[nb][db], 0, 0, 0);
+        }
+    }
+}
+
+// Operand fragments of one 16-key block stored (swizzled) at kb / vb in LDS:
+// K rows as the A operand of the score product, V^T through transposed reads.
+template <int D>
+__device__ __forceinline__ void load_fragments(const char* kb, const char* vb, bf16x8_t (&kf)[Geo<D>::KS],
+                                               bf16x4_t (&vf)[Geo<D>::DB], int grp, int col) {
+    using G = Geo<D>;
+#pragma unroll
+    for (int ks = 0; ks < G::KS; ++ks)
+        kf[ks] = *reinterpret_cast<const bf16x8_t*>(kb + swz<D>(col, grp + 4 * ks));
+    const int r = 4 * grp + (col >> 2);
+    const int q4 = col & 3;
+#pragma unroll
+    for (int db = 0; db < G::DB; ++db) vf[db] = tr_read(vb + swz<D>(r, 2 * db + (q4 >> 1)) + 8 * (q4 & 1));
+    lds_settle(vf);
+}
+
 template <int D, int NB, bool CAUSAL>
 __global__ __launch_bounds__(kMT) void fd_mfma_partial_kernel(PartialArgs a) {
     using G = Geo<D>;
@@ -268,65 +344,11 @@ __global__ __launch_bounds__(kMT) void fd_mfma_partial_kernel(PartialArgs a) {
         const char* vb = kb + G::BLKB;
 
         bf16x8_t kf[G::KS];
-#pragma unroll
-        for (int ks = 0; ks < G::KS; ++ks)
-            kf[ks] = *reinterpret_cast<const bf16x8_t*>(kb + swz<D>(col, grp + 4 * ks));
         bf16x4_t vf[G::DB];
-        {
-            const int r = 4 * grp + (col >> 2);
-            const int q4 = col & 3;
-#pragma unroll
-            for (int db = 0; db < G::DB; ++db)
-                vf[db] = tr_read(vb + swz<D>(r, 2 * db + (q4 >> 1)) + 8 * (q4 & 1));
-        }
-        lds_settle(vf);
+        load_fragments<D>(kb, vb, kf, vf, grp, col);
 
         const int key0 = lo + (w + j * kMW) * kKB;  // first key of the block
-        const bool edge = key0 + kKB > mask_from;
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-            f32x4_t st = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < G::KS; ++ks)
-                st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks], qf[nb][ks], st, 0, 0, 0);
-            float x[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) x[i] = st[i] * c;
-            if (edge) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    if (key0 + 4 * grp + i >= rend[nb]) x[i] = -INFINITY;
-            }
-            const float bm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-            mx[nb] = fmaxf(mx[nb], bm);
-            if (__any(bm > m[nb] + kTau)) {
-                float bw = fmaxf(bm, __shfl_xor(bm, 16));
-                bw = fmaxf(bw, __shfl_xor(bw, 32));
-                const float mn = fmaxf(m[nb], bw);
-                const float alpha = m[nb] == -INFINITY ? 0.f : fast_exp2(m[nb] - mn);
-                l[nb] *= alpha;
-#pragma unroll
-                for (int db = 0; db < G::DB; ++db) acc[nb][db] *= alpha;
-                m[nb] = mn;
-            }
-            const float mref = m[nb] == -INFINITY ? 0.f : m[nb];
-            float p[4];
-            bf16x4_t ph, pl;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                p[i] = fast_exp2(x[i] - mref);
-                ph[i] = (__bf16)p[i];
-                pl[i] = (__bf16)(p[i] - (float)ph[i]);
-            }
-            l[nb] += (p[0] + p[1]) + (p[2] + p[3]);
-#pragma unroll
-            for (int db = 0; db < G::DB; ++db) {
-                acc[nb][db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
-                    __builtin_bit_cast(s16x4_t, vf[db]), __builtin_bit_cast(s16x4_t, ph), acc[nb][db], 0, 0, 0);
-                acc[nb][db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
-                    __builtin_bit_cast(s16x4_t, vf[db]), __builtin_bit_cast(s16x4_t, pl), acc[nb][db], 0, 0, 0);
-            }
-        }
+        block_math<D, NB>(kf, vf, qf, acc, m, l, mx, key0, key0 + kKB > mask_from, rend, c, grp);
     }
 
     // Merge: the four lane groups of a column, then the four waves via LDS.
@@ -393,6 +415,228 @@ __global__ __launch_bounds__(kMT) void fd_mfma_partial_kernel(PartialArgs a) {
     }
 }
 
+
+// ---------------------------------------------------------------------------
+// Chunked prefill: row groups of more than 32 query rows (page
+// "ChunkedPrefill与FlashDecoding技术解析" §2.1: a chunk of q_len new tokens,
+// causal inside the chunk, full view of the cached prefix).  Here the work is
+// a dense contraction, so the four waves split the rows instead of the keys:
+// a workgroup takes kChunkRows packed rows (row p = t * n_rep + i is position
+// t of query head i of the GQA group, so a tile's rows span few positions and
+// share one causal limit), and all its waves consume every key through one
+// LDS ring of FD_CHUNK_STAGES stages of 16 * FD_CHUNK_BLOCKS keys, loaded
+// cooperatively.  Keys that no row of the tile can see are never loaded.
+// Each wave owns its rows to the end, so no cross-wave merge is needed.
+
+#ifndef FD_CHUNK_STAGES
+#define FD_CHUNK_STAGES 3
+#endif
+#ifndef FD_CHUNK_BLOCKS
+#define FD_CHUNK_BLOCKS 4
+#endif
+constexpr int kCNS = FD_CHUNK_STAGES;
+constexpr int kCKB = FD_CHUNK_BLOCKS;
+constexpr int kChunkNB = 2;                        // 16-row blocks per wave
+constexpr int kChunkRows = kMW * 16 * kChunkNB;    // rows per workgroup
+
+// Start this wave's share of the loads of one stage: the tile's bytes
+// [off, off + stage) of K and of V, `left` bytes of the tile remaining from
+// off (none if left <= 0; rows past it read as zeros), into the stage buffer
+// at dst (K blocks first, then V blocks).
+template <int D, int DPW>
+__device__ __forceinline__ void load_stage(const char* kt, const char* vt, int left, int off, char* dst,
+                                           const uint32_t* dma_off, const int* lds_off) {
+    const uint32_t n = left > 0 ? (uint32_t)left : 0u;
+    const __amdgpu_buffer_rsrc_t rk = tile_rsrc(kt + off, n);
+    const __amdgpu_buffer_rsrc_t rv = tile_rsrc(vt + off, n);
+#pragma unroll
+    for (int k = 0; k < DPW; ++k) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t*)(dst + lds_off[k]), 16, dma_off[k], 0, 0,
+                                                 FD_LOAD_AUX);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)(dst + kCKB * Geo<D>::BLKB + lds_off[k]), 16,
+                                                 dma_off[k], 0, 0, FD_LOAD_AUX);
+    }
+}
+
+template <int D, int NB>
+__global__ __launch_bounds__(kMT) void fd_mfma_chunk_kernel(PartialArgs a) {
+    using G = Geo<D>;
+    constexpr int BM = kMW * 16 * NB;
+    constexpr int STG = kCKB * G::STAGEB;  // bytes per stage: kCKB K blocks, then kCKB V blocks
+    constexpr int NDMA = kCKB * G::IPB;    // 1 KiB load instructions per tensor per stage
+    static_assert(NDMA % kMW == 0, "stage loads split evenly over the waves");
+    constexpr int DPW = NDMA / kMW;        // per wave, per tensor
+    __shared__ __attribute__((aligned(16))) char smem[kCNS * STG];
+
+    const int s = blockIdx.x;
+    const int g = blockIdx.y / a.row_blocks;
+    const int rt = blockIdx.y - g * a.row_blocks;
+    const int b = blockIdx.z;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = (int)uniform((uint32_t)(tid >> 6));
+    const int grp = lane >> 4;
+    const int col = lane & 15;
+
+    int L = a.cache_lens[b];
+    L = L < 0 ? 0 : (L > a.Lmax ? a.Lmax : L);
+    int lo, hi, S;
+    tile_of(a.rule, L, s, lo, hi, S);
+    lo = (int)uniform((uint32_t)lo);
+    hi = (int)uniform((uint32_t)hi);
+
+    const int R = a.rows;
+    const int n_rep = a.n_rep;
+    const int q_len = a.q_len;
+    const int p0 = rt * BM;
+    const int64_t rowbase = ((int64_t)b * a.Hq + (int64_t)g * n_rep) * q_len;
+    const int slots = a.rule.slots;
+    const int nrows = min(BM, R - p0);
+
+    if (s >= S) {
+        for (int idx = tid; idx < nrows; idx += kMT) {
+            const int p = p0 + idx;
+            const int64_t row = rowbase + (int64_t)(p % n_rep) * q_len + p / n_rep;
+            if (a.direct) {
+                uint4* o = reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(a.out) + row * D);
+                for (int k = 0; k < D / 8; ++k) o[k] = make_uint4(0, 0, 0, 0);
+                if (a.lse) a.lse[row] = -INFINITY;
+            } else {
+                a.m_part[row * slots + s] = -INFINITY;
+                a.lse_part[row * slots + s] = -INFINITY;
+            }
+        }
+        return;
+    }
+
+    // Keys the tile's rows can see inside [lo, hi): the last row's limit
+    // bounds them all, the first row's limit is where masking starts.
+    const int t_first = p0 / n_rep;
+    const int t_last = (p0 + nrows - 1) / n_rep;
+    const int kend = max(lo, min(hi, L - q_len + t_last + 1));
+    const int mask_from = max(lo, min(hi, L - q_len + t_first + 1));
+
+    int rend[NB];
+    int64_t mrow[NB];
+    bool valid[NB];
+    bf16x8_t qf[NB][G::KS];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+        const int p = p0 + w * 16 * NB + nb * 16 + col;
+        valid[nb] = p < R;
+        const int t = p / n_rep;
+        mrow[nb] = rowbase + (int64_t)(p % n_rep) * q_len + t;
+        rend[nb] = valid[nb] ? max(lo, min(hi, L - q_len + t + 1)) : lo;
+#pragma unroll
+        for (int ks = 0; ks < G::KS; ++ks) {
+            if (valid[nb]) {
+                const uint4 x = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q) + mrow[nb] * D +
+                                                                8 * grp + 32 * ks);
+                qf[nb][ks] = __builtin_bit_cast(bf16x8_t, x);
+            } else {
+                qf[nb][ks] = __builtin_bit_cast(bf16x8_t, make_uint4(0, 0, 0, 0));
+            }
+        }
+    }
+    const float c = a.qk_scale;
+
+    f32x4_t acc[NB][G::DB];
+    float m[NB], l[NB], mx[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+        m[nb] = -INFINITY;
+        l[nb] = 0.f;
+        mx[nb] = -INFINITY;
+#pragma unroll
+        for (int db = 0; db < G::DB; ++db) acc[nb][db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+
+    const int64_t tile_row = ((int64_t)b * a.Hkv + g) * a.Lmax + lo;
+    const char* kt = static_cast<const char*>(a.k) + tile_row * G::ROWB;
+    const char* vt = static_cast<const char*>(a.v) + tile_row * G::ROWB;
+    const int tile_bytes = (kend - lo) * G::ROWB;
+    constexpr int SKEYS = kKB * kCKB;  // keys per stage
+    const int nst = (kend - lo + SKEYS - 1) / SKEYS;
+
+    // This wave's load instructions of a stage: instruction n = w + 4k covers
+    // rows (n % IPB) * RPI .. of block n / IPB.
+    uint32_t dma_off[DPW];
+    int lds_off[DPW];
+#pragma unroll
+    for (int k = 0; k < DPW; ++k) {
+        const int n = w + k * kMW;
+        const int bb = n / G::IPB;
+        const int i = n - bb * G::IPB;
+        const int r = i * G::RPI + lane / G::CH;
+        const int cg = (lane % G::CH) ^ (r & (G::CH - 1));
+        dma_off[k] = (uint32_t)((bb * kKB + r) * G::ROWB + cg * 16);
+        lds_off[k] = bb * G::BLKB + i * 1024;
+    }
+#pragma unroll
+    for (int j = 0; j < kCNS - 1; ++j)
+        load_stage<D, DPW>(kt, vt, tile_bytes - j * SKEYS * G::ROWB, j * SKEYS * G::ROWB, smem + j * STG, dma_off,
+                           lds_off);
+    for (int j = 0; j < nst; ++j) {
+        wait_vmcnt_le<(kCNS - 1) * 2 * DPW>();  // this wave's loads of stage j
+        __syncthreads();                        // everyone's, and stage j - 1 is free
+        {
+            const int jn = j + kCNS - 1;
+            load_stage<D, DPW>(kt, vt, tile_bytes - jn * SKEYS * G::ROWB, jn * SKEYS * G::ROWB,
+                               smem + (jn % kCNS) * STG, dma_off, lds_off);
+        }
+        const char* sk = smem + (j % kCNS) * STG;
+        const char* sv = sk + kCKB * G::BLKB;
+#pragma unroll
+        for (int bb = 0; bb < kCKB; ++bb) {
+            const int key0 = lo + j * SKEYS + bb * kKB;
+            if (key0 >= kend) break;
+            bf16x8_t kf[G::KS];
+            bf16x4_t vf[G::DB];
+            load_fragments<D>(sk + bb * G::BLKB, sv + bb * G::BLKB, kf, vf, grp, col);
+            block_math<D, NB>(kf, vf, qf, acc, m, l, mx, key0, key0 + kKB > mask_from, rend, c, grp);
+        }
+    }
+    wait_vmcnt_le<0>();
+
+    // Each wave writes its own rows.
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+        l[nb] += __shfl_xor(l[nb], 16);
+        l[nb] += __shfl_xor(l[nb], 32);
+        mx[nb] = fmaxf(mx[nb], __shfl_xor(mx[nb], 16));
+        mx[nb] = fmaxf(mx[nb], __shfl_xor(mx[nb], 32));
+        if (!valid[nb]) continue;
+        const bool empty = m[nb] == -INFINITY;
+        const float inv = empty ? 0.f : 1.f / l[nb];
+        const float lse_v = empty ? -INFINITY : (m[nb] + log2f(l[nb])) * kLn2;
+        const int64_t row = mrow[nb];
+        if (a.direct) {
+            uint16_t* o = reinterpret_cast<uint16_t*>(a.out) + row * D;
+#pragma unroll
+            for (int db = 0; db < G::DB; ++db) {
+                uint2 packed;
+                packed.x = (uint32_t)f32_to_bf16(acc[nb][db][0] * inv) |
+                           ((uint32_t)f32_to_bf16(acc[nb][db][1] * inv) << 16);
+                packed.y = (uint32_t)f32_to_bf16(acc[nb][db][2] * inv) |
+                           ((uint32_t)f32_to_bf16(acc[nb][db][3] * inv) << 16);
+                *reinterpret_cast<uint2*>(o + 16 * db + 4 * grp) = packed;
+            }
+            if (grp == 0 && a.lse) a.lse[row] = lse_v;
+        } else {
+            if (!empty) {
+                float* o = a.o_part + (row * slots + s) * D;
+#pragma unroll
+                for (int db = 0; db < G::DB; ++db)
+                    *reinterpret_cast<f32x4_t*>(o + 16 * db + 4 * grp) = acc[nb][db] * inv;
+            }
+            if (grp == 0) {
+                a.m_part[row * slots + s] = empty ? -INFINITY : mx[nb] * kLn2;
+                a.lse_part[row * slots + s] = lse_v;
+            }
+        }
+    }
+}
+
 template <int D, int NB>
 void launch_nb(int batch, const PartialArgs& a, hipStream_t stream) {
     dim3 grid(a.rule.slots, a.Hkv, batch), block(kMT);
@@ -405,10 +649,20 @@ void launch_nb(int batch, const PartialArgs& a, hipStream_t stream) {
 }  // namespace
 
 bool mfma_partials_supported(int dtype, int head_dim, int rows) {
-    return dtype == 1 && (head_dim == 64 || head_dim == 128) && rows >= 1 && rows <= 32;
+    return dtype == 1 && (head_dim == 64 || head_dim == 128) && rows >= 1;
 }
 
+int mfma_block_rows(int rows) { return rows <= 32 ? rows : kChunkRows; }
+
 hipError_t launch_partials_mfma(int head_dim, int batch, const PartialArgs& a, hipStream_t stream) {
+    if (a.rows > 32) {
+        dim3 grid(a.rule.slots, a.Hkv * a.row_blocks, batch), block(kMT);
+        if (head_dim == 64)
+            hipLaunchKernelGGL((fd_mfma_chunk_kernel<64, kChunkNB>), grid, block, 0, stream, a);
+        else
+            hipLaunchKernelGGL((fd_mfma_chunk_kernel<128, kChunkNB>), grid, block, 0, stream, a);
+        return hipGetLastError();
+    }
     const bool two = a.rows > 16;
     if (head_dim == 64) {
         if (two) launch_nb<64, 2>(batch, a, stream);

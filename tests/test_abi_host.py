@@ -75,7 +75,11 @@ def test_planner_on_workloads(name):
         assert p.tile_len == 0 and p.max_splits == w.num_splits
     else:
         assert p.tile_len % 64 == 0
-        assert 256 <= p.tile_len <= 1024 or max(lens) > 1024 * 256
+        if w.q_len == 1:
+            assert 256 <= p.tile_len <= 1024 or max(lens) > 1024 * 256
+        else:
+            # a long chunk's row tiles: one unit per CU, tiles not capped
+            assert p.tile_len >= 256 and p.plan.work_units <= 256 + 8 * 16
     for L, S in zip(lens, p.splits_per_seq):
         t = tiles_of(L, p.tile_len, w.num_splits, p.max_splits)
         assert len(t) == S

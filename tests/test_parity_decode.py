@@ -85,14 +85,18 @@ def test_workload_gqa_128k_b4_sampled():
     assert torch.isfinite(lse).all()
 
 
-def test_workload_prefill_chunk_sampled():
+def test_workload_prefill_chunk_full_oracle():
     w = WORKLOADS["prefill_chunk_512"]
-    say(f"[case] workload {w.name} (sampled heads, whole chunk, against the oracle)")
+    say(f"[case] workload {w.name} (planner splits, every row against the oracle)")
     q, k, v, cl = workload_inputs(w)
     plan = fd.plan_for(q, k, cl)
     say(f"  plan {plan.plan}")
+    ref_out, ref_lse = run_oracle(q, k, v, cl, w.scale)
     out, lse = run_gpu(q, k, v, cl, w.scale, plan=plan)
-    _sampled_rows(w, q, k, v, cl, out, lse, [(0, 0), (0, 13), (0, 31)])
+    err, lerr = compare(w.name, out, lse, ref_out, ref_lse, TOL[w.dtype])
+    say(f"  max abs err out {err:.2e} lse {lerr:.2e}")
+    out1, lse1 = run_gpu(q, k, v, cl, w.scale)
+    compare(w.name + " one split", out1, lse1, ref_out, ref_lse, TOL[w.dtype])
 
 
 # ---------------------------------------------------------------------------
@@ -139,6 +143,20 @@ def test_chunk_lengths(dt):
     check_case("q_len > L", 1, 4, 1, 64, 6, 16, dt, 590, [4], num_splits=2)
 
 
+@pytest.mark.parametrize("D", [128, 64])
+def test_long_chunks(D):
+    """Row groups of more than 32 rows: the chunk tiles of the matrix-core path."""
+    for T, Hq, Hkv, lens in [(33, 1, 1, [40, 33]), (100, 4, 1, [900, 100]), (128, 8, 2, [128, 700]),
+                             (200, 4, 2, [1500, 150]), (37, 8, 1, [37, 1000]), (64, 16, 2, [64, 64])]:
+        for S in (1, 3):
+            check_case(f"chunk q_len={T} Hq={Hq} Hkv={Hkv} D={D} S={S}", len(lens), Hq, Hkv, D, T,
+                       max(lens), "bf16", 1400 + T + S, lens, num_splits=S)
+    check_case(f"chunk planned D={D}", 2, 8, 2, D, 96, 2000, "bf16", 1490, [2000, 96], use_plan=True)
+    check_case(f"chunk q x10 D={D}", 1, 4, 1, D, 80, 900, "bf16", 1491, [900], q_mul=10.0, num_splits=2)
+    check_case(f"chunk poison D={D}", 2, 4, 2, D, 48, 400, "bf16", 1492, [300, 60], num_splits=2,
+               poison=True)
+
+
 def test_poisoned_padding():
     for dt in ("bf16", "f32"):
         check_case(f"poison {dt}", 3, 8, 2, 128, 1, 520, dt, 600, [5, 257, 300], num_splits=4,
@@ -183,7 +201,7 @@ def test_split_count_invariance_on_gpu():
 # The two passes separately
 
 
-@pytest.mark.parametrize("dt,T", [("bf16", 1), ("f32", 1), ("bf16", 3)])
+@pytest.mark.parametrize("dt,T", [("bf16", 1), ("f32", 1), ("bf16", 3), ("bf16", 40)])
 def test_partials_match_oracle_tiles(dt, T):
     say(f"[case] partials {dt} q_len={T}")
     lens = [1000, 77, 0]
