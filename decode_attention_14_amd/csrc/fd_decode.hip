@@ -15,8 +15,9 @@
 //                      the key row and finished with DPP row reductions.
 //                      Output: per-tile (o_s, m_s, lse_s), or out/lse
 //                      directly when there is a single tile.
-//   fd_combine_kernel  one workgroup per query row.  It merges the row's
-//                      tiles: LSE = ln sum_s exp(lse_s), out = sum_s
+//   fd_combine_kernel  one wave per query row (four per row when a row has
+//                      many tiles).  It merges the row's tiles:
+//                      LSE = ln sum_s exp(lse_s), out = sum_s
 //                      exp(lse_s - LSE) o_s.
 //
 // Decode is matrix-vector work (about 4 flop per byte of K/V at a GQA ratio
@@ -406,41 +407,60 @@ __global__ __launch_bounds__(kPThreads) FD_OCCUPANCY void fd_partial_kernel(Part
 }
 
 // ---------------------------------------------------------------------------
-// Merge pass: one workgroup of kCThreads per query row.  Wave w accumulates
-// the slots w, w + kCWaves, ... (merge_slots_wave), then wave 0 merges the
-// wave states through LDS and writes the row.
+// Merge pass.  WPR waves per query row: with few slots one wave per row (four
+// rows per workgroup); with many, four waves split the row's slots (wave w
+// takes slots w, w + 4, ...) and wave 0 merges their states through LDS.
 
 constexpr int kCThreads = 256;
 constexpr int kCWaves = kCThreads / 64;
+constexpr int kCombineWideSlots = 32;  // above this, four waves per row
 
-template <int D, bool OUT_BF16>
+template <int D, bool OUT_BF16, int WPR>
 __global__ __launch_bounds__(kCThreads) void fd_combine_kernel(const float* __restrict__ o_part,
                                                                const float* __restrict__ lse_part, int slots,
-                                                               void* out, float* lse) {
+                                                               int64_t rows, void* out, float* lse) {
     constexpr int C4 = D / 4;
-    __shared__ float sm_m[kCWaves], sm_z[kCWaves];
-    __shared__ float4 sm_acc[kCWaves][C4];
-    const int64_t row = blockIdx.x;
+    constexpr int RPB = kCWaves / WPR;  // rows per workgroup
     const int w = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
-    const MergeState st = merge_slots_wave<D>(o_part + row * slots * D, lse_part + row * slots, slots, w,
-                                              kCWaves, lane);
-    if (lane < C4) {
-        sm_acc[w][lane] = st.acc;
-        if (lane == 0) {
-            sm_m[w] = st.m;
-            sm_z[w] = st.z;
+    const int64_t row = (int64_t)blockIdx.x * RPB + w / WPR;
+    const int64_t r = row < rows ? row : rows - 1;  // spare waves read a valid row, write nothing
+    MergeState st = merge_slots_wave<D>(o_part + r * slots * D, lse_part + r * slots, slots, w % WPR, WPR, lane);
+    if constexpr (WPR > 1) {
+        __shared__ float sm_m[kCWaves], sm_z[kCWaves];
+        __shared__ float4 sm_acc[kCWaves][C4];
+        if (lane < C4) {
+            sm_acc[w][lane] = st.acc;
+            if (lane == 0) {
+                sm_m[w] = st.m;
+                sm_z[w] = st.z;
+            }
+        }
+        __syncthreads();
+        if (w != 0) return;
+        if (lane < C4) {
+            st = MergeState{sm_m[0], sm_z[0], sm_acc[0][lane]};
+#pragma unroll
+            for (int x = 1; x < WPR; ++x) merge_into(st, MergeState{sm_m[x], sm_z[x], sm_acc[x][lane]});
         }
     }
-    __syncthreads();
-    if (w == 0 && lane < C4) {
-        MergeState t{sm_m[0], sm_z[0], sm_acc[0][lane]};
-#pragma unroll
-        for (int x = 1; x < kCWaves; ++x) merge_into(t, MergeState{sm_m[x], sm_z[x], sm_acc[x][lane]});
+    if (row < rows && lane < C4) {
         void* orow = OUT_BF16 ? (void*)(reinterpret_cast<uint16_t*>(out) + row * D)
                               : (void*)(reinterpret_cast<float*>(out) + row * D);
-        write_merged<OUT_BF16>(t, orow, lane, lse ? lse + row : nullptr);
+        write_merged<OUT_BF16>(st, orow, lane, lse ? lse + row : nullptr);
     }
+}
+
+template <int D, bool OUT_BF16>
+void launch_combine_d(int64_t rows, int slots, const float* o_part, const float* lse_part, void* out, float* lse,
+                      hipStream_t stream) {
+    dim3 block(kCThreads);
+    if (slots > kCombineWideSlots)
+        hipLaunchKernelGGL((fd_combine_kernel<D, OUT_BF16, kCWaves>), dim3((unsigned)rows), block, 0, stream,
+                           o_part, lse_part, slots, rows, out, lse);
+    else
+        hipLaunchKernelGGL((fd_combine_kernel<D, OUT_BF16, 1>), dim3((unsigned)((rows + kCWaves - 1) / kCWaves)),
+                           block, 0, stream, o_part, lse_part, slots, rows, out, lse);
 }
 
 // Rows per workgroup of the vector kernel.
@@ -494,18 +514,13 @@ hipError_t launch_partials(int dtype, int head_dim, int batch, const PartialArgs
 hipError_t launch_combine(int head_dim, int out_dtype, int64_t rows, int slots,
                           const float* o_part, const float* lse_part, void* out, float* lse,
                           hipStream_t stream) {
-    dim3 grid((unsigned)rows), block(kCThreads);
     const bool bf16 = out_dtype == 1;
     if (head_dim == 64) {
-        if (bf16)
-            hipLaunchKernelGGL((fd_combine_kernel<64, true>), grid, block, 0, stream, o_part, lse_part, slots, out, lse);
-        else
-            hipLaunchKernelGGL((fd_combine_kernel<64, false>), grid, block, 0, stream, o_part, lse_part, slots, out, lse);
+        if (bf16) launch_combine_d<64, true>(rows, slots, o_part, lse_part, out, lse, stream);
+        else launch_combine_d<64, false>(rows, slots, o_part, lse_part, out, lse, stream);
     } else {
-        if (bf16)
-            hipLaunchKernelGGL((fd_combine_kernel<128, true>), grid, block, 0, stream, o_part, lse_part, slots, out, lse);
-        else
-            hipLaunchKernelGGL((fd_combine_kernel<128, false>), grid, block, 0, stream, o_part, lse_part, slots, out, lse);
+        if (bf16) launch_combine_d<128, true>(rows, slots, o_part, lse_part, out, lse, stream);
+        else launch_combine_d<128, false>(rows, slots, o_part, lse_part, out, lse, stream);
     }
     return hipGetLastError();
 }

@@ -53,7 +53,7 @@ namespace fdk {
 namespace {
 
 #ifndef FD_MFMA_STAGES
-#define FD_MFMA_STAGES 4
+#define FD_MFMA_STAGES 2
 #endif
 #ifndef FD_LOAD_AUX
 #define FD_LOAD_AUX 2
@@ -88,10 +88,25 @@ struct Geo {
     static_assert(CH == 8 || CH == 16, "D = 64 or 128");
 };
 
-// Byte offset inside a block of global chunk c of row r (XOR swizzle).
+// XOR swizzle of the 16-byte chunks of row r (CH chunks per row).  Two read
+// patterns must be free of LDS bank conflicts: 16 consecutive rows at one
+// chunk (K operands), and 4 aligned consecutive rows at an even/odd chunk
+// pair (transposed V reads).  For CH = 16 the map sends row bits (1:0) to
+// chunk bits (2:1), row bit 2 to bit 3 and row bit 3 to bit 0: a bijection on
+// 16 rows that keeps bit 0 fixed within an aligned group of 4.  For CH = 8,
+// two 128-byte rows share a bank cycle, so the same construction applies to
+// the row pair index r >> 1.
+template <int CH>
+__device__ __forceinline__ int swf(int r) {
+    if constexpr (CH == 16) return ((r & 3) << 1) | (((r >> 2) & 1) << 3) | ((r >> 3) & 1);
+    const int u = (r >> 1) & 7;
+    return ((u & 1) << 1) | (((u >> 1) & 1) << 2) | ((u >> 2) & 1);
+}
+
+// Byte offset inside a block of global chunk c of row r.
 template <int D>
 __device__ __forceinline__ int swz(int r, int c) {
-    return r * Geo<D>::ROWB + ((c ^ (r & (Geo<D>::CH - 1))) << 4);
+    return r * Geo<D>::ROWB + ((c ^ swf<Geo<D>::CH>(r)) << 4);
 }
 
 // s_waitcnt with only the vector-memory counter constrained: wait until at
@@ -322,7 +337,7 @@ __global__ __launch_bounds__(kMT) void fd_mfma_partial_kernel(PartialArgs a) {
 #pragma unroll
     for (int i = 0; i < G::IPB; ++i) {
         const int r = i * G::RPI + lane / G::CH;
-        const int cg = (lane % G::CH) ^ (r & (G::CH - 1));
+        const int cg = (lane % G::CH) ^ swf<G::CH>(r);
         dma_off[i] = (uint32_t)(r * G::ROWB + cg * 16);
     }
 
@@ -420,53 +435,98 @@ __global__ __launch_bounds__(kMT) void fd_mfma_partial_kernel(PartialArgs a) {
 // Chunked prefill: row groups of more than 32 query rows (page
 // "ChunkedPrefill与FlashDecoding技术解析" §2.1: a chunk of q_len new tokens,
 // causal inside the chunk, full view of the cached prefix).  Here the work is
-// a dense contraction, so the four waves split the rows instead of the keys:
-// a workgroup takes kChunkRows packed rows (row p = t * n_rep + i is position
-// t of query head i of the GQA group, so a tile's rows span few positions and
-// share one causal limit), and all its waves consume every key through one
-// LDS ring of FD_CHUNK_STAGES stages of 16 * FD_CHUNK_BLOCKS keys, loaded
-// cooperatively.  Keys that no row of the tile can see are never loaded.
-// Each wave owns its rows to the end, so no cross-wave merge is needed.
+// a dense contraction, run on the 32x32x16 matrix instructions (twice the
+// rate of the 16x16 shapes on gfx950).
+//
+// A workgroup takes kChunkRows packed rows; packed row p = t * n_rep + i is
+// position t of query head i of the GQA group, so a tile's rows span few
+// positions and share one causal limit.  Its eight waves form four row groups
+// of 32 rows times two key halves: in every 64-key stage, wave (rg, kh) takes
+// the 32-key block kh for the rows of group rg, and the two halves of a group
+// are merged through LDS at the end.  Two waves per SIMD hide each other's
+// LDS and softmax latency.  Stages stream through one LDS ring of
+// FD_CHUNK_STAGES stages, loaded cooperatively with buffer-to-LDS loads, one
+// barrier per stage.  Keys that no row of the tile can see are never loaded.
+//
+//   S^T = K Q^T  (32 keys x 32 rows, k = 16 dims per instruction)
+//   O^T = V^T P^T (32 dims x 32 rows, k = 16 keys per instruction): lane
+//                (half G, column q) holds the scores of keys 8a + 4G + b of
+//                the block (a, b = 0..3), which are exactly its B operand
+//                for the two 16-key steps, so P stays in place; V^T comes
+//                from transposed LDS reads.  P is split into a bf16 head and
+//                remainder as in the decode kernel while single keys still
+//                carry a visible share of a row's weight (see need_lo).
 
 #ifndef FD_CHUNK_STAGES
 #define FD_CHUNK_STAGES 3
 #endif
-#ifndef FD_CHUNK_BLOCKS
-#define FD_CHUNK_BLOCKS 4
-#endif
+constexpr int kCT = 512;                // threads per workgroup
+constexpr int kCW = kCT / 64;           // waves
+constexpr int kCRG = 4;                 // row groups of 32 rows
+constexpr int kCKW = kCW / kCRG;        // waves per row group: key halves
+constexpr int kChunkRows = 32 * kCRG;   // rows per workgroup
+constexpr int kCBK = 32;                // keys per block
 constexpr int kCNS = FD_CHUNK_STAGES;
-constexpr int kCKB = FD_CHUNK_BLOCKS;
-constexpr int kChunkNB = 2;                        // 16-row blocks per wave
-constexpr int kChunkRows = kMW * 16 * kChunkNB;    // rows per workgroup
 
-// Start this wave's share of the loads of one stage: the tile's bytes
-// [off, off + stage) of K and of V, `left` bytes of the tile remaining from
-// off (none if left <= 0; rows past it read as zeros), into the stage buffer
-// at dst (K blocks first, then V blocks).
-template <int D, int DPW>
-__device__ __forceinline__ void load_stage(const char* kt, const char* vt, int left, int off, char* dst,
-                                           const uint32_t* dma_off, const int* lds_off) {
+typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+
+template <int D>
+struct CGeo {
+    static constexpr int ROWB = 2 * D;
+    static constexpr int CH = ROWB / 16;            // 16-byte chunks per row
+    static constexpr int RPI = 64 / CH;             // rows per 1 KiB load instruction
+    static constexpr int IPB = kCBK / RPI;          // instructions per block per tensor
+    static constexpr int BLKB = kCBK * ROWB;        // bytes per block per tensor
+    static constexpr int SKB = kCKW;                // blocks per stage
+    static constexpr int SKEYS = SKB * kCBK;        // keys per stage
+    static constexpr int STGB = 2 * SKB * BLKB;     // K blocks, then V blocks
+    static constexpr int NDMA = SKB * IPB;          // instructions per tensor per stage
+    static constexpr int DPW = NDMA / kCW;          // per wave, per tensor
+    static constexpr int KS = D / 16;               // k-steps of S^T = K Q^T
+    static constexpr int DB = D / 32;               // 32-dim blocks of O^T
+    static_assert(NDMA % kCW == 0 && DPW >= 1, "stage loads split evenly over the waves");
+};
+
+// Byte offset inside a 32-row block of global chunk c of row r (the swizzle
+// of swf repeats every 16 rows).
+template <int D>
+__device__ __forceinline__ int cswz(int r, int c) {
+    return r * CGeo<D>::ROWB + ((c ^ swf<CGeo<D>::CH>(r)) << 4);
+}
+
+// Start this wave's share of one stage's loads: bytes [off, off + stage) of
+// the K and V tiles, `left` bytes of the tile remaining from off (none if
+// left <= 0; rows past it read as zeros), into the stage buffer at dst.
+template <int D>
+__device__ __forceinline__ void chunk_load_stage(const char* kt, const char* vt, int left, int off, char* dst,
+                                                 const uint32_t* dma_off, const int* lds_off) {
+    using G = CGeo<D>;
     const uint32_t n = left > 0 ? (uint32_t)left : 0u;
     const __amdgpu_buffer_rsrc_t rk = tile_rsrc(kt + off, n);
     const __amdgpu_buffer_rsrc_t rv = tile_rsrc(vt + off, n);
 #pragma unroll
-    for (int k = 0; k < DPW; ++k) {
+    for (int k = 0; k < G::DPW; ++k) {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t*)(dst + lds_off[k]), 16, dma_off[k], 0, 0,
                                                  FD_LOAD_AUX);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)(dst + kCKB * Geo<D>::BLKB + lds_off[k]), 16,
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)(dst + G::SKB * G::BLKB + lds_off[k]), 16,
                                                  dma_off[k], 0, 0, FD_LOAD_AUX);
     }
 }
 
-template <int D, int NB>
-__global__ __launch_bounds__(kMT) void fd_mfma_chunk_kernel(PartialArgs a) {
-    using G = Geo<D>;
-    constexpr int BM = kMW * 16 * NB;
-    constexpr int STG = kCKB * G::STAGEB;  // bytes per stage: kCKB K blocks, then kCKB V blocks
-    constexpr int NDMA = kCKB * G::IPB;    // 1 KiB load instructions per tensor per stage
-    static_assert(NDMA % kMW == 0, "stage loads split evenly over the waves");
-    constexpr int DPW = NDMA / kMW;        // per wave, per tensor
-    __shared__ __attribute__((aligned(16))) char smem[kCNS * STG];
+template <int N>
+__device__ __forceinline__ void lds_settle8(bf16x8_t (&v)[N]) {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < N; ++i) asm volatile("" : "+v"(v[i]));
+}
+
+template <int D>
+__global__ __launch_bounds__(kCT) void fd_mfma_chunk_kernel(PartialArgs a) {
+    using G = CGeo<D>;
+    constexpr int RS = D + 4;  // padded row stride of the merge area (floats)
+    constexpr int MERGEB = kCRG * (32 * RS + 3 * 32) * 4;
+    constexpr int SMEMB = kCNS * G::STGB > MERGEB ? kCNS * G::STGB : MERGEB;
+    __shared__ __attribute__((aligned(16))) char smem[SMEMB];
 
     const int s = blockIdx.x;
     const int g = blockIdx.y / a.row_blocks;
@@ -475,8 +535,10 @@ __global__ __launch_bounds__(kMT) void fd_mfma_chunk_kernel(PartialArgs a) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int w = (int)uniform((uint32_t)(tid >> 6));
-    const int grp = lane >> 4;
-    const int col = lane & 15;
+    const int rg = w % kCRG;   // row group
+    const int kh = w / kCRG;   // key half
+    const int hl = lane >> 5;  // lane half: G of the 32x32 layouts
+    const int col = lane & 31;
 
     int L = a.cache_lens[b];
     L = L < 0 ? 0 : (L > a.Lmax ? a.Lmax : L);
@@ -488,13 +550,13 @@ __global__ __launch_bounds__(kMT) void fd_mfma_chunk_kernel(PartialArgs a) {
     const int R = a.rows;
     const int n_rep = a.n_rep;
     const int q_len = a.q_len;
-    const int p0 = rt * BM;
+    const int p0 = rt * kChunkRows;
     const int64_t rowbase = ((int64_t)b * a.Hq + (int64_t)g * n_rep) * q_len;
     const int slots = a.rule.slots;
-    const int nrows = min(BM, R - p0);
+    const int nrows = min(kChunkRows, R - p0);
 
     if (s >= S) {
-        for (int idx = tid; idx < nrows; idx += kMT) {
+        for (int idx = tid; idx < nrows; idx += kCT) {
             const int p = p0 + idx;
             const int64_t row = rowbase + (int64_t)(p % n_rep) * q_len + p / n_rep;
             if (a.direct) {
@@ -510,129 +572,228 @@ __global__ __launch_bounds__(kMT) void fd_mfma_chunk_kernel(PartialArgs a) {
     }
 
     // Keys the tile's rows can see inside [lo, hi): the last row's limit
-    // bounds them all, the first row's limit is where masking starts.
+    // bounds them all; masking starts at the first row's limit.
     const int t_first = p0 / n_rep;
     const int t_last = (p0 + nrows - 1) / n_rep;
     const int kend = max(lo, min(hi, L - q_len + t_last + 1));
     const int mask_from = max(lo, min(hi, L - q_len + t_first + 1));
 
-    int rend[NB];
-    int64_t mrow[NB];
-    bool valid[NB];
-    bf16x8_t qf[NB][G::KS];
+    // This lane's query row (column of the 32x32 layouts).
+    const int p = p0 + rg * 32 + col;
+    const bool valid = p < R;
+    const int t = p / n_rep;
+    const int64_t mrow = rowbase + (int64_t)(p % n_rep) * q_len + t;
+    const int rend = valid ? max(lo, min(hi, L - q_len + t + 1)) : lo;
+    bf16x8_t qf[G::KS];
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-        const int p = p0 + w * 16 * NB + nb * 16 + col;
-        valid[nb] = p < R;
-        const int t = p / n_rep;
-        mrow[nb] = rowbase + (int64_t)(p % n_rep) * q_len + t;
-        rend[nb] = valid[nb] ? max(lo, min(hi, L - q_len + t + 1)) : lo;
-#pragma unroll
-        for (int ks = 0; ks < G::KS; ++ks) {
-            if (valid[nb]) {
-                const uint4 x = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q) + mrow[nb] * D +
-                                                                8 * grp + 32 * ks);
-                qf[nb][ks] = __builtin_bit_cast(bf16x8_t, x);
-            } else {
-                qf[nb][ks] = __builtin_bit_cast(bf16x8_t, make_uint4(0, 0, 0, 0));
-            }
+    for (int ks = 0; ks < G::KS; ++ks) {
+        if (valid) {
+            const uint4 x = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q) + mrow * D +
+                                                            16 * ks + 8 * hl);
+            qf[ks] = __builtin_bit_cast(bf16x8_t, x);
+        } else {
+            qf[ks] = __builtin_bit_cast(bf16x8_t, make_uint4(0, 0, 0, 0));
         }
     }
     const float c = a.qk_scale;
 
-    f32x4_t acc[NB][G::DB];
-    float m[NB], l[NB], mx[NB];
+    f32x16_t acc[G::DB];
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-        m[nb] = -INFINITY;
-        l[nb] = 0.f;
-        mx[nb] = -INFINITY;
+    for (int db = 0; db < G::DB; ++db)
 #pragma unroll
-        for (int db = 0; db < G::DB; ++db) acc[nb][db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    }
+        for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
+    float m = -INFINITY, l = 0.f, mx = -INFINITY;
 
     const int64_t tile_row = ((int64_t)b * a.Hkv + g) * a.Lmax + lo;
     const char* kt = static_cast<const char*>(a.k) + tile_row * G::ROWB;
     const char* vt = static_cast<const char*>(a.v) + tile_row * G::ROWB;
     const int tile_bytes = (kend - lo) * G::ROWB;
-    constexpr int SKEYS = kKB * kCKB;  // keys per stage
-    const int nst = (kend - lo + SKEYS - 1) / SKEYS;
+    const int nst = (kend - lo + G::SKEYS - 1) / G::SKEYS;
 
-    // This wave's load instructions of a stage: instruction n = w + 4k covers
-    // rows (n % IPB) * RPI .. of block n / IPB.
-    uint32_t dma_off[DPW];
-    int lds_off[DPW];
+    uint32_t dma_off[G::DPW];
+    int lds_off[G::DPW];
 #pragma unroll
-    for (int k = 0; k < DPW; ++k) {
-        const int n = w + k * kMW;
+    for (int k = 0; k < G::DPW; ++k) {
+        const int n = w + k * kCW;
         const int bb = n / G::IPB;
         const int i = n - bb * G::IPB;
         const int r = i * G::RPI + lane / G::CH;
-        const int cg = (lane % G::CH) ^ (r & (G::CH - 1));
-        dma_off[k] = (uint32_t)((bb * kKB + r) * G::ROWB + cg * 16);
+        const int cg = (lane % G::CH) ^ swf<G::CH>(r);
+        dma_off[k] = (uint32_t)((bb * kCBK + r) * G::ROWB + cg * 16);
         lds_off[k] = bb * G::BLKB + i * 1024;
     }
+
 #pragma unroll
     for (int j = 0; j < kCNS - 1; ++j)
-        load_stage<D, DPW>(kt, vt, tile_bytes - j * SKEYS * G::ROWB, j * SKEYS * G::ROWB, smem + j * STG, dma_off,
-                           lds_off);
+        chunk_load_stage<D>(kt, vt, tile_bytes - j * G::SKEYS * G::ROWB, j * G::SKEYS * G::ROWB, smem + j * G::STGB,
+                            dma_off, lds_off);
+
     for (int j = 0; j < nst; ++j) {
-        wait_vmcnt_le<(kCNS - 1) * 2 * DPW>();  // this wave's loads of stage j
-        __syncthreads();                        // everyone's, and stage j - 1 is free
+        wait_vmcnt_le<(kCNS - 1) * 2 * G::DPW>();  // this wave's loads of stage j
+        __syncthreads();                           // everyone's; stage j - 1 is free
         {
             const int jn = j + kCNS - 1;
-            load_stage<D, DPW>(kt, vt, tile_bytes - jn * SKEYS * G::ROWB, jn * SKEYS * G::ROWB,
-                               smem + (jn % kCNS) * STG, dma_off, lds_off);
+            chunk_load_stage<D>(kt, vt, tile_bytes - jn * G::SKEYS * G::ROWB, jn * G::SKEYS * G::ROWB,
+                                smem + (jn % kCNS) * G::STGB, dma_off, lds_off);
         }
-        const char* sk = smem + (j % kCNS) * STG;
-        const char* sv = sk + kCKB * G::BLKB;
+        const int key0 = lo + j * G::SKEYS + kh * kCBK;
+        if (key0 >= kend) continue;
+        const char* kb = smem + (j % kCNS) * G::STGB + kh * G::BLKB;
+        const char* vb = kb + G::SKB * G::BLKB;
+
+        // Operands: K rows (A of S^T), V^T through transposed reads (A of O^T).
+        bf16x8_t kf[G::KS];
 #pragma unroll
-        for (int bb = 0; bb < kCKB; ++bb) {
-            const int key0 = lo + j * SKEYS + bb * kKB;
-            if (key0 >= kend) break;
-            bf16x8_t kf[G::KS];
-            bf16x4_t vf[G::DB];
-            load_fragments<D>(sk + bb * G::BLKB, sv + bb * G::BLKB, kf, vf, grp, col);
-            block_math<D, NB>(kf, vf, qf, acc, m, l, mx, key0, key0 + kKB > mask_from, rend, c, grp);
+        for (int ks = 0; ks < G::KS; ++ks)
+            kf[ks] = *reinterpret_cast<const bf16x8_t*>(kb + cswz<D>(col, 2 * ks + hl));
+        bf16x8_t vf[G::DB * 2];
+        {
+            const int g16 = lane >> 4;
+            const int i16 = lane & 15;
+            const int q4 = i16 & 3;
+#pragma unroll
+            for (int db = 0; db < G::DB; ++db)
+#pragma unroll
+                for (int k2 = 0; k2 < 2; ++k2) {
+                    const int d0 = 32 * db + 16 * (g16 & 1);
+                    const int cc = d0 / 8 + (q4 >> 1);
+                    bf16x4_t lo4 = tr_read(vb + cswz<D>(16 * k2 + 4 * hl + (i16 >> 2), cc) + 8 * (q4 & 1));
+                    bf16x4_t hi4 = tr_read(vb + cswz<D>(16 * k2 + 8 + 4 * hl + (i16 >> 2), cc) + 8 * (q4 & 1));
+                    vf[db * 2 + k2] = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+                }
+        }
+        lds_settle8(vf);
+
+        f32x16_t st;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) st[r] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < G::KS; ++ks) st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], st, 0, 0, 0);
+
+        float x[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) x[r] = st[r] * c;
+        if (key0 + kCBK > mask_from) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                if (key0 + 8 * (r >> 2) + 4 * hl + (r & 3) >= rend) x[r] = -INFINITY;
+        }
+        float bm = x[0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) bm = fmaxf(bm, x[r]);
+        mx = fmaxf(mx, bm);
+        if (__any(bm > m + kTau)) {
+            const float bw = fmaxf(bm, __shfl_xor(bm, 32));
+            const float mn = fmaxf(m, bw);
+            const float alpha = m == -INFINITY ? 0.f : fast_exp2(m - mn);
+            l *= alpha;
+#pragma unroll
+            for (int db = 0; db < G::DB; ++db) acc[db] *= alpha;
+            m = mn;
+        }
+        const float mref = m == -INFINITY ? 0.f : m;
+        // The bf16 remainder of P matters only while single keys can carry a
+        // visible share of a row's weight; once every weight of the block is
+        // below 1/64 of the running sum, rounding P to bf16 perturbs the row
+        // by at most 2^-15 of its sum per key, with random signs.
+        const bool need_lo = __any(fast_exp2(bm - mref) * 64.f > l);
+        float pr[16];
+        bf16x8_t ph[2];
+        float ls = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            pr[r] = fast_exp2(x[r] - mref);
+            ls += pr[r];
+            ph[r >> 3][r & 7] = (__bf16)pr[r];
+        }
+        l += ls;
+#pragma unroll
+        for (int db = 0; db < G::DB; ++db)
+#pragma unroll
+            for (int k2 = 0; k2 < 2; ++k2)
+                acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[db * 2 + k2], ph[k2], acc[db], 0, 0, 0);
+        if (need_lo) {
+            bf16x8_t pl[2];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) pl[r >> 3][r & 7] = (__bf16)(pr[r] - (float)ph[r >> 3][r & 7]);
+#pragma unroll
+            for (int db = 0; db < G::DB; ++db)
+#pragma unroll
+                for (int k2 = 0; k2 < 2; ++k2)
+                    acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[db * 2 + k2], pl[k2], acc[db], 0, 0, 0);
         }
     }
     wait_vmcnt_le<0>();
 
-    // Each wave writes its own rows.
+    // Per-row totals over the two lane halves; then merge the key halves.
+    l += __shfl_xor(l, 32);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    __syncthreads();  // the ring is free
+    float* sm_acc = reinterpret_cast<float*>(smem);  // [kCRG][32][RS]
+    float* sm_m = sm_acc + kCRG * 32 * RS;           // [kCRG][32]
+    float* sm_l = sm_m + kCRG * 32;
+    float* sm_x = sm_l + kCRG * 32;
+    if (kh == 1) {
+        float* o = sm_acc + (rg * 32 + col) * RS;
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-        l[nb] += __shfl_xor(l[nb], 16);
-        l[nb] += __shfl_xor(l[nb], 32);
-        mx[nb] = fmaxf(mx[nb], __shfl_xor(mx[nb], 16));
-        mx[nb] = fmaxf(mx[nb], __shfl_xor(mx[nb], 32));
-        if (!valid[nb]) continue;
-        const bool empty = m[nb] == -INFINITY;
-        const float inv = empty ? 0.f : 1.f / l[nb];
-        const float lse_v = empty ? -INFINITY : (m[nb] + log2f(l[nb])) * kLn2;
-        const int64_t row = mrow[nb];
-        if (a.direct) {
-            uint16_t* o = reinterpret_cast<uint16_t*>(a.out) + row * D;
+        for (int db = 0; db < G::DB; ++db)
 #pragma unroll
-            for (int db = 0; db < G::DB; ++db) {
+            for (int a4 = 0; a4 < 4; ++a4)
+                *reinterpret_cast<f32x4_t*>(o + 32 * db + 8 * a4 + 4 * hl) =
+                    f32x4_t{acc[db][4 * a4], acc[db][4 * a4 + 1], acc[db][4 * a4 + 2], acc[db][4 * a4 + 3]};
+        if (hl == 0) {
+            sm_m[rg * 32 + col] = m;
+            sm_l[rg * 32 + col] = l;
+            sm_x[rg * 32 + col] = mx;
+        }
+    }
+    __syncthreads();
+    if (kh == 1 || !valid) return;
+    const float m2 = sm_m[rg * 32 + col];
+    const float M = fmaxf(m, m2);
+    const float f1 = m == -INFINITY ? 0.f : fast_exp2(m - M);
+    const float f2 = m2 == -INFINITY ? 0.f : fast_exp2(m2 - M);
+    const float den = l * f1 + sm_l[rg * 32 + col] * f2;
+    const float X = fmaxf(mx, sm_x[rg * 32 + col]);
+    const bool empty = M == -INFINITY;
+    const float inv = empty ? 0.f : 1.f / den;
+    const float lse_v = empty ? -INFINITY : (M + log2f(den)) * kLn2;
+    const float* o2 = sm_acc + (rg * 32 + col) * RS;
+    if (a.direct) {
+        uint16_t* o = reinterpret_cast<uint16_t*>(a.out) + mrow * D;
+#pragma unroll
+        for (int db = 0; db < G::DB; ++db)
+#pragma unroll
+            for (int a4 = 0; a4 < 4; ++a4) {
+                const int d = 32 * db + 8 * a4 + 4 * hl;
+                const f32x4_t y = *reinterpret_cast<const f32x4_t*>(o2 + d);
+                float v[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = (acc[db][4 * a4 + e] * f1 + y[e] * f2) * inv;
                 uint2 packed;
-                packed.x = (uint32_t)f32_to_bf16(acc[nb][db][0] * inv) |
-                           ((uint32_t)f32_to_bf16(acc[nb][db][1] * inv) << 16);
-                packed.y = (uint32_t)f32_to_bf16(acc[nb][db][2] * inv) |
-                           ((uint32_t)f32_to_bf16(acc[nb][db][3] * inv) << 16);
-                *reinterpret_cast<uint2*>(o + 16 * db + 4 * grp) = packed;
+                packed.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+                packed.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+                *reinterpret_cast<uint2*>(o + d) = packed;
             }
-            if (grp == 0 && a.lse) a.lse[row] = lse_v;
-        } else {
-            if (!empty) {
-                float* o = a.o_part + (row * slots + s) * D;
+        if (hl == 0 && a.lse) a.lse[mrow] = lse_v;
+    } else {
+        if (!empty) {
+            float* o = a.o_part + (mrow * slots + s) * D;
 #pragma unroll
-                for (int db = 0; db < G::DB; ++db)
-                    *reinterpret_cast<f32x4_t*>(o + 16 * db + 4 * grp) = acc[nb][db] * inv;
-            }
-            if (grp == 0) {
-                a.m_part[row * slots + s] = empty ? -INFINITY : mx[nb] * kLn2;
-                a.lse_part[row * slots + s] = lse_v;
-            }
+            for (int db = 0; db < G::DB; ++db)
+#pragma unroll
+                for (int a4 = 0; a4 < 4; ++a4) {
+                    const int d = 32 * db + 8 * a4 + 4 * hl;
+                    const f32x4_t y = *reinterpret_cast<const f32x4_t*>(o2 + d);
+                    f32x4_t v;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[e] = (acc[db][4 * a4 + e] * f1 + y[e] * f2) * inv;
+                    *reinterpret_cast<f32x4_t*>(o + d) = v;
+                }
+        }
+        if (hl == 0) {
+            a.m_part[mrow * slots + s] = empty ? -INFINITY : X * kLn2;
+            a.lse_part[mrow * slots + s] = lse_v;
         }
     }
 }
@@ -656,11 +817,11 @@ int mfma_block_rows(int rows) { return rows <= 32 ? rows : kChunkRows; }
 
 hipError_t launch_partials_mfma(int head_dim, int batch, const PartialArgs& a, hipStream_t stream) {
     if (a.rows > 32) {
-        dim3 grid(a.rule.slots, a.Hkv * a.row_blocks, batch), block(kMT);
+        dim3 grid(a.rule.slots, a.Hkv * a.row_blocks, batch), block(kCT);
         if (head_dim == 64)
-            hipLaunchKernelGGL((fd_mfma_chunk_kernel<64, kChunkNB>), grid, block, 0, stream, a);
+            hipLaunchKernelGGL((fd_mfma_chunk_kernel<64>), grid, block, 0, stream, a);
         else
-            hipLaunchKernelGGL((fd_mfma_chunk_kernel<128, kChunkNB>), grid, block, 0, stream, a);
+            hipLaunchKernelGGL((fd_mfma_chunk_kernel<128>), grid, block, 0, stream, a);
         return hipGetLastError();
     }
     const bool two = a.rows > 16;
