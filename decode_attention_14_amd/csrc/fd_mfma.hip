@@ -458,7 +458,7 @@ __global__ __launch_bounds__(kMT) void fd_mfma_partial_kernel(PartialArgs a) {
 //                carry a visible share of a row's weight (see need_lo).
 
 #ifndef FD_CHUNK_STAGES
-#define FD_CHUNK_STAGES 3
+#define FD_CHUNK_STAGES 2
 #endif
 constexpr int kCT = 512;                // threads per workgroup
 constexpr int kCW = kCT / 64;           // waves
@@ -518,6 +518,109 @@ __device__ __forceinline__ void lds_settle8(bf16x8_t (&v)[N]) {
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
     for (int i = 0; i < N; ++i) asm volatile("" : "+v"(v[i]));
+}
+
+// LDS address (byte offset in the workgroup's LDS) of a shared-memory pointer.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char*)p));
+}
+
+// 16-byte LDS load at a lane address plus a compile-time offset (folded into
+// the instruction's offset field).
+template <int OFF>
+__device__ __forceinline__ bf16x8_t lds_b128(uint32_t addr) {
+    return *(const __attribute__((address_space(3))) bf16x8_t*)(uintptr_t)(addr + OFF);
+}
+
+// Transposed read (see tr_read) at a lane address plus a compile-time offset.
+template <int OFF>
+__device__ __forceinline__ bf16x4_t tr_read_at(uint32_t addr) {
+    static_assert(OFF >= 0 && OFF < 65536, "ds offset field");
+    bf16x4_t r;
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+    return r;
+}
+
+// One 32-key block of the chunk kernel for the wave's 32 rows: operands from
+// the stage buffer at compile-time offset OFF (K at ka[] + OFF, V^T through
+// va[][] + OFF), then scores, softmax update and the P.V product.  c > 0.
+template <int D, int OFF>
+__device__ __forceinline__ void chunk_block(const uint32_t (&ka)[CGeo<D>::KS], const uint32_t (&va)[CGeo<D>::DB][2],
+                                            const bf16x8_t (&qf)[CGeo<D>::KS], f32x16_t (&acc)[CGeo<D>::DB],
+                                            float& m, float& l, float& mx, int key0, bool edge, int rend, float c,
+                                            int hl) {
+    using G = CGeo<D>;
+    constexpr int K2 = 16 * G::ROWB;  // 16 rows further down the block
+    bf16x8_t kf[G::KS];
+#pragma unroll
+    for (int ks = 0; ks < G::KS; ++ks) kf[ks] = lds_b128<OFF>(ka[ks]);
+    bf16x8_t vf[G::DB * 2];
+#pragma unroll
+    for (int db = 0; db < G::DB; ++db) {
+        const bf16x4_t a0 = tr_read_at<OFF>(va[db][0]);
+        const bf16x4_t a1 = tr_read_at<OFF>(va[db][1]);
+        const bf16x4_t b0 = tr_read_at<OFF + K2>(va[db][0]);
+        const bf16x4_t b1 = tr_read_at<OFF + K2>(va[db][1]);
+        vf[db * 2] = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
+        vf[db * 2 + 1] = __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+    lds_settle8(vf);
+
+    f32x16_t st;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) st[r] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < G::KS; ++ks) st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], st, 0, 0, 0);
+
+    if (edge) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            if (key0 + 8 * (r >> 2) + 4 * hl + (r & 3) >= rend) st[r] = -INFINITY;
+    }
+    float sm = fmaxf(fmaxf(st[0], st[1]), fmaxf(st[2], st[3]));
+#pragma unroll
+    for (int r = 4; r < 16; r += 4) sm = fmaxf(sm, fmaxf(fmaxf(st[r], st[r + 1]), fmaxf(st[r + 2], st[r + 3])));
+    const float bm = sm == -INFINITY ? -INFINITY : sm * c;
+    mx = fmaxf(mx, bm);
+    if (__any(bm > m + kTau)) {
+        const float bw = fmaxf(bm, __shfl_xor(bm, 32));
+        const float mn = fmaxf(m, bw);
+        const float alpha = m == -INFINITY ? 0.f : fast_exp2(m - mn);
+        l *= alpha;
+#pragma unroll
+        for (int db = 0; db < G::DB; ++db) acc[db] *= alpha;
+        m = mn;
+    }
+    const float mref = m == -INFINITY ? 0.f : m;
+    // The bf16 remainder of P matters only while single keys can carry a
+    // visible share of a row's weight (see the kernel's comment).
+    const bool need_lo = __any(fast_exp2(bm - mref) * 64.f > l);
+    float pr[16];
+    bf16x8_t ph[2];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        pr[r] = fast_exp2(fmaf(st[r], c, -mref));
+        ph[r >> 3][r & 7] = (__bf16)pr[r];
+    }
+    float s4[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s4[i] = (pr[4 * i] + pr[4 * i + 1]) + (pr[4 * i + 2] + pr[4 * i + 3]);
+    l += (s4[0] + s4[1]) + (s4[2] + s4[3]);
+#pragma unroll
+    for (int db = 0; db < G::DB; ++db)
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2)
+            acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[db * 2 + k2], ph[k2], acc[db], 0, 0, 0);
+    if (need_lo) {
+        bf16x8_t pl[2];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) pl[r >> 3][r & 7] = (__bf16)(pr[r] - (float)ph[r >> 3][r & 7]);
+#pragma unroll
+        for (int db = 0; db < G::DB; ++db)
+#pragma unroll
+            for (int k2 = 0; k2 < 2; ++k2)
+                acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[db * 2 + k2], pl[k2], acc[db], 0, 0, 0);
+    }
 }
 
 template <int D>
@@ -584,18 +687,21 @@ __global__ __launch_bounds__(kCT) void fd_mfma_chunk_kernel(PartialArgs a) {
     const int t = p / n_rep;
     const int64_t mrow = rowbase + (int64_t)(p % n_rep) * q_len + t;
     const int rend = valid ? max(lo, min(hi, L - q_len + t + 1)) : lo;
+    // Scores are scaled inside the exponent's FMA, which needs c > 0: a
+    // negative scale moves into q (exact sign flips of bf16) and a zero scale
+    // becomes a tiny positive one (all weights then equal to within 1e-26).
+    const bool neg = a.qk_scale < 0.f;
+    const float c = fmaxf(fabsf(a.qk_scale), 1e-30f);
+    const uint32_t flip = neg ? 0x80008000u : 0u;
     bf16x8_t qf[G::KS];
 #pragma unroll
     for (int ks = 0; ks < G::KS; ++ks) {
-        if (valid) {
-            const uint4 x = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q) + mrow * D +
-                                                            16 * ks + 8 * hl);
-            qf[ks] = __builtin_bit_cast(bf16x8_t, x);
-        } else {
-            qf[ks] = __builtin_bit_cast(bf16x8_t, make_uint4(0, 0, 0, 0));
-        }
+        uint4 x = make_uint4(0, 0, 0, 0);
+        if (valid)
+            x = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q) + mrow * D + 16 * ks + 8 * hl);
+        x.x ^= flip; x.y ^= flip; x.z ^= flip; x.w ^= flip;
+        qf[ks] = __builtin_bit_cast(bf16x8_t, x);
     }
-    const float c = a.qk_scale;
 
     f32x16_t acc[G::DB];
 #pragma unroll
@@ -623,104 +729,53 @@ __global__ __launch_bounds__(kCT) void fd_mfma_chunk_kernel(PartialArgs a) {
         lds_off[k] = bb * G::BLKB + i * 1024;
     }
 
+    // Lane-constant LDS addresses of this wave's operands in stage 0; other
+    // stages and the second 16-key step add compile-time offsets.
+    uint32_t ka[G::KS];
+    uint32_t va[G::DB][2];
+    {
+        const uint32_t base = lds_addr(smem) + kh * G::BLKB;
+#pragma unroll
+        for (int ks = 0; ks < G::KS; ++ks) ka[ks] = base + cswz<D>(col, 2 * ks + hl);
+        const int g16 = lane >> 4;
+        const int i16 = lane & 15;
+        const int q4 = i16 & 3;
+#pragma unroll
+        for (int db = 0; db < G::DB; ++db)
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+                va[db][t] = base + G::SKB * G::BLKB +
+                            cswz<D>(8 * t + 4 * hl + (i16 >> 2), (32 * db + 16 * (g16 & 1)) / 8 + (q4 >> 1)) +
+                            8 * (q4 & 1);
+    }
+
 #pragma unroll
     for (int j = 0; j < kCNS - 1; ++j)
         chunk_load_stage<D>(kt, vt, tile_bytes - j * G::SKEYS * G::ROWB, j * G::SKEYS * G::ROWB, smem + j * G::STGB,
                             dma_off, lds_off);
 
-    for (int j = 0; j < nst; ++j) {
-        wait_vmcnt_le<(kCNS - 1) * 2 * G::DPW>();  // this wave's loads of stage j
-        __syncthreads();                           // everyone's; stage j - 1 is free
-        {
-            const int jn = j + kCNS - 1;
-            chunk_load_stage<D>(kt, vt, tile_bytes - jn * G::SKEYS * G::ROWB, jn * G::SKEYS * G::ROWB,
-                                smem + (jn % kCNS) * G::STGB, dma_off, lds_off);
-        }
-        const int key0 = lo + j * G::SKEYS + kh * kCBK;
-        if (key0 >= kend) continue;
-        const char* kb = smem + (j % kCNS) * G::STGB + kh * G::BLKB;
-        const char* vb = kb + G::SKB * G::BLKB;
-
-        // Operands: K rows (A of S^T), V^T through transposed reads (A of O^T).
-        bf16x8_t kf[G::KS];
+    // Stage j lives in ring slot j % kCNS; unrolling by kCNS makes the slot,
+    // and so every LDS offset, a compile-time constant.
+    for (int j0 = 0; j0 < nst; j0 += kCNS) {
 #pragma unroll
-        for (int ks = 0; ks < G::KS; ++ks)
-            kf[ks] = *reinterpret_cast<const bf16x8_t*>(kb + cswz<D>(col, 2 * ks + hl));
-        bf16x8_t vf[G::DB * 2];
-        {
-            const int g16 = lane >> 4;
-            const int i16 = lane & 15;
-            const int q4 = i16 & 3;
-#pragma unroll
-            for (int db = 0; db < G::DB; ++db)
-#pragma unroll
-                for (int k2 = 0; k2 < 2; ++k2) {
-                    const int d0 = 32 * db + 16 * (g16 & 1);
-                    const int cc = d0 / 8 + (q4 >> 1);
-                    bf16x4_t lo4 = tr_read(vb + cswz<D>(16 * k2 + 4 * hl + (i16 >> 2), cc) + 8 * (q4 & 1));
-                    bf16x4_t hi4 = tr_read(vb + cswz<D>(16 * k2 + 8 + 4 * hl + (i16 >> 2), cc) + 8 * (q4 & 1));
-                    vf[db * 2 + k2] = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
-                }
-        }
-        lds_settle8(vf);
-
-        f32x16_t st;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) st[r] = 0.f;
-#pragma unroll
-        for (int ks = 0; ks < G::KS; ++ks) st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], st, 0, 0, 0);
-
-        float x[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) x[r] = st[r] * c;
-        if (key0 + kCBK > mask_from) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-                if (key0 + 8 * (r >> 2) + 4 * hl + (r & 3) >= rend) x[r] = -INFINITY;
-        }
-        float bm = x[0];
-#pragma unroll
-        for (int r = 1; r < 16; ++r) bm = fmaxf(bm, x[r]);
-        mx = fmaxf(mx, bm);
-        if (__any(bm > m + kTau)) {
-            const float bw = fmaxf(bm, __shfl_xor(bm, 32));
-            const float mn = fmaxf(m, bw);
-            const float alpha = m == -INFINITY ? 0.f : fast_exp2(m - mn);
-            l *= alpha;
-#pragma unroll
-            for (int db = 0; db < G::DB; ++db) acc[db] *= alpha;
-            m = mn;
-        }
-        const float mref = m == -INFINITY ? 0.f : m;
-        // The bf16 remainder of P matters only while single keys can carry a
-        // visible share of a row's weight; once every weight of the block is
-        // below 1/64 of the running sum, rounding P to bf16 perturbs the row
-        // by at most 2^-15 of its sum per key, with random signs.
-        const bool need_lo = __any(fast_exp2(bm - mref) * 64.f > l);
-        float pr[16];
-        bf16x8_t ph[2];
-        float ls = 0.f;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            pr[r] = fast_exp2(x[r] - mref);
-            ls += pr[r];
-            ph[r >> 3][r & 7] = (__bf16)pr[r];
-        }
-        l += ls;
-#pragma unroll
-        for (int db = 0; db < G::DB; ++db)
-#pragma unroll
-            for (int k2 = 0; k2 < 2; ++k2)
-                acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[db * 2 + k2], ph[k2], acc[db], 0, 0, 0);
-        if (need_lo) {
-            bf16x8_t pl[2];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) pl[r >> 3][r & 7] = (__bf16)(pr[r] - (float)ph[r >> 3][r & 7]);
-#pragma unroll
-            for (int db = 0; db < G::DB; ++db)
-#pragma unroll
-                for (int k2 = 0; k2 < 2; ++k2)
-                    acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[db * 2 + k2], pl[k2], acc[db], 0, 0, 0);
+        for (int u = 0; u < kCNS; ++u) {
+            const int j = j0 + u;
+            if (j >= nst) break;
+            wait_vmcnt_le<(kCNS - 1) * 2 * G::DPW>();  // this wave's loads of stage j
+            __syncthreads();                           // everyone's; stage j - 1 is free
+            {
+                const int jn = j + kCNS - 1;
+                chunk_load_stage<D>(kt, vt, tile_bytes - jn * G::SKEYS * G::ROWB, jn * G::SKEYS * G::ROWB,
+                                    smem + ((u + kCNS - 1) % kCNS) * G::STGB, dma_off, lds_off);
+            }
+            const int key0 = lo + j * G::SKEYS + kh * kCBK;
+            if (key0 < kend) {
+                const bool edge = key0 + kCBK > mask_from;
+                if (u == 0) chunk_block<D, 0>(ka, va, qf, acc, m, l, mx, key0, edge, rend, c, hl);
+                if (u == 1) chunk_block<D, G::STGB>(ka, va, qf, acc, m, l, mx, key0, edge, rend, c, hl);
+                if constexpr (kCNS > 2)
+                    if (u == 2) chunk_block<D, 2 * G::STGB>(ka, va, qf, acc, m, l, mx, key0, edge, rend, c, hl);
+            }
         }
     }
     wait_vmcnt_le<0>();
