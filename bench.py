@@ -34,6 +34,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "decode-attention HBM GB/s (% of MI355X peak) and µs/step at 32k ctx"
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 matrix-core peak of MI355X
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "decode_attention_14_amd", "csrc", f)
                   for f in ("fd_decode.hip", "fd_mfma.hip", "fd_device.h", "fd_internal.h")] + [
@@ -75,9 +76,22 @@ def algorithmic_bytes(w, lens):
 
 def partial_kernel_name(w) -> str:
     """The partial-pass kernel the library dispatches to for this workload:
-    matrix cores for bf16 row groups of up to 32 rows, vector ALUs otherwise."""
+    matrix cores for bf16 (decode rows, or chunk tiles above 32 rows), vector
+    ALUs for fp32."""
     rows = w.num_q_heads // w.num_kv_heads * w.q_len
-    return "fd_mfma_partial_kernel" if w.dtype == "bf16" and rows <= 32 else "fd_partial_kernel"
+    if w.dtype != "bf16":
+        return "fd_partial_kernel"
+    return "fd_mfma_partial_kernel" if rows <= 32 else "fd_mfma_chunk_kernel"
+
+
+def algorithmic_flops(w, lens):
+    """4 * head_dim flops (the q.k and p.v products) per visible (query row,
+    key) pair; row t of a chunk sees keys 0 .. L - q_len + t."""
+    pairs = 0
+    for L in lens:
+        for t in range(w.q_len):
+            pairs += max(0, min(L, L - w.q_len + t + 1))
+    return 4 * w.head_dim * w.num_q_heads * pairs
 
 
 def cpu_baseline(w, q, k, v, cl, alg_bytes, seconds):
@@ -250,6 +264,17 @@ def main():
             "kernel": partial_kernel_name(w), "bytes_per_launch": partial_bytes,
         },
     }
+    if w.q_len > 1 and w.dtype == "bf16":
+        # A long chunk is a dense contraction: its partial pass is priced
+        # against the matrix cores, with the HBM figures kept beside it.
+        flops = algorithmic_flops(w, lens)
+        tflops = flops / (part_ms * 1e-3) / 1e12
+        result["roofline"] = {
+            "bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic,
+            "kernel": partial_kernel_name(w), "flops_per_launch": flops,
+            "hbm_achieved_GBs": round(achieved, 2),
+        }
     if not args.no_cpu_baseline:
         print("[bench] timing the fp64 oracle on host cores", file=sys.stderr, flush=True)
         qh, kh, vh, clh = workload_inputs(w)
