@@ -453,9 +453,9 @@ __global__ __launch_bounds__(kMT) void fd_mfma_partial_kernel(PartialArgs a) {
 //                (half G, column q) holds the scores of keys 8a + 4G + b of
 //                the block (a, b = 0..3), which are exactly its B operand
 //                for the two 16-key steps, so P stays in place; V^T comes
-//                from transposed LDS reads.  P is split into a bf16 head and
-//                remainder as in the decode kernel while single keys still
-//                carry a visible share of a row's weight (see need_lo).
+//                from transposed LDS reads.  P enters as bf16, plus its
+//                bf16 remainder while single keys still carry a visible
+//                share of a row's weight (see chunk_softmax).
 
 #ifndef FD_CHUNK_STAGES
 #define FD_CHUNK_STAGES 2
@@ -541,20 +541,35 @@ __device__ __forceinline__ bf16x4_t tr_read_at(uint32_t addr) {
     return r;
 }
 
-// One 32-key block of the chunk kernel for the wave's 32 rows: operands from
-// the stage buffer at compile-time offset OFF (K at ka[] + OFF, V^T through
-// va[][] + OFF), then scores, softmax update and the P.V product.  c > 0.
+// The chunk kernel's work on one 32-key block is spread over two steps so
+// that a wave keeps its matrix core fed while it runs the softmax: step j
+// issues the score product of block j and the head part of block j - 1's
+// P.V product back to back, runs block j's softmax on the vector units while
+// they execute, and ends with the (rare) rescale and, where needed, the
+// remainder part of block j's P.V product.
+
+// K operands of a block (stage buffer at compile-time offset OFF) and S^T.
 template <int D, int OFF>
-__device__ __forceinline__ void chunk_block(const uint32_t (&ka)[CGeo<D>::KS], const uint32_t (&va)[CGeo<D>::DB][2],
-                                            const bf16x8_t (&qf)[CGeo<D>::KS], f32x16_t (&acc)[CGeo<D>::DB],
-                                            float& m, float& l, float& mx, int key0, bool edge, int rend, float c,
-                                            int hl) {
+__device__ __forceinline__ void chunk_scores(const uint32_t (&ka)[CGeo<D>::KS], const bf16x8_t (&qf)[CGeo<D>::KS],
+                                             f32x16_t& st) {
     using G = CGeo<D>;
-    constexpr int K2 = 16 * G::ROWB;  // 16 rows further down the block
     bf16x8_t kf[G::KS];
 #pragma unroll
     for (int ks = 0; ks < G::KS; ++ks) kf[ks] = lds_b128<OFF>(ka[ks]);
-    bf16x8_t vf[G::DB * 2];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) st[r] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < G::KS; ++ks) st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], st, 0, 0, 0);
+    // All K reads first, so the products wait on LDS once.
+    __builtin_amdgcn_sched_group_barrier(0x100, G::KS, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, G::KS, 0);
+}
+
+// Start the transposed reads of a block's V operands; valid after lds_settle8.
+template <int D, int OFF>
+__device__ __forceinline__ void chunk_v_reads(const uint32_t (&va)[CGeo<D>::DB][2], bf16x8_t (&vf)[CGeo<D>::DB * 2]) {
+    using G = CGeo<D>;
+    constexpr int K2 = 16 * G::ROWB;  // 16 rows further down the block
 #pragma unroll
     for (int db = 0; db < G::DB; ++db) {
         const bf16x4_t a0 = tr_read_at<OFF>(va[db][0]);
@@ -564,63 +579,111 @@ __device__ __forceinline__ void chunk_block(const uint32_t (&ka)[CGeo<D>::KS], c
         vf[db * 2] = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
         vf[db * 2 + 1] = __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7);
     }
-    lds_settle8(vf);
+}
 
-    f32x16_t st;
+// O^T += V^T P^T for one block and one bf16 part of P.  The 16-key halves
+// are the outer loop so that consecutive instructions use different
+// accumulators.
+template <int D>
+__device__ __forceinline__ void chunk_pv(const bf16x8_t (&vf)[CGeo<D>::DB * 2], const bf16x8_t (&pp)[2],
+                                         f32x16_t (&acc)[CGeo<D>::DB]) {
+    using G = CGeo<D>;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) st[r] = 0.f;
+    for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
-    for (int ks = 0; ks < G::KS; ++ks) st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], st, 0, 0, 0);
+        for (int db = 0; db < G::DB; ++db)
+            acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[db * 2 + k2], pp[k2], acc[db], 0, 0, 0);
+}
 
-    if (edge) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-            if (key0 + 8 * (r >> 2) + 4 * hl + (r & 3) >= rend) st[r] = -INFINITY;
-    }
+// Online-softmax statistics and weights of one block (no access to the
+// accumulators, so it can overlap the matrix work of the previous block):
+// tracks the exact max mx, moves the lazy reference m when the block's max
+// passes it by more than kTau (alpha is then the factor that the
+// accumulators still owe, else 1), and writes P as bf16 head ph and, if lo,
+// remainder pl.
+//
+// The running sum l adds the weights that the products actually use: the
+// bf16 heads, plus the remainders where they are used.  With weights rounded
+// to bf16 (relative error at most 2^-9), a row's output is then still a
+// convex combination of the V rows, off by sum_i w_i d_i (v_i - o) with
+// centred errors d_i; a block that holds a key with more than 1/16 of the
+// row's running sum takes the remainder product as well, which bounds that
+// sum's spread by 2^-9 * sqrt(1/16 / 3) * rms(v - o) = 2.8e-4 rms(v - o), and
+// keeps few dominant keys (short rows, peaked scores) exact to 2^-17.  c > 0.
+__device__ __forceinline__ void chunk_softmax(const f32x16_t& st, float c, float& m, float& l, float& mx, float& alpha,
+                                              bool& moved, bf16x8_t (&ph)[2], bf16x8_t (&pl)[2], bool& lo) {
     float sm = fmaxf(fmaxf(st[0], st[1]), fmaxf(st[2], st[3]));
 #pragma unroll
     for (int r = 4; r < 16; r += 4) sm = fmaxf(sm, fmaxf(fmaxf(st[r], st[r + 1]), fmaxf(st[r + 2], st[r + 3])));
     const float bm = sm == -INFINITY ? -INFINITY : sm * c;
     mx = fmaxf(mx, bm);
-    if (__any(bm > m + kTau)) {
-        const float bw = fmaxf(bm, __shfl_xor(bm, 32));
-        const float mn = fmaxf(m, bw);
-        const float alpha = m == -INFINITY ? 0.f : fast_exp2(m - mn);
-        l *= alpha;
-#pragma unroll
-        for (int db = 0; db < G::DB; ++db) acc[db] *= alpha;
-        m = mn;
-    }
+    moved = __any(bm > m + kTau);
+    const float bw = fmaxf(bm, __shfl_xor(bm, 32));
+    const float mn = moved ? fmaxf(m, bw) : m;
+    alpha = m == -INFINITY ? 0.f : fast_exp2(m - mn);
+    m = mn;
+    l *= alpha;
     const float mref = m == -INFINITY ? 0.f : m;
-    // The bf16 remainder of P matters only while single keys can carry a
-    // visible share of a row's weight (see the kernel's comment).
-    const bool need_lo = __any(fast_exp2(bm - mref) * 64.f > l);
-    float pr[16];
-    bf16x8_t ph[2];
+    lo = __any(fast_exp2(bm - mref) * 16.f > l);
+    float pr[16], hf[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
         pr[r] = fast_exp2(fmaf(st[r], c, -mref));
         ph[r >> 3][r & 7] = (__bf16)pr[r];
+        hf[r] = (float)ph[r >> 3][r & 7];
+    }
+    if (lo) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const float d = pr[r] - hf[r];
+            pl[r >> 3][r & 7] = (__bf16)d;
+            hf[r] += (float)pl[r >> 3][r & 7];
+        }
     }
     float s4[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) s4[i] = (pr[4 * i] + pr[4 * i + 1]) + (pr[4 * i + 2] + pr[4 * i + 3]);
+    for (int i = 0; i < 4; ++i) s4[i] = (hf[4 * i] + hf[4 * i + 1]) + (hf[4 * i + 2] + hf[4 * i + 3]);
     l += (s4[0] + s4[1]) + (s4[2] + s4[3]);
+}
+
+// One step of the chunk kernel at stage buffer offset OFF (see above).  On
+// entry vf/ph hold block j - 1's V operands and P head (zeros before the
+// first block); on exit, block j's.  Keys of an edge block at or past rend
+// are masked (a block past the tile's last key is masked whole; its stage
+// area reads as zeros).
+template <int D, int OFF>
+__device__ __forceinline__ void chunk_step(bool edge, const uint32_t (&ka)[CGeo<D>::KS],
+                                           const uint32_t (&va)[CGeo<D>::DB][2], const bf16x8_t (&qf)[CGeo<D>::KS],
+                                           f32x16_t (&acc)[CGeo<D>::DB], bf16x8_t (&vf)[CGeo<D>::DB * 2],
+                                           bf16x8_t (&ph)[2], float& m, float& l, float& mx, int key0, int rend,
+                                           float c, int hl) {
+    using G = CGeo<D>;
+    f32x16_t st;
+    chunk_scores<D, OFF>(ka, qf, st);
+    if (edge) {
 #pragma unroll
-    for (int db = 0; db < G::DB; ++db)
-#pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2)
-            acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[db * 2 + k2], ph[k2], acc[db], 0, 0, 0);
-    if (need_lo) {
-        bf16x8_t pl[2];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) pl[r >> 3][r & 7] = (__bf16)(pr[r] - (float)ph[r >> 3][r & 7]);
-#pragma unroll
-        for (int db = 0; db < G::DB; ++db)
-#pragma unroll
-            for (int k2 = 0; k2 < 2; ++k2)
-                acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[db * 2 + k2], pl[k2], acc[db], 0, 0, 0);
+        for (int r = 0; r < 16; ++r)
+            if (key0 + 8 * (r >> 2) + 4 * hl + (r & 3) >= rend) st[r] = -INFINITY;
     }
+    chunk_pv<D>(vf, ph, acc);
+    float alpha;
+    bool moved, lo;
+    bf16x8_t pl[2];
+    chunk_softmax(st, c, m, l, mx, alpha, moved, ph, pl, lo);
+    chunk_v_reads<D, OFF>(va, vf);
+    // P.V products of the previous block with the softmax's vector work
+    // between them.
+#pragma unroll
+    for (int i = 0; i < 2 * G::DB; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+    }
+    lds_settle8(vf);
+    if (moved) {
+#pragma unroll
+        for (int db = 0; db < G::DB; ++db) acc[db] *= alpha;
+    }
+    if (lo) chunk_pv<D>(vf, pl, acc);
 }
 
 template <int D>
@@ -755,7 +818,12 @@ __global__ __launch_bounds__(kCT) void fd_mfma_chunk_kernel(PartialArgs a) {
                             dma_off, lds_off);
 
     // Stage j lives in ring slot j % kCNS; unrolling by kCNS makes the slot,
-    // and so every LDS offset, a compile-time constant.
+    // and so every LDS offset, a compile-time constant.  A wave whose block
+    // lies past kend masks it whole (its stage area reads as zeros).
+    bf16x8_t vf[G::DB * 2], ph[2];
+#pragma unroll
+    for (int i = 0; i < G::DB * 2; ++i) vf[i] = bf16x8_t{};
+    ph[0] = ph[1] = bf16x8_t{};
     for (int j0 = 0; j0 < nst; j0 += kCNS) {
 #pragma unroll
         for (int u = 0; u < kCNS; ++u) {
@@ -769,15 +837,14 @@ __global__ __launch_bounds__(kCT) void fd_mfma_chunk_kernel(PartialArgs a) {
                                     smem + ((u + kCNS - 1) % kCNS) * G::STGB, dma_off, lds_off);
             }
             const int key0 = lo + j * G::SKEYS + kh * kCBK;
-            if (key0 < kend) {
-                const bool edge = key0 + kCBK > mask_from;
-                if (u == 0) chunk_block<D, 0>(ka, va, qf, acc, m, l, mx, key0, edge, rend, c, hl);
-                if (u == 1) chunk_block<D, G::STGB>(ka, va, qf, acc, m, l, mx, key0, edge, rend, c, hl);
-                if constexpr (kCNS > 2)
-                    if (u == 2) chunk_block<D, 2 * G::STGB>(ka, va, qf, acc, m, l, mx, key0, edge, rend, c, hl);
-            }
+            const bool edge = key0 + kCBK > mask_from;
+            if (u == 0) chunk_step<D, 0>(edge, ka, va, qf, acc, vf, ph, m, l, mx, key0, rend, c, hl);
+            if (u == 1) chunk_step<D, G::STGB>(edge, ka, va, qf, acc, vf, ph, m, l, mx, key0, rend, c, hl);
+            if constexpr (kCNS > 2)
+                if (u == 2) chunk_step<D, 2 * G::STGB>(edge, ka, va, qf, acc, vf, ph, m, l, mx, key0, rend, c, hl);
         }
     }
+    chunk_pv<D>(vf, ph, acc);
     wait_vmcnt_le<0>();
 
     // Per-row totals over the two lane halves; then merge the key halves.
