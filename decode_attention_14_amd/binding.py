@@ -21,8 +21,11 @@ FD_OK, FD_ERR_INVALID, FD_ERR_UNSUPPORTED, FD_ERR_WORKSPACE, FD_ERR_DEVICE = 0, 
 FD_F32, FD_BF16 = 0, 1
 FD_MAX_SPLITS = 256
 
+FD_PAGES_NHD, FD_PAGES_HND = 0, 1
+
 EXPORTS = ("fd_plan_splits", "fd_workspace_bytes", "fd_decode_partials", "fd_combine_splits",
-           "fd_decode_attention", "fd_status_string", "fd_last_error", "fd_version")
+           "fd_decode_attention", "fd_decode_attention_paged", "fd_status_string", "fd_last_error",
+           "fd_version")
 
 
 class FdDims(ctypes.Structure):
@@ -40,6 +43,12 @@ class FdPlan(ctypes.Structure):
     def __repr__(self):
         return (f"FdPlan(tile_len={self.tile_len}, max_splits={self.max_splits}, "
                 f"workspace_bytes={self.workspace_bytes}, work_units={self.work_units})")
+
+
+class FdKvPages(ctypes.Structure):
+    _fields_ = [("block_table", ctypes.c_void_p), ("max_pages_per_seq", ctypes.c_int32),
+                ("page_size", ctypes.c_int32), ("num_pages", ctypes.c_int32),
+                ("layout", ctypes.c_int32)]
 
 
 class FdError(RuntimeError):
@@ -74,6 +83,9 @@ def load_library(path: str | None = None):
     lib.fd_decode_attention.argtypes = [dims_p, vp, vp, vp, vp, ctypes.c_float, i32, plan_p,
                                         vp, u64, vp, vp, vp]
     lib.fd_decode_attention.restype = i32
+    lib.fd_decode_attention_paged.argtypes = [dims_p, vp, vp, vp, ctypes.POINTER(FdKvPages), vp,
+                                              ctypes.c_float, i32, plan_p, vp, u64, vp, vp, vp]
+    lib.fd_decode_attention_paged.restype = i32
     lib.fd_status_string.argtypes = [i32]
     lib.fd_status_string.restype = ctypes.c_char_p
     lib.fd_last_error.argtypes = []
@@ -278,4 +290,74 @@ def combine(o_part, lse_part, out_dtype=torch.float32, out=None, lse=None):
     _check(lib.fd_combine_splits(B, H, T, D, S, _ptr(o_part), _ptr(lse_part),
                                  _dtype_code(out.dtype), _ptr(out), _ptr(lse),
                                  _stream(o_part.device)))
+    return out, lse
+
+
+_LAYOUTS = {"nhd": FD_PAGES_NHD, "hnd": FD_PAGES_HND}
+
+
+def paged_dims(q: torch.Tensor, k_pages: torch.Tensor, block_table: torch.Tensor, layout: str = "nhd"):
+    """(dims, page_size, num_kv_heads) of a paged call.
+
+    k_pages is [num_pages, page_size, Hkv, D] ("nhd") or [num_pages, Hkv, page_size, D]
+    ("hnd"); block_table [B, max_pages_per_seq] int32.
+    """
+    if layout not in _LAYOUTS:
+        raise FdError(FD_ERR_UNSUPPORTED, f"page layout {layout!r} unknown (nhd or hnd)")
+    if q.dim() != 4 or k_pages.dim() != 4 or block_table.dim() != 2:
+        raise FdError(FD_ERR_INVALID, "q must be [B,Hq,q_len,D], k_pages 4-d and block_table [B, pages]")
+    B, Hq, q_len, D = q.shape
+    if layout == "nhd":
+        _, P, Hkv, Dk = k_pages.shape
+    else:
+        _, Hkv, P, Dk = k_pages.shape
+    if Dk != D or block_table.shape[0] != B:
+        raise FdError(FD_ERR_INVALID, f"q {tuple(q.shape)}, k_pages {tuple(k_pages.shape)} and "
+                                      f"block_table {tuple(block_table.shape)} disagree")
+    return make_dims(B, Hq, Hkv, D, q_len, block_table.shape[1] * P, q.dtype), P
+
+
+def decode_attention_paged(q, k_pages, v_pages, block_table, cache_lens, layout: str = "nhd",
+                           scale=None, num_splits: int = 0, plan: Plan | FdPlan | None = None,
+                           out=None, lse=None, workspace=None):
+    """Split-KV attention over a paged K/V cache.  Returns (out, lse).
+
+    k_pages, v_pages: [num_pages, page_size, Hkv, D] (layout "nhd") or
+    [num_pages, Hkv, page_size, D] ("hnd"); block_table [B, max_pages_per_seq]
+    int32 on the device; key j of sequence b is row j % page_size of page
+    block_table[b, j // page_size].  Other arguments as decode_attention; a
+    plan comes from plan_splits(paged_dims(...)[0], lengths).
+    """
+    lib = load_library()
+    _require_cuda(q, k_pages, v_pages, block_table, cache_lens, out, lse, workspace)
+    dims, P = paged_dims(q, k_pages, block_table, layout)
+    if v_pages.shape != k_pages.shape:
+        raise FdError(FD_ERR_INVALID, f"v_pages {tuple(v_pages.shape)} != k_pages {tuple(k_pages.shape)}")
+    if not (q.dtype == k_pages.dtype == v_pages.dtype):
+        raise FdError(FD_ERR_INVALID, "q, k_pages and v_pages must share one dtype")
+    if block_table.dtype != torch.int32:
+        raise FdError(FD_ERR_INVALID, "block_table must be int32")
+    if cache_lens.dtype != torch.int32 or cache_lens.shape != (q.shape[0],):
+        raise FdError(FD_ERR_INVALID, "cache_lens must be int32 of shape [B]")
+    if len({t.device for t in (q, k_pages, v_pages, block_table, cache_lens)}) != 1:
+        raise FdError(FD_ERR_INVALID, "all tensors must be on one device")
+    _check_buffer(out, q.shape, q.dtype, "out")
+    _check_buffer(lse, q.shape[:3], torch.float32, "lse")
+    fp = plan.plan if isinstance(plan, Plan) else plan
+    slots = num_splits if num_splits > 0 else (fp.max_splits if fp is not None else 1)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    ws_bytes = workspace_bytes(dims, slots) if slots > 1 else 0
+    if workspace is None and ws_bytes:
+        workspace = new_workspace(ws_bytes, q.device)
+    given = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    pages = FdKvPages(block_table.data_ptr(), block_table.shape[1], P, k_pages.shape[0], _LAYOUTS[layout])
+    _check(lib.fd_decode_attention_paged(ctypes.byref(dims), _ptr(q), _ptr(k_pages), _ptr(v_pages),
+                                         ctypes.byref(pages), _ptr(cache_lens),
+                                         ctypes.c_float(_default_scale(q.shape[-1], scale)),
+                                         int(num_splits), ctypes.byref(fp) if fp is not None else None,
+                                         _ptr(workspace), given, _ptr(out), _ptr(lse),
+                                         _stream(q.device)))
     return out, lse

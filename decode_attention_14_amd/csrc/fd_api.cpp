@@ -97,11 +97,11 @@ fd_status resolve_rule(int32_t num_splits, const fd_plan* plan, fdk::SplitRule* 
     if (num_splits < 0 || num_splits > FD_MAX_SPLITS)
         return fail(FD_ERR_INVALID, "num_splits %d outside [0, %d]", num_splits, FD_MAX_SPLITS);
     if (num_splits > 0) {
-        *rule = {0, num_splits, num_splits};
+        *rule = {0, num_splits, num_splits, 1};
         return FD_OK;
     }
     if (!plan) {
-        *rule = {0, 1, 1};  // one tile holding every key
+        *rule = {0, 1, 1, 1};  // one tile holding every key
         return FD_OK;
     }
     if (plan->max_splits < 1 || plan->max_splits > FD_MAX_SPLITS)
@@ -109,7 +109,7 @@ fd_status resolve_rule(int32_t num_splits, const fd_plan* plan, fdk::SplitRule* 
     if (plan->tile_len < 1)
         return fail(FD_ERR_INVALID, "plan tile_len %d < 1 (a forced-count plan needs num_splits)",
                     plan->tile_len);
-    *rule = {plan->tile_len, 1, plan->max_splits};
+    *rule = {plan->tile_len, 1, plan->max_splits, 1};
     return FD_OK;
 }
 
@@ -164,7 +164,7 @@ const char* fd_status_string(int32_t status) {
 
 const char* fd_last_error(void) { return g_last_error; }
 
-int32_t fd_version(void) { return 100; }
+int32_t fd_version(void) { return 200; }
 
 uint64_t fd_workspace_bytes(const fd_dims* dims, int32_t max_splits) {
     if (max_splits <= 1 || max_splits > FD_MAX_SPLITS) return 0;
@@ -294,15 +294,64 @@ fd_status fd_combine_splits(int32_t batch, int32_t num_heads, int32_t q_len, int
                          "combine kernel launch");
 }
 
-fd_status fd_decode_attention(const fd_dims* dims, const void* q, const void* k_cache,
-                              const void* v_cache, const int32_t* cache_lens, float scale,
-                              int32_t num_splits, const fd_plan* plan, void* workspace,
-                              uint64_t workspace_bytes, void* out, float* lse, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Check a paged-cache description against dims; on success fill *pk and
+// make *rule cut tiles at multiples of 16 keys.
+fd_status resolve_pages(const fd_dims* d, const fd_kv_pages* pages, fdk::SplitRule* rule, fdk::PagedKV* pk) {
+    if (!pages) return fail(FD_ERR_INVALID, "pages is NULL");
+    if (!pages->block_table) return fail(FD_ERR_INVALID, "block_table is NULL");
+    if (misaligned(pages->block_table, 4)) return fail(FD_ERR_INVALID, "block_table must be 4-byte aligned");
+    if (pages->max_pages_per_seq < 1 || pages->num_pages < 1)
+        return fail(FD_ERR_INVALID, "max_pages_per_seq %d and num_pages %d must be >= 1", pages->max_pages_per_seq,
+                    pages->num_pages);
+    const int32_t P = pages->page_size;
+    if (P < 16 || (P & (P - 1)) != 0)
+        return fail(FD_ERR_UNSUPPORTED, "page_size %d is not a power of two >= 16", P);
+    if (pages->layout != FD_PAGES_NHD && pages->layout != FD_PAGES_HND)
+        return fail(FD_ERR_UNSUPPORTED, "page layout %d unknown", pages->layout);
+    if ((int64_t)pages->max_pages_per_seq * P != d->max_cache_len)
+        return fail(FD_ERR_INVALID, "max_cache_len %d != max_pages_per_seq %d x page_size %d", d->max_cache_len,
+                    pages->max_pages_per_seq, P);
+    if (rule->tile_len > 0 && rule->tile_len % 16 != 0)
+        return fail(FD_ERR_INVALID, "plan tile_len %d is not a multiple of 16 (paged caches)", rule->tile_len);
+    const int64_t D = d->head_dim, H = d->num_kv_heads;
+    const int64_t page_elems = (int64_t)P * H * D;
+    if ((int64_t)pages->num_pages * page_elems > ((int64_t)1 << 46))
+        return fail(FD_ERR_UNSUPPORTED, "page pool too large");
+    rule->granule = 16;
+    pk->table = pages->block_table;
+    pk->max_pages = pages->max_pages_per_seq;
+    pk->num_pages = pages->num_pages;
+    int shift = 0;
+    while ((1 << shift) < P) ++shift;
+    pk->page_shift = shift;
+    pk->page_stride = page_elems;
+    if (pages->layout == FD_PAGES_NHD) {
+        pk->row_stride = (int32_t)(H * D);
+        pk->head_stride = D;
+    } else {
+        pk->row_stride = (int32_t)D;
+        pk->head_stride = (int64_t)P * D;
+    }
+    return FD_OK;
+}
+
+// The two passes of the operation over contiguous (pk == nullptr) or paged
+// caches.
+fd_status run_attention(const fd_dims* dims, const void* q, const void* k_cache, const void* v_cache,
+                        const fd_kv_pages* pages, const int32_t* cache_lens, float scale, int32_t num_splits,
+                        const fd_plan* plan, void* workspace, uint64_t workspace_bytes, void* out, float* lse,
+                        void* stream) {
     clear_error();
     fd_status st = check_dims(dims);
     if (st != FD_OK) return st;
     fdk::SplitRule rule;
     if ((st = resolve_rule(num_splits, plan, &rule)) != FD_OK) return st;
+    fdk::PagedKV pk{};
+    if (pages && (st = resolve_pages(dims, pages, &rule, &pk)) != FD_OK) return st;
     if (dims->batch == 0) return FD_OK;
     if ((st = check_tensors(dims, q, k_cache, v_cache, cache_lens)) != FD_OK) return st;
     if (!out) return fail(FD_ERR_INVALID, "out is NULL");
@@ -310,6 +359,7 @@ fd_status fd_decode_attention(const fd_dims* dims, const void* q, const void* k_
     if (lse && misaligned(lse, 4)) return fail(FD_ERR_INVALID, "lse must be 4-byte aligned");
     hipStream_t s = static_cast<hipStream_t>(stream);
     fdk::PartialArgs a = make_args(dims, q, k_cache, v_cache, cache_lens, scale, rule);
+    a.pages = pk;
     if (rule.slots == 1) {
         a.out = out;
         a.lse = lse;
@@ -334,6 +384,31 @@ fd_status fd_decode_attention(const fd_dims* dims, const void* q, const void* k_
     return device_status(fdk::launch_combine(dims->head_dim, dims->dtype, total_rows(dims), rule.slots,
                                              a.o_part, a.lse_part, out, lse, s),
                          "combine kernel launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+fd_status fd_decode_attention(const fd_dims* dims, const void* q, const void* k_cache,
+                              const void* v_cache, const int32_t* cache_lens, float scale,
+                              int32_t num_splits, const fd_plan* plan, void* workspace,
+                              uint64_t workspace_bytes, void* out, float* lse, void* stream) {
+    return run_attention(dims, q, k_cache, v_cache, nullptr, cache_lens, scale, num_splits, plan, workspace,
+                         workspace_bytes, out, lse, stream);
+}
+
+fd_status fd_decode_attention_paged(const fd_dims* dims, const void* q, const void* k_pages,
+                                    const void* v_pages, const fd_kv_pages* pages,
+                                    const int32_t* cache_lens, float scale, int32_t num_splits,
+                                    const fd_plan* plan, void* workspace, uint64_t workspace_bytes,
+                                    void* out, float* lse, void* stream) {
+    if (!pages) {
+        clear_error();
+        return fail(FD_ERR_INVALID, "pages is NULL");
+    }
+    return run_attention(dims, q, k_pages, v_pages, pages, cache_lens, scale, num_splits, plan, workspace,
+                         workspace_bytes, out, lse, stream);
 }
 
 }  // extern "C"

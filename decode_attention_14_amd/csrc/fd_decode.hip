@@ -145,7 +145,7 @@ struct StepBuf {
     Slice<BF16> v[U];
 };
 
-template <bool BF16, int D, int ROWS, bool CAUSAL>
+template <bool BF16, int D, int ROWS, bool CAUSAL, bool PAGED>
 __global__ __launch_bounds__(kPThreads) FD_OCCUPANCY void fd_partial_kernel(PartialArgs a) {
     using S16 = Slice<BF16>;
     constexpr int E = S16::E;             // elements per lane per row slice
@@ -246,12 +246,27 @@ __global__ __launch_bounds__(kPThreads) FD_OCCUPANCY void fd_partial_kernel(Part
 
     // Each step reads through a buffer resource covering the rest of the
     // tile from that step on: the base and range are scalars, the lane
-    // offset is fixed, and the per-instruction offsets are immediates.
-    const int64_t tile_row = ((int64_t)b * a.Hkv + g) * a.Lmax + lo;
-    const char* kt = uniform(static_cast<const char*>(a.k) + tile_row * ROWB);
-    const char* vt = uniform(static_cast<const char*>(a.v) + tile_row * ROWB);
+    // offset is fixed, and the per-instruction offsets are immediates.  A
+    // paged cache takes one resource per load instruction instead, over the
+    // KPI rows it reads from their page.
+    constexpr int ESZ = BF16 ? 2 : 4;
+    const char* kt;
+    const char* vt;
+    const int32_t* tbl = nullptr;
+    int rsb = ROWB;  // bytes from one key row of the head to the next
+    if constexpr (PAGED) {
+        kt = uniform(static_cast<const char*>(a.k) + g * a.pages.head_stride * ESZ);
+        vt = uniform(static_cast<const char*>(a.v) + g * a.pages.head_stride * ESZ);
+        tbl = a.pages.table + (int64_t)b * a.pages.max_pages;
+        rsb = a.pages.row_stride * ESZ;
+    } else {
+        const int64_t tile_row = ((int64_t)b * a.Hkv + g) * a.Lmax + lo;
+        kt = uniform(static_cast<const char*>(a.k) + tile_row * ROWB);
+        vt = uniform(static_cast<const char*>(a.v) + tile_row * ROWB);
+    }
     const uint32_t tile_bytes = uniform((uint32_t)(hi - lo) * (uint32_t)ROWB);
-    const uint32_t lane_off = (uint32_t)((w * WKEYS + grp) * ROWB + pos * 16);
+    const uint32_t lane_off = PAGED ? (uint32_t)(grp * rsb + pos * 16)
+                                    : (uint32_t)((w * WKEYS + grp) * ROWB + pos * 16);
     const int lane_key = lo + w * WKEYS + grp;  // key of (step 0, u 0) for this lane
     const int nsteps = (hi - lo + KSTEP - 1) / KSTEP;
 
@@ -259,12 +274,21 @@ __global__ __launch_bounds__(kPThreads) FD_OCCUPANCY void fd_partial_kernel(Part
     auto load = [&](Buf& x, int step) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            // Scalar arithmetic only (tile_bytes < 2^31): bytes of the tile
-            // left from this instruction's first row on, or 0 past its end.
-            const int done = (int)uniform((uint32_t)step) * (int)SBYTES + u * (int)UBYTES;
-            const int left = max((int)tile_bytes - done, 0);
-            buffer_slice<BF16>(x.k[u], tile_rsrc(kt + done, (uint32_t)left), lane_off);
-            buffer_slice<BF16>(x.v[u], tile_rsrc(vt + done, (uint32_t)left), lane_off);
+            if constexpr (PAGED) {
+                const int key0 = lo + (int)uniform((uint32_t)step) * KSTEP + w * WKEYS + u * KPI;
+                int64_t off;
+                const uint32_t n = paged_rows(a.pages, tbl, key0, KPI, hi, rsb, ROWB, &off);
+                buffer_slice<BF16>(x.k[u], tile_rsrc(kt + off * ESZ, n), lane_off);
+                buffer_slice<BF16>(x.v[u], tile_rsrc(vt + off * ESZ, n), lane_off);
+            } else {
+                // Scalar arithmetic only (tile_bytes < 2^31): bytes of the
+                // tile left from this instruction's first row on, or 0 past
+                // its end.
+                const int done = (int)uniform((uint32_t)step) * (int)SBYTES + u * (int)UBYTES;
+                const int left = max((int)tile_bytes - done, 0);
+                buffer_slice<BF16>(x.k[u], tile_rsrc(kt + done, (uint32_t)left), lane_off);
+                buffer_slice<BF16>(x.v[u], tile_rsrc(vt + done, (uint32_t)left), lane_off);
+            }
         }
     };
 
@@ -471,25 +495,32 @@ int vector_block_rows(int rows) {
     return 8;
 }
 
-template <bool BF16, int D, bool CAUSAL>
+template <bool BF16, int D, bool CAUSAL, bool PAGED>
 void launch_partials_c(int batch, const PartialArgs& a, hipStream_t stream) {
     const int rpb = vector_block_rows(a.rows);
     dim3 grid(a.rule.slots, a.Hkv * a.row_blocks, batch);
     dim3 block(kPThreads);
     switch (rpb) {
-        case 1: hipLaunchKernelGGL((fd_partial_kernel<BF16, D, 1, CAUSAL>), grid, block, 0, stream, a); break;
-        case 2: hipLaunchKernelGGL((fd_partial_kernel<BF16, D, 2, CAUSAL>), grid, block, 0, stream, a); break;
-        case 4: hipLaunchKernelGGL((fd_partial_kernel<BF16, D, 4, CAUSAL>), grid, block, 0, stream, a); break;
-        default: hipLaunchKernelGGL((fd_partial_kernel<BF16, D, 8, CAUSAL>), grid, block, 0, stream, a); break;
+        case 1: hipLaunchKernelGGL((fd_partial_kernel<BF16, D, 1, CAUSAL, PAGED>), grid, block, 0, stream, a); break;
+        case 2: hipLaunchKernelGGL((fd_partial_kernel<BF16, D, 2, CAUSAL, PAGED>), grid, block, 0, stream, a); break;
+        case 4: hipLaunchKernelGGL((fd_partial_kernel<BF16, D, 4, CAUSAL, PAGED>), grid, block, 0, stream, a); break;
+        default: hipLaunchKernelGGL((fd_partial_kernel<BF16, D, 8, CAUSAL, PAGED>), grid, block, 0, stream, a); break;
     }
 }
 
+// bf16 caches go to the matrix-core kernels whenever those apply (every
+// supported head_dim), so the paged variants exist for fp32 only.
 template <bool BF16, int D>
 hipError_t launch_partials_d(int batch, const PartialArgs& a, hipStream_t stream) {
-    if (a.q_len > 1)
-        launch_partials_c<BF16, D, true>(batch, a, stream);
-    else
-        launch_partials_c<BF16, D, false>(batch, a, stream);
+    const bool paged = a.pages.table != nullptr;
+    if (paged && BF16) return hipErrorNotSupported;
+    if (a.q_len > 1) {
+        if (paged) launch_partials_c<BF16, D, true, !BF16>(batch, a, stream);
+        else launch_partials_c<BF16, D, true, false>(batch, a, stream);
+    } else {
+        if (paged) launch_partials_c<BF16, D, false, !BF16>(batch, a, stream);
+        else launch_partials_c<BF16, D, false, false>(batch, a, stream);
+    }
     return hipGetLastError();
 }
 

@@ -50,12 +50,33 @@ static __device__ __forceinline__ float group_sum(float x) {
 }
 
 static __device__ __forceinline__ void tile_of(const SplitRule& r, int L, int s, int& lo, int& hi, int& S) {
-    int T = r.tile_len > 0 ? r.tile_len : (L + r.num_splits - 1) / r.num_splits;
+    int T = r.tile_len;
+    if (T <= 0) {
+        T = (L + r.num_splits - 1) / r.num_splits;
+        T = (T + r.granule - 1) / r.granule * r.granule;
+    }
     if (T < 1) T = 1;
     S = (L + T - 1) / T;
     if (S > r.slots) S = r.slots;
     lo = s * T;
     hi = (s == S - 1) ? L : min(L, lo + T);
+}
+
+// Rows [key0, key0 + nkeys) of one KV head of a paged cache, cut at `hi`:
+// sets *off to the element offset of row key0 from the head's base and
+// returns the byte range that covers the rows below hi ((rows - 1) * rsb +
+// rowb), or 0 when there are none or the page id lies outside the pool (then
+// every row reads as zeros).  The rows must lie in one page: nkeys divides
+// the page size and key0 is a multiple of nkeys.
+static __device__ __forceinline__ uint32_t paged_rows(const PagedKV& pk, const int32_t* tbl, int key0, int nkeys, int hi,
+                                               int rsb, int rowb, int64_t* off) {
+    *off = 0;
+    const int nrow = min(nkeys, hi - key0);
+    if (nrow <= 0) return 0u;
+    const int page = tbl[key0 >> pk.page_shift];
+    if ((uint32_t)page >= (uint32_t)pk.num_pages) return 0u;
+    *off = (int64_t)page * pk.page_stride + (int64_t)(key0 & ((1 << pk.page_shift) - 1)) * pk.row_stride;
+    return (uint32_t)((nrow - 1) * rsb + rowb);
 }
 
 // Wave-uniform copies (scalar registers) of values the compiler cannot prove

@@ -9,12 +9,32 @@ namespace fdk {
 
 // How the keys [0, L_b) of sequence b are cut into tiles.
 //   tile_len > 0 : tiles of tile_len keys;
-//   tile_len == 0: num_splits tiles of ceil(L_b / num_splits) keys.
+//   tile_len == 0: num_splits tiles of ceil(L_b / num_splits) keys, rounded
+//                  up to a multiple of `granule` (1 for contiguous caches;
+//                  16 for paged ones, so a 16-key block never straddles a
+//                  page).
 // At most `slots` tiles; if more would be needed the last tile takes the rest.
 struct SplitRule {
     int32_t tile_len;
     int32_t num_splits;
     int32_t slots;
+    int32_t granule;
+};
+
+// Where the K/V rows of a paged cache live.  Key j of sequence b, KV head g
+// is row (j mod page_size) of page table[b * max_pages + j / page_size], at
+// element offset page * page_stride + (j mod page_size) * row_stride +
+// g * head_stride of k (and v).  page_size is a power of two >= 16.  A table
+// entry outside [0, num_pages) is never dereferenced: its keys read as zero
+// rows.
+struct PagedKV {
+    const int32_t* table;  // [B, max_pages] device; nullptr: contiguous caches
+    int32_t max_pages;
+    int32_t num_pages;
+    int32_t page_shift;    // log2(page_size)
+    int32_t row_stride;    // elements
+    int64_t page_stride;   // elements
+    int64_t head_stride;   // elements
 };
 
 struct PartialArgs {
@@ -33,6 +53,7 @@ struct PartialArgs {
     SplitRule rule;
     float qk_scale;     // scale * log2(e): scores are kept in base 2
     int32_t direct;     // 1: single slot, write out/lse instead of partials
+    PagedKV pages;      // pages.table == nullptr: k/v are [B, Hkv, Lmax, D]
 };
 
 // Query rows one workgroup of the partial pass serves, for calls with `rows`

@@ -160,6 +160,23 @@ __device__ __forceinline__ void load_block(const char* kp, const char* vp, int l
     }
 }
 
+// Start the loads of the wave's block `blk` of the tile [lo, hi) into dst:
+// contiguous caches address the tile directly (kt/vt: its first row);
+// paged caches look the block's page up (kt/vt: the KV head's base).
+template <int D, bool PAGED>
+__device__ __forceinline__ void load_block_at(const PagedKV& pk, const int32_t* tbl, const char* kt, const char* vt,
+                                              int lo, int hi, int blk, int rsb, char* dst, const uint32_t* dma_off) {
+    using G = Geo<D>;
+    if constexpr (PAGED) {
+        int64_t off;
+        const uint32_t n = paged_rows(pk, tbl, lo + blk * kKB, kKB, hi, rsb, G::ROWB, &off);
+        load_block<D>(kt + off * 2, vt + off * 2, (int)n, dst, dma_off);
+    } else {
+        const int off = blk * G::BLKB;
+        load_block<D>(kt + off, vt + off, (hi - lo) * G::ROWB - off, dst, dma_off);
+    }
+}
+
 // The math of one 16-key block for NB blocks of 16 query rows, given the
 // block's K fragments (A operand of S^T = K Q^T) and transposed V fragments
 // (A operand of O^T = V^T P^T) in registers.  Lane (group grp, column q)
@@ -236,7 +253,7 @@ __device__ __forceinline__ void load_fragments(const char* kb, const char* vb, b
     lds_settle(vf);
 }
 
-template <int D, int NB, bool CAUSAL>
+template <int D, int NB, bool CAUSAL, bool PAGED>
 __global__ __launch_bounds__(kMT) void fd_mfma_partial_kernel(PartialArgs a) {
     using G = Geo<D>;
     constexpr int NR = 16 * NB;  // query rows per workgroup
@@ -324,10 +341,21 @@ __global__ __launch_bounds__(kMT) void fd_mfma_partial_kernel(PartialArgs a) {
     }
 
     char* ring = smem + w * G::WAVEB;
-    const int64_t tile_row = ((int64_t)b * a.Hkv + g) * a.Lmax + lo;
-    const char* kt = static_cast<const char*>(a.k) + tile_row * G::ROWB;
-    const char* vt = static_cast<const char*>(a.v) + tile_row * G::ROWB;
-    const int tile_bytes = (hi - lo) * G::ROWB;
+    const char* kt;
+    const char* vt;
+    int rsb;  // bytes from one key row of the head to the next
+    const int32_t* tbl = nullptr;
+    if constexpr (PAGED) {
+        kt = static_cast<const char*>(a.k) + g * a.pages.head_stride * 2;
+        vt = static_cast<const char*>(a.v) + g * a.pages.head_stride * 2;
+        rsb = a.pages.row_stride * 2;
+        tbl = a.pages.table + (int64_t)b * a.pages.max_pages;
+    } else {
+        const int64_t tile_row = ((int64_t)b * a.Hkv + g) * a.Lmax + lo;
+        kt = static_cast<const char*>(a.k) + tile_row * G::ROWB;
+        vt = static_cast<const char*>(a.v) + tile_row * G::ROWB;
+        rsb = G::ROWB;
+    }
     const int nblk = (hi - lo + kKB - 1) / kKB;
     const int nw = w < nblk ? (nblk - w + kMW - 1) / kMW : 0;
 
@@ -338,21 +366,19 @@ __global__ __launch_bounds__(kMT) void fd_mfma_partial_kernel(PartialArgs a) {
     for (int i = 0; i < G::IPB; ++i) {
         const int r = i * G::RPI + lane / G::CH;
         const int cg = (lane % G::CH) ^ swf<G::CH>(r);
-        dma_off[i] = (uint32_t)(r * G::ROWB + cg * 16);
+        dma_off[i] = (uint32_t)(r * rsb + cg * 16);
     }
 
     // Wave block j is tile block w + 4j and goes to ring slot j % kNS.
 #pragma unroll
-    for (int j = 0; j < kNS - 1; ++j) {
-        const int off = (w + j * kMW) * G::BLKB;
-        load_block<D>(kt + off, vt + off, tile_bytes - off, ring + j * G::STAGEB, dma_off);
-    }
+    for (int j = 0; j < kNS - 1; ++j)
+        load_block_at<D, PAGED>(a.pages, tbl, kt, vt, lo, hi, w + j * kMW, rsb, ring + j * G::STAGEB, dma_off);
 
     for (int j = 0; j < nw; ++j) {
         {
             const int jn = j + kNS - 1;
-            const int off = (w + jn * kMW) * G::BLKB;
-            load_block<D>(kt + off, vt + off, tile_bytes - off, ring + (jn % kNS) * G::STAGEB, dma_off);
+            load_block_at<D, PAGED>(a.pages, tbl, kt, vt, lo, hi, w + jn * kMW, rsb, ring + (jn % kNS) * G::STAGEB,
+                                    dma_off);
         }
         wait_vmcnt_le<(kNS - 1) * 2 * G::IPB>();  // block j has landed
         const char* kb = ring + (j % kNS) * G::STAGEB;
@@ -510,6 +536,34 @@ __device__ __forceinline__ void chunk_load_stage(const char* kt, const char* vt,
                                                  FD_LOAD_AUX);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)(dst + G::SKB * G::BLKB + lds_off[k]), 16,
                                                  dma_off[k], 0, 0, FD_LOAD_AUX);
+    }
+}
+
+// Stage j of the tile [lo, kend) into dst.  Contiguous caches: kt/vt point
+// at the tile's first row and one buffer range covers the stage.  Paged
+// caches: kt/vt point at the KV head's base and each load instruction looks
+// up the page of its RPI rows (koff[k]: the instruction's first key within
+// the stage).
+template <int D, bool PAGED>
+__device__ __forceinline__ void chunk_stage_at(const PagedKV& pk, const int32_t* tbl, const char* kt, const char* vt,
+                                               int lo, int kend, int j, int rsb, char* dst, const uint32_t* dma_off,
+                                               const int* lds_off, const int* koff) {
+    using G = CGeo<D>;
+    if constexpr (PAGED) {
+#pragma unroll
+        for (int k = 0; k < G::DPW; ++k) {
+            int64_t off;
+            const uint32_t n = paged_rows(pk, tbl, lo + j * G::SKEYS + koff[k], G::RPI, kend, rsb, G::ROWB, &off);
+            const __amdgpu_buffer_rsrc_t rk = tile_rsrc(kt + off * 2, n);
+            const __amdgpu_buffer_rsrc_t rv = tile_rsrc(vt + off * 2, n);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t*)(dst + lds_off[k]), 16, dma_off[k], 0, 0,
+                                                     FD_LOAD_AUX);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)(dst + G::SKB * G::BLKB + lds_off[k]), 16,
+                                                     dma_off[k], 0, 0, FD_LOAD_AUX);
+        }
+    } else {
+        const int off = j * G::SKEYS * G::ROWB;
+        chunk_load_stage<D>(kt, vt, (kend - lo) * G::ROWB - off, off, dst, dma_off, lds_off);
     }
 }
 
@@ -686,7 +740,7 @@ __device__ __forceinline__ void chunk_step(bool edge, const uint32_t (&ka)[CGeo<
     if (lo) chunk_pv<D>(vf, pl, acc);
 }
 
-template <int D>
+template <int D, bool PAGED>
 __global__ __launch_bounds__(kCT) void fd_mfma_chunk_kernel(PartialArgs a) {
     using G = CGeo<D>;
     constexpr int RS = D + 4;  // padded row stride of the merge area (floats)
@@ -773,14 +827,28 @@ __global__ __launch_bounds__(kCT) void fd_mfma_chunk_kernel(PartialArgs a) {
         for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
     float m = -INFINITY, l = 0.f, mx = -INFINITY;
 
-    const int64_t tile_row = ((int64_t)b * a.Hkv + g) * a.Lmax + lo;
-    const char* kt = static_cast<const char*>(a.k) + tile_row * G::ROWB;
-    const char* vt = static_cast<const char*>(a.v) + tile_row * G::ROWB;
-    const int tile_bytes = (kend - lo) * G::ROWB;
+    const char* kt;
+    const char* vt;
+    int rsb;  // bytes from one key row of the head to the next
+    const int32_t* tbl = nullptr;
+    if constexpr (PAGED) {
+        kt = static_cast<const char*>(a.k) + g * a.pages.head_stride * 2;
+        vt = static_cast<const char*>(a.v) + g * a.pages.head_stride * 2;
+        rsb = a.pages.row_stride * 2;
+        tbl = a.pages.table + (int64_t)b * a.pages.max_pages;
+    } else {
+        const int64_t tile_row = ((int64_t)b * a.Hkv + g) * a.Lmax + lo;
+        kt = static_cast<const char*>(a.k) + tile_row * G::ROWB;
+        vt = static_cast<const char*>(a.v) + tile_row * G::ROWB;
+        rsb = G::ROWB;
+    }
     const int nst = (kend - lo + G::SKEYS - 1) / G::SKEYS;
 
+    // Load instruction k of this wave fills RPI rows of block bb of a stage;
+    // lane l takes row l / CH, global chunk (l % CH) ^ swizzle.
     uint32_t dma_off[G::DPW];
     int lds_off[G::DPW];
+    int koff[G::DPW];
 #pragma unroll
     for (int k = 0; k < G::DPW; ++k) {
         const int n = w + k * kCW;
@@ -788,7 +856,8 @@ __global__ __launch_bounds__(kCT) void fd_mfma_chunk_kernel(PartialArgs a) {
         const int i = n - bb * G::IPB;
         const int r = i * G::RPI + lane / G::CH;
         const int cg = (lane % G::CH) ^ swf<G::CH>(r);
-        dma_off[k] = (uint32_t)((bb * kCBK + r) * G::ROWB + cg * 16);
+        koff[k] = bb * kCBK + i * G::RPI;
+        dma_off[k] = (uint32_t)((PAGED ? lane / G::CH : koff[k] + lane / G::CH) * rsb + cg * 16);
         lds_off[k] = bb * G::BLKB + i * 1024;
     }
 
@@ -814,8 +883,7 @@ __global__ __launch_bounds__(kCT) void fd_mfma_chunk_kernel(PartialArgs a) {
 
 #pragma unroll
     for (int j = 0; j < kCNS - 1; ++j)
-        chunk_load_stage<D>(kt, vt, tile_bytes - j * G::SKEYS * G::ROWB, j * G::SKEYS * G::ROWB, smem + j * G::STGB,
-                            dma_off, lds_off);
+        chunk_stage_at<D, PAGED>(a.pages, tbl, kt, vt, lo, kend, j, rsb, smem + j * G::STGB, dma_off, lds_off, koff);
 
     // Stage j lives in ring slot j % kCNS; unrolling by kCNS makes the slot,
     // and so every LDS offset, a compile-time constant.  A wave whose block
@@ -831,11 +899,8 @@ __global__ __launch_bounds__(kCT) void fd_mfma_chunk_kernel(PartialArgs a) {
             if (j >= nst) break;
             wait_vmcnt_le<(kCNS - 1) * 2 * G::DPW>();  // this wave's loads of stage j
             __syncthreads();                           // everyone's; stage j - 1 is free
-            {
-                const int jn = j + kCNS - 1;
-                chunk_load_stage<D>(kt, vt, tile_bytes - jn * G::SKEYS * G::ROWB, jn * G::SKEYS * G::ROWB,
-                                    smem + ((u + kCNS - 1) % kCNS) * G::STGB, dma_off, lds_off);
-            }
+            chunk_stage_at<D, PAGED>(a.pages, tbl, kt, vt, lo, kend, j + kCNS - 1, rsb,
+                                     smem + ((u + kCNS - 1) % kCNS) * G::STGB, dma_off, lds_off, koff);
             const int key0 = lo + j * G::SKEYS + kh * kCBK;
             const bool edge = key0 + kCBK > mask_from;
             if (u == 0) chunk_step<D, 0>(edge, ka, va, qf, acc, vf, ph, m, l, mx, key0, rend, c, hl);
@@ -923,10 +988,18 @@ __global__ __launch_bounds__(kCT) void fd_mfma_chunk_kernel(PartialArgs a) {
 template <int D, int NB>
 void launch_nb(int batch, const PartialArgs& a, hipStream_t stream) {
     dim3 grid(a.rule.slots, a.Hkv, batch), block(kMT);
-    if (a.q_len > 1)
-        hipLaunchKernelGGL((fd_mfma_partial_kernel<D, NB, true>), grid, block, 0, stream, a);
-    else
-        hipLaunchKernelGGL((fd_mfma_partial_kernel<D, NB, false>), grid, block, 0, stream, a);
+    const bool paged = a.pages.table != nullptr;
+    if (a.q_len > 1) {
+        if (paged)
+            hipLaunchKernelGGL((fd_mfma_partial_kernel<D, NB, true, true>), grid, block, 0, stream, a);
+        else
+            hipLaunchKernelGGL((fd_mfma_partial_kernel<D, NB, true, false>), grid, block, 0, stream, a);
+    } else {
+        if (paged)
+            hipLaunchKernelGGL((fd_mfma_partial_kernel<D, NB, false, true>), grid, block, 0, stream, a);
+        else
+            hipLaunchKernelGGL((fd_mfma_partial_kernel<D, NB, false, false>), grid, block, 0, stream, a);
+    }
 }
 
 }  // namespace
@@ -940,10 +1013,18 @@ int mfma_block_rows(int rows) { return rows <= 32 ? rows : kChunkRows; }
 hipError_t launch_partials_mfma(int head_dim, int batch, const PartialArgs& a, hipStream_t stream) {
     if (a.rows > 32) {
         dim3 grid(a.rule.slots, a.Hkv * a.row_blocks, batch), block(kCT);
-        if (head_dim == 64)
-            hipLaunchKernelGGL((fd_mfma_chunk_kernel<64>), grid, block, 0, stream, a);
-        else
-            hipLaunchKernelGGL((fd_mfma_chunk_kernel<128>), grid, block, 0, stream, a);
+        const bool paged = a.pages.table != nullptr;
+        if (head_dim == 64) {
+            if (paged)
+                hipLaunchKernelGGL((fd_mfma_chunk_kernel<64, true>), grid, block, 0, stream, a);
+            else
+                hipLaunchKernelGGL((fd_mfma_chunk_kernel<64, false>), grid, block, 0, stream, a);
+        } else {
+            if (paged)
+                hipLaunchKernelGGL((fd_mfma_chunk_kernel<128, true>), grid, block, 0, stream, a);
+            else
+                hipLaunchKernelGGL((fd_mfma_chunk_kernel<128, false>), grid, block, 0, stream, a);
+        }
         return hipGetLastError();
     }
     const bool two = a.rows > 16;

@@ -122,3 +122,59 @@ def as_oracle_array(t: torch.Tensor) -> np.ndarray:
     if t.dtype == torch.float32:
         return t.numpy()
     raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+@dataclass(frozen=True)
+class PagedCache:
+    """A paged K/V cache built from contiguous caches (CPU tensors).
+
+    ``k_pages``/``v_pages``: ``[num_pages, page_size, Hkv, D]`` ("nhd") or
+    ``[num_pages, Hkv, page_size, D]`` ("hnd"); ``block_table`` ``[B, Lmax /
+    page_size]`` int32, -1 where a sequence has no page.
+    """
+    k_pages: torch.Tensor
+    v_pages: torch.Tensor
+    block_table: torch.Tensor
+    page_size: int
+    layout: str
+
+
+def paginate(k: torch.Tensor, v: torch.Tensor, cache_lens, page_size: int, layout: str = "nhd",
+             seed: int = 0, spare_pages: int = 3) -> PagedCache:
+    """Scatter contiguous caches ``[B, Hkv, Lmax, D]`` into a shuffled page pool.
+
+    Sequence b gets ceil(L_b / page_size) pages; page ids are a seeded random
+    permutation of the pool (``Generator(PCG64(seed)).permutation``), which
+    also holds ``spare_pages`` pages no sequence uses.  Rows of a page at or
+    past L_b and every spare page are filled with NaN, so a kernel that reads
+    them cannot go unnoticed.  Data movement only.
+    """
+    if layout not in ("nhd", "hnd"):
+        raise ValueError(f"unknown layout {layout!r}")
+    B, H, Lmax, D = k.shape
+    if Lmax % page_size:
+        raise ValueError("Lmax must be a multiple of page_size")
+    lens = [int(x) for x in torch.as_tensor(cache_lens).tolist()]
+    counts = [-(-L // page_size) for L in lens]
+    num_pages = sum(counts) + spare_pages
+    perm = np.random.Generator(np.random.PCG64(seed)).permutation(num_pages)
+    table = torch.full((B, Lmax // page_size), -1, dtype=torch.int32)
+    shape = (num_pages, page_size, H, D) if layout == "nhd" else (num_pages, H, page_size, D)
+    kp = torch.full(shape, float("nan"), dtype=k.dtype)
+    vp = torch.full(shape, float("nan"), dtype=v.dtype)
+    nxt = 0
+    for b in range(B):
+        for i in range(counts[b]):
+            pid = int(perm[nxt])
+            nxt += 1
+            table[b, i] = pid
+            lo, hi = i * page_size, min(lens[b], (i + 1) * page_size)
+            src_k = k[b, :, lo:hi, :]  # [H, rows, D]
+            src_v = v[b, :, lo:hi, :]
+            if layout == "nhd":
+                kp[pid, : hi - lo] = src_k.permute(1, 0, 2)
+                vp[pid, : hi - lo] = src_v.permute(1, 0, 2)
+            else:
+                kp[pid, :, : hi - lo] = src_k
+                vp[pid, :, : hi - lo] = src_v
+    return PagedCache(kp, vp, table, page_size, layout)

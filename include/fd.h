@@ -164,6 +164,57 @@ fd_status fd_decode_attention(const fd_dims* dims, const void* q, const void* k_
                               int32_t num_splits, const fd_plan* plan, void* workspace,
                               uint64_t workspace_bytes, void* out, float* lse, void* stream);
 
+/* Paged K/V caches.
+ *
+ * Page "FlashDecoding算法原理与多GPU并行解码实战" (deployment engineering
+ * details, item 1) names the PagedAttention cache layout, pages of page_size
+ * keys by num_kv_heads by head_dim, and notes that a split-KV kernel needing
+ * contiguous sequences pays for a page-to-contiguous copy before attention;
+ * the same page's section on combining methods pairs paged caches with the
+ * split-KV method.  The paged entry point below reads the pages in place:
+ * no copy.
+ *
+ * k_pages and v_pages hold num_pages pages of page_size keys each, laid out
+ *   FD_PAGES_NHD: [num_pages, page_size, Hkv, D]  (the page's layout)
+ *   FD_PAGES_HND: [num_pages, Hkv, page_size, D]
+ * block_table [B, max_pages_per_seq] int32 (device memory): key j of
+ * sequence b lives in page block_table[b][j / page_size], row
+ * j mod page_size.  Only the entries for keys below cache_lens[b] are read.
+ * An entry outside [0, num_pages) is never dereferenced: its keys read as
+ * zero vectors (score 0, value 0) -- callers must not rely on that, it only
+ * keeps a bad table from reading outside the pool.
+ * page_size is a power of two, at least 16. */
+typedef enum fd_page_layout { FD_PAGES_NHD = 0, FD_PAGES_HND = 1 } fd_page_layout;
+
+typedef struct fd_kv_pages {
+    const int32_t* block_table;  /* device [B, max_pages_per_seq] */
+    int32_t max_pages_per_seq;   /* >= 1 */
+    int32_t page_size;           /* keys per page: power of two, >= 16 */
+    int32_t num_pages;           /* pages in k_pages and v_pages, >= 1 */
+    int32_t layout;              /* fd_page_layout */
+} fd_kv_pages;
+
+/* fd_decode_attention_paged -- fd_decode_attention over a paged cache.
+ *
+ * Same operation, arguments and conventions as fd_decode_attention, with
+ * k_pages / v_pages / pages in place of k_cache / v_cache.
+ * dims->max_cache_len must equal max_pages_per_seq * page_size (the
+ * capacity of a sequence; cache_lens are clamped into [0, capacity] on the
+ * device).  Tiles start at multiples of 16 keys: a plan's tile_len must be a
+ * multiple of 16 (fd_plan_splits gives multiples of 64), and with a forced
+ * num_splits the tile is ceil(L_b / num_splits) rounded up to a multiple of
+ * 16, which may give fewer tiles.  Plans and workspace sizes are those of
+ * fd_plan_splits / fd_workspace_bytes for the same dims.
+ * Errors: as fd_decode_attention; FD_ERR_INVALID for a NULL pages or
+ * block_table, bad page counts or sizes, or max_cache_len mismatch;
+ * FD_ERR_UNSUPPORTED for page sizes that are not powers of two >= 16 or an
+ * unknown layout. */
+fd_status fd_decode_attention_paged(const fd_dims* dims, const void* q, const void* k_pages,
+                                    const void* v_pages, const fd_kv_pages* pages,
+                                    const int32_t* cache_lens, float scale, int32_t num_splits,
+                                    const fd_plan* plan, void* workspace, uint64_t workspace_bytes,
+                                    void* out, float* lse, void* stream);
+
 /* Diagnostics.  fd_status_string returns a static name for a status.
  * fd_last_error returns the message of the last failed call on this thread
  * ("" if none); the pointer stays valid until the next call on the thread. */

@@ -172,3 +172,40 @@ def merge_lse(o_part, lse_part, lib=None):
     rc = lib.orc_merge_lse(rows, S, D, _ptr(o_part), _ptr(lse_part), _ptr(out), _ptr(lse))
     _check(rc, "merge_lse")
     return out, lse
+
+
+def gather_pages(pages, block_table, cache_lens, layout: str = "nhd"):
+    """Contiguous ``[B, Hkv, Lmax, D]`` copy of a paged cache, key by key.
+
+    ``pages``: ``[num_pages, page_size, Hkv, D]`` (layout "nhd", the page
+    layout named in page "FlashDecoding算法原理与多GPU并行解码实战",
+    deployment engineering details item 1) or ``[num_pages, Hkv, page_size, D]``
+    ("hnd").  Key j of sequence b is row ``j % page_size`` of page
+    ``block_table[b, j // page_size]``; ``Lmax = block_table.shape[1] *
+    page_size``.  Keys at or past ``cache_lens[b]`` are left zero (the
+    attention never reads them).
+    """
+    pages = np.asarray(pages)
+    table = np.asarray(block_table)
+    if layout == "nhd":
+        _, P, H, D = pages.shape
+    elif layout == "hnd":
+        _, H, P, D = pages.shape
+    else:
+        raise ValueError(f"unknown layout {layout!r}")
+    B, max_pages = table.shape
+    out = np.zeros((B, H, max_pages * P, D), pages.dtype)
+    for b in range(B):
+        for j in range(int(cache_lens[b])):
+            page, row = int(table[b, j // P]), j % P
+            out[b, :, j, :] = pages[page, row, :, :] if layout == "nhd" else pages[page, :, row, :]
+    return out
+
+
+def attention_paged(q, k_pages, v_pages, block_table, cache_lens, scale, layout: str = "nhd",
+                    nthreads: int = 0, lib=None):
+    """The plain definition over a paged cache: gather, then ``attention``."""
+    lens = np.asarray(cache_lens, dtype=np.int32)
+    k = gather_pages(k_pages, block_table, lens, layout)
+    v = gather_pages(v_pages, block_table, lens, layout)
+    return attention(q, k, v, lens, scale, nthreads=nthreads, lib=lib)

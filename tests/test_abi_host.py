@@ -261,3 +261,48 @@ def test_workspace_layout_size():
     rows = 3 * 32
     expect = _up(rows * S * 128 * 4) + 2 * _up(rows * S * 4)
     assert fd.workspace_bytes(d, S) == expect
+
+
+def call_paged(lib, d, pages, num_splits=0, plan=None, ws=None, ws_bytes=0):
+    q, k, v, lens, o, lse = FAKE[:6]
+    return lib.fd_decode_attention_paged(ctypes.byref(d), q, k, v,
+                                         ctypes.byref(pages) if pages is not None else None, lens,
+                                         ctypes.c_float(0.1), num_splits,
+                                         ctypes.byref(plan) if plan is not None else None, ws, ws_bytes,
+                                         o, lse, None)
+
+
+def test_paged_rejects_bad_page_descriptions(lib):
+    d = dims(Lmax=64)  # 4 pages of 16 keys
+    ok = dict(block_table=FAKE[7].value, max_pages_per_seq=4, page_size=16, num_pages=10,
+              layout=fd.FD_PAGES_NHD)
+
+    def pages(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return fd.FdKvPages(**a)
+
+    assert call_paged(lib, d, None) == fd.FD_ERR_INVALID
+    assert call_paged(lib, d, pages(block_table=None)) == fd.FD_ERR_INVALID
+    assert call_paged(lib, d, pages(block_table=0x100002)) == fd.FD_ERR_INVALID
+    assert call_paged(lib, d, pages(num_pages=0)) == fd.FD_ERR_INVALID
+    assert call_paged(lib, d, pages(max_pages_per_seq=0)) == fd.FD_ERR_INVALID
+    assert call_paged(lib, d, pages(max_pages_per_seq=3)) == fd.FD_ERR_INVALID  # 48 != 64
+    assert "max_cache_len" in lib.fd_last_error().decode()
+    assert call_paged(lib, fd.make_dims(1, 32, 8, 128, 1, 96, fd.FD_BF16),
+                      pages(page_size=24, max_pages_per_seq=4)) == fd.FD_ERR_UNSUPPORTED
+    assert call_paged(lib, fd.make_dims(1, 32, 8, 128, 1, 32, fd.FD_BF16),
+                      pages(page_size=8)) == fd.FD_ERR_UNSUPPORTED
+    assert call_paged(lib, d, pages(layout=2)) == fd.FD_ERR_UNSUPPORTED
+    # tiles must start at multiples of 16 keys
+    assert call_paged(lib, d, pages(), plan=fd.FdPlan(tile_len=40, max_splits=2)) == fd.FD_ERR_INVALID
+    # the common checks still apply
+    assert call_paged(lib, dims(D=96, Lmax=64), pages()) == fd.FD_ERR_UNSUPPORTED
+    assert call_paged(lib, d, pages(), num_splits=4) == fd.FD_ERR_WORKSPACE
+
+
+def test_paged_empty_batch_is_a_no_op(lib):
+    d = dims(B=0, Lmax=64)
+    pages = fd.FdKvPages(FAKE[7].value, 4, 16, 10, fd.FD_PAGES_HND)
+    assert lib.fd_decode_attention_paged(ctypes.byref(d), None, None, None, ctypes.byref(pages), None,
+                                         ctypes.c_float(1.0), 0, None, None, 0, None, None, None) == fd.FD_OK
