@@ -13,6 +13,10 @@ synchronisations and events on the stream the kernels run on.  The K/V caches
 rotate over several identical copies (>= 1 GiB in total) so that the 256 MB
 last-level cache cannot hold them and every step reads HBM.
 
+``--page-size P`` runs the same workload on a paged cache (pages of P keys in
+a shuffled pool, read in place through the block table; ``--page-layout``
+picks [pages, P, Hkv, D] or [pages, Hkv, P, D]).
+
 Printed: one JSON line with the metric (algorithmic GB/s per step: the bytes
 any implementation must move -- K, V, q, out, lse -- over the step time), the
 roofline of the dominant kernel (the partial pass, timed per launch over a
@@ -61,6 +65,9 @@ def parse_args():
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of a graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target oracle time")
+    ap.add_argument("--page-size", type=int, default=0,
+                    help="read K/V from a paged cache with pages of this many keys (0: contiguous)")
+    ap.add_argument("--page-layout", default="nhd", choices=["nhd", "hnd"])
     ap.add_argument("--calibrate-copy", type=int, default=0,
                     help="also run N plain 512 MiB device copies (counter calibration)")
     return ap.parse_args()
@@ -127,7 +134,7 @@ def main():
     import torch
 
     from decode_attention_14_amd import binding as fd
-    from decode_attention_14_amd.inputs import WORKLOADS, workload_inputs
+    from decode_attention_14_amd.inputs import WORKLOADS, paginate, workload_inputs
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -149,6 +156,13 @@ def main():
     num_splits = args.num_splits
     slots = num_splits if num_splits else plan.max_splits
 
+    paged = args.page_size > 0
+    table = None
+    if paged:
+        print(f"[bench] paging the cache: {args.page_size}-key pages, {args.page_layout}", file=sys.stderr,
+              flush=True)
+        pc = paginate(k, v, cl, args.page_size, args.page_layout, seed=w.seed)
+        k, v, table = pc.k_pages, pc.v_pages, pc.block_table.to(dev)
     copies = int(min(8, max(2, math.ceil((1 << 30) / max(1, 2 * k.numel() * k.element_size())))))
     qd, cld = q.to(dev), cl.to(dev)
     kd0, vd0 = k.to(dev), v.to(dev)
@@ -156,7 +170,7 @@ def main():
     del q, k, v
     out = torch.empty_like(qd)
     lse = torch.empty(qd.shape[:3], dtype=torch.float32, device=dev)
-    dims = fd.dims_of(qd, kd0)
+    dims = fd.paged_dims(qd, kd0, table, args.page_layout)[0] if paged else fd.dims_of(qd, kd0)
     ws_bytes = fd.workspace_bytes(dims, slots) if slots > 1 else 0
     ws = fd.new_workspace(ws_bytes, dev)
     o_part = torch.empty(*qd.shape[:3], slots, w.head_dim, dtype=torch.float32, device=dev)
@@ -166,12 +180,24 @@ def main():
 
     def step(i):
         kd, vd = kvs[i % copies]
-        fd.decode_attention(qd, kd, vd, cld, scale=w.scale, num_splits=num_splits, plan=fplan,
-                            out=out, lse=lse, workspace=ws if ws_bytes else None)
+        if paged:
+            fd.decode_attention_paged(qd, kd, vd, table, cld, layout=args.page_layout, scale=w.scale,
+                                      num_splits=num_splits, plan=fplan, out=out, lse=lse,
+                                      workspace=ws if ws_bytes else None)
+        else:
+            fd.decode_attention(qd, kd, vd, cld, scale=w.scale, num_splits=num_splits, plan=fplan,
+                                out=out, lse=lse, workspace=ws if ws_bytes else None)
 
     def partial(i):
         kd, vd = kvs[i % copies]
-        if slots > 1:
+        if paged and slots > 1:
+            fd.decode_partials_paged(qd, kd, vd, table, cld, layout=args.page_layout, scale=w.scale,
+                                     num_splits=num_splits, plan=fplan, o_part=o_part, m_part=m_part,
+                                     lse_part=l_part)
+        elif paged:
+            fd.decode_attention_paged(qd, kd, vd, table, cld, layout=args.page_layout, scale=w.scale,
+                                      out=out, lse=lse)
+        elif slots > 1:
             fd.decode_partials(qd, kd, vd, cld, scale=w.scale, num_splits=num_splits, plan=fplan,
                                o_part=o_part, m_part=m_part, lse_part=l_part)
         else:
@@ -222,7 +248,8 @@ def main():
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
         try:
-            t = json.load(open(TRAFFIC_FILE)).get(w.name)
+            t = json.load(open(TRAFFIC_FILE)).get(w.name + (f"/paged{args.page_size}{args.page_layout}"
+                                                            if paged else ""))
             if t and t.get("kernel_hash") == kernel_source_hash() and t.get("tile_len") == plan.tile_len:
                 traffic = t.get("bytes_per_launch")
         except (OSError, ValueError):
@@ -255,6 +282,7 @@ def main():
             "cache_lens": "fixed %d" % lens[0] if len(set(lens)) == 1 else "U%s sum %d" % (
                 list(w.len_range), sum(lens)),
             "tile_len": plan.tile_len, "splits": slots, "kv_copies": copies,
+            "kv_cache": f"paged, {args.page_size}-key pages, {args.page_layout}" if paged else "contiguous",
             "step_bytes": step_bytes, "timing": "eager" if args.no_graph else "graph",
         },
         "kernels": {"partial_us": round(part_ms * 1e3, 3), "combine_us": round(comb_ms * 1e3, 3)},

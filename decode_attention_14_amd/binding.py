@@ -24,8 +24,8 @@ FD_MAX_SPLITS = 256
 FD_PAGES_NHD, FD_PAGES_HND = 0, 1
 
 EXPORTS = ("fd_plan_splits", "fd_workspace_bytes", "fd_decode_partials", "fd_combine_splits",
-           "fd_decode_attention", "fd_decode_attention_paged", "fd_status_string", "fd_last_error",
-           "fd_version")
+           "fd_decode_attention", "fd_decode_attention_paged", "fd_decode_partials_paged",
+           "fd_status_string", "fd_last_error", "fd_version")
 
 
 class FdDims(ctypes.Structure):
@@ -86,6 +86,9 @@ def load_library(path: str | None = None):
     lib.fd_decode_attention_paged.argtypes = [dims_p, vp, vp, vp, ctypes.POINTER(FdKvPages), vp,
                                               ctypes.c_float, i32, plan_p, vp, u64, vp, vp, vp]
     lib.fd_decode_attention_paged.restype = i32
+    lib.fd_decode_partials_paged.argtypes = [dims_p, vp, vp, vp, ctypes.POINTER(FdKvPages), vp,
+                                             ctypes.c_float, i32, plan_p, vp, vp, vp, vp]
+    lib.fd_decode_partials_paged.restype = i32
     lib.fd_status_string.argtypes = [i32]
     lib.fd_status_string.restype = ctypes.c_char_p
     lib.fd_last_error.argtypes = []
@@ -317,6 +320,22 @@ def paged_dims(q: torch.Tensor, k_pages: torch.Tensor, block_table: torch.Tensor
     return make_dims(B, Hq, Hkv, D, q_len, block_table.shape[1] * P, q.dtype), P
 
 
+def _paged_args(q, k_pages, v_pages, block_table, cache_lens, layout):
+    dims, P = paged_dims(q, k_pages, block_table, layout)
+    if v_pages.shape != k_pages.shape:
+        raise FdError(FD_ERR_INVALID, f"v_pages {tuple(v_pages.shape)} != k_pages {tuple(k_pages.shape)}")
+    if not (q.dtype == k_pages.dtype == v_pages.dtype):
+        raise FdError(FD_ERR_INVALID, "q, k_pages and v_pages must share one dtype")
+    if block_table.dtype != torch.int32:
+        raise FdError(FD_ERR_INVALID, "block_table must be int32")
+    if cache_lens.dtype != torch.int32 or cache_lens.shape != (q.shape[0],):
+        raise FdError(FD_ERR_INVALID, "cache_lens must be int32 of shape [B]")
+    if len({t.device for t in (q, k_pages, v_pages, block_table, cache_lens)}) != 1:
+        raise FdError(FD_ERR_INVALID, "all tensors must be on one device")
+    pages = FdKvPages(block_table.data_ptr(), block_table.shape[1], P, k_pages.shape[0], _LAYOUTS[layout])
+    return dims, pages
+
+
 def decode_attention_paged(q, k_pages, v_pages, block_table, cache_lens, layout: str = "nhd",
                            scale=None, num_splits: int = 0, plan: Plan | FdPlan | None = None,
                            out=None, lse=None, workspace=None):
@@ -330,17 +349,7 @@ def decode_attention_paged(q, k_pages, v_pages, block_table, cache_lens, layout:
     """
     lib = load_library()
     _require_cuda(q, k_pages, v_pages, block_table, cache_lens, out, lse, workspace)
-    dims, P = paged_dims(q, k_pages, block_table, layout)
-    if v_pages.shape != k_pages.shape:
-        raise FdError(FD_ERR_INVALID, f"v_pages {tuple(v_pages.shape)} != k_pages {tuple(k_pages.shape)}")
-    if not (q.dtype == k_pages.dtype == v_pages.dtype):
-        raise FdError(FD_ERR_INVALID, "q, k_pages and v_pages must share one dtype")
-    if block_table.dtype != torch.int32:
-        raise FdError(FD_ERR_INVALID, "block_table must be int32")
-    if cache_lens.dtype != torch.int32 or cache_lens.shape != (q.shape[0],):
-        raise FdError(FD_ERR_INVALID, "cache_lens must be int32 of shape [B]")
-    if len({t.device for t in (q, k_pages, v_pages, block_table, cache_lens)}) != 1:
-        raise FdError(FD_ERR_INVALID, "all tensors must be on one device")
+    dims, pages = _paged_args(q, k_pages, v_pages, block_table, cache_lens, layout)
     _check_buffer(out, q.shape, q.dtype, "out")
     _check_buffer(lse, q.shape[:3], torch.float32, "lse")
     fp = plan.plan if isinstance(plan, Plan) else plan
@@ -353,7 +362,6 @@ def decode_attention_paged(q, k_pages, v_pages, block_table, cache_lens, layout:
     if workspace is None and ws_bytes:
         workspace = new_workspace(ws_bytes, q.device)
     given = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    pages = FdKvPages(block_table.data_ptr(), block_table.shape[1], P, k_pages.shape[0], _LAYOUTS[layout])
     _check(lib.fd_decode_attention_paged(ctypes.byref(dims), _ptr(q), _ptr(k_pages), _ptr(v_pages),
                                          ctypes.byref(pages), _ptr(cache_lens),
                                          ctypes.c_float(_default_scale(q.shape[-1], scale)),
@@ -361,3 +369,32 @@ def decode_attention_paged(q, k_pages, v_pages, block_table, cache_lens, layout:
                                          _ptr(workspace), given, _ptr(out), _ptr(lse),
                                          _stream(q.device)))
     return out, lse
+
+
+def decode_partials_paged(q, k_pages, v_pages, block_table, cache_lens, layout: str = "nhd", scale=None,
+                          num_splits: int = 0, plan: Plan | FdPlan | None = None, o_part=None, m_part=None,
+                          lse_part=None):
+    """First pass only, over a paged cache: (o_part, m_part, lse_part) as decode_partials."""
+    lib = load_library()
+    _require_cuda(q, k_pages, v_pages, block_table, cache_lens, o_part, m_part, lse_part)
+    dims, pages = _paged_args(q, k_pages, v_pages, block_table, cache_lens, layout)
+    fp = plan.plan if isinstance(plan, Plan) else plan
+    slots = num_splits if num_splits > 0 else (fp.max_splits if fp is not None else 0)
+    if slots < 1:
+        raise FdError(FD_ERR_INVALID, "decode_partials_paged needs num_splits > 0 or a plan")
+    B, Hq, T, D = q.shape
+    _check_buffer(o_part, (B, Hq, T, slots, D), torch.float32, "o_part")
+    _check_buffer(m_part, (B, Hq, T, slots), torch.float32, "m_part")
+    _check_buffer(lse_part, (B, Hq, T, slots), torch.float32, "lse_part")
+    if o_part is None:
+        o_part = torch.empty(B, Hq, T, slots, D, dtype=torch.float32, device=q.device)
+    if m_part is None:
+        m_part = torch.empty(B, Hq, T, slots, dtype=torch.float32, device=q.device)
+    if lse_part is None:
+        lse_part = torch.empty(B, Hq, T, slots, dtype=torch.float32, device=q.device)
+    _check(lib.fd_decode_partials_paged(ctypes.byref(dims), _ptr(q), _ptr(k_pages), _ptr(v_pages),
+                                        ctypes.byref(pages), _ptr(cache_lens),
+                                        ctypes.c_float(_default_scale(D, scale)), int(num_splits),
+                                        ctypes.byref(fp) if fp is not None else None, _ptr(o_part),
+                                        _ptr(m_part), _ptr(lse_part), _stream(q.device)))
+    return o_part, m_part, lse_part

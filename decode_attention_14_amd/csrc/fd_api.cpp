@@ -243,17 +243,24 @@ fd_status fd_plan_splits(const fd_dims* dims, const int32_t* cache_lens_host, in
     return FD_OK;
 }
 
-fd_status fd_decode_partials(const fd_dims* dims, const void* q, const void* k_cache,
-                             const void* v_cache, const int32_t* cache_lens, float scale,
-                             int32_t num_splits, const fd_plan* plan, float* o_part,
-                             float* m_part, float* lse_part, void* stream) {
+}  // extern "C"
+
+namespace {
+
+fd_status resolve_pages(const fd_dims* d, const fd_kv_pages* pages, fdk::SplitRule* rule, fdk::PagedKV* pk);
+
+fd_status run_partials(const fd_dims* dims, const void* q, const void* k_cache, const void* v_cache,
+                       const fd_kv_pages* pages, const int32_t* cache_lens, float scale, int32_t num_splits,
+                       const fd_plan* plan, float* o_part, float* m_part, float* lse_part, void* stream) {
     clear_error();
     fd_status st = check_dims(dims);
     if (st != FD_OK) return st;
     if (num_splits == 0 && !plan)
-        return fail(FD_ERR_INVALID, "fd_decode_partials needs num_splits > 0 or a plan");
+        return fail(FD_ERR_INVALID, "the partial pass needs num_splits > 0 or a plan");
     fdk::SplitRule rule;
     if ((st = resolve_rule(num_splits, plan, &rule)) != FD_OK) return st;
+    fdk::PagedKV pk{};
+    if (pages && (st = resolve_pages(dims, pages, &rule, &pk)) != FD_OK) return st;
     if (dims->batch == 0) return FD_OK;
     if ((st = check_tensors(dims, q, k_cache, v_cache, cache_lens)) != FD_OK) return st;
     if (!o_part || !m_part || !lse_part)
@@ -261,6 +268,7 @@ fd_status fd_decode_partials(const fd_dims* dims, const void* q, const void* k_c
     if (misaligned(o_part, 16) || misaligned(m_part, 4) || misaligned(lse_part, 4))
         return fail(FD_ERR_INVALID, "o_part must be 16-byte aligned, m_part and lse_part 4-byte aligned");
     fdk::PartialArgs a = make_args(dims, q, k_cache, v_cache, cache_lens, scale, rule);
+    a.pages = pk;
     a.o_part = o_part;
     a.m_part = m_part;
     a.lse_part = lse_part;
@@ -268,6 +276,31 @@ fd_status fd_decode_partials(const fd_dims* dims, const void* q, const void* k_c
     return device_status(fdk::launch_partials(dims->dtype, dims->head_dim, dims->batch, a,
                                               static_cast<hipStream_t>(stream)),
                          "partial kernel launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+fd_status fd_decode_partials(const fd_dims* dims, const void* q, const void* k_cache,
+                             const void* v_cache, const int32_t* cache_lens, float scale,
+                             int32_t num_splits, const fd_plan* plan, float* o_part,
+                             float* m_part, float* lse_part, void* stream) {
+    return run_partials(dims, q, k_cache, v_cache, nullptr, cache_lens, scale, num_splits, plan, o_part, m_part,
+                        lse_part, stream);
+}
+
+fd_status fd_decode_partials_paged(const fd_dims* dims, const void* q, const void* k_pages,
+                                   const void* v_pages, const fd_kv_pages* pages,
+                                   const int32_t* cache_lens, float scale, int32_t num_splits,
+                                   const fd_plan* plan, float* o_part, float* m_part, float* lse_part,
+                                   void* stream) {
+    if (!pages) {
+        clear_error();
+        return fail(FD_ERR_INVALID, "pages is NULL");
+    }
+    return run_partials(dims, q, k_pages, v_pages, pages, cache_lens, scale, num_splits, plan, o_part, m_part,
+                        lse_part, stream);
 }
 
 fd_status fd_combine_splits(int32_t batch, int32_t num_heads, int32_t q_len, int32_t head_dim,

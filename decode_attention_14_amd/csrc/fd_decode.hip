@@ -275,7 +275,7 @@ __global__ __launch_bounds__(kPThreads) FD_OCCUPANCY void fd_partial_kernel(Part
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             if constexpr (PAGED) {
-                const int key0 = lo + (int)uniform((uint32_t)step) * KSTEP + w * WKEYS + u * KPI;
+                const int key0 = (int)uniform((uint32_t)(lo + step * KSTEP + w * WKEYS + u * KPI));
                 int64_t off;
                 const uint32_t n = paged_rows(a.pages, tbl, key0, KPI, hi, rsb, ROWB, &off);
                 buffer_slice<BF16>(x.k[u], tile_rsrc(kt + off * ESZ, n), lane_off);

@@ -62,21 +62,40 @@ static __device__ __forceinline__ void tile_of(const SplitRule& r, int L, int s,
     hi = (s == S - 1) ? L : min(L, lo + T);
 }
 
-// Rows [key0, key0 + nkeys) of one KV head of a paged cache, cut at `hi`:
-// sets *off to the element offset of row key0 from the head's base and
-// returns the byte range that covers the rows below hi ((rows - 1) * rsb +
-// rowb), or 0 when there are none or the page id lies outside the pool (then
-// every row reads as zeros).  The rows must lie in one page: nkeys divides
-// the page size and key0 is a multiple of nkeys.
-static __device__ __forceinline__ uint32_t paged_rows(const PagedKV& pk, const int32_t* tbl, int key0, int nkeys, int hi,
-                                               int rsb, int rowb, int64_t* off) {
+// Entry i of a block table row, read through the scalar cache: the table
+// does not change during a kernel, and a vector load here would make the
+// compiler wait for every load in flight (vmcnt counts in order) before the
+// page's own loads can issue.  i must be wave-uniform.
+static __device__ __forceinline__ int page_id(const int32_t* tbl, int i) {
+    typedef const __attribute__((address_space(4))) int32_t* const_ptr;
+    return ((const_ptr)(reinterpret_cast<uintptr_t>(tbl)))[i];
+}
+
+// Page id of the rows from key0 on (a wave-uniform key), or -1 if key0 is
+// at or past hi: then nothing is read, not even the table entry.
+static __device__ __forceinline__ int page_at(const PagedKV& pk, const int32_t* tbl, int key0, int hi) {
+    return key0 < hi ? page_id(tbl, key0 >> pk.page_shift) : -1;
+}
+
+// Rows [key0, key0 + nkeys) of one KV head of a paged cache held by page
+// `page`, cut at `hi`: sets *off to the element offset of row key0 from the
+// head's base and returns the byte range that covers the rows below hi
+// ((rows - 1) * rsb + rowb), or 0 when there are none or the page id lies
+// outside the pool (then every row reads as zeros).  The rows must lie in
+// one page: nkeys divides the page size and key0 is a multiple of nkeys.
+static __device__ __forceinline__ uint32_t paged_rows_in(const PagedKV& pk, int page, int key0, int nkeys, int hi,
+                                                         int rsb, int rowb, int64_t* off) {
     *off = 0;
     const int nrow = min(nkeys, hi - key0);
-    if (nrow <= 0) return 0u;
-    const int page = tbl[key0 >> pk.page_shift];
-    if ((uint32_t)page >= (uint32_t)pk.num_pages) return 0u;
+    if (nrow <= 0 || (uint32_t)page >= (uint32_t)pk.num_pages) return 0u;
     *off = (int64_t)page * pk.page_stride + (int64_t)(key0 & ((1 << pk.page_shift) - 1)) * pk.row_stride;
     return (uint32_t)((nrow - 1) * rsb + rowb);
+}
+
+// The same, looking the page up in the table row tbl.
+static __device__ __forceinline__ uint32_t paged_rows(const PagedKV& pk, const int32_t* tbl, int key0, int nkeys,
+                                                      int hi, int rsb, int rowb, int64_t* off) {
+    return paged_rows_in(pk, page_at(pk, tbl, key0, hi), key0, nkeys, hi, rsb, rowb, off);
 }
 
 // Wave-uniform copies (scalar registers) of values the compiler cannot prove

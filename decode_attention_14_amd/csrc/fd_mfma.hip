@@ -162,14 +162,14 @@ __device__ __forceinline__ void load_block(const char* kp, const char* vp, int l
 
 // Start the loads of the wave's block `blk` of the tile [lo, hi) into dst:
 // contiguous caches address the tile directly (kt/vt: its first row);
-// paged caches look the block's page up (kt/vt: the KV head's base).
+// paged caches read the block from page `page` (kt/vt: the KV head's base).
 template <int D, bool PAGED>
-__device__ __forceinline__ void load_block_at(const PagedKV& pk, const int32_t* tbl, const char* kt, const char* vt,
-                                              int lo, int hi, int blk, int rsb, char* dst, const uint32_t* dma_off) {
+__device__ __forceinline__ void load_block_at(const PagedKV& pk, int page, const char* kt, const char* vt, int lo,
+                                              int hi, int blk, int rsb, char* dst, const uint32_t* dma_off) {
     using G = Geo<D>;
     if constexpr (PAGED) {
         int64_t off;
-        const uint32_t n = paged_rows(pk, tbl, lo + blk * kKB, kKB, hi, rsb, G::ROWB, &off);
+        const uint32_t n = paged_rows_in(pk, page, lo + blk * kKB, kKB, hi, rsb, G::ROWB, &off);
         load_block<D>(kt + off * 2, vt + off * 2, (int)n, dst, dma_off);
     } else {
         const int off = blk * G::BLKB;
@@ -369,15 +369,22 @@ __global__ __launch_bounds__(kMT) void fd_mfma_partial_kernel(PartialArgs a) {
         dma_off[i] = (uint32_t)(r * rsb + cg * 16);
     }
 
-    // Wave block j is tile block w + 4j and goes to ring slot j % kNS.
+    // Wave block j is tile block w + 4j and goes to ring slot j % kNS.  A
+    // paged cache's page ids are read one block ahead of their loads, so the
+    // scalar table reads overlap the work of the previous block.
+    auto page_of = [&](int blk) { return PAGED ? page_at(a.pages, tbl, lo + blk * kKB, hi) : 0; };
 #pragma unroll
     for (int j = 0; j < kNS - 1; ++j)
-        load_block_at<D, PAGED>(a.pages, tbl, kt, vt, lo, hi, w + j * kMW, rsb, ring + j * G::STAGEB, dma_off);
+        load_block_at<D, PAGED>(a.pages, page_of(w + j * kMW), kt, vt, lo, hi, w + j * kMW, rsb,
+                                ring + j * G::STAGEB, dma_off);
+    int page_next = page_of(w + (kNS - 1) * kMW);
 
     for (int j = 0; j < nw; ++j) {
         {
             const int jn = j + kNS - 1;
-            load_block_at<D, PAGED>(a.pages, tbl, kt, vt, lo, hi, w + jn * kMW, rsb, ring + (jn % kNS) * G::STAGEB,
+            const int page = page_next;
+            page_next = page_of(w + (jn + 1) * kMW);
+            load_block_at<D, PAGED>(a.pages, page, kt, vt, lo, hi, w + jn * kMW, rsb, ring + (jn % kNS) * G::STAGEB,
                                     dma_off);
         }
         wait_vmcnt_le<(kNS - 1) * 2 * G::IPB>();  // block j has landed

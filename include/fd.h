@@ -215,6 +215,15 @@ fd_status fd_decode_attention_paged(const fd_dims* dims, const void* q, const vo
                                     const fd_plan* plan, void* workspace, uint64_t workspace_bytes,
                                     void* out, float* lse, void* stream);
 
+/* fd_decode_partials_paged -- fd_decode_partials over a paged cache: the
+ * first pass alone, with the page arguments and rules of
+ * fd_decode_attention_paged and the outputs of fd_decode_partials. */
+fd_status fd_decode_partials_paged(const fd_dims* dims, const void* q, const void* k_pages,
+                                   const void* v_pages, const fd_kv_pages* pages,
+                                   const int32_t* cache_lens, float scale, int32_t num_splits,
+                                   const fd_plan* plan, float* o_part, float* m_part, float* lse_part,
+                                   void* stream);
+
 /* Diagnostics.  fd_status_string returns a static name for a status.
  * fd_last_error returns the message of the last failed call on this thread
  * ("" if none); the pointer stays valid until the next call on the thread. */

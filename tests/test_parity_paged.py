@@ -122,3 +122,30 @@ def test_paged_headline_shape():
     torch.cuda.synchronize()
     assert torch.equal(_bits(out), _bits(co))
     assert torch.equal(lse, cls)
+
+
+@pytest.mark.parametrize("layout", ["nhd", "hnd"])
+def test_paged_partials(layout):
+    """The first pass alone over pages: every tile's partials against the
+    oracle's split form, and bit-equal to the contiguous first pass."""
+    say(f"[case] paged partials {layout}")
+    lens = [1000, 77, 0, 640]
+    q, k, v, cl = inputs(4, 8, 2, 128, 1, 1024, "bf16", 2500, lens)
+    pc = paginate(k, v, cl, 32, layout, seed=2501)
+    plan = fd.FdPlan(tile_len=256, max_splits=4)
+    sc = _scale(128)
+    o_p, m_p, l_p = fd.decode_partials_paged(q.cuda(), pc.k_pages.cuda(), pc.v_pages.cuda(), pc.block_table.cuda(),
+                                             cl.cuda(), layout=layout, scale=sc, plan=plan)
+    co, cm, cl_ = fd.decode_partials(q.cuda(), k.cuda(), v.cuda(), cl.cuda(), scale=sc, plan=plan)
+    torch.cuda.synchronize()
+    _, _, ro, rm, rl = oracle.attention_split(as_oracle_array(q), as_oracle_array(k), as_oracle_array(v),
+                                              cl.numpy(), sc, tile_len=256, slots=4)
+    gm, gl = m_p.cpu().double().numpy(), l_p.cpu().double().numpy()
+    assert np.array_equal(np.isinf(gl), np.isinf(rl)) and np.array_equal(np.isinf(gm), np.isinf(rm))
+    fin = np.isfinite(rl)
+    assert np.max(np.abs(gm[fin] - rm[fin])) <= TOL["bf16"]
+    assert np.max(np.abs(gl[fin] - rl[fin])) <= TOL["bf16"]
+    assert np.max(np.abs(o_p.cpu().double().numpy()[fin] - ro[fin])) <= TOL["bf16"]
+    assert torch.equal(m_p, cm) and torch.equal(l_p, cl_)
+    fin_t = torch.from_numpy(fin).cuda()
+    assert torch.equal(o_p[fin_t], co[fin_t])
