@@ -13,7 +13,8 @@ synchronisations and events on the stream the kernels run on.  The K/V caches
 rotate over several identical copies (>= 1 GiB in total) so that the 256 MB
 last-level cache cannot hold them and every step reads HBM.
 
-``--page-size P`` runs the same workload on a paged cache (pages of P keys in
+``--kv-fp8`` quantises K and V to FP8 E4M3 codes with per-tensor scales (bf16
+queries and output).  ``--page-size P`` runs the same workload on a paged cache (pages of P keys in
 a shuffled pool, read in place through the block table; ``--page-layout``
 picks [pages, P, Hkv, D] or [pages, Hkv, P, D]).
 
@@ -68,15 +69,17 @@ def parse_args():
     ap.add_argument("--page-size", type=int, default=0,
                     help="read K/V from a paged cache with pages of this many keys (0: contiguous)")
     ap.add_argument("--page-layout", default="nhd", choices=["nhd", "hnd"])
+    ap.add_argument("--kv-fp8", action="store_true",
+                    help="FP8 E4M3 K/V caches (per-tensor scales) with bf16 queries")
     ap.add_argument("--calibrate-copy", type=int, default=0,
                     help="also run N plain 512 MiB device copies (counter calibration)")
     return ap.parse_args()
 
 
-def algorithmic_bytes(w, lens):
+def algorithmic_bytes(w, lens, kv_fp8=False):
     """Bytes any implementation must move: visible K and V rows, q, out, lse."""
     el = 2 if w.dtype == "bf16" else 4
-    kv = 2 * sum(lens) * w.num_kv_heads * w.head_dim * el
+    kv = 2 * sum(lens) * w.num_kv_heads * w.head_dim * (1 if kv_fp8 else el)
     q = w.batch * w.num_q_heads * w.q_len * w.head_dim * el
     return kv, q, q, w.batch * w.num_q_heads * w.q_len * 4
 
@@ -134,7 +137,7 @@ def main():
     import torch
 
     from decode_attention_14_amd import binding as fd
-    from decode_attention_14_amd.inputs import WORKLOADS, paginate, workload_inputs
+    from decode_attention_14_amd.inputs import WORKLOADS, fp8_scale_for, paginate, quantize_fp8, workload_inputs
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -146,11 +149,19 @@ def main():
     print(f"[bench] generating {w.name}", file=sys.stderr, flush=True)
     q, k, v, cl = workload_inputs(w)
     lens = cl.tolist()
-    kv_b, q_b, out_b, lse_b = algorithmic_bytes(w, lens)
+    fp8 = args.kv_fp8
+    if fp8:
+        if w.dtype != "bf16":
+            print("--kv-fp8 needs a bf16 workload", file=sys.stderr)
+            sys.exit(2)
+        k_scale, v_scale = fp8_scale_for(k), fp8_scale_for(v)
+        k, v = quantize_fp8(k, k_scale), quantize_fp8(v, v_scale)
+    kv_b, q_b, out_b, lse_b = algorithmic_bytes(w, lens, fp8)
     step_bytes = kv_b + q_b + out_b + lse_b
     partial_bytes = kv_b + q_b
 
-    plan = fd.plan_for(q, k, cl, num_splits=args.num_splits)
+    plan = fd.plan_splits(fd.make_dims(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.q_len,
+                                       w.max_cache_len, q.dtype), cl, num_splits=args.num_splits)
     if args.tile_len:
         plan = fd.Plan(fd.FdPlan(args.tile_len, max(1, -(-max(lens) // args.tile_len))), [])
     num_splits = args.num_splits
@@ -171,6 +182,7 @@ def main():
     out = torch.empty_like(qd)
     lse = torch.empty(qd.shape[:3], dtype=torch.float32, device=dev)
     dims = fd.paged_dims(qd, kd0, table, args.page_layout)[0] if paged else fd.dims_of(qd, kd0)
+    dims.dtype = fd.FD_BF16 if w.dtype == "bf16" else fd.FD_F32
     ws_bytes = fd.workspace_bytes(dims, slots) if slots > 1 else 0
     ws = fd.new_workspace(ws_bytes, dev)
     o_part = torch.empty(*qd.shape[:3], slots, w.head_dim, dtype=torch.float32, device=dev)
@@ -180,7 +192,11 @@ def main():
 
     def step(i):
         kd, vd = kvs[i % copies]
-        if paged:
+        if fp8:
+            fd.decode_attention_fp8(qd, kd, vd, cld, k_scale, v_scale, block_table=table, layout=args.page_layout,
+                                    scale=w.scale, num_splits=num_splits, plan=fplan, out=out, lse=lse,
+                                    workspace=ws if ws_bytes else None)
+        elif paged:
             fd.decode_attention_paged(qd, kd, vd, table, cld, layout=args.page_layout, scale=w.scale,
                                       num_splits=num_splits, plan=fplan, out=out, lse=lse,
                                       workspace=ws if ws_bytes else None)
@@ -190,7 +206,14 @@ def main():
 
     def partial(i):
         kd, vd = kvs[i % copies]
-        if paged and slots > 1:
+        if fp8 and slots > 1:
+            fd.decode_partials_fp8(qd, kd, vd, cld, k_scale, v_scale, block_table=table, layout=args.page_layout,
+                                   scale=w.scale, num_splits=num_splits, plan=fplan, o_part=o_part,
+                                   m_part=m_part, lse_part=l_part)
+        elif fp8:
+            fd.decode_attention_fp8(qd, kd, vd, cld, k_scale, v_scale, block_table=table, layout=args.page_layout,
+                                    scale=w.scale, out=out, lse=lse)
+        elif paged and slots > 1:
             fd.decode_partials_paged(qd, kd, vd, table, cld, layout=args.page_layout, scale=w.scale,
                                      num_splits=num_splits, plan=fplan, o_part=o_part, m_part=m_part,
                                      lse_part=l_part)
@@ -248,8 +271,8 @@ def main():
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
         try:
-            t = json.load(open(TRAFFIC_FILE)).get(w.name + (f"/paged{args.page_size}{args.page_layout}"
-                                                            if paged else ""))
+            t = json.load(open(TRAFFIC_FILE)).get(w.name + ("/fp8" if fp8 else "") +
+                                                  (f"/paged{args.page_size}{args.page_layout}" if paged else ""))
             if t and t.get("kernel_hash") == kernel_source_hash() and t.get("tile_len") == plan.tile_len:
                 traffic = t.get("bytes_per_launch")
         except (OSError, ValueError):
@@ -274,7 +297,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": w.dtype,
+        "dtype": (w.dtype + " q/out, fp8 e4m3 k/v") if fp8 else w.dtype,
         "data": "synthetic",
         "config": {
             "workload": w.name, "batch": w.batch, "q_heads": w.num_q_heads,
@@ -282,7 +305,8 @@ def main():
             "cache_lens": "fixed %d" % lens[0] if len(set(lens)) == 1 else "U%s sum %d" % (
                 list(w.len_range), sum(lens)),
             "tile_len": plan.tile_len, "splits": slots, "kv_copies": copies,
-            "kv_cache": f"paged, {args.page_size}-key pages, {args.page_layout}" if paged else "contiguous",
+            "kv_cache": (f"paged, {args.page_size}-key pages, {args.page_layout}" if paged else "contiguous") +
+                        (", fp8 e4m3 (per-tensor scales)" if fp8 else ""),
             "step_bytes": step_bytes, "timing": "eager" if args.no_graph else "graph",
         },
         "kernels": {"partial_us": round(part_ms * 1e3, 3), "combine_us": round(comb_ms * 1e3, 3)},
@@ -303,7 +327,9 @@ def main():
             "kernel": partial_kernel_name(w), "flops_per_launch": flops,
             "hbm_achieved_GBs": round(achieved, 2),
         }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and (fp8 or paged):
+        print("[bench] cpu baseline is timed on the contiguous bf16/fp32 workload only", file=sys.stderr)
+    elif not args.no_cpu_baseline:
         print("[bench] timing the fp64 oracle on host cores", file=sys.stderr, flush=True)
         qh, kh, vh, clh = workload_inputs(w)
         result["cpu_baseline"] = cpu_baseline(w, qh, kh, vh, clh, step_bytes, args.cpu_seconds)

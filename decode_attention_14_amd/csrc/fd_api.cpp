@@ -7,6 +7,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
@@ -249,12 +250,41 @@ namespace {
 
 fd_status resolve_pages(const fd_dims* d, const fd_kv_pages* pages, fdk::SplitRule* rule, fdk::PagedKV* pk);
 
+// Per-tensor fp8 dequantisation scales of a call with E4M3 caches.
+struct Fp8Scales {
+    float k_scale, v_scale;
+};
+
+// Checks of an fp8-cache call: bf16 queries, rows the decode kernel serves,
+// finite scales.
+fd_status check_fp8(const fd_dims* d, const Fp8Scales* f8) {
+    if (d->dtype != FD_BF16) return fail(FD_ERR_UNSUPPORTED, "fp8 caches need bf16 q and out (dims->dtype)");
+    const int64_t rows = (int64_t)d->num_q_heads / d->num_kv_heads * d->q_len;
+    if (rows > 32)
+        return fail(FD_ERR_UNSUPPORTED, "fp8 caches serve up to 32 query rows per KV head (n_rep x q_len = %lld)",
+                    (long long)rows);
+    if (!std::isfinite(f8->k_scale) || !std::isfinite(f8->v_scale))
+        return fail(FD_ERR_INVALID, "k_scale and v_scale must be finite");
+    return FD_OK;
+}
+
+void apply_fp8(fdk::PartialArgs* a, const Fp8Scales* f8, float scale) {
+    a->v_scale = 1.f;
+    a->kv_fp8 = 0;
+    if (!f8) return;
+    a->kv_fp8 = 1;
+    a->v_scale = f8->v_scale;
+    a->qk_scale = (float)((double)scale * f8->k_scale * kLog2e);
+}
+
 fd_status run_partials(const fd_dims* dims, const void* q, const void* k_cache, const void* v_cache,
-                       const fd_kv_pages* pages, const int32_t* cache_lens, float scale, int32_t num_splits,
-                       const fd_plan* plan, float* o_part, float* m_part, float* lse_part, void* stream) {
+                       const fd_kv_pages* pages, const Fp8Scales* f8, const int32_t* cache_lens, float scale,
+                       int32_t num_splits, const fd_plan* plan, float* o_part, float* m_part, float* lse_part,
+                       void* stream) {
     clear_error();
     fd_status st = check_dims(dims);
     if (st != FD_OK) return st;
+    if (f8 && (st = check_fp8(dims, f8)) != FD_OK) return st;
     if (num_splits == 0 && !plan)
         return fail(FD_ERR_INVALID, "the partial pass needs num_splits > 0 or a plan");
     fdk::SplitRule rule;
@@ -269,6 +299,7 @@ fd_status run_partials(const fd_dims* dims, const void* q, const void* k_cache, 
         return fail(FD_ERR_INVALID, "o_part must be 16-byte aligned, m_part and lse_part 4-byte aligned");
     fdk::PartialArgs a = make_args(dims, q, k_cache, v_cache, cache_lens, scale, rule);
     a.pages = pk;
+    apply_fp8(&a, f8, scale);
     a.o_part = o_part;
     a.m_part = m_part;
     a.lse_part = lse_part;
@@ -286,8 +317,8 @@ fd_status fd_decode_partials(const fd_dims* dims, const void* q, const void* k_c
                              const void* v_cache, const int32_t* cache_lens, float scale,
                              int32_t num_splits, const fd_plan* plan, float* o_part,
                              float* m_part, float* lse_part, void* stream) {
-    return run_partials(dims, q, k_cache, v_cache, nullptr, cache_lens, scale, num_splits, plan, o_part, m_part,
-                        lse_part, stream);
+    return run_partials(dims, q, k_cache, v_cache, nullptr, nullptr, cache_lens, scale, num_splits, plan, o_part,
+                        m_part, lse_part, stream);
 }
 
 fd_status fd_decode_partials_paged(const fd_dims* dims, const void* q, const void* k_pages,
@@ -299,7 +330,16 @@ fd_status fd_decode_partials_paged(const fd_dims* dims, const void* q, const voi
         clear_error();
         return fail(FD_ERR_INVALID, "pages is NULL");
     }
-    return run_partials(dims, q, k_pages, v_pages, pages, cache_lens, scale, num_splits, plan, o_part, m_part,
+    return run_partials(dims, q, k_pages, v_pages, pages, nullptr, cache_lens, scale, num_splits, plan, o_part,
+                        m_part, lse_part, stream);
+}
+
+fd_status fd_decode_partials_fp8(const fd_dims* dims, const void* q, const void* k_cache, const void* v_cache,
+                                 const fd_kv_pages* pages, float k_scale, float v_scale,
+                                 const int32_t* cache_lens, float scale, int32_t num_splits, const fd_plan* plan,
+                                 float* o_part, float* m_part, float* lse_part, void* stream) {
+    const Fp8Scales f8{k_scale, v_scale};
+    return run_partials(dims, q, k_cache, v_cache, pages, &f8, cache_lens, scale, num_splits, plan, o_part, m_part,
                         lse_part, stream);
 }
 
@@ -375,12 +415,13 @@ fd_status resolve_pages(const fd_dims* d, const fd_kv_pages* pages, fdk::SplitRu
 // The two passes of the operation over contiguous (pk == nullptr) or paged
 // caches.
 fd_status run_attention(const fd_dims* dims, const void* q, const void* k_cache, const void* v_cache,
-                        const fd_kv_pages* pages, const int32_t* cache_lens, float scale, int32_t num_splits,
-                        const fd_plan* plan, void* workspace, uint64_t workspace_bytes, void* out, float* lse,
-                        void* stream) {
+                        const fd_kv_pages* pages, const Fp8Scales* f8, const int32_t* cache_lens, float scale,
+                        int32_t num_splits, const fd_plan* plan, void* workspace, uint64_t workspace_bytes,
+                        void* out, float* lse, void* stream) {
     clear_error();
     fd_status st = check_dims(dims);
     if (st != FD_OK) return st;
+    if (f8 && (st = check_fp8(dims, f8)) != FD_OK) return st;
     fdk::SplitRule rule;
     if ((st = resolve_rule(num_splits, plan, &rule)) != FD_OK) return st;
     fdk::PagedKV pk{};
@@ -393,6 +434,7 @@ fd_status run_attention(const fd_dims* dims, const void* q, const void* k_cache,
     hipStream_t s = static_cast<hipStream_t>(stream);
     fdk::PartialArgs a = make_args(dims, q, k_cache, v_cache, cache_lens, scale, rule);
     a.pages = pk;
+    apply_fp8(&a, f8, scale);
     if (rule.slots == 1) {
         a.out = out;
         a.lse = lse;
@@ -427,8 +469,8 @@ fd_status fd_decode_attention(const fd_dims* dims, const void* q, const void* k_
                               const void* v_cache, const int32_t* cache_lens, float scale,
                               int32_t num_splits, const fd_plan* plan, void* workspace,
                               uint64_t workspace_bytes, void* out, float* lse, void* stream) {
-    return run_attention(dims, q, k_cache, v_cache, nullptr, cache_lens, scale, num_splits, plan, workspace,
-                         workspace_bytes, out, lse, stream);
+    return run_attention(dims, q, k_cache, v_cache, nullptr, nullptr, cache_lens, scale, num_splits, plan,
+                         workspace, workspace_bytes, out, lse, stream);
 }
 
 fd_status fd_decode_attention_paged(const fd_dims* dims, const void* q, const void* k_pages,
@@ -440,7 +482,16 @@ fd_status fd_decode_attention_paged(const fd_dims* dims, const void* q, const vo
         clear_error();
         return fail(FD_ERR_INVALID, "pages is NULL");
     }
-    return run_attention(dims, q, k_pages, v_pages, pages, cache_lens, scale, num_splits, plan, workspace,
+    return run_attention(dims, q, k_pages, v_pages, pages, nullptr, cache_lens, scale, num_splits, plan,
+                         workspace, workspace_bytes, out, lse, stream);
+}
+
+fd_status fd_decode_attention_fp8(const fd_dims* dims, const void* q, const void* k_cache, const void* v_cache,
+                                  const fd_kv_pages* pages, float k_scale, float v_scale,
+                                  const int32_t* cache_lens, float scale, int32_t num_splits, const fd_plan* plan,
+                                  void* workspace, uint64_t workspace_bytes, void* out, float* lse, void* stream) {
+    const Fp8Scales f8{k_scale, v_scale};
+    return run_attention(dims, q, k_cache, v_cache, pages, &f8, cache_lens, scale, num_splits, plan, workspace,
                          workspace_bytes, out, lse, stream);
 }
 

@@ -54,6 +54,8 @@ struct PartialArgs {
     float qk_scale;     // scale * log2(e): scores are kept in base 2
     int32_t direct;     // 1: single slot, write out/lse instead of partials
     PagedKV pages;      // pages.table == nullptr: k/v are [B, Hkv, Lmax, D]
+    int32_t kv_fp8;     // 1: k/v hold OCP E4M3 codes (bf16 q/out); k_scale is in qk_scale
+    float v_scale;      // fp8: value of V = code * v_scale (applied to the output)
 };
 
 // Query rows one workgroup of the partial pass serves, for calls with `rows`

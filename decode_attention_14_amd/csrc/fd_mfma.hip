@@ -68,8 +68,12 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 #ifndef FD_MFMA_THREADS
 #define FD_MFMA_THREADS 256
 #endif
-constexpr int kMT = FD_MFMA_THREADS;  // threads per workgroup
+constexpr int kMT = FD_MFMA_THREADS;  // threads per workgroup (bf16 caches)
 constexpr int kMW = kMT / 64;     // waves per workgroup
+#ifndef FD_FP8_WAVES
+#define FD_FP8_WAVES 8
+#endif
+constexpr int kMW8 = FD_FP8_WAVES;  // waves per workgroup over fp8 caches
 constexpr int kKB = 16;           // keys per block
 constexpr int kNS = FD_MFMA_STAGES;
 constexpr float kTau = 8.f;       // lazy rescale threshold, log2 units
@@ -86,6 +90,27 @@ struct Geo {
     static constexpr int KS = D / 32;           // k-steps of the score product
     static constexpr int DB = D / 16;           // output blocks of the P.V product
     static_assert(CH == 8 || CH == 16, "D = 64 or 128");
+};
+
+// Stored-row geometry of the decode kernel's LDS ring: bf16 caches keep
+// 2D-byte rows (the operand layout itself); fp8 caches keep D-byte rows,
+// dequantised per block into a bf16 block of the operand layout.  An fp8
+// block carries half the bytes, so the ring keeps twice the blocks in flight.
+#ifndef FD_FP8_STAGES
+#define FD_FP8_STAGES 2
+#endif
+template <int D, bool FP8>
+struct LGeo {
+    static constexpr int ROWB = FP8 ? D : 2 * D;    // bytes per stored key row
+    static constexpr int CH = ROWB / 16;            // 16-byte chunks per row
+    static constexpr int RPI = 64 / CH;             // rows per 1 KiB LDS-load instruction
+    static constexpr int IPB = kKB / RPI;           // instructions per block per tensor
+    static constexpr int BLKB = kKB * ROWB;         // bytes per block per tensor
+    static constexpr int STAGEB = 2 * BLKB;         // K then V
+    static constexpr int NS = FP8 ? FD_FP8_STAGES : kNS;
+    static constexpr int CONVB = FP8 ? 2 * Geo<D>::BLKB : 0;  // bf16 K and V block
+    static constexpr int WAVEB = NS * STAGEB + CONVB;
+    static_assert(IPB >= 1, "whole load instructions per block");
 };
 
 // XOR swizzle of the 16-byte chunks of row r (CH chunks per row).  Two read
@@ -118,6 +143,11 @@ __device__ __forceinline__ void wait_vmcnt_le() {
     __builtin_amdgcn_s_waitcnt((N & 0xf) | ((N >> 4) << 14) | (0x7 << 4) | (0xf << 8));
 }
 
+// LDS address (byte offset in the workgroup's LDS) of a shared-memory pointer.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char*)p));
+}
+
 // Transposing LDS read, ds_read_b64_tr_b16: in each 16-lane group, lane
 // 4j + q names 4 consecutive bf16 of a row; lane i receives element i % 4 of
 // lane 4j + i / 4 for j = 0..3.  Issued as inline assembly because the
@@ -145,35 +175,99 @@ __device__ __forceinline__ void lds_settle(bf16x4_t (&v)[N]) {
 // V rows.  Lane l of load instruction i reads its row's global chunk
 // dma_off[i]; the data lands at dst + i * 1024 + 16 * l.  Rows past `left`
 // read as zeros and cost no memory traffic.
-template <int D>
+template <int D, bool FP8>
 __device__ __forceinline__ void load_block(const char* kp, const char* vp, int left, char* dst,
                                            const uint32_t* dma_off) {
+    using L = LGeo<D, FP8>;
     const uint32_t n = left > 0 ? (uint32_t)left : 0u;
     const __amdgpu_buffer_rsrc_t rk = tile_rsrc(kp, n);
     const __amdgpu_buffer_rsrc_t rv = tile_rsrc(vp, n);
 #pragma unroll
-    for (int i = 0; i < Geo<D>::IPB; ++i) {
+    for (int i = 0; i < L::IPB; ++i) {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t*)(dst + i * 1024), 16, dma_off[i], 0, 0,
                                                  FD_LOAD_AUX);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)(dst + Geo<D>::BLKB + i * 1024), 16,
-                                                 dma_off[i], 0, 0, FD_LOAD_AUX);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)(dst + L::BLKB + i * 1024), 16, dma_off[i], 0, 0,
+                                                 FD_LOAD_AUX);
     }
 }
 
 // Start the loads of the wave's block `blk` of the tile [lo, hi) into dst:
 // contiguous caches address the tile directly (kt/vt: its first row);
 // paged caches read the block from page `page` (kt/vt: the KV head's base).
-template <int D, bool PAGED>
+// ESZ: bytes per stored element.
+template <int D, bool FP8, bool PAGED>
 __device__ __forceinline__ void load_block_at(const PagedKV& pk, int page, const char* kt, const char* vt, int lo,
                                               int hi, int blk, int rsb, char* dst, const uint32_t* dma_off) {
-    using G = Geo<D>;
+    using L = LGeo<D, FP8>;
+    constexpr int ESZ = FP8 ? 1 : 2;
     if constexpr (PAGED) {
         int64_t off;
-        const uint32_t n = paged_rows_in(pk, page, lo + blk * kKB, kKB, hi, rsb, G::ROWB, &off);
-        load_block<D>(kt + off * 2, vt + off * 2, (int)n, dst, dma_off);
+        const uint32_t n = paged_rows_in(pk, page, lo + blk * kKB, kKB, hi, rsb, L::ROWB, &off);
+        load_block<D, FP8>(kt + off * ESZ, vt + off * ESZ, (int)n, dst, dma_off);
     } else {
-        const int off = blk * G::BLKB;
-        load_block<D>(kt + off, vt + off, (hi - lo) * G::ROWB - off, dst, dma_off);
+        const int off = blk * L::BLKB;
+        load_block<D, FP8>(kt + off, vt + off, (hi - lo) * L::ROWB - off, dst, dma_off);
+    }
+}
+
+// Dequantise one landed fp8 block (K at src, V at src + LGeo::BLKB, rows of
+// D one-byte OCP E4M3 codes) into bf16 blocks of the operand layout (K at
+// dst, V at dst + Geo::BLKB, swizzled as swz).  Every E4M3 value is exact in
+// bf16; the per-tensor scales are applied outside (k_scale in the score
+// scale, v_scale to the output).  Lane l converts 16-byte chunks l, l + 64,
+// ... of each tensor: consecutive lanes read consecutive LDS bytes.
+//
+// The LDS accesses are inline assembly: as plain loads and stores the
+// compiler would treat them as possibly aliasing the buffer-to-LDS loads in
+// flight and wait for all of those first, which serialises the ring.  The
+// block at src has landed (the caller waited for it), and dst is this
+// wave's own area, read only by its own later reads; LDS executes one wave's
+// accesses in order.
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
+
+__device__ __forceinline__ u32x4_t lds_read_b128(const char* p) {
+    u32x4_t r;
+    asm volatile("ds_read_b128 %0, %1" : "=v"(r) : "v"(lds_addr(p)));
+    return r;
+}
+
+__device__ __forceinline__ void lds_write_b128(char* p, u32x4_t x) {
+    asm volatile("ds_write_b128 %0, %1" : : "v"(lds_addr(p)), "v"(x) : "memory");
+}
+
+template <int D>
+__device__ __forceinline__ void dequant_block(const char* src, char* dst, int lane) {
+    using L = LGeo<D, true>;
+    using G = Geo<D>;
+    constexpr int NQ = L::BLKB / 16 / 64;  // 16-byte chunks per lane per tensor
+    u32x4_t x[2][NQ];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int n = 0; n < NQ; ++n) x[t][n] = lds_read_b128(src + t * L::BLKB + (n * 64 + lane) * 16);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int n = 0; n < NQ; ++n) asm volatile("" : "+v"(x[t][n]));
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+        for (int n = 0; n < NQ; ++n) {
+            const int q = n * 64 + lane;
+            const int r = q / L::CH;
+            const int c = q % L::CH;  // 16 codes = dims 16c .. 16c + 15
+            const uint32_t w[4] = {x[t][n][0], x[t][n][1], x[t][n][2], x[t][n][3]};
+            uint32_t b[8];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                b[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.f, false));
+                b[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.f, true));
+            }
+            char* o = dst + t * G::BLKB;
+            lds_write_b128(o + swz<D>(r, 2 * c), u32x4_t{b[0], b[1], b[2], b[3]});
+            lds_write_b128(o + swz<D>(r, 2 * c + 1), u32x4_t{b[4], b[5], b[6], b[7]});
+        }
     }
 }
 
@@ -253,13 +347,18 @@ __device__ __forceinline__ void load_fragments(const char* kb, const char* vb, b
     lds_settle(vf);
 }
 
-template <int D, int NB, bool CAUSAL, bool PAGED>
-__global__ __launch_bounds__(kMT) void fd_mfma_partial_kernel(PartialArgs a) {
+template <int D, int NB, bool CAUSAL, bool PAGED, bool FP8>
+__global__ __launch_bounds__(FP8 ? 64 * kMW8 : kMT) void fd_mfma_partial_kernel(PartialArgs a) {
     using G = Geo<D>;
+    using LG = LGeo<D, FP8>;
+    constexpr int MW = FP8 ? kMW8 : kMW;  // waves per workgroup
+    constexpr int MT = 64 * MW;
+    constexpr int NS = LG::NS;
+    constexpr int ESZ = FP8 ? 1 : 2;  // bytes per stored K/V element
     constexpr int NR = 16 * NB;  // query rows per workgroup
     constexpr int RS = D + 4;    // padded row stride of the merge area (floats)
-    constexpr int MERGEB = kMW * (NR * RS + 3 * NR) * 4;
-    constexpr int SMEMB = kMW * G::WAVEB > MERGEB ? kMW * G::WAVEB : MERGEB;
+    constexpr int MERGEB = MW * (NR * RS + 3 * NR) * 4;
+    constexpr int SMEMB = MW * LG::WAVEB > MERGEB ? MW * LG::WAVEB : MERGEB;
     __shared__ __attribute__((aligned(16))) char smem[SMEMB];
 
     const int s = blockIdx.x;
@@ -284,7 +383,7 @@ __global__ __launch_bounds__(kMT) void fd_mfma_partial_kernel(PartialArgs a) {
 
     if (s >= S) {
         if (a.direct) {
-            for (int idx = tid; idx < nrows * D; idx += kMT)
+            for (int idx = tid; idx < nrows * D; idx += MT)
                 reinterpret_cast<uint16_t*>(a.out)[row0 * D + idx] = 0;
             if (a.lse && tid < nrows) a.lse[row0 + tid] = -INFINITY;
             return;
@@ -340,62 +439,69 @@ __global__ __launch_bounds__(kMT) void fd_mfma_partial_kernel(PartialArgs a) {
         for (int db = 0; db < G::DB; ++db) acc[nb][db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
 
-    char* ring = smem + w * G::WAVEB;
+    char* ring = smem + w * LG::WAVEB;
+    char* conv = ring + NS * LG::STAGEB;  // fp8: this wave's dequantised block
     const char* kt;
     const char* vt;
-    int rsb;  // bytes from one key row of the head to the next
+    int rsb;  // bytes from one stored key row of the head to the next
     const int32_t* tbl = nullptr;
     if constexpr (PAGED) {
-        kt = static_cast<const char*>(a.k) + g * a.pages.head_stride * 2;
-        vt = static_cast<const char*>(a.v) + g * a.pages.head_stride * 2;
-        rsb = a.pages.row_stride * 2;
+        kt = static_cast<const char*>(a.k) + g * a.pages.head_stride * ESZ;
+        vt = static_cast<const char*>(a.v) + g * a.pages.head_stride * ESZ;
+        rsb = a.pages.row_stride * ESZ;
         tbl = a.pages.table + (int64_t)b * a.pages.max_pages;
     } else {
         const int64_t tile_row = ((int64_t)b * a.Hkv + g) * a.Lmax + lo;
-        kt = static_cast<const char*>(a.k) + tile_row * G::ROWB;
-        vt = static_cast<const char*>(a.v) + tile_row * G::ROWB;
-        rsb = G::ROWB;
+        kt = static_cast<const char*>(a.k) + tile_row * LG::ROWB;
+        vt = static_cast<const char*>(a.v) + tile_row * LG::ROWB;
+        rsb = LG::ROWB;
     }
     const int nblk = (hi - lo + kKB - 1) / kKB;
-    const int nw = w < nblk ? (nblk - w + kMW - 1) / kMW : 0;
+    const int nw = w < nblk ? (nblk - w + MW - 1) / MW : 0;
 
     // Lane l of load instruction i fills LDS slot (row i*RPI + l/CH, chunk
-    // l%CH) of the block with the row's global chunk (l%CH) ^ row.
-    uint32_t dma_off[G::IPB];
+    // l%CH) of the block: bf16 rows with the row's global chunk (l%CH) ^
+    // row (the operand swizzle), fp8 rows in their stored order.
+    uint32_t dma_off[LG::IPB];
 #pragma unroll
-    for (int i = 0; i < G::IPB; ++i) {
-        const int r = i * G::RPI + lane / G::CH;
-        const int cg = (lane % G::CH) ^ swf<G::CH>(r);
+    for (int i = 0; i < LG::IPB; ++i) {
+        const int r = i * LG::RPI + lane / LG::CH;
+        const int cg = FP8 ? lane % LG::CH : (lane % LG::CH) ^ swf<LG::CH>(r);
         dma_off[i] = (uint32_t)(r * rsb + cg * 16);
     }
 
-    // Wave block j is tile block w + 4j and goes to ring slot j % kNS.  A
+    // Wave block j is tile block w + 4j and goes to ring slot j % NS.  A
     // paged cache's page ids are read one block ahead of their loads, so the
     // scalar table reads overlap the work of the previous block.
     auto page_of = [&](int blk) { return PAGED ? page_at(a.pages, tbl, lo + blk * kKB, hi) : 0; };
 #pragma unroll
-    for (int j = 0; j < kNS - 1; ++j)
-        load_block_at<D, PAGED>(a.pages, page_of(w + j * kMW), kt, vt, lo, hi, w + j * kMW, rsb,
-                                ring + j * G::STAGEB, dma_off);
-    int page_next = page_of(w + (kNS - 1) * kMW);
+    for (int j = 0; j < NS - 1; ++j)
+        load_block_at<D, FP8, PAGED>(a.pages, page_of(w + j * MW), kt, vt, lo, hi, w + j * MW, rsb,
+                                     ring + j * LG::STAGEB, dma_off);
+    int page_next = page_of(w + (NS - 1) * MW);
 
     for (int j = 0; j < nw; ++j) {
         {
-            const int jn = j + kNS - 1;
+            const int jn = j + NS - 1;
             const int page = page_next;
-            page_next = page_of(w + (jn + 1) * kMW);
-            load_block_at<D, PAGED>(a.pages, page, kt, vt, lo, hi, w + jn * kMW, rsb, ring + (jn % kNS) * G::STAGEB,
-                                    dma_off);
+            page_next = page_of(w + (jn + 1) * MW);
+            load_block_at<D, FP8, PAGED>(a.pages, page, kt, vt, lo, hi, w + jn * MW, rsb,
+                                         ring + (jn % NS) * LG::STAGEB, dma_off);
         }
-        wait_vmcnt_le<(kNS - 1) * 2 * G::IPB>();  // block j has landed
-        const char* kb = ring + (j % kNS) * G::STAGEB;
-        const char* vb = kb + G::BLKB;
+        wait_vmcnt_le<(NS - 1) * 2 * LG::IPB>();  // block j has landed
+        const char* kb = ring + (j % NS) * LG::STAGEB;
+        const char* vb = kb + LG::BLKB;
+        if constexpr (FP8) {
+            dequant_block<D>(kb, conv, lane);
+            kb = conv;
+            vb = conv + G::BLKB;
+        }
 
         bf16x8_t kf[G::KS];
         bf16x4_t vf[G::DB];
         load_fragments<D>(kb, vb, kf, vf, grp, col);
 
-        const int key0 = lo + (w + j * kMW) * kKB;  // first key of the block
+        const int key0 = lo + (w + j * MW) * kKB;  // first key of the block
         block_math<D, NB>(kf, vf, qf, acc, m, l, mx, key0, key0 + kKB > mask_from, rend, c, grp);
     }
 
@@ -409,10 +515,10 @@ __global__ __launch_bounds__(kMT) void fd_mfma_partial_kernel(PartialArgs a) {
         mx[nb] = fmaxf(mx[nb], __shfl_xor(mx[nb], 32));
     }
     __syncthreads();  // every wave is done with its ring
-    float* sm_acc = reinterpret_cast<float*>(smem);  // [kMW][NR][RS]
-    float* sm_m = sm_acc + kMW * NR * RS;            // [kMW][NR]
-    float* sm_l = sm_m + kMW * NR;
-    float* sm_x = sm_l + kMW * NR;
+    float* sm_acc = reinterpret_cast<float*>(smem);  // [MW][NR][RS]
+    float* sm_m = sm_acc + MW * NR * RS;            // [MW][NR]
+    float* sm_l = sm_m + MW * NR;
+    float* sm_x = sm_l + MW * NR;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
         const int r = nb * 16 + col;
@@ -427,19 +533,19 @@ __global__ __launch_bounds__(kMT) void fd_mfma_partial_kernel(PartialArgs a) {
     }
     __syncthreads();
 
-    for (int idx = tid; idx < nrows * D; idx += kMT) {
+    for (int idx = tid; idx < nrows * D; idx += MT) {
         const int r = idx / D;
         const int d = idx - r * D;
         float M = -INFINITY, X = -INFINITY;
 #pragma unroll
-        for (int x = 0; x < kMW; ++x) {
+        for (int x = 0; x < MW; ++x) {
             M = fmaxf(M, sm_m[x * NR + r]);
             X = fmaxf(X, sm_x[x * NR + r]);
         }
         float num = 0.f, den = 0.f;
         if (M != -INFINITY) {
 #pragma unroll
-            for (int x = 0; x < kMW; ++x) {
+            for (int x = 0; x < MW; ++x) {
                 const float mw = sm_m[x * NR + r];
                 const float f = mw == -INFINITY ? 0.f : fast_exp2(mw - M);
                 num = fmaf(f, sm_acc[(x * NR + r) * RS + d], num);
@@ -447,7 +553,8 @@ __global__ __launch_bounds__(kMT) void fd_mfma_partial_kernel(PartialArgs a) {
             }
         }
         const bool empty = M == -INFINITY;
-        const float o = empty ? 0.f : num / den;
+        float o = empty ? 0.f : num / den;
+        if constexpr (FP8) o *= a.v_scale;  // V was dequantised without its scale
         const float lse_v = empty ? -INFINITY : (M + log2f(den)) * kLn2;
         const int64_t row = row0 + r;
         if (a.direct) {
@@ -581,10 +688,6 @@ __device__ __forceinline__ void lds_settle8(bf16x8_t (&v)[N]) {
     for (int i = 0; i < N; ++i) asm volatile("" : "+v"(v[i]));
 }
 
-// LDS address (byte offset in the workgroup's LDS) of a shared-memory pointer.
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char*)p));
-}
 
 // 16-byte LDS load at a lane address plus a compile-time offset (folded into
 // the instruction's offset field).
@@ -992,21 +1095,29 @@ __global__ __launch_bounds__(kCT) void fd_mfma_chunk_kernel(PartialArgs a) {
     }
 }
 
-template <int D, int NB>
-void launch_nb(int batch, const PartialArgs& a, hipStream_t stream) {
-    dim3 grid(a.rule.slots, a.Hkv, batch), block(kMT);
+template <int D, int NB, bool FP8>
+void launch_nb_kv(int batch, const PartialArgs& a, hipStream_t stream) {
+    dim3 grid(a.rule.slots, a.Hkv, batch), block(FP8 ? 64 * kMW8 : kMT);
     const bool paged = a.pages.table != nullptr;
     if (a.q_len > 1) {
         if (paged)
-            hipLaunchKernelGGL((fd_mfma_partial_kernel<D, NB, true, true>), grid, block, 0, stream, a);
+            hipLaunchKernelGGL((fd_mfma_partial_kernel<D, NB, true, true, FP8>), grid, block, 0, stream, a);
         else
-            hipLaunchKernelGGL((fd_mfma_partial_kernel<D, NB, true, false>), grid, block, 0, stream, a);
+            hipLaunchKernelGGL((fd_mfma_partial_kernel<D, NB, true, false, FP8>), grid, block, 0, stream, a);
     } else {
         if (paged)
-            hipLaunchKernelGGL((fd_mfma_partial_kernel<D, NB, false, true>), grid, block, 0, stream, a);
+            hipLaunchKernelGGL((fd_mfma_partial_kernel<D, NB, false, true, FP8>), grid, block, 0, stream, a);
         else
-            hipLaunchKernelGGL((fd_mfma_partial_kernel<D, NB, false, false>), grid, block, 0, stream, a);
+            hipLaunchKernelGGL((fd_mfma_partial_kernel<D, NB, false, false, FP8>), grid, block, 0, stream, a);
     }
+}
+
+template <int D, int NB>
+void launch_nb(int batch, const PartialArgs& a, hipStream_t stream) {
+    if (a.kv_fp8)
+        launch_nb_kv<D, NB, true>(batch, a, stream);
+    else
+        launch_nb_kv<D, NB, false>(batch, a, stream);
 }
 
 }  // namespace
@@ -1019,6 +1130,7 @@ int mfma_block_rows(int rows) { return rows <= 32 ? rows : kChunkRows; }
 
 hipError_t launch_partials_mfma(int head_dim, int batch, const PartialArgs& a, hipStream_t stream) {
     if (a.rows > 32) {
+        if (a.kv_fp8) return hipErrorNotSupported;  // the chunk tiles read bf16 caches only
         dim3 grid(a.rule.slots, a.Hkv * a.row_blocks, batch), block(kCT);
         const bool paged = a.pages.table != nullptr;
         if (head_dim == 64) {

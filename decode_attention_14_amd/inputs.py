@@ -146,8 +146,9 @@ def paginate(k: torch.Tensor, v: torch.Tensor, cache_lens, page_size: int, layou
     Sequence b gets ceil(L_b / page_size) pages; page ids are a seeded random
     permutation of the pool (``Generator(PCG64(seed)).permutation``), which
     also holds ``spare_pages`` pages no sequence uses.  Rows of a page at or
-    past L_b and every spare page are filled with NaN, so a kernel that reads
-    them cannot go unnoticed.  Data movement only.
+    past L_b and every spare page are filled with NaN (for uint8 FP8 codes,
+    0x7F: the E4M3 NaN), so a kernel that reads them cannot go unnoticed.
+    Data movement only.
     """
     if layout not in ("nhd", "hnd"):
         raise ValueError(f"unknown layout {layout!r}")
@@ -160,8 +161,9 @@ def paginate(k: torch.Tensor, v: torch.Tensor, cache_lens, page_size: int, layou
     perm = np.random.Generator(np.random.PCG64(seed)).permutation(num_pages)
     table = torch.full((B, Lmax // page_size), -1, dtype=torch.int32)
     shape = (num_pages, page_size, H, D) if layout == "nhd" else (num_pages, H, page_size, D)
-    kp = torch.full(shape, float("nan"), dtype=k.dtype)
-    vp = torch.full(shape, float("nan"), dtype=v.dtype)
+    fill = 0x7F if k.dtype == torch.uint8 else float("nan")  # uint8: the E4M3 NaN code
+    kp = torch.full(shape, fill, dtype=k.dtype)
+    vp = torch.full(shape, fill, dtype=v.dtype)
     nxt = 0
     for b in range(B):
         for i in range(counts[b]):
@@ -178,3 +180,18 @@ def paginate(k: torch.Tensor, v: torch.Tensor, cache_lens, page_size: int, layou
                 kp[pid, :, : hi - lo] = src_k
                 vp[pid, :, : hi - lo] = src_v
     return PagedCache(kp, vp, table, page_size, layout)
+
+
+def quantize_fp8(t: torch.Tensor, scale: float) -> torch.Tensor:
+    """OCP FP8 E4M3 codes (uint8) of ``t / scale``, rounded to nearest even by
+    torch's float8_e4m3fn conversion; |t / scale| must stay within 448."""
+    x = t.float() / float(np.float32(scale))
+    if float(x.abs().max()) > 448.0:
+        raise ValueError("values exceed the E4M3 range at this scale")
+    return x.to(torch.float8_e4m3fn).view(torch.uint8)
+
+
+def fp8_scale_for(t: torch.Tensor) -> float:
+    """Per-tensor scale mapping the largest |value| to 240 (headroom below the
+    E4M3 maximum of 448), as an fp32 value."""
+    return float(np.float32(float(t.float().abs().max()) / 240.0))

@@ -61,7 +61,7 @@ typedef enum fd_status {
     FD_ERR_DEVICE = -4       /* HIP runtime error */
 } fd_status;
 
-typedef enum fd_dtype { FD_F32 = 0, FD_BF16 = 1 } fd_dtype;
+typedef enum fd_dtype { FD_F32 = 0, FD_BF16 = 1, FD_FP8_E4M3 = 2 /* K/V caches only */ } fd_dtype;
 
 /* Most partial slots a row may have. */
 #define FD_MAX_SPLITS 256
@@ -223,6 +223,39 @@ fd_status fd_decode_partials_paged(const fd_dims* dims, const void* q, const voi
                                    const int32_t* cache_lens, float scale, int32_t num_splits,
                                    const fd_plan* plan, float* o_part, float* m_part, float* lse_part,
                                    void* stream);
+
+/* FP8 K/V caches.
+ *
+ * Page "FlashDecoding算法原理与多GPU并行解码实战" (section on combining
+ * methods) pairs the split-KV method with INT8/FP8 caches to save memory and
+ * bandwidth, and advises dequantising to bf16 for the score computation.
+ * Here k_cache and v_cache hold one-byte OCP FP8 E4M3 codes (the
+ * "e4m3fn" format: bias 7, no infinities, 0x7F/0xFF are NaN, largest finite
+ * 448) with one scale per tensor: the key is code * k_scale and the value is
+ * code * v_scale.  q and out stay bf16 (dims->dtype must be FD_BF16).  Every
+ * E4M3 value is exact in bf16, so the kernels dequantise each block to bf16
+ * and run the bf16 products; k_scale is folded into the score scale and
+ * v_scale into the output, so the arithmetic is that of the bf16 path.
+ *
+ * Layouts as for bf16 caches with one byte per element: contiguous
+ * [B, Hkv, Lmax, D] when pages is NULL, else the paged layouts of
+ * fd_kv_pages.  Served: up to 32 query rows per KV head (n_rep * q_len <= 32:
+ * decode and short verification chunks); more rows give FD_ERR_UNSUPPORTED.
+ * Errors: as the bf16 calls; FD_ERR_UNSUPPORTED if dims->dtype is not
+ * FD_BF16; FD_ERR_INVALID for non-finite scales. */
+fd_status fd_decode_attention_fp8(const fd_dims* dims, const void* q, const void* k_cache,
+                                  const void* v_cache, const fd_kv_pages* pages, float k_scale,
+                                  float v_scale, const int32_t* cache_lens, float scale,
+                                  int32_t num_splits, const fd_plan* plan, void* workspace,
+                                  uint64_t workspace_bytes, void* out, float* lse, void* stream);
+
+/* fd_decode_partials_fp8 -- the first pass alone over fp8 caches (outputs as
+ * fd_decode_partials; o_part already carries v_scale). */
+fd_status fd_decode_partials_fp8(const fd_dims* dims, const void* q, const void* k_cache,
+                                 const void* v_cache, const fd_kv_pages* pages, float k_scale,
+                                 float v_scale, const int32_t* cache_lens, float scale,
+                                 int32_t num_splits, const fd_plan* plan, float* o_part,
+                                 float* m_part, float* lse_part, void* stream);
 
 /* Diagnostics.  fd_status_string returns a static name for a status.
  * fd_last_error returns the message of the last failed call on this thread

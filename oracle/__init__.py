@@ -209,3 +209,42 @@ def attention_paged(q, k_pages, v_pages, block_table, cache_lens, scale, layout:
     k = gather_pages(k_pages, block_table, lens, layout)
     v = gather_pages(v_pages, block_table, lens, layout)
     return attention(q, k, v, lens, scale, nthreads=nthreads, lib=lib)
+
+
+def fp8_e4m3_to_float(codes):
+    """Values of OCP FP8 E4M3 ("e4m3fn") codes as float64, from the format's
+    definition: sign bit 7, exponent bits 6:3 with bias 7, mantissa bits 2:0;
+    exponent 0 is subnormal (m * 2^-9); exponent 15 with mantissa 7 is NaN; no
+    infinities."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c >> 7, -1.0, 1.0)
+    e = (c >> 3) & 15
+    m = c & 7
+    mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    mag = np.where((e == 15) & (m == 7), np.nan, mag)
+    return sign * mag
+
+
+def attention_fp8(q, k_codes, v_codes, cache_lens, scale, k_scale, v_scale, nthreads: int = 0, lib=None):
+    """The plain definition over FP8 E4M3 caches: key = code * k_scale and
+    value = code * v_scale (the dequantisation of page "FlashDecoding算法原理与
+    多GPU并行解码实战", section on combining methods).  ``q`` holds bf16 bit
+    patterns (uint16) or float32 values; ``k_codes``/``v_codes`` uint8 codes of
+    shape [B, Hkv, Lmax, D].  The code values are exact in float32; k_scale
+    enters as the exact fp64 product scale * k_scale (scores are linear in the
+    key), and v_scale multiplies the output (the output is linear in V).
+    """
+    lib = lib or load()
+    qf = np.ascontiguousarray(q)
+    if qf.dtype == np.uint16:
+        qf = (qf.astype(np.uint32) << 16).view(np.float32)
+    kf = np.ascontiguousarray(fp8_e4m3_to_float(k_codes).astype(np.float32))
+    vf = np.ascontiguousarray(fp8_e4m3_to_float(v_codes).astype(np.float32))
+    qf, kf, vf, lens, dims = _prep(qf, kf, vf, cache_lens)
+    B, Hq, Hkv, D, q_len, Lmax, code = dims
+    out = np.empty((B, Hq, q_len, D), np.float64)
+    lse = np.empty((B, Hq, q_len), np.float64)
+    s = float(np.float32(scale)) * float(np.float32(k_scale))
+    rc = lib.orc_attention(*dims, _ptr(qf), _ptr(kf), _ptr(vf), _ptr(lens), s, _ptr(out), _ptr(lse), nthreads)
+    _check(rc, "attention_fp8")
+    return out * float(np.float32(v_scale)), lse

@@ -30,7 +30,7 @@ def lib():
 def header_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(fd_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(fd_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_exports_every_declared_symbol(lib):
@@ -306,3 +306,21 @@ def test_paged_empty_batch_is_a_no_op(lib):
     pages = fd.FdKvPages(FAKE[7].value, 4, 16, 10, fd.FD_PAGES_HND)
     assert lib.fd_decode_attention_paged(ctypes.byref(d), None, None, None, ctypes.byref(pages), None,
                                          ctypes.c_float(1.0), 0, None, None, 0, None, None, None) == fd.FD_OK
+
+
+def test_fp8_rejects_unsupported_calls(lib):
+    q, k, v, lens, o, lse = FAKE[:6]
+
+    def call(d, ks=1.0, vs=1.0):
+        return lib.fd_decode_attention_fp8(ctypes.byref(d), q, k, v, None, ctypes.c_float(ks), ctypes.c_float(vs),
+                                           lens, ctypes.c_float(0.1), 0, None, None, 0, o, lse, None)
+
+    assert call(dims(Lmax=64, dt=fd.FD_F32)) == fd.FD_ERR_UNSUPPORTED        # q must be bf16
+    assert call(dims(Lmax=64, T=9)) == fd.FD_ERR_UNSUPPORTED                 # 4 x 9 rows > 32
+    assert "32" in lib.fd_last_error().decode()
+    assert call(dims(Lmax=64), ks=float("inf")) == fd.FD_ERR_INVALID
+    assert call(dims(Lmax=64), vs=float("nan")) == fd.FD_ERR_INVALID
+    assert call(dims(D=96, Lmax=64)) == fd.FD_ERR_UNSUPPORTED
+    assert lib.fd_decode_partials_fp8(ctypes.byref(dims(Lmax=64)), q, k, v, None, ctypes.c_float(1.0),
+                                      ctypes.c_float(1.0), lens, ctypes.c_float(0.1), 0, None, o, FAKE[6],
+                                      FAKE[7], None) == fd.FD_ERR_INVALID     # neither splits nor plan
