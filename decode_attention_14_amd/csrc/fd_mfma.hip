@@ -361,8 +361,13 @@ __global__ __launch_bounds__(FP8 ? 64 * kMW8 : kMT) void fd_mfma_partial_kernel(
     constexpr int SMEMB = MW * LG::WAVEB > MERGEB ? MW * LG::WAVEB : MERGEB;
     __shared__ __attribute__((aligned(16))) char smem[SMEMB];
 
-    const int s = blockIdx.x;
-    const int g = blockIdx.y;
+    // KV head fastest: workgroups are dealt to the eight XCDs round-robin in
+    // launch order, so consecutive ids take the heads of one (tile, sequence)
+    // and every XCD gets the same mix of tiles (all heads of a sequence have
+    // the same length).  With the tile fastest instead, a tile index would
+    // pin to a subset of XCDs and short sequences would leave some idle.
+    const int g = blockIdx.x;
+    const int s = blockIdx.y;
     const int b = blockIdx.z;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -1097,7 +1102,7 @@ __global__ __launch_bounds__(kCT) void fd_mfma_chunk_kernel(PartialArgs a) {
 
 template <int D, int NB, bool FP8>
 void launch_nb_kv(int batch, const PartialArgs& a, hipStream_t stream) {
-    dim3 grid(a.rule.slots, a.Hkv, batch), block(FP8 ? 64 * kMW8 : kMT);
+    dim3 grid(a.Hkv, a.rule.slots, batch), block(FP8 ? 64 * kMW8 : kMT);
     const bool paged = a.pages.table != nullptr;
     if (a.q_len > 1) {
         if (paged)

@@ -99,7 +99,8 @@ typedef struct fd_plan {
  * num_splits tiles; plan->tile_len is then 0 and plan->max_splits =
  * num_splits (<= FD_MAX_SPLITS).  With num_splits == 0 the planner picks one
  * tile length for the batch: the batch's (sequence, KV head, row block) key
- * rows spread over one work unit per compute unit, at least 256 keys (below
+ * rows spread over one work unit per compute unit when all lengths are equal
+ * and four per compute unit otherwise, at least 256 keys (below
  * about 256 keys per chunk launch overhead eats the gain, page
  * "FlashDecoding算法原理..." benchmark section), at most the longest sequence,
  * raised if needed so no sequence needs more than FD_MAX_SPLITS.

@@ -77,12 +77,14 @@ def test_planner_on_workloads(name):
         assert p.tile_len % 64 == 0
         # at least 256 keys, at most the longest sequence (rounded to 64)
         assert 256 <= p.tile_len <= max(256, -(-max(lens) // 64) * 64)
-        # about one work unit per compute unit: each (sequence, KV head, row
-        # block) adds at most one unit beyond an even share
+        # about one work unit per compute unit for equal lengths, four for
+        # mixed ones: each (sequence, KV head, row block) adds at most one
+        # unit beyond an even share
         rows = w.num_q_heads // w.num_kv_heads * w.q_len
         row_blocks = 1 if rows <= 32 else -(-rows // 128)
         lanes = w.num_kv_heads * row_blocks
-        assert p.plan.work_units <= 256 + w.batch * lanes
+        per_cu = 1 if min(lens) == max(lens) else 4
+        assert p.plan.work_units <= per_cu * 256 + w.batch * lanes
     for L, S in zip(lens, p.splits_per_seq):
         t = tiles_of(L, p.tile_len, w.num_splits, p.max_splits)
         assert len(t) == S
@@ -132,7 +134,9 @@ def test_planner_varlen_balances_units():
     tiles = [hi - lo for L in lens for lo, hi in tiles_of(L, p.tile_len, 0, p.max_splits)]
     assert max(tiles) <= p.tile_len
     assert p.plan.work_units == 8 * len(tiles)
-    assert p.plan.work_units >= 256
+    assert p.plan.work_units >= 4 * 256  # four units per CU for mixed lengths
+    # the tile is the even share of four units per CU, rounded up to 64 keys
+    assert p.tile_len == -(-(-(-sum(lens) * 8 // 1024)) // 64) * 64
 
 
 @pytest.mark.parametrize("bad,status", [
