@@ -11,6 +11,7 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 
 #include "fd_internal.h"
@@ -149,6 +150,30 @@ fdk::PartialArgs make_args(const fd_dims* d, const void* q, const void* k, const
     a.rule = rule;
     a.qk_scale = scale * kLog2e;
     return a;
+}
+
+// FD_TRACE=1 in the environment prints each launch's plan and grid on
+// stderr (read once per process).
+bool trace_enabled() {
+    static const bool on = [] {
+        const char* e = std::getenv("FD_TRACE");
+        return e != nullptr && e[0] != '\0' && e[0] != '0';
+    }();
+    return on;
+}
+
+void trace_launch(const char* entry, const fd_dims* d, const fdk::PartialArgs& a) {
+    if (!trace_enabled()) return;
+    const bool mfma = a.kv_fp8 || fdk::use_mfma_partials(d->dtype, d->head_dim, a.rows);
+    const char* kernel = !mfma ? "fd_partial_kernel (vector)"
+                         : a.rows > 32 ? "fd_mfma_chunk_kernel" : "fd_mfma_partial_kernel";
+    std::fprintf(stderr,
+                 "[fd] %s: B=%d Hq=%d Hkv=%d D=%d q_len=%d Lmax=%d dtype=%d%s%s | tile_len=%d num_splits=%d "
+                 "slots=%d granule=%d | rows/KV head=%d row_blocks=%d | %s, %s\n",
+                 entry, d->batch, d->num_q_heads, d->num_kv_heads, d->head_dim, d->q_len, d->max_cache_len,
+                 d->dtype, a.pages.table ? " paged" : "", a.kv_fp8 ? " fp8-kv" : "", a.rule.tile_len,
+                 a.rule.num_splits, a.rule.slots, a.rule.granule, a.rows, a.row_blocks, kernel,
+                 a.rule.slots > 1 && !a.direct ? "partials + merge" : "direct output");
 }
 
 fd_status device_status(hipError_t e, const char* what) {
@@ -314,6 +339,7 @@ fd_status run_partials(const fd_dims* dims, const void* q, const void* k_cache, 
     a.m_part = m_part;
     a.lse_part = lse_part;
     a.direct = 0;
+    trace_launch("partials", dims, a);
     return device_status(fdk::launch_partials(dims->dtype, dims->head_dim, dims->batch, a,
                                               static_cast<hipStream_t>(stream)),
                          "partial kernel launch");
@@ -449,6 +475,7 @@ fd_status run_attention(const fd_dims* dims, const void* q, const void* k_cache,
         a.out = out;
         a.lse = lse;
         a.direct = 1;
+        trace_launch("attention", dims, a);
         return device_status(fdk::launch_partials(dims->dtype, dims->head_dim, dims->batch, a, s),
                              "partial kernel launch");
     }
@@ -463,6 +490,7 @@ fd_status run_attention(const fd_dims* dims, const void* q, const void* k_cache,
     a.m_part = reinterpret_cast<float*>(ws + lay.m_off);
     a.lse_part = reinterpret_cast<float*>(ws + lay.lse_off);
     a.direct = 0;
+    trace_launch("attention", dims, a);
     if ((st = device_status(fdk::launch_partials(dims->dtype, dims->head_dim, dims->batch, a, s),
                             "partial kernel launch")) != FD_OK)
         return st;

@@ -35,6 +35,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <cstdlib>
+#include <cstring>
+
 #include "fd_device.h"
 #include "fd_internal.h"
 
@@ -526,13 +529,26 @@ hipError_t launch_partials_d(int batch, const PartialArgs& a, hipStream_t stream
 
 }  // namespace
 
+bool vector_kernel_forced() {
+    static const bool forced = [] {
+        const char* e = std::getenv("FD_DECODE_KERNEL");
+        return e != nullptr && std::strcmp(e, "vector") == 0;
+    }();
+    return forced;
+}
+
+bool use_mfma_partials(int dtype, int head_dim, int rows) {
+    return mfma_partials_supported(dtype, head_dim, rows) && !vector_kernel_forced();
+}
+
 int partial_block_rows(int dtype, int head_dim, int rows) {
-    return mfma_partials_supported(dtype, head_dim, rows) ? mfma_block_rows(rows) : vector_block_rows(rows);
+    return use_mfma_partials(dtype, head_dim, rows) ? mfma_block_rows(rows) : vector_block_rows(rows);
 }
 
 hipError_t launch_partials(int dtype, int head_dim, int batch, const PartialArgs& a,
                            hipStream_t stream) {
-    if (mfma_partials_supported(dtype, head_dim, a.rows)) return launch_partials_mfma(head_dim, batch, a, stream);
+    // FP8 caches are read by the matrix-core decode kernel only.
+    if (a.kv_fp8 || use_mfma_partials(dtype, head_dim, a.rows)) return launch_partials_mfma(head_dim, batch, a, stream);
     const bool bf16 = dtype == 1;
     if (bf16) {
         return head_dim == 64 ? launch_partials_d<true, 64>(batch, a, stream)

@@ -71,6 +71,12 @@ hipError_t launch_partials(int dtype, int head_dim, int batch, const PartialArgs
 // Matrix-core partial kernels (fd_mfma.hip): their applicability and the
 // rows of a workgroup (all of a group of up to 32 rows; else a chunk tile).
 bool mfma_partials_supported(int dtype, int head_dim, int rows);
+// Whether the partial pass of a (dtype, head_dim, rows) call runs on the
+// matrix cores: where supported, unless the environment variable
+// FD_DECODE_KERNEL=vector forces the vector kernel (an ablation switch for
+// bf16 caches; read once per process).
+bool use_mfma_partials(int dtype, int head_dim, int rows);
+bool vector_kernel_forced();
 int mfma_block_rows(int rows);
 hipError_t launch_partials_mfma(int head_dim, int batch, const PartialArgs& a, hipStream_t stream);
 

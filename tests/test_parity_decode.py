@@ -295,3 +295,27 @@ def test_graph_replays_match_eager():
         fd.decode_attention(qd, kd, vd, cld, scale=sc, num_splits=5, workspace=ws)
         torch.cuda.synchronize()
     compare("graph replay", out, lse, *run_oracle(q, k, v, cl, sc), TOL["bf16"])
+
+
+def test_vector_kernel_ablation_switch_in_subprocess():
+    """FD_DECODE_KERNEL=vector (read once per process) runs bf16 caches on the
+    vector-ALU kernel; FD_TRACE=1 names the kernel.  Parity in a child process."""
+    import os
+    import subprocess
+    import sys
+    say("[case] bf16 through the vector kernel (child process)")
+    code = (
+        "import sys; sys.path.insert(0, 'tests'); sys.path.insert(0, '.')\n"
+        "from gpu_cases import check_case\n"
+        "check_case('vector bf16 S=3', 2, 32, 8, 128, 1, 3000, 'bf16', 1500, [3000, 777], num_splits=3)\n"
+        "check_case('vector bf16 planned', 3, 8, 2, 64, 1, 1000, 'bf16', 1501, [1000, 1, 0], use_plan=True)\n"
+        "check_case('vector bf16 chunk', 2, 8, 2, 128, 5, 600, 'bf16', 1502, [600, 20], num_splits=2)\n"
+        "print('child ok')\n"
+    )
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    env = dict(os.environ, FD_DECODE_KERNEL="vector", FD_TRACE="1")
+    r = subprocess.run([sys.executable, "-c", code], cwd=root, env=env, capture_output=True, text=True,
+                       timeout=240)
+    print(r.stdout[-2000:], r.stderr[-2000:])
+    assert r.returncode == 0 and "child ok" in r.stdout
+    assert "fd_partial_kernel (vector)" in r.stderr and "fd_mfma" not in r.stderr
