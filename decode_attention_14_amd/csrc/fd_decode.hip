@@ -35,9 +35,6 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include <cstdlib>
-#include <cstring>
-
 #include "fd_device.h"
 #include "fd_internal.h"
 
@@ -490,13 +487,6 @@ void launch_combine_d(int64_t rows, int slots, const float* o_part, const float*
                            block, 0, stream, o_part, lse_part, slots, rows, out, lse);
 }
 
-// Rows per workgroup of the vector kernel.
-int vector_block_rows(int rows) {
-    if (rows <= 1) return 1;
-    if (rows <= 2) return 2;
-    if (rows <= 4) return 4;
-    return 8;
-}
 
 template <bool BF16, int D, bool CAUSAL, bool PAGED>
 void launch_partials_c(int batch, const PartialArgs& a, hipStream_t stream) {
@@ -528,22 +518,6 @@ hipError_t launch_partials_d(int batch, const PartialArgs& a, hipStream_t stream
 }
 
 }  // namespace
-
-bool vector_kernel_forced() {
-    static const bool forced = [] {
-        const char* e = std::getenv("FD_DECODE_KERNEL");
-        return e != nullptr && std::strcmp(e, "vector") == 0;
-    }();
-    return forced;
-}
-
-bool use_mfma_partials(int dtype, int head_dim, int rows) {
-    return mfma_partials_supported(dtype, head_dim, rows) && !vector_kernel_forced();
-}
-
-int partial_block_rows(int dtype, int head_dim, int rows) {
-    return use_mfma_partials(dtype, head_dim, rows) ? mfma_block_rows(rows) : vector_block_rows(rows);
-}
 
 hipError_t launch_partials(int dtype, int head_dim, int batch, const PartialArgs& a,
                            hipStream_t stream) {

@@ -58,6 +58,12 @@ struct PartialArgs {
     float v_scale;      // fp8: value of V = code * v_scale (applied to the output)
 };
 
+// Packed query rows per workgroup of the matrix-core chunk kernel (row
+// groups of more than 32 rows per KV head).
+constexpr int kChunkTileRows = 128;
+
+// Kernel selection (fd_select.cpp, host code only).
+//
 // Query rows one workgroup of the partial pass serves, for calls with `rows`
 // = n_rep * q_len rows per (sequence, KV head).  The grid has
 // ceil(rows / partial_block_rows) row blocks per (sequence, KV head, tile).
@@ -68,16 +74,20 @@ int partial_block_rows(int dtype, int head_dim, int rows);
 hipError_t launch_partials(int dtype, int head_dim, int batch, const PartialArgs& a,
                            hipStream_t stream);
 
-// Matrix-core partial kernels (fd_mfma.hip): their applicability and the
-// rows of a workgroup (all of a group of up to 32 rows; else a chunk tile).
+// Matrix-core partial kernels: their applicability and the rows of a
+// workgroup (all of a group of up to 32 rows; else a chunk tile); the rows
+// of a vector-kernel workgroup.
 bool mfma_partials_supported(int dtype, int head_dim, int rows);
+int mfma_block_rows(int rows);
+int vector_block_rows(int rows);
 // Whether the partial pass of a (dtype, head_dim, rows) call runs on the
 // matrix cores: where supported, unless the environment variable
 // FD_DECODE_KERNEL=vector forces the vector kernel (an ablation switch for
 // bf16 caches; read once per process).
 bool use_mfma_partials(int dtype, int head_dim, int rows);
 bool vector_kernel_forced();
-int mfma_block_rows(int rows);
+
+// Matrix-core launches (fd_mfma.hip).
 hipError_t launch_partials_mfma(int head_dim, int batch, const PartialArgs& a, hipStream_t stream);
 
 hipError_t launch_combine(int head_dim, int out_dtype, int64_t rows, int slots,

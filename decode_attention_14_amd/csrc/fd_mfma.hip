@@ -610,6 +610,7 @@ constexpr int kCW = kCT / 64;           // waves
 constexpr int kCRG = 4;                 // row groups of 32 rows
 constexpr int kCKW = kCW / kCRG;        // waves per row group: key halves
 constexpr int kChunkRows = 32 * kCRG;   // rows per workgroup
+static_assert(kChunkRows == kChunkTileRows, "row tile of the chunk kernel");
 constexpr int kCBK = 32;                // keys per block
 constexpr int kCNS = FD_CHUNK_STAGES;
 
@@ -1126,12 +1127,6 @@ void launch_nb(int batch, const PartialArgs& a, hipStream_t stream) {
 }
 
 }  // namespace
-
-bool mfma_partials_supported(int dtype, int head_dim, int rows) {
-    return dtype == 1 && (head_dim == 64 || head_dim == 128) && rows >= 1;
-}
-
-int mfma_block_rows(int rows) { return rows <= 32 ? rows : kChunkRows; }
 
 hipError_t launch_partials_mfma(int head_dim, int batch, const PartialArgs& a, hipStream_t stream) {
     if (a.rows > 32) {
