@@ -605,6 +605,11 @@ __global__ __launch_bounds__(FP8 ? 64 * kMW8 : kMT) void fd_mfma_partial_kernel(
 #ifndef FD_CHUNK_STAGES
 #define FD_CHUNK_STAGES 2
 #endif
+// Vector instructions the scheduler places after each P.V instruction of
+// the previous block (the rest of the softmax follows them).
+#ifndef FD_CHUNK_VALU_PER_MFMA
+#define FD_CHUNK_VALU_PER_MFMA 8
+#endif
 constexpr int kCT = 512;                // threads per workgroup
 constexpr int kCW = kCT / 64;           // waves
 constexpr int kCRG = 4;                 // row groups of 32 rows
@@ -765,6 +770,14 @@ __device__ __forceinline__ void chunk_pv(const bf16x8_t (&vf)[CGeo<D>::DB * 2], 
             acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[db * 2 + k2], pp[k2], acc[db], 0, 0, 0);
 }
 
+typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+
+__device__ __forceinline__ bf16x8_t pack8(bf16x2_t a, bf16x2_t b, bf16x2_t c, bf16x2_t d) {
+    const bf16x4_t ab = __builtin_shufflevector(a, b, 0, 1, 2, 3);
+    const bf16x4_t cd = __builtin_shufflevector(c, d, 0, 1, 2, 3);
+    return __builtin_shufflevector(ab, cd, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
 // Online-softmax statistics and weights of one block (no access to the
 // accumulators, so it can overlap the matrix work of the previous block):
 // tracks the exact max mx, moves the lazy reference m when the block's max
@@ -782,9 +795,11 @@ __device__ __forceinline__ void chunk_pv(const bf16x8_t (&vf)[CGeo<D>::DB * 2], 
 // keeps few dominant keys (short rows, peaked scores) exact to 2^-17.  c > 0.
 __device__ __forceinline__ void chunk_softmax(const f32x16_t& st, float c, float& m, float& l, float& mx, float& alpha,
                                               bool& moved, bf16x8_t (&ph)[2], bf16x8_t (&pl)[2], bool& lo) {
-    float sm = fmaxf(fmaxf(st[0], st[1]), fmaxf(st[2], st[3]));
+    // IEEE maximum (v_maximum3_f32): unlike fmaxf it needs no quieting of
+    // the matrix results first; a NaN score propagates either way.
+    float sm = st[0];
 #pragma unroll
-    for (int r = 4; r < 16; r += 4) sm = fmaxf(sm, fmaxf(fmaxf(st[r], st[r + 1]), fmaxf(st[r + 2], st[r + 3])));
+    for (int r = 1; r < 16; ++r) sm = __builtin_elementwise_maximum(sm, st[r]);
     const float bm = sm == -INFINITY ? -INFINITY : sm * c;
     mx = fmaxf(mx, bm);
     moved = __any(bm > m + kTau);
@@ -795,25 +810,34 @@ __device__ __forceinline__ void chunk_softmax(const f32x16_t& st, float c, float
     l *= alpha;
     const float mref = m == -INFINITY ? 0.f : m;
     lo = __any(fast_exp2(bm - mref) * 16.f > l);
-    float pr[16], hf[16];
+    // P rounded to bf16 two values per instruction; the block's share of
+    // the running sum accumulates the rounded values with bf16 dot products
+    // against ones (exact products, fp32 sums).
+    float pr[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        pr[r] = fast_exp2(fmaf(st[r], c, -mref));
-        ph[r >> 3][r & 7] = (__bf16)pr[r];
-        hf[r] = (float)ph[r >> 3][r & 7];
+    for (int r = 0; r < 16; ++r) pr[r] = fast_exp2(fmaf(st[r], c, -mref));
+    const bf16x2_t ones = {(__bf16)1.f, (__bf16)1.f};
+    bf16x2_t h2[8];
+    float bs = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        h2[i] = __builtin_convertvector(f32x2_t{pr[2 * i], pr[2 * i + 1]}, bf16x2_t);
+        bs = __builtin_amdgcn_fdot2_f32_bf16(h2[i], ones, bs, false);
     }
+    ph[0] = pack8(h2[0], h2[1], h2[2], h2[3]);
+    ph[1] = pack8(h2[4], h2[5], h2[6], h2[7]);
     if (lo) {
+        bf16x2_t l2[8];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const float d = pr[r] - hf[r];
-            pl[r >> 3][r & 7] = (__bf16)d;
-            hf[r] += (float)pl[r >> 3][r & 7];
+        for (int i = 0; i < 8; ++i) {
+            const f32x2_t d = {pr[2 * i] - (float)h2[i][0], pr[2 * i + 1] - (float)h2[i][1]};
+            l2[i] = __builtin_convertvector(d, bf16x2_t);
+            bs = __builtin_amdgcn_fdot2_f32_bf16(l2[i], ones, bs, false);
         }
+        pl[0] = pack8(l2[0], l2[1], l2[2], l2[3]);
+        pl[1] = pack8(l2[4], l2[5], l2[6], l2[7]);
     }
-    float s4[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) s4[i] = (hf[4 * i] + hf[4 * i + 1]) + (hf[4 * i + 2] + hf[4 * i + 3]);
-    l += (s4[0] + s4[1]) + (s4[2] + s4[3]);
+    l += bs;
 }
 
 // One step of the chunk kernel at stage buffer offset OFF (see above).  On
@@ -846,7 +870,7 @@ __device__ __forceinline__ void chunk_step(bool edge, const uint32_t (&ka)[CGeo<
 #pragma unroll
     for (int i = 0; i < 2 * G::DB; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, FD_CHUNK_VALU_PER_MFMA, 0);
     }
     lds_settle8(vf);
     if (moved) {
