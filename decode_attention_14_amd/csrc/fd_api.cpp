@@ -290,14 +290,9 @@ struct Fp8Scales {
     float k_scale, v_scale;
 };
 
-// Checks of an fp8-cache call: bf16 queries, rows the decode kernel serves,
-// finite scales.
+// Checks of an fp8-cache call: bf16 queries, finite scales.
 fd_status check_fp8(const fd_dims* d, const Fp8Scales* f8) {
     if (d->dtype != FD_BF16) return fail(FD_ERR_UNSUPPORTED, "fp8 caches need bf16 q and out (dims->dtype)");
-    const int64_t rows = (int64_t)d->num_q_heads / d->num_kv_heads * d->q_len;
-    if (rows > 32)
-        return fail(FD_ERR_UNSUPPORTED, "fp8 caches serve up to 32 query rows per KV head (n_rep x q_len = %lld)",
-                    (long long)rows);
     if (!std::isfinite(f8->k_scale) || !std::isfinite(f8->v_scale))
         return fail(FD_ERR_INVALID, "k_scale and v_scale must be finite");
     return FD_OK;

@@ -692,6 +692,84 @@ __device__ __forceinline__ void chunk_stage_at(const PagedKV& pk, const int32_t*
     }
 }
 
+// FP8 caches in the chunk kernel: each stage's E4M3 rows (D bytes, stored
+// order) stream into a second two-stage ring, and the workgroup dequantises
+// stage j + 1 into the bf16 ring while it computes on stage j, so the
+// products run unchanged on bf16 operands.
+template <int D>
+struct CGeo8 {
+    static constexpr int ROWB = D;                    // bytes per stored key row
+    static constexpr int CH = ROWB / 16;              // 16-byte chunks per row
+    static constexpr int RPI = 64 / CH;               // rows per 1 KiB load instruction
+    static constexpr int NDMA = CGeo<D>::SKEYS / RPI; // instructions per tensor per stage
+    static constexpr int PW = 2 * NDMA / kCW;         // instructions per wave per stage (K and V)
+    static constexpr int TENB = CGeo<D>::SKEYS * ROWB;
+    static constexpr int STGB = 2 * TENB;             // K rows, then V rows
+    static constexpr int NQ = STGB / 16 / kCT;        // 16-byte chunks each thread dequantises
+    static_assert((2 * NDMA) % kCW == 0 && PW >= 1 && STGB % (16 * kCT) == 0, "even split");
+};
+
+// Start this wave's loads of fp8 stage j into dst (see chunk_stage_at).
+// Instruction k covers RPI rows of K (isv 0) or V (isv 1) from key koff[k]
+// of the stage.
+template <int D, bool PAGED>
+__device__ __forceinline__ void chunk_stage8_at(const PagedKV& pk, const int32_t* tbl, const char* kt,
+                                                const char* vt, int lo, int kend, int j, int rsb, char* dst,
+                                                const uint32_t* dma_off, const int* lds_off, const int* koff,
+                                                const int* isv) {
+    using G8 = CGeo8<D>;
+    constexpr int SKEYS = CGeo<D>::SKEYS;
+#pragma unroll
+    for (int k = 0; k < G8::PW; ++k) {
+        const char* base = isv[k] ? vt : kt;
+        __amdgpu_buffer_rsrc_t r;
+        if constexpr (PAGED) {
+            int64_t off;
+            const uint32_t n = paged_rows(pk, tbl, lo + j * SKEYS + koff[k], G8::RPI, kend, rsb, G8::ROWB, &off);
+            r = tile_rsrc(base + off, n);
+        } else {
+            const int soff = j * SKEYS * G8::ROWB;
+            const int left = (kend - lo) * G8::ROWB - soff;
+            r = tile_rsrc(base + soff, left > 0 ? (uint32_t)left : 0u);
+        }
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(dst + lds_off[k]), 16, dma_off[k], 0, 0,
+                                                 FD_LOAD_AUX);
+    }
+}
+
+// Dequantise a landed fp8 stage (src) into the bf16 stage layout (dst):
+// thread t converts 16-byte chunks t, t + kCT, ... (inline-assembly LDS
+// accesses, as in dequant_block).
+template <int D>
+__device__ __forceinline__ void chunk_dequant_stage(const char* src, char* dst, int tid) {
+    using G = CGeo<D>;
+    using G8 = CGeo8<D>;
+    constexpr int QPT = G8::TENB / 16;  // chunks per tensor
+    u32x4_t x[G8::NQ];
+#pragma unroll
+    for (int n = 0; n < G8::NQ; ++n) x[n] = lds_read_b128(src + (n * kCT + tid) * 16);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int n = 0; n < G8::NQ; ++n) asm volatile("" : "+v"(x[n]));
+#pragma unroll
+    for (int n = 0; n < G8::NQ; ++n) {
+        const int q = n * kCT + tid;
+        const int tsr = q / QPT;  // 0: K, 1: V
+        const int rem = q - tsr * QPT;
+        const int r = rem / G8::CH;
+        const int c8 = rem - r * G8::CH;  // codes of dims 16 c8 .. 16 c8 + 15
+        uint32_t bw[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            bw[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[n][i], 1.f, false));
+            bw[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[n][i], 1.f, true));
+        }
+        char* o = dst + tsr * G::SKB * G::BLKB + (r / kCBK) * G::BLKB;
+        lds_write_b128(o + cswz<D>(r % kCBK, 2 * c8), u32x4_t{bw[0], bw[1], bw[2], bw[3]});
+        lds_write_b128(o + cswz<D>(r % kCBK, 2 * c8 + 1), u32x4_t{bw[4], bw[5], bw[6], bw[7]});
+    }
+}
+
 template <int N>
 __device__ __forceinline__ void lds_settle8(bf16x8_t (&v)[N]) {
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -880,12 +958,16 @@ __device__ __forceinline__ void chunk_step(bool edge, const uint32_t (&ka)[CGeo<
     if (lo) chunk_pv<D>(vf, pl, acc);
 }
 
-template <int D, bool PAGED>
+template <int D, bool PAGED, bool FP8>
 __global__ __launch_bounds__(kCT) void fd_mfma_chunk_kernel(PartialArgs a) {
     using G = CGeo<D>;
+    using G8 = CGeo8<D>;
+    static_assert(!FP8 || kCNS == 2, "the fp8 pipeline keeps two stages in each ring");
+    constexpr int ESZ = FP8 ? 1 : 2;  // bytes per stored K/V element
     constexpr int RS = D + 4;  // padded row stride of the merge area (floats)
     constexpr int MERGEB = kCRG * (32 * RS + 3 * 32) * 4;
-    constexpr int SMEMB = kCNS * G::STGB > MERGEB ? kCNS * G::STGB : MERGEB;
+    constexpr int RINGB = kCNS * G::STGB + (FP8 ? 2 * G8::STGB : 0);
+    constexpr int SMEMB = RINGB > MERGEB ? RINGB : MERGEB;
     __shared__ __attribute__((aligned(16))) char smem[SMEMB];
 
     const int s = blockIdx.x;
@@ -972,17 +1054,33 @@ __global__ __launch_bounds__(kCT) void fd_mfma_chunk_kernel(PartialArgs a) {
     int rsb;  // bytes from one key row of the head to the next
     const int32_t* tbl = nullptr;
     if constexpr (PAGED) {
-        kt = static_cast<const char*>(a.k) + g * a.pages.head_stride * 2;
-        vt = static_cast<const char*>(a.v) + g * a.pages.head_stride * 2;
-        rsb = a.pages.row_stride * 2;
+        kt = static_cast<const char*>(a.k) + g * a.pages.head_stride * ESZ;
+        vt = static_cast<const char*>(a.v) + g * a.pages.head_stride * ESZ;
+        rsb = a.pages.row_stride * ESZ;
         tbl = a.pages.table + (int64_t)b * a.pages.max_pages;
     } else {
         const int64_t tile_row = ((int64_t)b * a.Hkv + g) * a.Lmax + lo;
-        kt = static_cast<const char*>(a.k) + tile_row * G::ROWB;
-        vt = static_cast<const char*>(a.v) + tile_row * G::ROWB;
-        rsb = G::ROWB;
+        kt = static_cast<const char*>(a.k) + tile_row * (D * ESZ);
+        vt = static_cast<const char*>(a.v) + tile_row * (D * ESZ);
+        rsb = D * ESZ;
     }
     const int nst = (kend - lo + G::SKEYS - 1) / G::SKEYS;
+
+    // fp8 loads: instruction n = w + k * kCW of a stage covers RPI rows of K
+    // (n < NDMA) or V, in stored order.
+    uint32_t dma8[FP8 ? G8::PW : 1];
+    int lds8[FP8 ? G8::PW : 1], koff8[FP8 ? G8::PW : 1], isv8[FP8 ? G8::PW : 1];
+    if constexpr (FP8) {
+#pragma unroll
+        for (int k = 0; k < G8::PW; ++k) {
+            const int n = w + k * kCW;
+            isv8[k] = n / G8::NDMA;
+            const int i = n - isv8[k] * G8::NDMA;
+            koff8[k] = i * G8::RPI;
+            lds8[k] = isv8[k] * G8::TENB + i * 1024;
+            dma8[k] = (uint32_t)((PAGED ? lane / G8::CH : koff8[k] + lane / G8::CH) * rsb + (lane % G8::CH) * 16);
+        }
+    }
 
     // Load instruction k of this wave fills RPI rows of block bb of a stage;
     // lane l takes row l / CH, global chunk (l % CH) ^ swizzle.
@@ -1021,9 +1119,21 @@ __global__ __launch_bounds__(kCT) void fd_mfma_chunk_kernel(PartialArgs a) {
                             8 * (q4 & 1);
     }
 
+    char* ring8 = smem + kCNS * G::STGB;  // fp8: the stored-row ring
+    if constexpr (FP8) {
+        // fp8 stages 0 and 1 in flight; stage 0 dequantised into bf16 slot 0.
+        chunk_stage8_at<D, PAGED>(a.pages, tbl, kt, vt, lo, kend, 0, rsb, ring8, dma8, lds8, koff8, isv8);
+        chunk_stage8_at<D, PAGED>(a.pages, tbl, kt, vt, lo, kend, 1, rsb, ring8 + G8::STGB, dma8, lds8, koff8,
+                                  isv8);
+        wait_vmcnt_le<G8::PW>();
+        __syncthreads();
+        chunk_dequant_stage<D>(ring8, smem, tid);
+    } else {
 #pragma unroll
-    for (int j = 0; j < kCNS - 1; ++j)
-        chunk_stage_at<D, PAGED>(a.pages, tbl, kt, vt, lo, kend, j, rsb, smem + j * G::STGB, dma_off, lds_off, koff);
+        for (int j = 0; j < kCNS - 1; ++j)
+            chunk_stage_at<D, PAGED>(a.pages, tbl, kt, vt, lo, kend, j, rsb, smem + j * G::STGB, dma_off, lds_off,
+                                     koff);
+    }
 
     // Stage j lives in ring slot j % kCNS; unrolling by kCNS makes the slot,
     // and so every LDS offset, a compile-time constant.  A wave whose block
@@ -1037,10 +1147,22 @@ __global__ __launch_bounds__(kCT) void fd_mfma_chunk_kernel(PartialArgs a) {
         for (int u = 0; u < kCNS; ++u) {
             const int j = j0 + u;
             if (j >= nst) break;
-            wait_vmcnt_le<(kCNS - 1) * 2 * G::DPW>();  // this wave's loads of stage j
-            __syncthreads();                           // everyone's; stage j - 1 is free
-            chunk_stage_at<D, PAGED>(a.pages, tbl, kt, vt, lo, kend, j + kCNS - 1, rsb,
-                                     smem + ((u + kCNS - 1) % kCNS) * G::STGB, dma_off, lds_off, koff);
+            if constexpr (FP8) {
+                // Own loads of fp8 stage j + 1 landed; after the barrier
+                // everyone's have, bf16 slot u holds stage j, slot 1 - u and
+                // fp8 slot u are free.
+                wait_vmcnt_le<0>();
+                __syncthreads();
+                chunk_stage8_at<D, PAGED>(a.pages, tbl, kt, vt, lo, kend, j + 2, rsb, ring8 + u * G8::STGB, dma8,
+                                          lds8, koff8, isv8);
+                if (j + 1 < nst)
+                    chunk_dequant_stage<D>(ring8 + (1 - u) * G8::STGB, smem + (1 - u) * G::STGB, tid);
+            } else {
+                wait_vmcnt_le<(kCNS - 1) * 2 * G::DPW>();  // this wave's loads of stage j
+                __syncthreads();                           // everyone's; stage j - 1 is free
+                chunk_stage_at<D, PAGED>(a.pages, tbl, kt, vt, lo, kend, j + kCNS - 1, rsb,
+                                         smem + ((u + kCNS - 1) % kCNS) * G::STGB, dma_off, lds_off, koff);
+            }
             const int key0 = lo + j * G::SKEYS + kh * kCBK;
             const bool edge = key0 + kCBK > mask_from;
             if (u == 0) chunk_step<D, 0>(edge, ka, va, qf, acc, vf, ph, m, l, mx, key0, rend, c, hl);
@@ -1083,7 +1205,8 @@ __global__ __launch_bounds__(kCT) void fd_mfma_chunk_kernel(PartialArgs a) {
     const float den = l * f1 + sm_l[rg * 32 + col] * f2;
     const float X = fmaxf(mx, sm_x[rg * 32 + col]);
     const bool empty = M == -INFINITY;
-    const float inv = empty ? 0.f : 1.f / den;
+    // fp8: V was dequantised without its scale
+    const float inv = empty ? 0.f : (FP8 ? a.v_scale : 1.f) / den;
     const float lse_v = empty ? -INFINITY : (M + log2f(den)) * kLn2;
     const float* o2 = sm_acc + (rg * 32 + col) * RS;
     if (a.direct) {
@@ -1125,6 +1248,23 @@ __global__ __launch_bounds__(kCT) void fd_mfma_chunk_kernel(PartialArgs a) {
     }
 }
 
+template <int D, bool PAGED>
+void launch_chunk_p(int batch, const PartialArgs& a, hipStream_t stream) {
+    dim3 grid(a.rule.slots, a.Hkv * a.row_blocks, batch), block(kCT);
+    if (a.kv_fp8)
+        hipLaunchKernelGGL((fd_mfma_chunk_kernel<D, PAGED, true>), grid, block, 0, stream, a);
+    else
+        hipLaunchKernelGGL((fd_mfma_chunk_kernel<D, PAGED, false>), grid, block, 0, stream, a);
+}
+
+template <int D>
+void launch_chunk(int batch, const PartialArgs& a, hipStream_t stream) {
+    if (a.pages.table != nullptr)
+        launch_chunk_p<D, true>(batch, a, stream);
+    else
+        launch_chunk_p<D, false>(batch, a, stream);
+}
+
 template <int D, int NB, bool FP8>
 void launch_nb_kv(int batch, const PartialArgs& a, hipStream_t stream) {
     dim3 grid(a.Hkv, a.rule.slots, batch), block(FP8 ? 64 * kMW8 : kMT);
@@ -1154,20 +1294,10 @@ void launch_nb(int batch, const PartialArgs& a, hipStream_t stream) {
 
 hipError_t launch_partials_mfma(int head_dim, int batch, const PartialArgs& a, hipStream_t stream) {
     if (a.rows > 32) {
-        if (a.kv_fp8) return hipErrorNotSupported;  // the chunk tiles read bf16 caches only
-        dim3 grid(a.rule.slots, a.Hkv * a.row_blocks, batch), block(kCT);
-        const bool paged = a.pages.table != nullptr;
-        if (head_dim == 64) {
-            if (paged)
-                hipLaunchKernelGGL((fd_mfma_chunk_kernel<64, true>), grid, block, 0, stream, a);
-            else
-                hipLaunchKernelGGL((fd_mfma_chunk_kernel<64, false>), grid, block, 0, stream, a);
-        } else {
-            if (paged)
-                hipLaunchKernelGGL((fd_mfma_chunk_kernel<128, true>), grid, block, 0, stream, a);
-            else
-                hipLaunchKernelGGL((fd_mfma_chunk_kernel<128, false>), grid, block, 0, stream, a);
-        }
+        if (head_dim == 64)
+            launch_chunk<64>(batch, a, stream);
+        else
+            launch_chunk<128>(batch, a, stream);
         return hipGetLastError();
     }
     const bool two = a.rows > 16;

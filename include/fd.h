@@ -240,8 +240,8 @@ fd_status fd_decode_partials_paged(const fd_dims* dims, const void* q, const voi
  *
  * Layouts as for bf16 caches with one byte per element: contiguous
  * [B, Hkv, Lmax, D] when pages is NULL, else the paged layouts of
- * fd_kv_pages.  Served: up to 32 query rows per KV head (n_rep * q_len <= 32:
- * decode and short verification chunks); more rows give FD_ERR_UNSUPPORTED.
+ * fd_kv_pages.  Every q_len is served (decode, verification chunks and long
+ * prefill chunks).
  * Errors: as the bf16 calls; FD_ERR_UNSUPPORTED if dims->dtype is not
  * FD_BF16; FD_ERR_INVALID for non-finite scales. */
 fd_status fd_decode_attention_fp8(const fd_dims* dims, const void* q, const void* k_cache,

@@ -150,8 +150,8 @@ void validation_paths() {
                                     fake(4), nullptr, nullptr);
     CHECK(fd_decode_attention_fp8(&good, fake(0), fake(1), fake(2), nullptr, NAN, 1.f, dl, 0.1f, 0, nullptr,
                                   nullptr, 0, fake(4), nullptr, nullptr) == FD_ERR_INVALID);
-    const fd_dims chunk{1, 32, 8, 128, 9, 64, FD_BF16};
-    CHECK(fd_decode_attention_fp8(&chunk, fake(0), fake(1), fake(2), nullptr, 1.f, 1.f, dl, 0.1f, 0, nullptr,
+    const fd_dims f32q{1, 32, 8, 128, 9, 64, FD_F32};
+    CHECK(fd_decode_attention_fp8(&f32q, fake(0), fake(1), fake(2), nullptr, 1.f, 1.f, dl, 0.1f, 0, nullptr,
                                   nullptr, 0, fake(4), nullptr, nullptr) == FD_ERR_UNSUPPORTED);
     // Calls that pass validation reach the (stubbed) launch and report a
     // device error, with the message recorded.

@@ -114,3 +114,35 @@ def test_fp8_headline_shape():
     torch.cuda.synchronize()
     err, lerr = compare("fp8 gqa_32k", out, lse, ref_out, ref_lse, TOL["bf16"])
     say(f"  max abs err out {err:.2e} lse {lerr:.2e}")
+
+
+@pytest.mark.parametrize("D", [128, 64])
+def test_fp8_long_chunks(D):
+    """Row groups of more than 32 rows over FP8 caches: the chunk kernel's
+    fp8 ring, dequantised a stage ahead."""
+    for T, Hq, Hkv, lens in [(33, 1, 1, [40, 33]), (100, 4, 1, [900, 100]), (128, 8, 2, [128, 700]),
+                             (200, 4, 2, [1500, 150])]:
+        for S in (1, 3):
+            check_fp8(f"chunk q_len={T} Hq={Hq} Hkv={Hkv} D={D} S={S}", len(lens), Hq, Hkv, D, T, max(lens),
+                      3500 + T + S, lens, num_splits=S)
+    check_fp8(f"chunk planned D={D}", 2, 8, 2, D, 96, 2000, 3590, [2000, 96], use_plan=True)
+    check_fp8(f"chunk q x10 D={D}", 1, 4, 1, D, 80, 900, 3591, [900], q_mul=10.0, num_splits=2)
+    for P, layout in ((16, "nhd"), (64, "hnd")):
+        check_fp8(f"chunk paged {P} {layout} D={D}", 2, 8, 2, D, 64, 1024, 3592 + P, [1024, 100], num_splits=2,
+                  page=(P, layout))
+
+
+def test_fp8_prefill_workload():
+    """The 512-query prefill chunk over FP8 caches: every row against the oracle."""
+    w = WORKLOADS["prefill_chunk_512"]
+    say(f"[case] fp8 workload {w.name}")
+    q, k, v, cl = workload_inputs(w)
+    ks, vs = fp8_scale_for(k), fp8_scale_for(v)
+    kc, vc = quantize_fp8(k, ks), quantize_fp8(v, vs)
+    del k, v
+    plan = fd.plan_for(q, kc, cl)
+    ref_out, ref_lse = oracle.attention_fp8(as_oracle_array(q), kc.numpy(), vc.numpy(), cl.numpy(), w.scale, ks, vs)
+    out, lse = fd.decode_attention_fp8(q.cuda(), kc.cuda(), vc.cuda(), cl.cuda(), ks, vs, scale=w.scale, plan=plan)
+    torch.cuda.synchronize()
+    err, lerr = compare("fp8 prefill_chunk_512", out, lse, ref_out, ref_lse, TOL["bf16"])
+    say(f"  max abs err out {err:.2e} lse {lerr:.2e}")
