@@ -316,10 +316,12 @@ def main():
             "kernel": partial_kernel_name(w), "bytes_per_launch": partial_bytes,
         },
     }
-    if w.q_len > 1 and w.dtype == "bf16":
-        # A long chunk is a dense contraction: its partial pass is priced
-        # against the matrix cores, with the HBM figures kept beside it.
-        flops = algorithmic_flops(w, lens)
+    flops = algorithmic_flops(w, lens)
+    if w.dtype == "bf16" and flops / partial_bytes > MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9):
+        # Above the machine balance (about 312 flop per byte) the partial
+        # pass is a dense contraction (a long chunk) and is priced against the
+        # matrix cores, with the HBM figures kept beside it; decode and short
+        # verification chunks stay HBM-bound.
         tflops = flops / (part_ms * 1e-3) / 1e12
         result["roofline"] = {
             "bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",

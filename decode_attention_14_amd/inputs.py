@@ -61,6 +61,8 @@ WORKLOADS = {
                  notes="long-context GQA decode, 4 x 128k"),
         Workload("prefill_chunk_512", 1, 32, 8, 128, 512, 8192, "bf16", 14005, cache_len=8192,
                  notes="chunked-prefill chunk: 512 queries over 7680 cached + 512 new keys"),
+        Workload("verify_q4_32k", 1, 32, 8, 128, 4, 32768, "bf16", 14006, cache_len=32768,
+                 notes="speculative-decoding verification: 4 draft tokens (causal) over a 32k cache"),
     ]
 }
 

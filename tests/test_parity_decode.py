@@ -43,7 +43,7 @@ def test_workload_mha_tiny_1k():
     compare(w.name + " planned", out, lse, *ref, TOL[w.dtype])
 
 
-@pytest.mark.parametrize("name", ["gqa_32k", "varlen_b32"])
+@pytest.mark.parametrize("name", ["gqa_32k", "varlen_b32", "verify_q4_32k"])
 def test_workload_full_oracle(name):
     w = WORKLOADS[name]
     say(f"[case] workload {w.name} (planner splits, whole output against the oracle)")
