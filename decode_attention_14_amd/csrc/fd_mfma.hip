@@ -638,11 +638,28 @@ struct CGeo {
     static_assert(NDMA % kCW == 0 && DPW >= 1, "stage loads split evenly over the waves");
 };
 
+// XOR swizzle of the chunk kernel's 16-byte chunks (CH chunks per row).
+// Its read patterns: 16 consecutive rows at one chunk (K operands), and an
+// aligned group of 4 rows at 4 consecutive chunks 4d .. 4d + 3 (transposed
+// V reads of 32 lanes, 256 bytes per LDS cycle).  For CH = 16 (256-byte
+// rows, one bank cycle each) row bits 1:0 go to chunk bits 3:2 and row bits
+// 3:2 to bits 1:0: a bijection on 16 rows, and within a 4-row group it
+// moves only bits 3:2, which the 4 consecutive chunks leave apart.  For
+// CH = 8 two 128-byte rows share a bank cycle, so the rows of one parity
+// must differ: the row pair index u = r >> 1 gives bit 2 from u bit 0 and
+// bits 1:0 from u bits 2:1.
+template <int CH>
+__device__ __forceinline__ int cswf(int r) {
+    if constexpr (CH == 16) return ((r & 3) << 2) | ((r >> 2) & 3);
+    const int u = (r >> 1) & 7;
+    return ((u & 1) << 2) | (u >> 1);
+}
+
 // Byte offset inside a 32-row block of global chunk c of row r (the swizzle
-// of swf repeats every 16 rows).
+// of cswf repeats every 16 rows).
 template <int D>
 __device__ __forceinline__ int cswz(int r, int c) {
-    return r * CGeo<D>::ROWB + ((c ^ swf<CGeo<D>::CH>(r)) << 4);
+    return r * CGeo<D>::ROWB + ((c ^ cswf<CGeo<D>::CH>(r)) << 4);
 }
 
 // Start this wave's share of one stage's loads: bytes [off, off + stage) of
@@ -1093,7 +1110,7 @@ __global__ __launch_bounds__(kCT) void fd_mfma_chunk_kernel(PartialArgs a) {
         const int bb = n / G::IPB;
         const int i = n - bb * G::IPB;
         const int r = i * G::RPI + lane / G::CH;
-        const int cg = (lane % G::CH) ^ swf<G::CH>(r);
+        const int cg = (lane % G::CH) ^ cswf<G::CH>(r);
         koff[k] = bb * kCBK + i * G::RPI;
         dma_off[k] = (uint32_t)((PAGED ? lane / G::CH : koff[k] + lane / G::CH) * rsb + cg * 16);
         lds_off[k] = bb * G::BLKB + i * 1024;
