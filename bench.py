@@ -41,15 +41,23 @@ METRIC = "decode-attention HBM GB/s (% of MI355X peak) and µs/step at 32k ctx"
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 matrix-core peak of MI355X
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCES = [os.path.join(ROOT, "decode_attention_14_amd", "csrc", f)
-                  for f in ("fd_decode.hip", "fd_mfma.hip", "fd_device.h", "fd_internal.h")] + [
-                      os.path.join(ROOT, "decode_attention_14_amd", "build.py")]
+CSRC = os.path.join(ROOT, "decode_attention_14_amd", "csrc")
+# The sources that decide each partial-pass kernel's machine code (its own
+# file, the headers it includes, and the build flags).
+_COMMON_SOURCES = [os.path.join(CSRC, "fd_device.h"), os.path.join(CSRC, "fd_internal.h"),
+                   os.path.join(ROOT, "decode_attention_14_amd", "build.py")]
+KERNEL_SOURCES = {
+    "fd_partial_kernel": [os.path.join(CSRC, "fd_decode.hip")],
+    "fd_mfma_partial_kernel": [os.path.join(CSRC, "fd_mfma.hip"), os.path.join(CSRC, "fd_mfma_common.h")],
+    "fd_mfma_chunk_kernel": [os.path.join(CSRC, "fd_chunk.hip"), os.path.join(CSRC, "fd_mfma_common.h")],
+}
 
 
-def kernel_source_hash() -> str:
-    """Hash of the kernel sources and build flags; counter data is tied to it."""
+def kernel_source_hash(kernel: str) -> str:
+    """Hash of one kernel's sources and the build flags; counter data taken
+    for that kernel is tied to it."""
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in KERNEL_SOURCES[kernel] + _COMMON_SOURCES:
         with open(p, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -273,7 +281,9 @@ def main():
         try:
             t = json.load(open(TRAFFIC_FILE)).get(w.name + ("/fp8" if fp8 else "") +
                                                   (f"/paged{args.page_size}{args.page_layout}" if paged else ""))
-            if t and t.get("kernel_hash") == kernel_source_hash() and t.get("tile_len") == plan.tile_len:
+            if (t and t.get("kernel") == partial_kernel_name(w)
+                    and t.get("kernel_hash") == kernel_source_hash(t["kernel"])
+                    and t.get("tile_len") == plan.tile_len):
                 traffic = t.get("bytes_per_launch")
         except (OSError, ValueError):
             traffic = None

@@ -1,5 +1,5 @@
 // fd_device.h -- device helpers shared by the HIP kernels of the library
-// (fd_decode.hip, fd_mfma.hip).  Not installed; not part of the ABI.
+// (fd_decode.hip, fd_mfma.hip, fd_chunk.hip).  Not installed; not part of the ABI.
 #pragma once
 
 #include <hip/hip_runtime.h>

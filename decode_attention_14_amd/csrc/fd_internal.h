@@ -87,8 +87,10 @@ int vector_block_rows(int rows);
 bool use_mfma_partials(int dtype, int head_dim, int rows);
 bool vector_kernel_forced();
 
-// Matrix-core launches (fd_mfma.hip).
+// Matrix-core launches: row groups of up to 32 rows (fd_mfma.hip), which
+// hands larger ones to the chunk kernel (fd_chunk.hip).
 hipError_t launch_partials_mfma(int head_dim, int batch, const PartialArgs& a, hipStream_t stream);
+hipError_t launch_chunk_mfma(int head_dim, int batch, const PartialArgs& a, hipStream_t stream);
 
 hipError_t launch_combine(int head_dim, int out_dtype, int64_t rows, int slots,
                           const float* o_part, const float* lse_part, void* out, float* lse,
