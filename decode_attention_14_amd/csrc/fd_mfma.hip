@@ -489,39 +489,60 @@ __global__ __launch_bounds__(FP8 ? 64 * kMW8 : kMT) void fd_mfma_partial_kernel(
     }
     __syncthreads();
 
-    for (int idx = tid; idx < nrows * D; idx += MT) {
-        const int r = idx / D;
-        const int d = idx - r * D;
+    // Per row (one thread each): the merged max, the log-sum-exp, and each
+    // wave's weight exp2(m_w - M) / sum, written over that wave's l entry.
+    if (tid < nrows) {
+        const int r = tid;
         float M = -INFINITY, X = -INFINITY;
 #pragma unroll
         for (int x = 0; x < MW; ++x) {
             M = fmaxf(M, sm_m[x * NR + r]);
             X = fmaxf(X, sm_x[x * NR + r]);
         }
-        float num = 0.f, den = 0.f;
-        if (M != -INFINITY) {
+        float f[MW];
+        float den = 0.f;
 #pragma unroll
-            for (int x = 0; x < MW; ++x) {
-                const float mw = sm_m[x * NR + r];
-                const float f = mw == -INFINITY ? 0.f : fast_exp2(mw - M);
-                num = fmaf(f, sm_acc[(x * NR + r) * RS + d], num);
-                den = fmaf(f, sm_l[x * NR + r], den);
-            }
+        for (int x = 0; x < MW; ++x) {
+            const float mw = sm_m[x * NR + r];
+            f[x] = (M == -INFINITY || mw == -INFINITY) ? 0.f : fast_exp2(mw - M);
+            den = fmaf(f[x], sm_l[x * NR + r], den);
         }
         const bool empty = M == -INFINITY;
-        float o = empty ? 0.f : num / den;
-        if constexpr (FP8) o *= a.v_scale;  // V was dequantised without its scale
+        // fp8: V was dequantised without its scale
+        const float inv = empty ? 0.f : (FP8 ? a.v_scale : 1.f) / den;
+#pragma unroll
+        for (int x = 0; x < MW; ++x) sm_l[x * NR + r] = f[x] * inv;
+        sm_m[r] = M;  // row r's entries are this thread's alone
         const float lse_v = empty ? -INFINITY : (M + log2f(den)) * kLn2;
         const int64_t row = row0 + r;
         if (a.direct) {
-            reinterpret_cast<uint16_t*>(a.out)[row * D + d] = f32_to_bf16(o);
-            if (d == 0 && a.lse) a.lse[row] = lse_v;
+            if (a.lse) a.lse[row] = lse_v;
         } else {
-            if (!empty) a.o_part[(row * slots + s) * D + d] = o;
-            if (d == 0) {
-                a.m_part[row * slots + s] = empty ? -INFINITY : X * kLn2;
-                a.lse_part[row * slots + s] = lse_v;
-            }
+            a.m_part[row * slots + s] = empty ? -INFINITY : X * kLn2;
+            a.lse_part[row * slots + s] = lse_v;
+        }
+    }
+    __syncthreads();
+
+    // Outputs, four columns per thread: the weighted sum of the waves' rows.
+    // A row with no visible key gets zeros (direct) or no o_part entry.
+    constexpr int C4 = D / 4;
+    for (int idx = tid; idx < nrows * C4; idx += MT) {
+        const int r = idx / C4;
+        const int c4 = idx - r * C4;
+        if (!a.direct && sm_m[r] == -INFINITY) continue;
+        f32x4_t o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int x = 0; x < MW; ++x)
+            o += sm_l[x * NR + r] * *reinterpret_cast<const f32x4_t*>(sm_acc + (x * NR + r) * RS + 4 * c4);
+        const int64_t row = row0 + r;
+        if (a.direct) {
+            uint2 pk;
+            pk.x = (uint32_t)f32_to_bf16(o[0]) | ((uint32_t)f32_to_bf16(o[1]) << 16);
+            pk.y = (uint32_t)f32_to_bf16(o[2]) | ((uint32_t)f32_to_bf16(o[3]) << 16);
+            *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.out) + row * D + 4 * c4) = pk;
+        } else {
+            *reinterpret_cast<f32x4_t*>(a.o_part + (row * slots + s) * D + 4 * c4) = o;
         }
     }
 }

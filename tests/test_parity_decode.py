@@ -207,8 +207,11 @@ def test_partials_match_oracle_tiles(dt, T):
     lens = [1000, 77, 0]
     q, k, v, cl = inputs(3, 8, 2, 128, T, 1000, dt, 1000 + T, lens)
     S = 6
+    # Slots with no visible key must leave their o_part entries alone.
+    sentinel = 12345.0
+    o_p = torch.full((3, 8, T, S, 128), sentinel, dtype=torch.float32, device="cuda")
     o_p, m_p, l_p = fd.decode_partials(q.cuda(), k.cuda(), v.cuda(), cl.cuda(), scale=_scale(128),
-                                       num_splits=S)
+                                       num_splits=S, o_part=o_p)
     torch.cuda.synchronize()
     _, _, ro, rm, rl = oracle.attention_split(as_oracle_array(q), as_oracle_array(k),
                                               as_oracle_array(v), cl.numpy(), _scale(128),
@@ -222,6 +225,7 @@ def test_partials_match_oracle_tiles(dt, T):
     assert np.max(np.abs(gl[fin] - rl[fin])) <= tol
     go = o_p.cpu().double().numpy()
     assert np.max(np.abs(go[fin] - ro[fin])) <= tol
+    assert (go[~fin] == sentinel).all(), "an empty slot's o_part entry was written"
 
 
 def test_combine_matches_oracle_merge():
