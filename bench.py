@@ -13,8 +13,8 @@ synchronisations and events on the stream the kernels run on.  The K/V caches
 rotate over several identical copies (>= 1 GiB in total) so that the 256 MB
 last-level cache cannot hold them and every step reads HBM.
 
-``--kv-fp8`` quantises K and V to FP8 E4M3 codes with per-tensor scales (bf16
-queries and output).  ``--page-size P`` runs the same workload on a paged cache (pages of P keys in
+``--kv-fp8`` / ``--kv-int8`` quantise K and V to FP8 E4M3 or INT8 codes with
+per-tensor scales (bf16 queries and output).  ``--page-size P`` runs the same workload on a paged cache (pages of P keys in
 a shuffled pool, read in place through the block table; ``--page-layout``
 picks [pages, P, Hkv, D] or [pages, Hkv, P, D]).
 
@@ -77,6 +77,8 @@ def parse_args():
     ap.add_argument("--page-size", type=int, default=0,
                     help="read K/V from a paged cache with pages of this many keys (0: contiguous)")
     ap.add_argument("--page-layout", default="nhd", choices=["nhd", "hnd"])
+    ap.add_argument("--kv-int8", action="store_true",
+                    help="INT8 K/V caches (symmetric per-tensor scales) with bf16 queries")
     ap.add_argument("--kv-fp8", action="store_true",
                     help="FP8 E4M3 K/V caches (per-tensor scales) with bf16 queries")
     ap.add_argument("--calibrate-copy", type=int, default=0,
@@ -84,10 +86,10 @@ def parse_args():
     return ap.parse_args()
 
 
-def algorithmic_bytes(w, lens, kv_fp8=False):
+def algorithmic_bytes(w, lens, kv_codes=False):
     """Bytes any implementation must move: visible K and V rows, q, out, lse."""
     el = 2 if w.dtype == "bf16" else 4
-    kv = 2 * sum(lens) * w.num_kv_heads * w.head_dim * (1 if kv_fp8 else el)
+    kv = 2 * sum(lens) * w.num_kv_heads * w.head_dim * (1 if kv_codes else el)
     q = w.batch * w.num_q_heads * w.q_len * w.head_dim * el
     return kv, q, q, w.batch * w.num_q_heads * w.q_len * 4
 
@@ -145,7 +147,8 @@ def main():
     import torch
 
     from decode_attention_14_amd import binding as fd
-    from decode_attention_14_amd.inputs import WORKLOADS, fp8_scale_for, paginate, quantize_fp8, workload_inputs
+    from decode_attention_14_amd.inputs import (WORKLOADS, fp8_scale_for, int8_scale_for, paginate, quantize_fp8,
+                                                quantize_int8, workload_inputs)
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -157,14 +160,21 @@ def main():
     print(f"[bench] generating {w.name}", file=sys.stderr, flush=True)
     q, k, v, cl = workload_inputs(w)
     lens = cl.tolist()
-    fp8 = args.kv_fp8
-    if fp8:
+    if args.kv_fp8 and args.kv_int8:
+        print("--kv-fp8 and --kv-int8 exclude each other", file=sys.stderr)
+        sys.exit(2)
+    codes = "fp8" if args.kv_fp8 else "int8" if args.kv_int8 else None  # one-byte K/V codes
+    coded = codes is not None
+    if coded:
         if w.dtype != "bf16":
-            print("--kv-fp8 needs a bf16 workload", file=sys.stderr)
+            print(f"--kv-{codes} needs a bf16 workload", file=sys.stderr)
             sys.exit(2)
-        k_scale, v_scale = fp8_scale_for(k), fp8_scale_for(v)
-        k, v = quantize_fp8(k, k_scale), quantize_fp8(v, v_scale)
-    kv_b, q_b, out_b, lse_b = algorithmic_bytes(w, lens, fp8)
+        scale_for, quantize = (fp8_scale_for, quantize_fp8) if codes == "fp8" else (int8_scale_for, quantize_int8)
+        k_scale, v_scale = scale_for(k), scale_for(v)
+        k, v = quantize(k, k_scale), quantize(v, v_scale)
+        attn_codes = fd.decode_attention_fp8 if codes == "fp8" else fd.decode_attention_int8
+        partials_codes = fd.decode_partials_fp8 if codes == "fp8" else fd.decode_partials_int8
+    kv_b, q_b, out_b, lse_b = algorithmic_bytes(w, lens, coded)
     step_bytes = kv_b + q_b + out_b + lse_b
     partial_bytes = kv_b + q_b
 
@@ -200,8 +210,8 @@ def main():
 
     def step(i):
         kd, vd = kvs[i % copies]
-        if fp8:
-            fd.decode_attention_fp8(qd, kd, vd, cld, k_scale, v_scale, block_table=table, layout=args.page_layout,
+        if coded:
+            attn_codes(qd, kd, vd, cld, k_scale, v_scale, block_table=table, layout=args.page_layout,
                                     scale=w.scale, num_splits=num_splits, plan=fplan, out=out, lse=lse,
                                     workspace=ws if ws_bytes else None)
         elif paged:
@@ -214,12 +224,12 @@ def main():
 
     def partial(i):
         kd, vd = kvs[i % copies]
-        if fp8 and slots > 1:
-            fd.decode_partials_fp8(qd, kd, vd, cld, k_scale, v_scale, block_table=table, layout=args.page_layout,
+        if coded and slots > 1:
+            partials_codes(qd, kd, vd, cld, k_scale, v_scale, block_table=table, layout=args.page_layout,
                                    scale=w.scale, num_splits=num_splits, plan=fplan, o_part=o_part,
                                    m_part=m_part, lse_part=l_part)
-        elif fp8:
-            fd.decode_attention_fp8(qd, kd, vd, cld, k_scale, v_scale, block_table=table, layout=args.page_layout,
+        elif coded:
+            attn_codes(qd, kd, vd, cld, k_scale, v_scale, block_table=table, layout=args.page_layout,
                                     scale=w.scale, out=out, lse=lse)
         elif paged and slots > 1:
             fd.decode_partials_paged(qd, kd, vd, table, cld, layout=args.page_layout, scale=w.scale,
@@ -279,7 +289,7 @@ def main():
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
         try:
-            t = json.load(open(TRAFFIC_FILE)).get(w.name + ("/fp8" if fp8 else "") +
+            t = json.load(open(TRAFFIC_FILE)).get(w.name + (f"/{codes}" if coded else "") +
                                                   (f"/paged{args.page_size}{args.page_layout}" if paged else ""))
             if (t and t.get("kernel") == partial_kernel_name(w)
                     and t.get("kernel_hash") == kernel_source_hash(t["kernel"])
@@ -307,7 +317,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": (w.dtype + " q/out, fp8 e4m3 k/v") if fp8 else w.dtype,
+        "dtype": (w.dtype + (" q/out, fp8 e4m3 k/v" if codes == "fp8" else " q/out, int8 k/v")) if coded else w.dtype,
         "data": "synthetic",
         "config": {
             "workload": w.name, "batch": w.batch, "q_heads": w.num_q_heads,
@@ -316,7 +326,8 @@ def main():
                 list(w.len_range), sum(lens)),
             "tile_len": plan.tile_len, "splits": slots, "kv_copies": copies,
             "kv_cache": (f"paged, {args.page_size}-key pages, {args.page_layout}" if paged else "contiguous") +
-                        (", fp8 e4m3 (per-tensor scales)" if fp8 else ""),
+                        ({"fp8": ", fp8 e4m3 (per-tensor scales)", "int8": ", int8 (symmetric per-tensor scales)",
+                          None: ""}[codes]),
             "step_bytes": step_bytes, "timing": "eager" if args.no_graph else "graph",
         },
         "kernels": {"partial_us": round(part_ms * 1e3, 3), "combine_us": round(comb_ms * 1e3, 3)},
@@ -339,7 +350,7 @@ def main():
             "kernel": partial_kernel_name(w), "flops_per_launch": flops,
             "hbm_achieved_GBs": round(achieved, 2),
         }
-    if not args.no_cpu_baseline and (fp8 or paged):
+    if not args.no_cpu_baseline and (coded or paged):
         print("[bench] cpu baseline is timed on the contiguous bf16/fp32 workload only", file=sys.stderr)
     elif not args.no_cpu_baseline:
         print("[bench] timing the fp64 oracle on host cores", file=sys.stderr, flush=True)

@@ -18,15 +18,15 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("FD_LIBRARY", os.path.join(_PKG, "libfd.so"))
 
 FD_OK, FD_ERR_INVALID, FD_ERR_UNSUPPORTED, FD_ERR_WORKSPACE, FD_ERR_DEVICE = 0, -1, -2, -3, -4
-FD_F32, FD_BF16, FD_FP8_E4M3 = 0, 1, 2
+FD_F32, FD_BF16, FD_FP8_E4M3, FD_INT8 = 0, 1, 2, 3
 FD_MAX_SPLITS = 256
 
 FD_PAGES_NHD, FD_PAGES_HND = 0, 1
 
 EXPORTS = ("fd_plan_splits", "fd_workspace_bytes", "fd_decode_partials", "fd_combine_splits",
            "fd_decode_attention", "fd_decode_attention_paged", "fd_decode_partials_paged",
-           "fd_decode_attention_fp8", "fd_decode_partials_fp8", "fd_status_string", "fd_last_error",
-           "fd_version")
+           "fd_decode_attention_fp8", "fd_decode_partials_fp8", "fd_decode_attention_int8",
+           "fd_decode_partials_int8", "fd_status_string", "fd_last_error", "fd_version")
 
 
 class FdDims(ctypes.Structure):
@@ -97,6 +97,10 @@ def load_library(path: str | None = None):
     lib.fd_decode_partials_fp8.argtypes = [dims_p, vp, vp, vp, pages_p, f32, f32, vp, f32, i32, plan_p,
                                            vp, vp, vp, vp]
     lib.fd_decode_partials_fp8.restype = i32
+    lib.fd_decode_attention_int8.argtypes = lib.fd_decode_attention_fp8.argtypes
+    lib.fd_decode_attention_int8.restype = i32
+    lib.fd_decode_partials_int8.argtypes = lib.fd_decode_partials_fp8.argtypes
+    lib.fd_decode_partials_int8.restype = i32
     lib.fd_status_string.argtypes = [i32]
     lib.fd_status_string.restype = ctypes.c_char_p
     lib.fd_last_error.argtypes = []
@@ -408,14 +412,19 @@ def decode_partials_paged(q, k_pages, v_pages, block_table, cache_lens, layout: 
     return o_part, m_part, lse_part
 
 
-def _fp8_call_args(q, k_cache, v_cache, cache_lens, block_table, layout):
-    """(dims, pages or None) of an fp8-cache call; k/v are uint8 E4M3 codes."""
-    if k_cache.dtype != torch.uint8 or v_cache.dtype != torch.uint8:
-        raise FdError(FD_ERR_INVALID, "fp8 caches are passed as uint8 tensors of E4M3 codes")
+_CODE_DTYPES = {"fp8": torch.uint8, "int8": torch.int8}
+
+
+def _code_call_args(fmt, q, k_cache, v_cache, cache_lens, block_table, layout):
+    """(dims, pages or None) of a call over one-byte codes: uint8 E4M3 codes
+    ("fp8") or int8 codes ("int8")."""
+    want = _CODE_DTYPES[fmt]
+    if k_cache.dtype != want or v_cache.dtype != want:
+        raise FdError(FD_ERR_INVALID, f"{fmt} caches are passed as {want} tensors of codes")
     if v_cache.shape != k_cache.shape:
         raise FdError(FD_ERR_INVALID, f"v_cache {tuple(v_cache.shape)} != k_cache {tuple(k_cache.shape)}")
     if q.dtype != torch.bfloat16:
-        raise FdError(FD_ERR_UNSUPPORTED, "fp8 caches need a bf16 q")
+        raise FdError(FD_ERR_UNSUPPORTED, f"{fmt} caches need a bf16 q")
     if cache_lens.dtype != torch.int32 or cache_lens.shape != (q.shape[0],):
         raise FdError(FD_ERR_INVALID, "cache_lens must be int32 of shape [B]")
     if block_table is None:
@@ -429,15 +438,11 @@ def _fp8_call_args(q, k_cache, v_cache, cache_lens, block_table, layout):
     return dims, FdKvPages(block_table.data_ptr(), block_table.shape[1], P, k_cache.shape[0], _LAYOUTS[layout])
 
 
-def decode_attention_fp8(q, k_cache, v_cache, cache_lens, k_scale: float, v_scale: float, block_table=None,
-                         layout: str = "nhd", scale=None, num_splits: int = 0, plan: Plan | FdPlan | None = None,
-                         out=None, lse=None, workspace=None):
-    """Split-KV attention over FP8 E4M3 caches (uint8 codes; key = code * k_scale,
-    value = code * v_scale).  Contiguous [B,Hkv,Lmax,D] caches, or pages with a
-    block table as in decode_attention_paged.  q and out are bf16.  Returns (out, lse)."""
+def _codes_attention(fmt, q, k_cache, v_cache, cache_lens, k_scale, v_scale, block_table, layout, scale,
+                     num_splits, plan, out, lse, workspace):
     lib = load_library()
     _require_cuda(q, k_cache, v_cache, cache_lens, block_table, out, lse, workspace)
-    dims, pages = _fp8_call_args(q, k_cache, v_cache, cache_lens, block_table, layout)
+    dims, pages = _code_call_args(fmt, q, k_cache, v_cache, cache_lens, block_table, layout)
     _check_buffer(out, q.shape, q.dtype, "out")
     _check_buffer(lse, q.shape[:3], torch.float32, "lse")
     fp = plan.plan if isinstance(plan, Plan) else plan
@@ -450,26 +455,25 @@ def decode_attention_fp8(q, k_cache, v_cache, cache_lens, k_scale: float, v_scal
     if workspace is None and ws_bytes:
         workspace = new_workspace(ws_bytes, q.device)
     given = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    _check(lib.fd_decode_attention_fp8(ctypes.byref(dims), _ptr(q), _ptr(k_cache), _ptr(v_cache),
-                                       ctypes.byref(pages) if pages is not None else None,
-                                       ctypes.c_float(k_scale), ctypes.c_float(v_scale), _ptr(cache_lens),
-                                       ctypes.c_float(_default_scale(q.shape[-1], scale)), int(num_splits),
-                                       ctypes.byref(fp) if fp is not None else None, _ptr(workspace), given,
-                                       _ptr(out), _ptr(lse), _stream(q.device)))
+    fn = lib.fd_decode_attention_fp8 if fmt == "fp8" else lib.fd_decode_attention_int8
+    _check(fn(ctypes.byref(dims), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+              ctypes.byref(pages) if pages is not None else None,
+              ctypes.c_float(k_scale), ctypes.c_float(v_scale), _ptr(cache_lens),
+              ctypes.c_float(_default_scale(q.shape[-1], scale)), int(num_splits),
+              ctypes.byref(fp) if fp is not None else None, _ptr(workspace), given,
+              _ptr(out), _ptr(lse), _stream(q.device)))
     return out, lse
 
 
-def decode_partials_fp8(q, k_cache, v_cache, cache_lens, k_scale: float, v_scale: float, block_table=None,
-                        layout: str = "nhd", scale=None, num_splits: int = 0, plan: Plan | FdPlan | None = None,
-                        o_part=None, m_part=None, lse_part=None):
-    """First pass only over FP8 caches: (o_part, m_part, lse_part) as decode_partials."""
+def _codes_partials(fmt, q, k_cache, v_cache, cache_lens, k_scale, v_scale, block_table, layout, scale,
+                    num_splits, plan, o_part, m_part, lse_part):
     lib = load_library()
     _require_cuda(q, k_cache, v_cache, cache_lens, block_table, o_part, m_part, lse_part)
-    dims, pages = _fp8_call_args(q, k_cache, v_cache, cache_lens, block_table, layout)
+    dims, pages = _code_call_args(fmt, q, k_cache, v_cache, cache_lens, block_table, layout)
     fp = plan.plan if isinstance(plan, Plan) else plan
     slots = num_splits if num_splits > 0 else (fp.max_splits if fp is not None else 0)
     if slots < 1:
-        raise FdError(FD_ERR_INVALID, "decode_partials_fp8 needs num_splits > 0 or a plan")
+        raise FdError(FD_ERR_INVALID, f"decode_partials_{fmt} needs num_splits > 0 or a plan")
     B, Hq, T, D = q.shape
     _check_buffer(o_part, (B, Hq, T, slots, D), torch.float32, "o_part")
     _check_buffer(m_part, (B, Hq, T, slots), torch.float32, "m_part")
@@ -480,10 +484,46 @@ def decode_partials_fp8(q, k_cache, v_cache, cache_lens, k_scale: float, v_scale
         m_part = torch.empty(B, Hq, T, slots, dtype=torch.float32, device=q.device)
     if lse_part is None:
         lse_part = torch.empty(B, Hq, T, slots, dtype=torch.float32, device=q.device)
-    _check(lib.fd_decode_partials_fp8(ctypes.byref(dims), _ptr(q), _ptr(k_cache), _ptr(v_cache),
-                                      ctypes.byref(pages) if pages is not None else None,
-                                      ctypes.c_float(k_scale), ctypes.c_float(v_scale), _ptr(cache_lens),
-                                      ctypes.c_float(_default_scale(D, scale)), int(num_splits),
-                                      ctypes.byref(fp) if fp is not None else None, _ptr(o_part), _ptr(m_part),
-                                      _ptr(lse_part), _stream(q.device)))
+    fn = lib.fd_decode_partials_fp8 if fmt == "fp8" else lib.fd_decode_partials_int8
+    _check(fn(ctypes.byref(dims), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+              ctypes.byref(pages) if pages is not None else None,
+              ctypes.c_float(k_scale), ctypes.c_float(v_scale), _ptr(cache_lens),
+              ctypes.c_float(_default_scale(D, scale)), int(num_splits),
+              ctypes.byref(fp) if fp is not None else None, _ptr(o_part), _ptr(m_part),
+              _ptr(lse_part), _stream(q.device)))
     return o_part, m_part, lse_part
+
+
+def decode_attention_fp8(q, k_cache, v_cache, cache_lens, k_scale: float, v_scale: float, block_table=None,
+                         layout: str = "nhd", scale=None, num_splits: int = 0, plan: Plan | FdPlan | None = None,
+                         out=None, lse=None, workspace=None):
+    """Split-KV attention over FP8 E4M3 caches (uint8 codes; key = code * k_scale,
+    value = code * v_scale).  Contiguous [B,Hkv,Lmax,D] caches, or pages with a
+    block table as in decode_attention_paged.  q and out are bf16.  Returns (out, lse)."""
+    return _codes_attention("fp8", q, k_cache, v_cache, cache_lens, k_scale, v_scale, block_table, layout, scale,
+                            num_splits, plan, out, lse, workspace)
+
+
+def decode_partials_fp8(q, k_cache, v_cache, cache_lens, k_scale: float, v_scale: float, block_table=None,
+                        layout: str = "nhd", scale=None, num_splits: int = 0, plan: Plan | FdPlan | None = None,
+                        o_part=None, m_part=None, lse_part=None):
+    """First pass only over FP8 caches: (o_part, m_part, lse_part) as decode_partials."""
+    return _codes_partials("fp8", q, k_cache, v_cache, cache_lens, k_scale, v_scale, block_table, layout, scale,
+                           num_splits, plan, o_part, m_part, lse_part)
+
+
+def decode_attention_int8(q, k_cache, v_cache, cache_lens, k_scale: float, v_scale: float, block_table=None,
+                          layout: str = "nhd", scale=None, num_splits: int = 0, plan: Plan | FdPlan | None = None,
+                          out=None, lse=None, workspace=None):
+    """Split-KV attention over INT8 caches (int8 codes; key = code * k_scale,
+    value = code * v_scale), otherwise as decode_attention_fp8.  Returns (out, lse)."""
+    return _codes_attention("int8", q, k_cache, v_cache, cache_lens, k_scale, v_scale, block_table, layout, scale,
+                            num_splits, plan, out, lse, workspace)
+
+
+def decode_partials_int8(q, k_cache, v_cache, cache_lens, k_scale: float, v_scale: float, block_table=None,
+                         layout: str = "nhd", scale=None, num_splits: int = 0, plan: Plan | FdPlan | None = None,
+                         o_part=None, m_part=None, lse_part=None):
+    """First pass only over INT8 caches: (o_part, m_part, lse_part) as decode_partials."""
+    return _codes_partials("int8", q, k_cache, v_cache, cache_lens, k_scale, v_scale, block_table, layout, scale,
+                           num_splits, plan, o_part, m_part, lse_part)

@@ -164,14 +164,16 @@ bool trace_enabled() {
 
 void trace_launch(const char* entry, const fd_dims* d, const fdk::PartialArgs& a) {
     if (!trace_enabled()) return;
-    const bool mfma = a.kv_fp8 || fdk::use_mfma_partials(d->dtype, d->head_dim, a.rows);
+    const bool mfma = a.kv_codes != fdk::kKvBf16 || fdk::use_mfma_partials(d->dtype, d->head_dim, a.rows);
     const char* kernel = !mfma ? "fd_partial_kernel (vector)"
                          : a.rows > 32 ? "fd_mfma_chunk_kernel" : "fd_mfma_partial_kernel";
     std::fprintf(stderr,
                  "[fd] %s: B=%d Hq=%d Hkv=%d D=%d q_len=%d Lmax=%d dtype=%d%s%s | tile_len=%d num_splits=%d "
                  "slots=%d granule=%d | rows/KV head=%d row_blocks=%d | %s, %s\n",
                  entry, d->batch, d->num_q_heads, d->num_kv_heads, d->head_dim, d->q_len, d->max_cache_len,
-                 d->dtype, a.pages.table ? " paged" : "", a.kv_fp8 ? " fp8-kv" : "", a.rule.tile_len,
+                 d->dtype, a.pages.table ? " paged" : "",
+                 a.kv_codes == fdk::kKvE4M3 ? " fp8-kv" : a.kv_codes == fdk::kKvInt8 ? " int8-kv" : "",
+                 a.rule.tile_len,
                  a.rule.num_splits, a.rule.slots, a.rule.granule, a.rows, a.row_blocks, kernel,
                  a.rule.slots > 1 && !a.direct ? "partials + merge" : "direct output");
 }
@@ -198,7 +200,7 @@ const char* fd_status_string(int32_t status) {
 
 const char* fd_last_error(void) { return g_last_error; }
 
-int32_t fd_version(void) { return 200; }
+int32_t fd_version(void) { return 300; }
 
 uint64_t fd_workspace_bytes(const fd_dims* dims, int32_t max_splits) {
     if (max_splits <= 1 || max_splits > FD_MAX_SPLITS) return 0;
@@ -285,36 +287,39 @@ namespace {
 
 fd_status resolve_pages(const fd_dims* d, const fd_kv_pages* pages, fdk::SplitRule* rule, fdk::PagedKV* pk);
 
-// Per-tensor fp8 dequantisation scales of a call with E4M3 caches.
-struct Fp8Scales {
+// Format and per-tensor dequantisation scales of a call with caches of
+// one-byte codes (FP8 E4M3 or INT8).
+struct CodeScales {
+    int32_t format;  // fdk::kKvE4M3 or fdk::kKvInt8
     float k_scale, v_scale;
 };
 
-// Checks of an fp8-cache call: bf16 queries, finite scales.
-fd_status check_fp8(const fd_dims* d, const Fp8Scales* f8) {
-    if (d->dtype != FD_BF16) return fail(FD_ERR_UNSUPPORTED, "fp8 caches need bf16 q and out (dims->dtype)");
-    if (!std::isfinite(f8->k_scale) || !std::isfinite(f8->v_scale))
+// Checks of a call over one-byte codes: bf16 queries, finite scales.
+fd_status check_codes(const fd_dims* d, const CodeScales* cs) {
+    const char* name = cs->format == fdk::kKvInt8 ? "int8" : "fp8";
+    if (d->dtype != FD_BF16) return fail(FD_ERR_UNSUPPORTED, "%s caches need bf16 q and out (dims->dtype)", name);
+    if (!std::isfinite(cs->k_scale) || !std::isfinite(cs->v_scale))
         return fail(FD_ERR_INVALID, "k_scale and v_scale must be finite");
     return FD_OK;
 }
 
-void apply_fp8(fdk::PartialArgs* a, const Fp8Scales* f8, float scale) {
+void apply_codes(fdk::PartialArgs* a, const CodeScales* cs, float scale) {
     a->v_scale = 1.f;
-    a->kv_fp8 = 0;
-    if (!f8) return;
-    a->kv_fp8 = 1;
-    a->v_scale = f8->v_scale;
-    a->qk_scale = (float)((double)scale * f8->k_scale * kLog2e);
+    a->kv_codes = fdk::kKvBf16;
+    if (!cs) return;
+    a->kv_codes = cs->format;
+    a->v_scale = cs->v_scale;
+    a->qk_scale = (float)((double)scale * cs->k_scale * kLog2e);
 }
 
 fd_status run_partials(const fd_dims* dims, const void* q, const void* k_cache, const void* v_cache,
-                       const fd_kv_pages* pages, const Fp8Scales* f8, const int32_t* cache_lens, float scale,
+                       const fd_kv_pages* pages, const CodeScales* cs, const int32_t* cache_lens, float scale,
                        int32_t num_splits, const fd_plan* plan, float* o_part, float* m_part, float* lse_part,
                        void* stream) {
     clear_error();
     fd_status st = check_dims(dims);
     if (st != FD_OK) return st;
-    if (f8 && (st = check_fp8(dims, f8)) != FD_OK) return st;
+    if (cs && (st = check_codes(dims, cs)) != FD_OK) return st;
     if (num_splits == 0 && !plan)
         return fail(FD_ERR_INVALID, "the partial pass needs num_splits > 0 or a plan");
     fdk::SplitRule rule;
@@ -329,7 +334,7 @@ fd_status run_partials(const fd_dims* dims, const void* q, const void* k_cache, 
         return fail(FD_ERR_INVALID, "o_part must be 16-byte aligned, m_part and lse_part 4-byte aligned");
     fdk::PartialArgs a = make_args(dims, q, k_cache, v_cache, cache_lens, scale, rule);
     a.pages = pk;
-    apply_fp8(&a, f8, scale);
+    apply_codes(&a, cs, scale);
     a.o_part = o_part;
     a.m_part = m_part;
     a.lse_part = lse_part;
@@ -369,8 +374,17 @@ fd_status fd_decode_partials_fp8(const fd_dims* dims, const void* q, const void*
                                  const fd_kv_pages* pages, float k_scale, float v_scale,
                                  const int32_t* cache_lens, float scale, int32_t num_splits, const fd_plan* plan,
                                  float* o_part, float* m_part, float* lse_part, void* stream) {
-    const Fp8Scales f8{k_scale, v_scale};
-    return run_partials(dims, q, k_cache, v_cache, pages, &f8, cache_lens, scale, num_splits, plan, o_part, m_part,
+    const CodeScales cs{fdk::kKvE4M3, k_scale, v_scale};
+    return run_partials(dims, q, k_cache, v_cache, pages, &cs, cache_lens, scale, num_splits, plan, o_part, m_part,
+                        lse_part, stream);
+}
+
+fd_status fd_decode_partials_int8(const fd_dims* dims, const void* q, const void* k_cache, const void* v_cache,
+                                  const fd_kv_pages* pages, float k_scale, float v_scale,
+                                  const int32_t* cache_lens, float scale, int32_t num_splits, const fd_plan* plan,
+                                  float* o_part, float* m_part, float* lse_part, void* stream) {
+    const CodeScales cs{fdk::kKvInt8, k_scale, v_scale};
+    return run_partials(dims, q, k_cache, v_cache, pages, &cs, cache_lens, scale, num_splits, plan, o_part, m_part,
                         lse_part, stream);
 }
 
@@ -446,13 +460,13 @@ fd_status resolve_pages(const fd_dims* d, const fd_kv_pages* pages, fdk::SplitRu
 // The two passes of the operation over contiguous (pk == nullptr) or paged
 // caches.
 fd_status run_attention(const fd_dims* dims, const void* q, const void* k_cache, const void* v_cache,
-                        const fd_kv_pages* pages, const Fp8Scales* f8, const int32_t* cache_lens, float scale,
+                        const fd_kv_pages* pages, const CodeScales* cs, const int32_t* cache_lens, float scale,
                         int32_t num_splits, const fd_plan* plan, void* workspace, uint64_t workspace_bytes,
                         void* out, float* lse, void* stream) {
     clear_error();
     fd_status st = check_dims(dims);
     if (st != FD_OK) return st;
-    if (f8 && (st = check_fp8(dims, f8)) != FD_OK) return st;
+    if (cs && (st = check_codes(dims, cs)) != FD_OK) return st;
     fdk::SplitRule rule;
     if ((st = resolve_rule(num_splits, plan, &rule)) != FD_OK) return st;
     fdk::PagedKV pk{};
@@ -465,7 +479,7 @@ fd_status run_attention(const fd_dims* dims, const void* q, const void* k_cache,
     hipStream_t s = static_cast<hipStream_t>(stream);
     fdk::PartialArgs a = make_args(dims, q, k_cache, v_cache, cache_lens, scale, rule);
     a.pages = pk;
-    apply_fp8(&a, f8, scale);
+    apply_codes(&a, cs, scale);
     if (rule.slots == 1) {
         a.out = out;
         a.lse = lse;
@@ -523,8 +537,17 @@ fd_status fd_decode_attention_fp8(const fd_dims* dims, const void* q, const void
                                   const fd_kv_pages* pages, float k_scale, float v_scale,
                                   const int32_t* cache_lens, float scale, int32_t num_splits, const fd_plan* plan,
                                   void* workspace, uint64_t workspace_bytes, void* out, float* lse, void* stream) {
-    const Fp8Scales f8{k_scale, v_scale};
-    return run_attention(dims, q, k_cache, v_cache, pages, &f8, cache_lens, scale, num_splits, plan, workspace,
+    const CodeScales cs{fdk::kKvE4M3, k_scale, v_scale};
+    return run_attention(dims, q, k_cache, v_cache, pages, &cs, cache_lens, scale, num_splits, plan, workspace,
+                         workspace_bytes, out, lse, stream);
+}
+
+fd_status fd_decode_attention_int8(const fd_dims* dims, const void* q, const void* k_cache, const void* v_cache,
+                                   const fd_kv_pages* pages, float k_scale, float v_scale,
+                                   const int32_t* cache_lens, float scale, int32_t num_splits, const fd_plan* plan,
+                                   void* workspace, uint64_t workspace_bytes, void* out, float* lse, void* stream) {
+    const CodeScales cs{fdk::kKvInt8, k_scale, v_scale};
+    return run_attention(dims, q, k_cache, v_cache, pages, &cs, cache_lens, scale, num_splits, plan, workspace,
                          workspace_bytes, out, lse, stream);
 }
 

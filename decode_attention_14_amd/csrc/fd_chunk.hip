@@ -1,5 +1,5 @@
 // fd_chunk.hip -- split-KV partial kernel on the matrix cores for chunked
-// prefill on gfx950 (CDNA4): bf16 queries over bf16 or FP8 E4M3 caches,
+// prefill on gfx950 (CDNA4): bf16 queries over bf16, FP8 E4M3 or INT8 caches,
 // contiguous or paged.
 //
 // It serves row groups of more than 32 query rows per KV head (page
@@ -144,8 +144,9 @@ __device__ __forceinline__ void chunk_stage_at(const PagedKV& pk, const int32_t*
     }
 }
 
-// FP8 caches in the chunk kernel: each stage's E4M3 rows (D bytes, stored
-// order) stream into a second two-stage ring, and the workgroup dequantises
+// Caches of one-byte codes (FP8 E4M3 or INT8) in the chunk kernel: each
+// stage's rows of codes (D bytes, stored order) stream into a second
+// two-stage ring, and the workgroup dequantises
 // stage j + 1 into the bf16 ring while it computes on stage j, so the
 // products run unchanged on bf16 operands.
 template <int D>
@@ -161,7 +162,7 @@ struct CGeo8 {
     static_assert((2 * NDMA) % kCW == 0 && PW >= 1 && STGB % (16 * kCT) == 0, "even split");
 };
 
-// Start this wave's loads of fp8 stage j into dst (see chunk_stage_at).
+// Start this wave's loads of code stage j into dst (see chunk_stage_at).
 // Instruction k covers RPI rows of K (isv 0) or V (isv 1) from key koff[k]
 // of the stage.
 template <int D, bool PAGED>
@@ -189,10 +190,11 @@ __device__ __forceinline__ void chunk_stage8_at(const PagedKV& pk, const int32_t
     }
 }
 
-// Dequantise a landed fp8 stage (src) into the bf16 stage layout (dst):
+// Dequantise a landed code stage (src, format KV) into the bf16 stage layout
+// (dst), exactly (see codes_to_bf16):
 // thread t converts 16-byte chunks t, t + kCT, ... through lds_read_b128 /
 // lds_write_b128, so the stage loads still in flight are not waited for.
-template <int D>
+template <int D, int KV>
 __device__ __forceinline__ void chunk_dequant_stage(const char* src, char* dst, int tid) {
     using G = CGeo<D>;
     using G8 = CGeo8<D>;
@@ -212,10 +214,7 @@ __device__ __forceinline__ void chunk_dequant_stage(const char* src, char* dst, 
         const int c8 = rem - r * G8::CH;  // codes of dims 16 c8 .. 16 c8 + 15
         uint32_t bw[8];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            bw[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[n][i], 1.f, false));
-            bw[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[n][i], 1.f, true));
-        }
+        for (int i = 0; i < 4; ++i) codes_to_bf16<KV>(x[n][i], bw[2 * i], bw[2 * i + 1]);
         char* o = dst + tsr * G::SKB * G::BLKB + (r / kCBK) * G::BLKB;
         lds_write_b128(o + cswz<D>(r % kCBK, 2 * c8), u32x4_t{bw[0], bw[1], bw[2], bw[3]});
         lds_write_b128(o + cswz<D>(r % kCBK, 2 * c8 + 1), u32x4_t{bw[4], bw[5], bw[6], bw[7]});
@@ -300,7 +299,6 @@ __device__ __forceinline__ void chunk_pv(const bf16x8_t (&vf)[CGeo<D>::DB * 2], 
             acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[db * 2 + k2], pp[k2], acc[db], 0, 0, 0);
 }
 
-typedef __attribute__((ext_vector_type(2))) float f32x2_t;
 
 __device__ __forceinline__ bf16x8_t pack8(bf16x2_t a, bf16x2_t b, bf16x2_t c, bf16x2_t d) {
     const bf16x4_t ab = __builtin_shufflevector(a, b, 0, 1, 2, 3);
@@ -410,15 +408,16 @@ __device__ __forceinline__ void chunk_step(bool edge, const uint32_t (&ka)[CGeo<
     if (lo) chunk_pv<D>(vf, pl, acc);
 }
 
-template <int D, bool PAGED, bool FP8>
+template <int D, bool PAGED, int KV>
 __global__ __launch_bounds__(kCT) void fd_mfma_chunk_kernel(PartialArgs a) {
     using G = CGeo<D>;
     using G8 = CGeo8<D>;
-    static_assert(!FP8 || kCNS == 2, "the fp8 pipeline keeps two stages in each ring");
-    constexpr int ESZ = FP8 ? 1 : 2;  // bytes per stored K/V element
+    constexpr bool C8 = KV != kKvBf16;  // one-byte codes
+    static_assert(!C8 || kCNS == 2, "the code pipeline keeps two stages in each ring");
+    constexpr int ESZ = C8 ? 1 : 2;  // bytes per stored K/V element
     constexpr int RS = D + 4;  // padded row stride of the merge area (floats)
     constexpr int MERGEB = kCRG * (32 * RS + 3 * 32) * 4;
-    constexpr int RINGB = kCNS * G::STGB + (FP8 ? 2 * G8::STGB : 0);
+    constexpr int RINGB = kCNS * G::STGB + (C8 ? 2 * G8::STGB : 0);
     constexpr int SMEMB = RINGB > MERGEB ? RINGB : MERGEB;
     __shared__ __attribute__((aligned(16))) char smem[SMEMB];
 
@@ -528,11 +527,11 @@ __global__ __launch_bounds__(kCT) void fd_mfma_chunk_kernel(PartialArgs a) {
     }
     const int nst = (kend - lo + G::SKEYS - 1) / G::SKEYS;
 
-    // fp8 loads: instruction n = w + k * kCW of a stage covers RPI rows of K
+    // Code loads: instruction n = w + k * kCW of a stage covers RPI rows of K
     // (n < NDMA) or V, in stored order.
-    uint32_t dma8[FP8 ? G8::PW : 1];
-    int lds8[FP8 ? G8::PW : 1], koff8[FP8 ? G8::PW : 1], isv8[FP8 ? G8::PW : 1];
-    if constexpr (FP8) {
+    uint32_t dma8[C8 ? G8::PW : 1];
+    int lds8[C8 ? G8::PW : 1], koff8[C8 ? G8::PW : 1], isv8[C8 ? G8::PW : 1];
+    if constexpr (C8) {
 #pragma unroll
         for (int k = 0; k < G8::PW; ++k) {
             const int n = w + k * kCW;
@@ -581,15 +580,15 @@ __global__ __launch_bounds__(kCT) void fd_mfma_chunk_kernel(PartialArgs a) {
                             8 * (q4 & 1);
     }
 
-    char* ring8 = smem + kCNS * G::STGB;  // fp8: the stored-row ring
-    if constexpr (FP8) {
-        // fp8 stages 0 and 1 in flight; stage 0 dequantised into bf16 slot 0.
+    char* ring8 = smem + kCNS * G::STGB;  // codes: the stored-row ring
+    if constexpr (C8) {
+        // Code stages 0 and 1 in flight; stage 0 dequantised into bf16 slot 0.
         chunk_stage8_at<D, PAGED>(a.pages, tbl, kt, vt, lo, kend, 0, rsb, ring8, dma8, lds8, koff8, isv8);
         chunk_stage8_at<D, PAGED>(a.pages, tbl, kt, vt, lo, kend, 1, rsb, ring8 + G8::STGB, dma8, lds8, koff8,
                                   isv8);
         wait_vmcnt_le<G8::PW>();
         __syncthreads();
-        chunk_dequant_stage<D>(ring8, smem, tid);
+        chunk_dequant_stage<D, KV>(ring8, smem, tid);
     } else {
 #pragma unroll
         for (int j = 0; j < kCNS - 1; ++j)
@@ -609,16 +608,16 @@ __global__ __launch_bounds__(kCT) void fd_mfma_chunk_kernel(PartialArgs a) {
         for (int u = 0; u < kCNS; ++u) {
             const int j = j0 + u;
             if (j >= nst) break;
-            if constexpr (FP8) {
-                // Own loads of fp8 stage j + 1 landed; after the barrier
+            if constexpr (C8) {
+                // Own loads of code stage j + 1 landed; after the barrier
                 // everyone's have, bf16 slot u holds stage j, slot 1 - u and
-                // fp8 slot u are free.
+                // code slot u are free.
                 wait_vmcnt_le<0>();
                 __syncthreads();
                 chunk_stage8_at<D, PAGED>(a.pages, tbl, kt, vt, lo, kend, j + 2, rsb, ring8 + u * G8::STGB, dma8,
                                           lds8, koff8, isv8);
                 if (j + 1 < nst)
-                    chunk_dequant_stage<D>(ring8 + (1 - u) * G8::STGB, smem + (1 - u) * G::STGB, tid);
+                    chunk_dequant_stage<D, KV>(ring8 + (1 - u) * G8::STGB, smem + (1 - u) * G::STGB, tid);
             } else {
                 wait_vmcnt_le<(kCNS - 1) * 2 * G::DPW>();  // this wave's loads of stage j
                 __syncthreads();                           // everyone's; stage j - 1 is free
@@ -667,8 +666,8 @@ __global__ __launch_bounds__(kCT) void fd_mfma_chunk_kernel(PartialArgs a) {
     const float den = l * f1 + sm_l[rg * 32 + col] * f2;
     const float X = fmaxf(mx, sm_x[rg * 32 + col]);
     const bool empty = M == -INFINITY;
-    // fp8: V was dequantised without its scale
-    const float inv = empty ? 0.f : (FP8 ? a.v_scale : 1.f) / den;
+    // codes: V was dequantised without its scale
+    const float inv = empty ? 0.f : (C8 ? a.v_scale : 1.f) / den;
     const float lse_v = empty ? -INFINITY : (M + log2f(den)) * kLn2;
     const float* o2 = sm_acc + (rg * 32 + col) * RS;
     if (a.direct) {
@@ -713,10 +712,17 @@ __global__ __launch_bounds__(kCT) void fd_mfma_chunk_kernel(PartialArgs a) {
 template <int D, bool PAGED>
 void launch_chunk_p(int batch, const PartialArgs& a, hipStream_t stream) {
     dim3 grid((uint32_t)a.rule.slots * a.Hkv * a.row_blocks, batch), block(kCT);
-    if (a.kv_fp8)
-        hipLaunchKernelGGL((fd_mfma_chunk_kernel<D, PAGED, true>), grid, block, 0, stream, a);
-    else
-        hipLaunchKernelGGL((fd_mfma_chunk_kernel<D, PAGED, false>), grid, block, 0, stream, a);
+    switch (a.kv_codes) {
+        case kKvE4M3:
+            hipLaunchKernelGGL((fd_mfma_chunk_kernel<D, PAGED, kKvE4M3>), grid, block, 0, stream, a);
+            break;
+        case kKvInt8:
+            hipLaunchKernelGGL((fd_mfma_chunk_kernel<D, PAGED, kKvInt8>), grid, block, 0, stream, a);
+            break;
+        default:
+            hipLaunchKernelGGL((fd_mfma_chunk_kernel<D, PAGED, kKvBf16>), grid, block, 0, stream, a);
+            break;
+    }
 }
 
 template <int D>

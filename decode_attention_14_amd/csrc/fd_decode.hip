@@ -521,8 +521,9 @@ hipError_t launch_partials_d(int batch, const PartialArgs& a, hipStream_t stream
 
 hipError_t launch_partials(int dtype, int head_dim, int batch, const PartialArgs& a,
                            hipStream_t stream) {
-    // FP8 caches are read by the matrix-core decode kernel only.
-    if (a.kv_fp8 || use_mfma_partials(dtype, head_dim, a.rows)) return launch_partials_mfma(head_dim, batch, a, stream);
+    // Caches of one-byte codes are read by the matrix-core kernels only.
+    if (a.kv_codes != kKvBf16 || use_mfma_partials(dtype, head_dim, a.rows))
+        return launch_partials_mfma(head_dim, batch, a, stream);
     const bool bf16 = dtype == 1;
     if (bf16) {
         return head_dim == 64 ? launch_partials_d<true, 64>(batch, a, stream)

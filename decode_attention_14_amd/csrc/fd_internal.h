@@ -37,6 +37,15 @@ struct PagedKV {
     int64_t head_stride;   // elements
 };
 
+// Element formats of the K/V caches: the query's dtype, or one-byte codes
+// with per-tensor scales (value = code value * scale), dequantised to bf16
+// inside the matrix-core kernels.
+enum KvFormat : int32_t {
+    kKvBf16 = 0,  // same dtype as q (bf16 or fp32)
+    kKvE4M3 = 1,  // OCP FP8 E4M3 ("e4m3fn") codes
+    kKvInt8 = 2,  // two's-complement INT8 codes
+};
+
 struct PartialArgs {
     const void* q;
     const void* k;
@@ -54,8 +63,8 @@ struct PartialArgs {
     float qk_scale;     // scale * log2(e): scores are kept in base 2
     int32_t direct;     // 1: single slot, write out/lse instead of partials
     PagedKV pages;      // pages.table == nullptr: k/v are [B, Hkv, Lmax, D]
-    int32_t kv_fp8;     // 1: k/v hold OCP E4M3 codes (bf16 q/out); k_scale is in qk_scale
-    float v_scale;      // fp8: value of V = code * v_scale (applied to the output)
+    int32_t kv_codes;   // kKvBf16, or the one-byte code format of k/v (bf16 q/out); k_scale is in qk_scale
+    float v_scale;      // codes: value of V = code * v_scale (applied to the output)
 };
 
 // Packed query rows per workgroup of the matrix-core chunk kernel (row

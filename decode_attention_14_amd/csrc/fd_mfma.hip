@@ -1,5 +1,5 @@
 // fd_mfma.hip -- split-KV partial kernel on the matrix cores for decode-sized
-// row groups on gfx950 (CDNA4): bf16 queries over bf16 or FP8 E4M3 caches,
+// row groups on gfx950 (CDNA4): bf16 queries over bf16, FP8 E4M3 or INT8 caches,
 // contiguous or paged.
 //
 // Same operation as the vector kernel in fd_decode.hip: one workgroup per
@@ -63,10 +63,10 @@ namespace {
 #endif
 constexpr int kMT = FD_MFMA_THREADS;  // threads per workgroup (bf16 caches)
 constexpr int kMW = kMT / 64;     // waves per workgroup
-#ifndef FD_FP8_WAVES
-#define FD_FP8_WAVES 8
+#ifndef FD_CODE8_WAVES
+#define FD_CODE8_WAVES 8
 #endif
-constexpr int kMW8 = FD_FP8_WAVES;  // waves per workgroup over fp8 caches
+constexpr int kMW8 = FD_CODE8_WAVES;  // waves per workgroup over one-byte caches
 constexpr int kKB = 16;           // keys per block
 constexpr int kNS = FD_MFMA_STAGES;
 
@@ -85,22 +85,22 @@ struct Geo {
 };
 
 // Stored-row geometry of the decode kernel's LDS ring: bf16 caches keep
-// 2D-byte rows (the operand layout itself); fp8 caches keep D-byte rows,
-// dequantised per block into a bf16 block of the operand layout.  An fp8
-// block carries half the bytes, so the ring keeps twice the blocks in flight.
-#ifndef FD_FP8_STAGES
-#define FD_FP8_STAGES 2
+// 2D-byte rows (the operand layout itself); caches of one-byte codes (C8:
+// FP8 E4M3 or INT8) keep D-byte rows, dequantised per block into a bf16
+// block of the operand layout.
+#ifndef FD_CODE8_STAGES
+#define FD_CODE8_STAGES 2
 #endif
-template <int D, bool FP8>
+template <int D, bool C8>
 struct LGeo {
-    static constexpr int ROWB = FP8 ? D : 2 * D;    // bytes per stored key row
+    static constexpr int ROWB = C8 ? D : 2 * D;     // bytes per stored key row
     static constexpr int CH = ROWB / 16;            // 16-byte chunks per row
     static constexpr int RPI = 64 / CH;             // rows per 1 KiB LDS-load instruction
     static constexpr int IPB = kKB / RPI;           // instructions per block per tensor
     static constexpr int BLKB = kKB * ROWB;         // bytes per block per tensor
     static constexpr int STAGEB = 2 * BLKB;         // K then V
-    static constexpr int NS = FP8 ? FD_FP8_STAGES : kNS;
-    static constexpr int CONVB = FP8 ? 2 * Geo<D>::BLKB : 0;  // bf16 K and V block
+    static constexpr int NS = C8 ? FD_CODE8_STAGES : kNS;
+    static constexpr int CONVB = C8 ? 2 * Geo<D>::BLKB : 0;  // bf16 K and V block
     static constexpr int WAVEB = NS * STAGEB + CONVB;
     static_assert(IPB >= 1, "whole load instructions per block");
 };
@@ -140,10 +140,10 @@ __device__ __forceinline__ void lds_settle(bf16x4_t (&v)[N]) {
 // V rows.  Lane l of load instruction i reads its row's global chunk
 // dma_off[i]; the data lands at dst + i * 1024 + 16 * l.  Rows past `left`
 // read as zeros and cost no memory traffic.
-template <int D, bool FP8>
+template <int D, bool C8>
 __device__ __forceinline__ void load_block(const char* kp, const char* vp, int left, char* dst,
                                            const uint32_t* dma_off) {
-    using L = LGeo<D, FP8>;
+    using L = LGeo<D, C8>;
     const uint32_t n = left > 0 ? (uint32_t)left : 0u;
     const __amdgpu_buffer_rsrc_t rk = tile_rsrc(kp, n);
     const __amdgpu_buffer_rsrc_t rv = tile_rsrc(vp, n);
@@ -160,33 +160,32 @@ __device__ __forceinline__ void load_block(const char* kp, const char* vp, int l
 // contiguous caches address the tile directly (kt/vt: its first row);
 // paged caches read the block from page `page` (kt/vt: the KV head's base).
 // ESZ: bytes per stored element.
-template <int D, bool FP8, bool PAGED>
+template <int D, bool C8, bool PAGED>
 __device__ __forceinline__ void load_block_at(const PagedKV& pk, int page, const char* kt, const char* vt, int lo,
                                               int hi, int blk, int rsb, char* dst, const uint32_t* dma_off) {
-    using L = LGeo<D, FP8>;
-    constexpr int ESZ = FP8 ? 1 : 2;
+    using L = LGeo<D, C8>;
+    constexpr int ESZ = C8 ? 1 : 2;
     if constexpr (PAGED) {
         int64_t off;
         const uint32_t n = paged_rows_in(pk, page, lo + blk * kKB, kKB, hi, rsb, L::ROWB, &off);
-        load_block<D, FP8>(kt + off * ESZ, vt + off * ESZ, (int)n, dst, dma_off);
+        load_block<D, C8>(kt + off * ESZ, vt + off * ESZ, (int)n, dst, dma_off);
     } else {
         const int off = blk * L::BLKB;
-        load_block<D, FP8>(kt + off, vt + off, (hi - lo) * L::ROWB - off, dst, dma_off);
+        load_block<D, C8>(kt + off, vt + off, (hi - lo) * L::ROWB - off, dst, dma_off);
     }
 }
 
-// Dequantise one landed fp8 block (K at src, V at src + LGeo::BLKB, rows of
-// D one-byte OCP E4M3 codes) into bf16 blocks of the operand layout (K at
-// dst, V at dst + Geo::BLKB, swizzled as swz).  Every E4M3 value is exact in
-// bf16; the per-tensor scales are applied outside (k_scale in the score
-// scale, v_scale to the output).  Lane l converts 16-byte chunks l, l + 64,
-// ... of each tensor: consecutive lanes read consecutive LDS bytes.
+// Dequantise one landed block of one-byte codes (K at src, V at src +
+// LGeo::BLKB, rows of D codes in format KV) into bf16 blocks of the operand
+// layout (K at dst, V at dst + Geo::BLKB, swizzled as swz), exactly (see
+// codes_to_bf16).  Lane l converts 16-byte chunks l, l + 64, ... of each
+// tensor: consecutive lanes read consecutive LDS bytes.
 //
 // The LDS accesses go through lds_read_b128 / lds_write_b128: the block at
 // src has landed (the caller waited for it), and dst is this wave's own
 // area, read only by its own later reads.
 
-template <int D>
+template <int D, int KV>
 __device__ __forceinline__ void dequant_block(const char* src, char* dst, int lane) {
     using L = LGeo<D, true>;
     using G = Geo<D>;
@@ -211,10 +210,7 @@ __device__ __forceinline__ void dequant_block(const char* src, char* dst, int la
             const uint32_t w[4] = {x[t][n][0], x[t][n][1], x[t][n][2], x[t][n][3]};
             uint32_t b[8];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                b[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.f, false));
-                b[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.f, true));
-            }
+            for (int i = 0; i < 4; ++i) codes_to_bf16<KV>(w[i], b[2 * i], b[2 * i + 1]);
             char* o = dst + t * G::BLKB;
             lds_write_b128(o + swz<D>(r, 2 * c), u32x4_t{b[0], b[1], b[2], b[3]});
             lds_write_b128(o + swz<D>(r, 2 * c + 1), u32x4_t{b[4], b[5], b[6], b[7]});
@@ -298,14 +294,15 @@ __device__ __forceinline__ void load_fragments(const char* kb, const char* vb, b
     lds_settle(vf);
 }
 
-template <int D, int NB, bool CAUSAL, bool PAGED, bool FP8>
-__global__ __launch_bounds__(FP8 ? 64 * kMW8 : kMT) void fd_mfma_partial_kernel(PartialArgs a) {
+template <int D, int NB, bool CAUSAL, bool PAGED, int KV>
+__global__ __launch_bounds__(KV != kKvBf16 ? 64 * kMW8 : kMT) void fd_mfma_partial_kernel(PartialArgs a) {
+    constexpr bool C8 = KV != kKvBf16;  // one-byte codes
     using G = Geo<D>;
-    using LG = LGeo<D, FP8>;
-    constexpr int MW = FP8 ? kMW8 : kMW;  // waves per workgroup
+    using LG = LGeo<D, C8>;
+    constexpr int MW = C8 ? kMW8 : kMW;  // waves per workgroup
     constexpr int MT = 64 * MW;
     constexpr int NS = LG::NS;
-    constexpr int ESZ = FP8 ? 1 : 2;  // bytes per stored K/V element
+    constexpr int ESZ = C8 ? 1 : 2;  // bytes per stored K/V element
     constexpr int NR = 16 * NB;  // query rows per workgroup
     constexpr int RS = D + 4;    // padded row stride of the merge area (floats)
     constexpr int MERGEB = MW * (NR * RS + 3 * NR) * 4;
@@ -396,7 +393,7 @@ __global__ __launch_bounds__(FP8 ? 64 * kMW8 : kMT) void fd_mfma_partial_kernel(
     }
 
     char* ring = smem + w * LG::WAVEB;
-    char* conv = ring + NS * LG::STAGEB;  // fp8: this wave's dequantised block
+    char* conv = ring + NS * LG::STAGEB;  // codes: this wave's dequantised block
     const char* kt;
     const char* vt;
     int rsb;  // bytes from one stored key row of the head to the next
@@ -417,12 +414,12 @@ __global__ __launch_bounds__(FP8 ? 64 * kMW8 : kMT) void fd_mfma_partial_kernel(
 
     // Lane l of load instruction i fills LDS slot (row i*RPI + l/CH, chunk
     // l%CH) of the block: bf16 rows with the row's global chunk (l%CH) ^
-    // row (the operand swizzle), fp8 rows in their stored order.
+    // row (the operand swizzle), rows of codes in their stored order.
     uint32_t dma_off[LG::IPB];
 #pragma unroll
     for (int i = 0; i < LG::IPB; ++i) {
         const int r = i * LG::RPI + lane / LG::CH;
-        const int cg = FP8 ? lane % LG::CH : (lane % LG::CH) ^ swf<LG::CH>(r);
+        const int cg = C8 ? lane % LG::CH : (lane % LG::CH) ^ swf<LG::CH>(r);
         dma_off[i] = (uint32_t)(r * rsb + cg * 16);
     }
 
@@ -432,7 +429,7 @@ __global__ __launch_bounds__(FP8 ? 64 * kMW8 : kMT) void fd_mfma_partial_kernel(
     auto page_of = [&](int blk) { return PAGED ? page_at(a.pages, tbl, lo + blk * kKB, hi) : 0; };
 #pragma unroll
     for (int j = 0; j < NS - 1; ++j)
-        load_block_at<D, FP8, PAGED>(a.pages, page_of(w + j * MW), kt, vt, lo, hi, w + j * MW, rsb,
+        load_block_at<D, C8, PAGED>(a.pages, page_of(w + j * MW), kt, vt, lo, hi, w + j * MW, rsb,
                                      ring + j * LG::STAGEB, dma_off);
     int page_next = page_of(w + (NS - 1) * MW);
 
@@ -441,14 +438,14 @@ __global__ __launch_bounds__(FP8 ? 64 * kMW8 : kMT) void fd_mfma_partial_kernel(
             const int jn = j + NS - 1;
             const int page = page_next;
             page_next = page_of(w + (jn + 1) * MW);
-            load_block_at<D, FP8, PAGED>(a.pages, page, kt, vt, lo, hi, w + jn * MW, rsb,
+            load_block_at<D, C8, PAGED>(a.pages, page, kt, vt, lo, hi, w + jn * MW, rsb,
                                          ring + (jn % NS) * LG::STAGEB, dma_off);
         }
         wait_vmcnt_le<(NS - 1) * 2 * LG::IPB>();  // block j has landed
         const char* kb = ring + (j % NS) * LG::STAGEB;
         const char* vb = kb + LG::BLKB;
-        if constexpr (FP8) {
-            dequant_block<D>(kb, conv, lane);
+        if constexpr (C8) {
+            dequant_block<D, KV>(kb, conv, lane);
             kb = conv;
             vb = conv + G::BLKB;
         }
@@ -508,8 +505,8 @@ __global__ __launch_bounds__(FP8 ? 64 * kMW8 : kMT) void fd_mfma_partial_kernel(
             den = fmaf(f[x], sm_l[x * NR + r], den);
         }
         const bool empty = M == -INFINITY;
-        // fp8: V was dequantised without its scale
-        const float inv = empty ? 0.f : (FP8 ? a.v_scale : 1.f) / den;
+        // codes: V was dequantised without its scale
+        const float inv = empty ? 0.f : (C8 ? a.v_scale : 1.f) / den;
 #pragma unroll
         for (int x = 0; x < MW; ++x) sm_l[x * NR + r] = f[x] * inv;
         sm_m[r] = M;  // row r's entries are this thread's alone
@@ -548,29 +545,30 @@ __global__ __launch_bounds__(FP8 ? 64 * kMW8 : kMT) void fd_mfma_partial_kernel(
 }
 
 
-template <int D, int NB, bool FP8>
+template <int D, int NB, int KV>
 void launch_nb_kv(int batch, const PartialArgs& a, hipStream_t stream) {
-    dim3 grid(a.Hkv, a.rule.slots, batch), block(FP8 ? 64 * kMW8 : kMT);
+    dim3 grid(a.Hkv, a.rule.slots, batch), block(KV != kKvBf16 ? 64 * kMW8 : kMT);
     const bool paged = a.pages.table != nullptr;
     if (a.q_len > 1) {
         if (paged)
-            hipLaunchKernelGGL((fd_mfma_partial_kernel<D, NB, true, true, FP8>), grid, block, 0, stream, a);
+            hipLaunchKernelGGL((fd_mfma_partial_kernel<D, NB, true, true, KV>), grid, block, 0, stream, a);
         else
-            hipLaunchKernelGGL((fd_mfma_partial_kernel<D, NB, true, false, FP8>), grid, block, 0, stream, a);
+            hipLaunchKernelGGL((fd_mfma_partial_kernel<D, NB, true, false, KV>), grid, block, 0, stream, a);
     } else {
         if (paged)
-            hipLaunchKernelGGL((fd_mfma_partial_kernel<D, NB, false, true, FP8>), grid, block, 0, stream, a);
+            hipLaunchKernelGGL((fd_mfma_partial_kernel<D, NB, false, true, KV>), grid, block, 0, stream, a);
         else
-            hipLaunchKernelGGL((fd_mfma_partial_kernel<D, NB, false, false, FP8>), grid, block, 0, stream, a);
+            hipLaunchKernelGGL((fd_mfma_partial_kernel<D, NB, false, false, KV>), grid, block, 0, stream, a);
     }
 }
 
 template <int D, int NB>
 void launch_nb(int batch, const PartialArgs& a, hipStream_t stream) {
-    if (a.kv_fp8)
-        launch_nb_kv<D, NB, true>(batch, a, stream);
-    else
-        launch_nb_kv<D, NB, false>(batch, a, stream);
+    switch (a.kv_codes) {
+        case kKvE4M3: launch_nb_kv<D, NB, kKvE4M3>(batch, a, stream); break;
+        case kKvInt8: launch_nb_kv<D, NB, kKvInt8>(batch, a, stream); break;
+        default: launch_nb_kv<D, NB, kKvBf16>(batch, a, stream); break;
+    }
 }
 
 }  // namespace

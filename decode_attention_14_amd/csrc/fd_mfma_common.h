@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "fd_internal.h"
+
 namespace fdk {
 
 // Cache policy bits of the buffer-to-LDS loads (the `aux` operand).
@@ -17,6 +19,7 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
 typedef __attribute__((ext_vector_type(4))) short s16x4_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((ext_vector_type(2))) float f32x2_t;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
 typedef __attribute__((address_space(3))) void lds_void_t;
 
@@ -65,6 +68,26 @@ static __device__ __forceinline__ u32x4_t lds_read_b128(const char* p) {
 
 static __device__ __forceinline__ void lds_write_b128(char* p, u32x4_t x) {
     asm volatile("ds_write_b128 %0, %1" : : "v"(lds_addr(p)), "v"(x) : "memory");
+}
+
+// Four one-byte K/V codes (bytes 0..3 of w) as four bf16 values: lo holds
+// codes 0 and 1, hi codes 2 and 3.  Exact: every E4M3 value and every
+// integer in [-128, 127] is a bf16 value.  The per-tensor scales are applied
+// outside (k_scale in the score scale, v_scale to the output).
+template <int KV>
+static __device__ __forceinline__ void codes_to_bf16(uint32_t w, uint32_t& lo, uint32_t& hi) {
+    if constexpr (KV == kKvE4M3) {
+        lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.f, false));
+        hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.f, true));
+    } else {
+        static_assert(KV == kKvInt8, "one-byte code format");
+        float f[4];
+#pragma unroll
+        for (int n = 0; n < 4; ++n) f[n] = (float)(int)(int8_t)(w >> (8 * n));  // sign-extended byte n
+        typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_v;
+        lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{f[0], f[1]}, bf16x2_v));
+        hi = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{f[2], f[3]}, bf16x2_v));
+    }
 }
 
 }  // namespace fdk

@@ -149,7 +149,9 @@ def paginate(k: torch.Tensor, v: torch.Tensor, cache_lens, page_size: int, layou
     permutation of the pool (``Generator(PCG64(seed)).permutation``), which
     also holds ``spare_pages`` pages no sequence uses.  Rows of a page at or
     past L_b and every spare page are filled with NaN (for uint8 FP8 codes,
-    0x7F: the E4M3 NaN), so a kernel that reads them cannot go unnoticed.
+    0x7F: the E4M3 NaN), so a kernel that reads them cannot go unnoticed;
+    INT8 codes have no NaN, so their pools get 127, the largest code, which
+    takes over the softmax of every query whose elements sum above zero.
     Data movement only.
     """
     if layout not in ("nhd", "hnd"):
@@ -163,7 +165,7 @@ def paginate(k: torch.Tensor, v: torch.Tensor, cache_lens, page_size: int, layou
     perm = np.random.Generator(np.random.PCG64(seed)).permutation(num_pages)
     table = torch.full((B, Lmax // page_size), -1, dtype=torch.int32)
     shape = (num_pages, page_size, H, D) if layout == "nhd" else (num_pages, H, page_size, D)
-    fill = 0x7F if k.dtype == torch.uint8 else float("nan")  # uint8: the E4M3 NaN code
+    fill = {torch.uint8: 0x7F, torch.int8: 127}.get(k.dtype, float("nan"))  # uint8: the E4M3 NaN code
     kp = torch.full(shape, fill, dtype=k.dtype)
     vp = torch.full(shape, fill, dtype=v.dtype)
     nxt = 0
@@ -191,6 +193,18 @@ def quantize_fp8(t: torch.Tensor, scale: float) -> torch.Tensor:
     if float(x.abs().max()) > 448.0:
         raise ValueError("values exceed the E4M3 range at this scale")
     return x.to(torch.float8_e4m3fn).view(torch.uint8)
+
+
+def quantize_int8(t: torch.Tensor, scale: float) -> torch.Tensor:
+    """Symmetric INT8 codes of ``t / scale``: rounded to nearest even, then
+    clamped to [-127, 127]."""
+    x = torch.round(t.float() / float(np.float32(scale)))
+    return x.clamp_(-127, 127).to(torch.int8)
+
+
+def int8_scale_for(t: torch.Tensor) -> float:
+    """Per-tensor scale mapping the largest |value| to 127, as an fp32 value."""
+    return float(np.float32(float(t.float().abs().max()) / 127.0))
 
 
 def fp8_scale_for(t: torch.Tensor) -> float:

@@ -61,7 +61,12 @@ typedef enum fd_status {
     FD_ERR_DEVICE = -4       /* HIP runtime error */
 } fd_status;
 
-typedef enum fd_dtype { FD_F32 = 0, FD_BF16 = 1, FD_FP8_E4M3 = 2 /* K/V caches only */ } fd_dtype;
+typedef enum fd_dtype {
+    FD_F32 = 0,
+    FD_BF16 = 1,
+    FD_FP8_E4M3 = 2, /* K/V caches only */
+    FD_INT8 = 3      /* K/V caches only */
+} fd_dtype;
 
 /* Most partial slots a row may have. */
 #define FD_MAX_SPLITS 256
@@ -257,6 +262,30 @@ fd_status fd_decode_partials_fp8(const fd_dims* dims, const void* q, const void*
                                  float v_scale, const int32_t* cache_lens, float scale,
                                  int32_t num_splits, const fd_plan* plan, float* o_part,
                                  float* m_part, float* lse_part, void* stream);
+
+/* INT8 K/V caches.
+ *
+ * The other cache format that the same section of page "FlashDecoding算法原理
+ * 与多GPU并行解码实战" names (and page 3's memory section: INT8-quantised
+ * cache data).  k_cache and v_cache hold one-byte two's-complement codes in
+ * [-128, 127] with one scale per tensor, symmetric: the key is code * k_scale
+ * and the value is code * v_scale.  Every such integer is exact in bf16, so
+ * the arithmetic, layouts, arguments and errors are those of the FP8 calls
+ * above (bf16 q and out, k_scale folded into the score scale, v_scale into
+ * the output, every q_len served, contiguous or paged caches). */
+fd_status fd_decode_attention_int8(const fd_dims* dims, const void* q, const void* k_cache,
+                                   const void* v_cache, const fd_kv_pages* pages, float k_scale,
+                                   float v_scale, const int32_t* cache_lens, float scale,
+                                   int32_t num_splits, const fd_plan* plan, void* workspace,
+                                   uint64_t workspace_bytes, void* out, float* lse, void* stream);
+
+/* fd_decode_partials_int8 -- the first pass alone over int8 caches (outputs
+ * as fd_decode_partials; o_part already carries v_scale). */
+fd_status fd_decode_partials_int8(const fd_dims* dims, const void* q, const void* k_cache,
+                                  const void* v_cache, const fd_kv_pages* pages, float k_scale,
+                                  float v_scale, const int32_t* cache_lens, float scale,
+                                  int32_t num_splits, const fd_plan* plan, float* o_part,
+                                  float* m_part, float* lse_part, void* stream);
 
 /* Diagnostics.  fd_status_string returns a static name for a status.
  * fd_last_error returns the message of the last failed call on this thread

@@ -225,26 +225,49 @@ def fp8_e4m3_to_float(codes):
     return sign * mag
 
 
-def attention_fp8(q, k_codes, v_codes, cache_lens, scale, k_scale, v_scale, nthreads: int = 0, lib=None):
-    """The plain definition over FP8 E4M3 caches: key = code * k_scale and
-    value = code * v_scale (the dequantisation of page "FlashDecoding算法原理与
-    多GPU并行解码实战", section on combining methods).  ``q`` holds bf16 bit
-    patterns (uint16) or float32 values; ``k_codes``/``v_codes`` uint8 codes of
-    shape [B, Hkv, Lmax, D].  The code values are exact in float32; k_scale
-    enters as the exact fp64 product scale * k_scale (scores are linear in the
-    key), and v_scale multiplies the output (the output is linear in V).
-    """
+def _attention_codes(q, kf, vf, cache_lens, scale, k_scale, v_scale, nthreads, lib, what):
+    """The plain definition over dequantised caches: kf/vf hold the code
+    values (exact in float32); key = code * k_scale enters through the exact
+    fp64 product scale * k_scale (scores are linear in the key), and v_scale
+    multiplies the output (the output is linear in V)."""
     lib = lib or load()
     qf = np.ascontiguousarray(q)
     if qf.dtype == np.uint16:
         qf = (qf.astype(np.uint32) << 16).view(np.float32)
-    kf = np.ascontiguousarray(fp8_e4m3_to_float(k_codes).astype(np.float32))
-    vf = np.ascontiguousarray(fp8_e4m3_to_float(v_codes).astype(np.float32))
-    qf, kf, vf, lens, dims = _prep(qf, kf, vf, cache_lens)
+    qf, kf, vf, lens, dims = _prep(qf, np.ascontiguousarray(kf), np.ascontiguousarray(vf), cache_lens)
     B, Hq, Hkv, D, q_len, Lmax, code = dims
     out = np.empty((B, Hq, q_len, D), np.float64)
     lse = np.empty((B, Hq, q_len), np.float64)
     s = float(np.float32(scale)) * float(np.float32(k_scale))
     rc = lib.orc_attention(*dims, _ptr(qf), _ptr(kf), _ptr(vf), _ptr(lens), s, _ptr(out), _ptr(lse), nthreads)
-    _check(rc, "attention_fp8")
+    _check(rc, what)
     return out * float(np.float32(v_scale)), lse
+
+
+def attention_fp8(q, k_codes, v_codes, cache_lens, scale, k_scale, v_scale, nthreads: int = 0, lib=None):
+    """The plain definition over FP8 E4M3 caches: key = code * k_scale and
+    value = code * v_scale (the dequantisation of page "FlashDecoding算法原理与
+    多GPU并行解码实战", section on combining methods).  ``q`` holds bf16 bit
+    patterns (uint16) or float32 values; ``k_codes``/``v_codes`` uint8 codes of
+    shape [B, Hkv, Lmax, D].
+    """
+    kf = fp8_e4m3_to_float(k_codes).astype(np.float32)
+    vf = fp8_e4m3_to_float(v_codes).astype(np.float32)
+    return _attention_codes(q, kf, vf, cache_lens, scale, k_scale, v_scale, nthreads, lib, "attention_fp8")
+
+
+def int8_to_float(codes):
+    """Values of two's-complement INT8 codes as float64, from the encoding's
+    definition: a byte c (0..255) stands for c - 256 when its bit 7 is set,
+    else for c."""
+    c = np.asarray(codes).view(np.uint8).astype(np.int64)
+    return np.where(c >= 128, c - 256, c).astype(np.float64)
+
+
+def attention_int8(q, k_codes, v_codes, cache_lens, scale, k_scale, v_scale, nthreads: int = 0, lib=None):
+    """The plain definition over INT8 caches (the other cache format of the
+    same section): key = code * k_scale, value = code * v_scale, with int8
+    (or uint8-viewed) codes of shape [B, Hkv, Lmax, D]; as attention_fp8."""
+    kf = int8_to_float(k_codes).astype(np.float32)
+    vf = int8_to_float(v_codes).astype(np.float32)
+    return _attention_codes(q, kf, vf, cache_lens, scale, k_scale, v_scale, nthreads, lib, "attention_int8")

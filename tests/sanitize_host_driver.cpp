@@ -162,6 +162,13 @@ void validation_paths() {
                                     fake(4), nullptr, nullptr) == FD_ERR_DEVICE);
     CHECK(fd_decode_attention_fp8(&good, fake(0), fake(1), fake(2), &pg, 0.5f, 2.f, dl, 0.1f, 3, nullptr, fake(6),
                                   1 << 20, fake(4), nullptr, nullptr) == FD_ERR_DEVICE);
+    CHECK(fd_decode_attention_int8(&good, fake(0), fake(1), fake(2), nullptr, 1.f, INFINITY, dl, 0.1f, 0, nullptr,
+                                   nullptr, 0, fake(4), nullptr, nullptr) == FD_ERR_INVALID);
+    CHECK(fd_decode_attention_int8(&f32q, fake(0), fake(1), fake(2), nullptr, 1.f, 1.f, dl, 0.1f, 0, nullptr,
+                                   nullptr, 0, fake(4), nullptr, nullptr) == FD_ERR_UNSUPPORTED);
+    CHECK(std::strstr(fd_last_error(), "int8") != nullptr);
+    CHECK(fd_decode_partials_int8(&good, fake(0), fake(1), fake(2), &pg, 0.5f, 2.f, dl, 0.1f, 3, nullptr,
+                                  (float*)fake(5), (float*)fake(6), (float*)fake(7), nullptr) == FD_ERR_DEVICE);
     // status strings and a long error message
     for (int s = -10; s <= 1; ++s) CHECK(std::strlen(fd_status_string(s)) > 0);
     const fd_dims huge{1, 32, 8, 128, 1, 64, FD_BF16};
