@@ -216,8 +216,14 @@ __device__ __forceinline__ void chunk_dequant_stage(const char* src, char* dst, 
 #pragma unroll
         for (int i = 0; i < 4; ++i) codes_to_bf16<KV>(x[n][i], bw[2 * i], bw[2 * i + 1]);
         char* o = dst + tsr * G::SKB * G::BLKB + (r / kCBK) * G::BLKB;
-        lds_write_b128(o + cswz<D>(r % kCBK, 2 * c8), u32x4_t{bw[0], bw[1], bw[2], bw[3]});
-        lds_write_b128(o + cswz<D>(r % kCBK, 2 * c8 + 1), u32x4_t{bw[4], bw[5], bw[6], bw[7]});
+        // 8 lanes per LDS write cycle over 128 bytes of banks: lanes in the
+        // upper half of a code row (and, for 64-byte code rows, lanes of odd
+        // rows) write their odd chunk first, so each 8-lane group covers 8
+        // distinct chunks modulo 8.
+        const bool odd_first = (c8 >= G8::CH / 2) != (G8::CH == 4 && (r & 1));
+        const u32x4_t lo4 = u32x4_t{bw[0], bw[1], bw[2], bw[3]}, hi4 = u32x4_t{bw[4], bw[5], bw[6], bw[7]};
+        lds_write_b128(o + cswz<D>(r % kCBK, 2 * c8 + (odd_first ? 1 : 0)), odd_first ? hi4 : lo4);
+        lds_write_b128(o + cswz<D>(r % kCBK, 2 * c8 + (odd_first ? 0 : 1)), odd_first ? lo4 : hi4);
     }
 }
 

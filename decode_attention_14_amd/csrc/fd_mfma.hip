@@ -107,15 +107,17 @@ struct LGeo {
 
 // XOR swizzle of the 16-byte chunks of row r (CH chunks per row).  Two read
 // patterns must be free of LDS bank conflicts: 16 consecutive rows at one
-// chunk (K operands), and 4 aligned consecutive rows at an even/odd chunk
-// pair (transposed V reads).  For CH = 16 the map sends row bits (1:0) to
-// chunk bits (2:1), row bit 2 to bit 3 and row bit 3 to bit 0: a bijection on
-// 16 rows that keeps bit 0 fixed within an aligned group of 4.  For CH = 8,
-// two 128-byte rows share a bank cycle, so the same construction applies to
-// the row pair index r >> 1.
+// chunk (K operands, ds_read_b128), and 4 aligned consecutive rows at an
+// even/odd chunk pair (transposed V reads).  For CH = 16 the map is the
+// linear bijection r -> (r1 r0) in chunk bits 1:0, r2 ^ r3 in bit 2 and
+// r0 ^ r3 in bit 3: the hardware's SQ_LDS_BANK_CONFLICT counter reads zero
+// for both patterns with it, where a map sending row bits 1:0 to chunk bits
+// 2:1 (conflict-free under a plain 64-bank model) cost 4 cycles on every K
+// read.  For CH = 8, two 128-byte rows share a bank cycle, and the map acts
+// on the row pair index r >> 1.
 template <int CH>
 __device__ __forceinline__ int swf(int r) {
-    if constexpr (CH == 16) return ((r & 3) << 1) | (((r >> 2) & 1) << 3) | ((r >> 3) & 1);
+    if constexpr (CH == 16) return (r & 3) | ((((r >> 2) ^ (r >> 3)) & 1) << 2) | (((r ^ (r >> 3)) & 1) << 3);
     const int u = (r >> 1) & 7;
     return ((u & 1) << 1) | (((u >> 1) & 1) << 2) | ((u >> 2) & 1);
 }
@@ -178,23 +180,49 @@ __device__ __forceinline__ void load_block_at(const PagedKV& pk, int page, const
 // Dequantise one landed block of one-byte codes (K at src, V at src +
 // LGeo::BLKB, rows of D codes in format KV) into bf16 blocks of the operand
 // layout (K at dst, V at dst + Geo::BLKB, swizzled as swz), exactly (see
-// codes_to_bf16).  Lane l converts 16-byte chunks l, l + 64, ... of each
-// tensor: consecutive lanes read consecutive LDS bytes.
+// codes_to_bf16), as a read half and a convert-and-write half.  Lane l
+// converts the chunks that dq_row_chunk assigns.
 //
 // The LDS accesses go through lds_read_b128 / lds_write_b128: the block at
 // src has landed (the caller waited for it), and dst is this wave's own
 // area, read only by its own later reads.
 
+template <int D>
+struct DQ {
+    static constexpr int NQ = LGeo<D, true>::BLKB / 16 / 64;  // 16-byte chunks per lane per tensor
+};
+
+// The code chunk (row r, chunk c of 16 codes) that lane `lane` converts in
+// its n-th round: consecutive lanes take consecutive 16-byte chunks of the
+// block, so the reads cover the LDS banks in order.
+template <int D>
+__device__ __forceinline__ void dq_row_chunk(int n, int lane, int& r, int& c) {
+    constexpr int CH8 = LGeo<D, true>::CH;  // 16-byte chunks per code row
+    const int q = n * 64 + lane;
+    r = q / CH8;
+    c = q % CH8;
+}
+
+// First half: start the LDS reads of the block's codes into x (valid after
+// dequant_write's wait).
+template <int D>
+__device__ __forceinline__ void dequant_read(const char* src, int lane, u32x4_t (&x)[2][DQ<D>::NQ]) {
+    using L = LGeo<D, true>;
+#pragma unroll
+    for (int n = 0; n < DQ<D>::NQ; ++n) {
+        int r, c;
+        dq_row_chunk<D>(n, lane, r, c);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) x[t][n] = lds_read_b128(src + t * L::BLKB + r * L::ROWB + c * 16);
+    }
+}
+
+// Second half: wait for the reads, convert, and write the bf16 blocks.
 template <int D, int KV>
-__device__ __forceinline__ void dequant_block(const char* src, char* dst, int lane) {
+__device__ __forceinline__ void dequant_write(u32x4_t (&x)[2][DQ<D>::NQ], char* dst, int lane) {
     using L = LGeo<D, true>;
     using G = Geo<D>;
-    constexpr int NQ = L::BLKB / 16 / 64;  // 16-byte chunks per lane per tensor
-    u32x4_t x[2][NQ];
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int n = 0; n < NQ; ++n) x[t][n] = lds_read_b128(src + t * L::BLKB + (n * 64 + lane) * 16);
+    constexpr int NQ = DQ<D>::NQ;
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
     for (int t = 0; t < 2; ++t)
@@ -204,16 +232,21 @@ __device__ __forceinline__ void dequant_block(const char* src, char* dst, int la
     for (int t = 0; t < 2; ++t) {
 #pragma unroll
         for (int n = 0; n < NQ; ++n) {
-            const int q = n * 64 + lane;
-            const int r = q / L::CH;
-            const int c = q % L::CH;  // 16 codes = dims 16c .. 16c + 15
-            const uint32_t w[4] = {x[t][n][0], x[t][n][1], x[t][n][2], x[t][n][3]};
+            int r, c;  // 16 codes of row r = dims 16c .. 16c + 15
+            dq_row_chunk<D>(n, lane, r, c);
             uint32_t b[8];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) codes_to_bf16<KV>(w[i], b[2 * i], b[2 * i + 1]);
+            for (int i = 0; i < 4; ++i) codes_to_bf16<KV>(x[t][n][i], b[2 * i], b[2 * i + 1]);
             char* o = dst + t * G::BLKB;
-            lds_write_b128(o + swz<D>(r, 2 * c), u32x4_t{b[0], b[1], b[2], b[3]});
-            lds_write_b128(o + swz<D>(r, 2 * c + 1), u32x4_t{b[4], b[5], b[6], b[7]});
+            // A 16-byte write serves 8 lanes per LDS cycle over 128 bytes of
+            // banks.  Lanes whose chunk pair lies in the upper half of the
+            // code row (and, for 64-byte code rows, lanes of odd rows) write
+            // their odd chunk first, so each write instruction's 8-lane
+            // groups cover 8 distinct chunks modulo 8.
+            const bool odd_first = (c >= L::CH / 2) != (L::CH == 4 && (r & 1));
+            const u32x4_t lo4 = u32x4_t{b[0], b[1], b[2], b[3]}, hi4 = u32x4_t{b[4], b[5], b[6], b[7]};
+            lds_write_b128(o + swz<D>(r, 2 * c + (odd_first ? 1 : 0)), odd_first ? hi4 : lo4);
+            lds_write_b128(o + swz<D>(r, 2 * c + (odd_first ? 0 : 1)), odd_first ? lo4 : hi4);
         }
     }
 }
@@ -427,33 +460,33 @@ __global__ __launch_bounds__(KV != kKvBf16 ? 64 * kMW8 : kMT) void fd_mfma_parti
     // paged cache's page ids are read one block ahead of their loads, so the
     // scalar table reads overlap the work of the previous block.
     auto page_of = [&](int blk) { return PAGED ? page_at(a.pages, tbl, lo + blk * kKB, hi) : 0; };
-#pragma unroll
-    for (int j = 0; j < NS - 1; ++j)
-        load_block_at<D, C8, PAGED>(a.pages, page_of(w + j * MW), kt, vt, lo, hi, w + j * MW, rsb,
-                                     ring + j * LG::STAGEB, dma_off);
-    int page_next = page_of(w + (NS - 1) * MW);
+    int page_next = page_of(w);
+    // Start the loads of wave block jn (issued in order jn = 0, 1, ...) into
+    // ring slot jn % NS.
+    auto issue = [&](int jn) {
+        const int page = page_next;
+        page_next = page_of(w + (jn + 1) * MW);
+        load_block_at<D, C8, PAGED>(a.pages, page, kt, vt, lo, hi, w + jn * MW, rsb, ring + (jn % NS) * LG::STAGEB,
+                                    dma_off);
+    };
 
+#pragma unroll
+    for (int j = 0; j < NS - 1; ++j) issue(j);
     for (int j = 0; j < nw; ++j) {
-        {
-            const int jn = j + NS - 1;
-            const int page = page_next;
-            page_next = page_of(w + (jn + 1) * MW);
-            load_block_at<D, C8, PAGED>(a.pages, page, kt, vt, lo, hi, w + jn * MW, rsb,
-                                         ring + (jn % NS) * LG::STAGEB, dma_off);
-        }
+        issue(j + NS - 1);
         wait_vmcnt_le<(NS - 1) * 2 * LG::IPB>();  // block j has landed
         const char* kb = ring + (j % NS) * LG::STAGEB;
         const char* vb = kb + LG::BLKB;
         if constexpr (C8) {
-            dequant_block<D, KV>(kb, conv, lane);
+            u32x4_t x[2][DQ<D>::NQ];
+            dequant_read<D>(kb, lane, x);
+            dequant_write<D, KV>(x, conv, lane);
             kb = conv;
             vb = conv + G::BLKB;
         }
-
         bf16x8_t kf[G::KS];
         bf16x4_t vf[G::DB];
         load_fragments<D>(kb, vb, kf, vf, grp, col);
-
         const int key0 = lo + (w + j * MW) * kKB;  // first key of the block
         block_math<D, NB>(kf, vf, qf, acc, m, l, mx, key0, key0 + kKB > mask_from, rend, c, grp);
     }
