@@ -42,6 +42,10 @@
  *   - Supported: dtype FD_F32 or FD_BF16; D = 64 or 128; any Hq/Hkv ratio;
  *     any q_len >= 1.  Arithmetic is fp32 throughout (scores, softmax,
  *     accumulation); out is rounded to its dtype with round-to-nearest-even.
+ *     Caches of one-byte codes (FP8 E4M3, INT8) with bf16 q and out have
+ *     calls of their own (fd_decode_attention_fp8, fd_decode_attention_int8),
+ *     and paged caches take a block table (fd_decode_attention_paged and the
+ *     pages argument of the one-byte calls).
  */
 #ifndef FD_H
 #define FD_H
