@@ -16,7 +16,9 @@
 //                      Output: per-tile (o_s, m_s, lse_s), or out/lse
 //                      directly when there is a single tile.
 //   fd_combine_kernel  one wave per query row (four per row when a row has
-//                      many tiles).  It merges the row's tiles:
+//                      many tiles; fd_combine_narrow_kernel, one thread per
+//                      float4 column of four rows, when it has at most four).
+//                      It merges the row's tiles:
 //                      LSE = ln sum_s exp(lse_s), out = sum_s
 //                      exp(lse_s - LSE) o_s.
 //
@@ -431,9 +433,10 @@ __global__ __launch_bounds__(kPThreads) FD_OCCUPANCY void fd_partial_kernel(Part
 }
 
 // ---------------------------------------------------------------------------
-// Merge pass.  WPR waves per query row: with few slots one wave per row (four
-// rows per workgroup); with many, four waves split the row's slots (wave w
+// Merge pass.  WPR waves per query row: up to 32 slots one wave per row (four
+// rows per workgroup); with more, four waves split the row's slots (wave w
 // takes slots w, w + 4, ...) and wave 0 merges their states through LDS.
+// At most four slots go to fd_combine_narrow_kernel below.
 
 constexpr int kCThreads = 256;
 constexpr int kCWaves = kCThreads / 64;
@@ -475,10 +478,80 @@ __global__ __launch_bounds__(kCThreads) void fd_combine_kernel(const float* __re
     }
 }
 
+// Few slots (a long prefill chunk cut into 2-4 tiles): one thread per (row,
+// float4 column), kCombineRowsPerThread rows per thread whose loads are all
+// issued before any arithmetic, so each thread keeps several 16-byte loads
+// in flight instead of one per wave-row.
+constexpr int kCombineNarrowSlots = 4;
+constexpr int kCombineRowsPerThread = 4;
+
+template <int D, bool OUT_BF16, int S>
+__global__ __launch_bounds__(kCThreads) void fd_combine_narrow_kernel(const float* __restrict__ o_part,
+                                                                      const float* __restrict__ lse_part,
+                                                                      int64_t rows, void* out, float* lse) {
+    constexpr int C4 = D / 4;                  // float4 columns
+    constexpr int RPB = kCThreads / C4;        // rows of the workgroup per round
+    constexpr int RPT = kCombineRowsPerThread;
+    const int c4 = threadIdx.x % C4;
+    const int64_t row0 = (int64_t)blockIdx.x * RPB * RPT + threadIdx.x / C4;
+    float lv[RPT][S];
+    float4 ov[RPT][S];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        const int64_t row = row0 + (int64_t)i * RPB;
+        const int64_t r = row < rows ? row : rows - 1;  // spare rows read a valid row, write nothing
+#pragma unroll
+        for (int sl = 0; sl < S; ++sl) {
+            lv[i][sl] = lse_part[r * S + sl];
+            ov[i][sl] = reinterpret_cast<const float4*>(o_part)[(r * S + sl) * C4 + c4];
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        const int64_t row = row0 + (int64_t)i * RPB;
+        if (row >= rows) continue;
+        MergeState st{-INFINITY, 0.f, make_float4(0.f, 0.f, 0.f, 0.f)};
+#pragma unroll
+        for (int sl = 0; sl < S; ++sl) st.m = fmaxf(st.m, lv[i][sl]);
+        if (st.m != -INFINITY) {
+#pragma unroll
+            for (int sl = 0; sl < S; ++sl) {
+                if (lv[i][sl] == -INFINITY) continue;  // empty slot: its o entry never enters
+                const float wgt = __expf(lv[i][sl] - st.m);
+                st.z += wgt;
+                st.acc.x = fmaf(wgt, ov[i][sl].x, st.acc.x);
+                st.acc.y = fmaf(wgt, ov[i][sl].y, st.acc.y);
+                st.acc.z = fmaf(wgt, ov[i][sl].z, st.acc.z);
+                st.acc.w = fmaf(wgt, ov[i][sl].w, st.acc.w);
+            }
+        }
+        void* orow = OUT_BF16 ? (void*)(reinterpret_cast<uint16_t*>(out) + row * D)
+                              : (void*)(reinterpret_cast<float*>(out) + row * D);
+        write_merged<OUT_BF16>(st, orow, c4, lse ? lse + row : nullptr);
+    }
+}
+
+template <int D, bool OUT_BF16, int S>
+void launch_combine_narrow(int64_t rows, const float* o_part, const float* lse_part, void* out, float* lse,
+                           hipStream_t stream) {
+    constexpr int rows_per_block = kCThreads / (D / 4) * kCombineRowsPerThread;
+    hipLaunchKernelGGL((fd_combine_narrow_kernel<D, OUT_BF16, S>),
+                       dim3((unsigned)((rows + rows_per_block - 1) / rows_per_block)), dim3(kCThreads), 0, stream,
+                       o_part, lse_part, rows, out, lse);
+}
+
 template <int D, bool OUT_BF16>
 void launch_combine_d(int64_t rows, int slots, const float* o_part, const float* lse_part, void* out, float* lse,
                       hipStream_t stream) {
     dim3 block(kCThreads);
+    if (slots <= kCombineNarrowSlots) {
+        switch (slots) {
+            case 1: launch_combine_narrow<D, OUT_BF16, 1>(rows, o_part, lse_part, out, lse, stream); return;
+            case 2: launch_combine_narrow<D, OUT_BF16, 2>(rows, o_part, lse_part, out, lse, stream); return;
+            case 3: launch_combine_narrow<D, OUT_BF16, 3>(rows, o_part, lse_part, out, lse, stream); return;
+            default: launch_combine_narrow<D, OUT_BF16, 4>(rows, o_part, lse_part, out, lse, stream); return;
+        }
+    }
     if (slots > kCombineWideSlots)
         hipLaunchKernelGGL((fd_combine_kernel<D, OUT_BF16, kCWaves>), dim3((unsigned)rows), block, 0, stream,
                            o_part, lse_part, slots, rows, out, lse);

@@ -231,8 +231,8 @@ def test_partials_match_oracle_tiles(dt, T):
 def test_combine_matches_oracle_merge():
     say("[case] standalone combine")
     rng = np.random.Generator(np.random.PCG64(1100))
-    for D, S in [(128, 1), (128, 7), (64, 33), (128, 256)]:
-        B, H, T = 2, 4, 3
+    for D, S, (B, H, T) in [(128, 1, (2, 4, 3)), (128, 2, (3, 8, 37)), (64, 3, (3, 8, 37)), (128, 4, (2, 4, 3)),
+                            (64, 4, (1, 5, 41)), (128, 7, (2, 4, 3)), (64, 33, (2, 4, 3)), (128, 256, (2, 4, 3))]:
         o = rng.standard_normal((B, H, T, S, D)).astype(np.float32)
         lp = (rng.standard_normal((B, H, T, S)) * 3).astype(np.float32)
         empty = rng.random((B, H, T, S)) < 0.3
@@ -244,7 +244,7 @@ def test_combine_matches_oracle_merge():
             go, gl = fd.combine(torch.from_numpy(o).cuda(), torch.from_numpy(lp).cuda(),
                                 out_dtype=out_dtype)
             torch.cuda.synchronize()
-            compare(f"combine D={D} S={S} {out_dtype}", go, gl, ro, rl, tol)
+            compare(f"combine D={D} S={S} rows={B * H * T} {out_dtype}", go, gl, ro, rl, tol)
 
 
 # ---------------------------------------------------------------------------
