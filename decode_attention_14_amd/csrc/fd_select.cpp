@@ -8,7 +8,8 @@
 
 namespace fdk {
 
-// The matrix-core kernels read bf16 (or FP8) caches at head_dim 64 or 128.
+// The matrix-core kernels read bf16 caches (or one-byte FP8/INT8 codes) at
+// head_dim 64 or 128.
 bool mfma_partials_supported(int dtype, int head_dim, int rows) {
     return dtype == 1 && (head_dim == 64 || head_dim == 128) && rows >= 1;
 }
