@@ -6,6 +6,7 @@ sweep lengths around tile and step boundaries, forced split counts, GQA
 ratios, head dims, dtypes, chunk lengths, empty sequences and poisoned
 padding.
 """
+import ctypes
 import math
 
 import numpy as np
@@ -323,3 +324,31 @@ def test_vector_kernel_ablation_switch_in_subprocess():
     print(r.stdout[-2000:], r.stderr[-2000:])
     assert r.returncode == 0 and "child ok" in r.stdout
     assert "fd_partial_kernel (vector)" in r.stderr and "fd_mfma" not in r.stderr
+
+
+def test_lse_null_through_the_abi():
+    """lse may be NULL: the C call with a null lse pointer writes the same out
+    bits as with one, for direct single-tile calls (decode and chunk kernels,
+    vector kernel) and for split calls that end in the merge."""
+    lib = fd.load_library()
+    for name, (B, Hq, Hkv, D, T, L, dt), S in [("decode bf16", (2, 32, 8, 128, 1, 900, "bf16"), 1),
+                                               ("decode bf16 split", (2, 32, 8, 128, 1, 900, "bf16"), 4),
+                                               ("chunk bf16", (1, 8, 2, 128, 40, 500, "bf16"), 1),
+                                               ("chunk bf16 split", (1, 8, 2, 128, 40, 500, "bf16"), 3),
+                                               ("vector f32 split", (2, 8, 2, 64, 1, 700, "f32"), 3)]:
+        say(f"[case] lse NULL: {name}")
+        q, k, v, cl = inputs(B, Hq, Hkv, D, T, L, dt, 1400 + S + T, [L, L // 2 + 1][:B])
+        qd, kd, vd, cld = q.cuda(), k.cuda(), v.cuda(), cl.cuda()
+        sc = _scale(D)
+        ref_out, ref_lse = fd.decode_attention(qd, kd, vd, cld, scale=sc, num_splits=S)
+        dims = fd.dims_of(qd, kd)
+        ws = fd.new_workspace(max(fd.workspace_bytes(dims, S), 256), "cuda")
+        out = torch.full_like(qd, float("nan"))
+        st = lib.fd_decode_attention(ctypes.byref(dims), fd._ptr(qd), fd._ptr(kd), fd._ptr(vd), fd._ptr(cld),
+                                     ctypes.c_float(sc), S, None, fd._ptr(ws), ws.numel(), fd._ptr(out), None,
+                                     fd._stream(qd.device))
+        torch.cuda.synchronize()
+        assert st == fd.FD_OK, lib.fd_last_error().decode()
+        bits = torch.int16 if dt == "bf16" else torch.int32
+        assert torch.equal(out.view(bits), ref_out.view(bits)), f"{name}: out differs with lse = NULL"
+        compare(f"lse NULL {name}", out, ref_lse, *run_oracle(q, k, v, cl, sc), TOL[dt])
