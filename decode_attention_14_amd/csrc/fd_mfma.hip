@@ -519,53 +519,48 @@ __global__ __launch_bounds__(KV != kKvBf16 ? 64 * kMW8 : kMT) void fd_mfma_parti
     }
     __syncthreads();
 
-    // Per row (one thread each): the merged max, the log-sum-exp, and each
-    // wave's weight exp2(m_w - M) / sum, written over that wave's l entry.
-    if (tid < nrows) {
-        const int r = tid;
-        float M = -INFINITY, X = -INFINITY;
+    // Outputs, four columns per thread: the weighted sum of the waves' rows
+    // with weights exp2(m_w - M) / sum.  Every thread derives its row's
+    // weights from the wave states itself (the reads of one row's entries
+    // are LDS broadcasts), so no further barrier is needed; the thread at
+    // column 0 also writes the row's statistics.  A row with no visible key
+    // gets zeros (direct) or no o_part entry.
+    constexpr int C4 = D / 4;
+    for (int idx = tid; idx < nrows * C4; idx += MT) {
+        const int r = idx / C4;
+        const int c4 = idx - r * C4;
+        float M = -INFINITY;
 #pragma unroll
-        for (int x = 0; x < MW; ++x) {
-            M = fmaxf(M, sm_m[x * NR + r]);
-            X = fmaxf(X, sm_x[x * NR + r]);
-        }
+        for (int x = 0; x < MW; ++x) M = fmaxf(M, sm_m[x * NR + r]);
+        const bool empty = M == -INFINITY;
         float f[MW];
         float den = 0.f;
 #pragma unroll
         for (int x = 0; x < MW; ++x) {
             const float mw = sm_m[x * NR + r];
-            f[x] = (M == -INFINITY || mw == -INFINITY) ? 0.f : fast_exp2(mw - M);
+            f[x] = (empty || mw == -INFINITY) ? 0.f : fast_exp2(mw - M);
             den = fmaf(f[x], sm_l[x * NR + r], den);
         }
-        const bool empty = M == -INFINITY;
-        // codes: V was dequantised without its scale
-        const float inv = empty ? 0.f : (C8 ? a.v_scale : 1.f) / den;
-#pragma unroll
-        for (int x = 0; x < MW; ++x) sm_l[x * NR + r] = f[x] * inv;
-        sm_m[r] = M;  // row r's entries are this thread's alone
-        const float lse_v = empty ? -INFINITY : (M + log2f(den)) * kLn2;
         const int64_t row = row0 + r;
-        if (a.direct) {
-            if (a.lse) a.lse[row] = lse_v;
-        } else {
-            a.m_part[row * slots + s] = empty ? -INFINITY : X * kLn2;
-            a.lse_part[row * slots + s] = lse_v;
+        if (c4 == 0) {
+            const float lse_v = empty ? -INFINITY : (M + log2f(den)) * kLn2;
+            if (a.direct) {
+                if (a.lse) a.lse[row] = lse_v;
+            } else {
+                float X = -INFINITY;
+#pragma unroll
+                for (int x = 0; x < MW; ++x) X = fmaxf(X, sm_x[x * NR + r]);
+                a.m_part[row * slots + s] = empty ? -INFINITY : X * kLn2;
+                a.lse_part[row * slots + s] = lse_v;
+            }
         }
-    }
-    __syncthreads();
-
-    // Outputs, four columns per thread: the weighted sum of the waves' rows.
-    // A row with no visible key gets zeros (direct) or no o_part entry.
-    constexpr int C4 = D / 4;
-    for (int idx = tid; idx < nrows * C4; idx += MT) {
-        const int r = idx / C4;
-        const int c4 = idx - r * C4;
-        if (!a.direct && sm_m[r] == -INFINITY) continue;
+        if (!a.direct && empty) continue;
+        // codes: V was dequantised without its scale
+        const float inv = empty ? 0.f : (C8 ? a.v_scale : 1.f) * __builtin_amdgcn_rcpf(den);
         f32x4_t o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int x = 0; x < MW; ++x)
-            o += sm_l[x * NR + r] * *reinterpret_cast<const f32x4_t*>(sm_acc + (x * NR + r) * RS + 4 * c4);
-        const int64_t row = row0 + r;
+            o += (f[x] * inv) * *reinterpret_cast<const f32x4_t*>(sm_acc + (x * NR + r) * RS + 4 * c4);
         if (a.direct) {
             uint2 pk;
             pk.x = (uint32_t)f32_to_bf16(o[0]) | ((uint32_t)f32_to_bf16(o[1]) << 16);

@@ -166,6 +166,27 @@ def test_poisoned_padding():
                    poison=True)
 
 
+def test_tile_ends_and_plans_from_other_lengths():
+    """Tiles whose end is not a multiple of the tile length, and plans made
+    from host lengths other than those the device holds (tiles that come out
+    empty, a last tile that runs past the plan's tile length).  Padding past
+    each length is poisoned (NaN keys, Inf values), so any row read past a
+    sequence's end would show."""
+    for D in (128, 64):
+        # equal lengths below capacity: the last tile is shorter than the others
+        check_case(f"short last tile D={D}", 2, 32, 8, D, 1, 3000, "bf16", 1610,
+                   [2500, 2500], use_plan=True, poison=True)
+    # plans made from other host lengths than the device holds
+    for name, host, dev in (("device shorter", [3000, 3000], [2500, 1234]),
+                            ("device longer", [1000, 1000], [3000, 2000])):
+        say(f"[case] plan from other lengths, {name}: plan lens {host}, device lens {dev}")
+        q, k, v, cl = inputs(2, 32, 8, 128, 1, 3000, "bf16", 1611, dev, poison=True)
+        plan = fd.plan_for(q, k, torch.tensor(host, dtype=torch.int32))
+        ref = run_oracle(q, k, v, cl, _scale(128))
+        out, lse = run_gpu(q, k, v, cl, _scale(128), plan=plan)
+        compare(f"plan from other lengths, {name}", out, lse, *ref, TOL["bf16"])
+
+
 def test_peaked_scores():
     check_case("q x10", 2, 32, 8, 128, 1, 4096, "bf16", 700, [4096, 1500], q_mul=10.0, use_plan=True)
     check_case("q x10 f32", 1, 8, 8, 64, 1, 1024, "f32", 701, [1024], q_mul=10.0, num_splits=4)
