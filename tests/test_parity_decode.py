@@ -187,6 +187,31 @@ def test_tile_ends_and_plans_from_other_lengths():
         compare(f"plan from other lengths, {name}", out, lse, *ref, TOL["bf16"])
 
 
+@pytest.mark.parametrize("q_len,rows_kernel", [(48, "chunk"), (4, "decode")])
+def test_chunk_rows_equal_decode_at_their_lengths(q_len, rows_kernel):
+    """Row t of a causal chunk over a cache of L keys is the decode step of
+    the same query row over the first L - q_len + t + 1 keys (page
+    "ChunkedPrefill与FlashDecoding技术解析" §2.1: a chunk token sees itself
+    and earlier positions).  GPU against GPU: a 48-token chunk (192 rows per
+    KV head, the matrix-core chunk kernel) or a 4-token one (16 rows, the
+    decode kernel's causal path), and single-row decode calls."""
+    B, Hq, Hkv, D, L = 2, 16, 4, 128, 1500
+    say(f"[case] chunk rows vs decode: q_len={q_len} ({rows_kernel} kernel)")
+    q, k, v, cl = inputs(B, Hq, Hkv, D, q_len, L, "bf16", 1700 + q_len, [L, L - 333])
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    out, lse = fd.decode_attention(qd, kd, vd, cl.cuda(), scale=_scale(128),
+                                   plan=fd.plan_for(q, k, cl))
+    for t in sorted({0, 1, q_len // 2, q_len - 1}):
+        lens = torch.tensor([int(x) - q_len + t + 1 for x in cl], dtype=torch.int32)
+        q1 = qd[:, :, t:t + 1].contiguous()
+        o1, l1 = fd.decode_attention(q1, kd, vd, lens.cuda(), scale=_scale(128),
+                                     plan=fd.plan_for(q1.cpu(), k, lens))
+        torch.cuda.synchronize()
+        d_out = float((out[:, :, t].float() - o1[:, :, 0].float()).abs().max())
+        d_lse = float((lse[:, :, t] - l1[:, :, 0]).abs().max())
+        assert d_out <= TOL["bf16"] and d_lse <= TOL["bf16"], (t, d_out, d_lse)
+
+
 def test_peaked_scores():
     check_case("q x10", 2, 32, 8, 128, 1, 4096, "bf16", 700, [4096, 1500], q_mul=10.0, use_plan=True)
     check_case("q x10 f32", 1, 8, 8, 64, 1, 1024, "f32", 701, [1024], q_mul=10.0, num_splits=4)
