@@ -112,6 +112,15 @@ def load_library(path: str | None = None):
     return lib
 
 
+def use_library(path: str):
+    """Load the library build at ``path`` (same ABI, e.g. the workgroup-
+    timeline diagnostic build) and route every later call of this module
+    through it."""
+    global _lib
+    _lib = load_library(path)
+    return _lib
+
+
 def status_string(status: int) -> str:
     return load_library().fd_status_string(status).decode()
 

@@ -45,5 +45,15 @@ def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
     return out
 
 
+# The workgroup-timeline diagnostic build of the library (see timeline.py):
+# the same sources with FD_WG_TIMELINE=1.
+TIMELINE_LIB = os.path.join(PKG, "libfd_timeline.so")
+
+
+def build_timeline(verbose: bool = False) -> str:
+    return build(verbose=verbose, out=TIMELINE_LIB, defines=("FD_WG_TIMELINE=1",))
+
+
 if __name__ == "__main__":
     print(build(verbose=True))
+    print(build_timeline(verbose=True))

@@ -51,8 +51,38 @@
 #include "fd_internal.h"
 #include "fd_mfma_common.h"
 
+#ifndef FD_WG_TIMELINE
+#define FD_WG_TIMELINE 0
+#endif
+
+// Workgroup timeline (a diagnostic build only, FD_WG_TIMELINE=1; the
+// library proper compiles none of it).  Workgroup i of the last launch (in
+// dispatch order, i < kTimelineWGs) leaves at [i * kTimelineSlots]: its start,
+// the landing of wave 0's first block, each wave's exit from its block loop
+// (up to 8 waves), its end, all in the 100 MHz s_memrealtime clock, and the
+// XCD it ran on.  fd_debug_timeline copies the array to host memory.
+#if FD_WG_TIMELINE
+namespace fdk {
+constexpr int kTimelineWGs = 4096;
+constexpr int kTimelineSlots = 16;
+enum { kTlStart = 0, kTlFirst = 1, kTlLoop = 2, kTlEnd = 10, kTlXcc = 11 };
+}  // namespace fdk
+__device__ uint64_t fd_wg_timeline[fdk::kTimelineWGs * fdk::kTimelineSlots];
+extern "C" int fd_debug_timeline(void* host_dst, uint64_t bytes) {
+    if (bytes > sizeof(fd_wg_timeline)) bytes = sizeof(fd_wg_timeline);
+    return (int)hipMemcpyFromSymbol(host_dst, HIP_SYMBOL(fd_wg_timeline), bytes, 0, hipMemcpyDeviceToHost);
+}
+#endif
+
 namespace fdk {
 namespace {
+
+#if FD_WG_TIMELINE
+__device__ __forceinline__ uint64_t* timeline_row() {
+    const uint32_t i = (blockIdx.z * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x;
+    return i < (uint32_t)kTimelineWGs ? fd_wg_timeline + (uint64_t)i * kTimelineSlots : nullptr;
+}
+#endif
 
 #ifndef FD_MFMA_STAGES
 #define FD_MFMA_STAGES 2
@@ -355,6 +385,10 @@ __global__ __launch_bounds__(KV != kKvBf16 ? 64 * kMW8 : kMT) void fd_mfma_parti
     const int w = (int)uniform((uint32_t)(tid >> 6));
     const int grp = lane >> 4;
     const int col = lane & 15;
+#if FD_WG_TIMELINE
+    const uint64_t tl_start = __builtin_amdgcn_s_memrealtime();
+    uint64_t tl_first = 0;
+#endif
 
     int L = a.cache_lens[b];
     L = L < 0 ? 0 : (L > a.Lmax ? a.Lmax : L);
@@ -475,6 +509,9 @@ __global__ __launch_bounds__(KV != kKvBf16 ? 64 * kMW8 : kMT) void fd_mfma_parti
     for (int j = 0; j < nw; ++j) {
         issue(j + NS - 1);
         wait_vmcnt_le<(NS - 1) * 2 * LG::IPB>();  // block j has landed
+#if FD_WG_TIMELINE
+        if (j == 0) tl_first = __builtin_amdgcn_s_memrealtime();
+#endif
         const char* kb = ring + (j % NS) * LG::STAGEB;
         const char* vb = kb + LG::BLKB;
         if constexpr (C8) {
@@ -493,6 +530,13 @@ __global__ __launch_bounds__(KV != kKvBf16 ? 64 * kMW8 : kMT) void fd_mfma_parti
 
     // Merge: the four lane groups of a column, then the four waves via LDS.
     wait_vmcnt_le<0>();
+#if FD_WG_TIMELINE
+    {
+        const uint64_t t = __builtin_amdgcn_s_memrealtime();
+        uint64_t* row = timeline_row();
+        if (row && lane == 0 && w < 8) row[kTlLoop + w] = t;
+    }
+#endif
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
         l[nb] += __shfl_xor(l[nb], 16);
@@ -570,6 +614,18 @@ __global__ __launch_bounds__(KV != kKvBf16 ? 64 * kMW8 : kMT) void fd_mfma_parti
             *reinterpret_cast<f32x4_t*>(a.o_part + (row * slots + s) * D + 4 * c4) = o;
         }
     }
+#if FD_WG_TIMELINE
+    if (tid == 0) {
+        const uint64_t t = __builtin_amdgcn_s_memrealtime();
+        uint64_t* row = timeline_row();
+        if (row) {
+            row[kTlStart] = tl_start;
+            row[kTlFirst] = tl_first;
+            row[kTlEnd] = t;
+            row[kTlXcc] = __builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20);  // HW_REG_XCC_ID bits 3:0
+        }
+    }
+#endif
 }
 
 
