@@ -130,7 +130,7 @@ struct LGeo {
     static constexpr int BLKB = kKB * ROWB;         // bytes per block per tensor
     static constexpr int STAGEB = 2 * BLKB;         // K then V
     static constexpr int NS = C8 ? FD_CODE8_STAGES : kNS;
-    static constexpr int CONVB = C8 ? 2 * Geo<D>::BLKB : 0;  // bf16 K and V block
+    static constexpr int CONVB = C8 ? Geo<D>::BLKB : 0;  // bf16 V block (K is converted in registers)
     static constexpr int WAVEB = NS * STAGEB + CONVB;
     static_assert(IPB >= 1, "whole load instructions per block");
 };
@@ -207,76 +207,111 @@ __device__ __forceinline__ void load_block_at(const PagedKV& pk, int page, const
     }
 }
 
-// Dequantise one landed block of one-byte codes (K at src, V at src +
-// LGeo::BLKB, rows of D codes in format KV) into bf16 blocks of the operand
-// layout (K at dst, V at dst + Geo::BLKB, swizzled as swz), exactly (see
-// codes_to_bf16), as a read half and a convert-and-write half.  Lane l
-// converts the chunks that dq_row_chunk assigns.
-//
-// The LDS accesses go through lds_read_b128 / lds_write_b128: the block at
-// src has landed (the caller waited for it), and dst is this wave's own
-// area, read only by its own later reads.
+// Caches of one-byte codes.  A landed block holds 16 rows of K codes, then
+// 16 of V codes (D bytes a row).  Row r's 16-byte chunks are stored XOR-
+// swizzled by cswz8(r): physical chunk p holds chunk p ^ cswz8(r).  The K
+// operands are read straight from these rows and converted in registers
+// (lane (grp, col) takes the D / 4 codes of row col for dims grp * D / 4 ..,
+// read as D / 64 16-byte chunks): each 16-byte read covers 16 consecutive
+// rows at one chunk.  For 128-byte code rows that is the pattern of the K
+// operands of bf16 caches at D = 64, and swf<8> (measured free of bank
+// conflicts for it) serves; 64-byte rows take the row group r / 4 (four rows
+// per 256 bytes of banks).  V goes
+// through LDS: each wave converts its block's V codes into a bf16 block of
+// the operand layout (swz) for the transposed reads, exactly (see
+// codes_to_bf16).  The query rows of such a call are loaded in the same
+// order of dims as the K operands (qf_dims), so each score is the same dot
+// product.
+template <int D>
+__device__ __forceinline__ int cswz8(int r) {
+    constexpr int CH8 = LGeo<D, true>::CH;  // 16-byte chunks per code row
+    if constexpr (CH8 == 8) return swf<8>(r);
+    return (r >> 2) & (CH8 - 1);
+}
+
+// First dim of query fragment ks of lane group grp: the order of the K
+// operands (bf16 caches: 8 grp + 32 ks; codes: grp D / 4 + 8 ks).
+template <int D, bool C8>
+__device__ __forceinline__ int qf_dim(int grp, int ks) {
+    return C8 ? grp * (D / 4) + 8 * ks : 8 * grp + 32 * ks;
+}
 
 template <int D>
 struct DQ {
-    static constexpr int NQ = LGeo<D, true>::BLKB / 16 / 64;  // 16-byte chunks per lane per tensor
+    static constexpr int NQ = LGeo<D, true>::BLKB / 16 / 64;  // 16-byte V chunks per lane
+    static constexpr int KC = D / 64;                          // 16-byte K chunks per lane
 };
 
-// The code chunk (row r, chunk c of 16 codes) that lane `lane` converts in
-// its n-th round: consecutive lanes take consecutive 16-byte chunks of the
-// block, so the reads cover the LDS banks in order.
+// The code chunk (row r, physical chunk p) that lane `lane` reads in its
+// n-th round of the V conversion: consecutive lanes take consecutive 16-byte
+// chunks of the block, so the reads cover the LDS banks in order.
 template <int D>
-__device__ __forceinline__ void dq_row_chunk(int n, int lane, int& r, int& c) {
-    constexpr int CH8 = LGeo<D, true>::CH;  // 16-byte chunks per code row
+__device__ __forceinline__ void dq_row_chunk(int n, int lane, int& r, int& p) {
+    constexpr int CH8 = LGeo<D, true>::CH;
     const int q = n * 64 + lane;
     r = q / CH8;
-    c = q % CH8;
+    p = q % CH8;
 }
 
-// First half: start the LDS reads of the block's codes into x (valid after
-// dequant_write's wait).
+// Start the LDS reads of one landed code block (at src): the lane's V
+// chunks (xv) and its K operand chunks (xk); valid after codes_settle.
 template <int D>
-__device__ __forceinline__ void dequant_read(const char* src, int lane, u32x4_t (&x)[2][DQ<D>::NQ]) {
+__device__ __forceinline__ void codes_read(const char* src, int lane, int grp, int col,
+                                           u32x4_t (&xv)[DQ<D>::NQ], u32x4_t (&xk)[DQ<D>::KC]) {
     using L = LGeo<D, true>;
 #pragma unroll
     for (int n = 0; n < DQ<D>::NQ; ++n) {
-        int r, c;
-        dq_row_chunk<D>(n, lane, r, c);
+        int r, p;
+        dq_row_chunk<D>(n, lane, r, p);
+        xv[n] = lds_read_b128(src + L::BLKB + r * L::ROWB + p * 16);
+    }
 #pragma unroll
-        for (int t = 0; t < 2; ++t) x[t][n] = lds_read_b128(src + t * L::BLKB + r * L::ROWB + c * 16);
+    for (int k = 0; k < DQ<D>::KC; ++k) {
+        const int c = grp * DQ<D>::KC + k;  // chunk of dims 16 c .. 16 c + 15
+        xk[k] = lds_read_b128(src + col * L::ROWB + ((c ^ cswz8<D>(col)) << 4));
     }
 }
 
-// Second half: wait for the reads, convert, and write the bf16 blocks.
+// Wait for codes_read, write the bf16 V block at dst and turn the K chunks
+// into the score product's A operands.
 template <int D, int KV>
-__device__ __forceinline__ void dequant_write(u32x4_t (&x)[2][DQ<D>::NQ], char* dst, int lane) {
+__device__ __forceinline__ void codes_settle(u32x4_t (&xv)[DQ<D>::NQ], u32x4_t (&xk)[DQ<D>::KC], char* dst,
+                                             int lane, bf16x8_t (&kf)[Geo<D>::KS]) {
     using L = LGeo<D, true>;
-    using G = Geo<D>;
     constexpr int NQ = DQ<D>::NQ;
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int n = 0; n < NQ; ++n) asm volatile("" : "+v"(xv[n]));
 #pragma unroll
-        for (int n = 0; n < NQ; ++n) asm volatile("" : "+v"(x[t][n]));
+    for (int k = 0; k < DQ<D>::KC; ++k) asm volatile("" : "+v"(xk[k]));
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+    for (int n = 0; n < NQ; ++n) {
+        int r, p;
+        dq_row_chunk<D>(n, lane, r, p);
+        const int c = p ^ cswz8<D>(r);  // 16 codes of row r = dims 16c .. 16c + 15
+        uint32_t b[8];
 #pragma unroll
-        for (int n = 0; n < NQ; ++n) {
-            int r, c;  // 16 codes of row r = dims 16c .. 16c + 15
-            dq_row_chunk<D>(n, lane, r, c);
-            uint32_t b[8];
+        for (int i = 0; i < 4; ++i) codes_to_bf16<KV>(xv[n][i], b[2 * i], b[2 * i + 1]);
+        // A 16-byte write serves 8 lanes per LDS cycle over 128 bytes of
+        // banks.  Lanes whose chunk pair lies in the upper half of the code
+        // row (and, for 64-byte code rows, lanes of odd rows) write their odd
+        // chunk first, so each write instruction's 8-lane groups cover 8
+        // distinct chunks modulo 8 (the swizzle only reorders the chunks of a
+        // row among its lanes).
+        const bool odd_first = (c >= L::CH / 2) != (L::CH == 4 && (r & 1));
+        const u32x4_t lo4 = u32x4_t{b[0], b[1], b[2], b[3]}, hi4 = u32x4_t{b[4], b[5], b[6], b[7]};
+        lds_write_b128(dst + swz<D>(r, 2 * c + (odd_first ? 1 : 0)), odd_first ? hi4 : lo4);
+        lds_write_b128(dst + swz<D>(r, 2 * c + (odd_first ? 0 : 1)), odd_first ? lo4 : hi4);
+    }
+    // K: 16 codes per chunk, 8 per operand (ks = 2 k + half).
 #pragma unroll
-            for (int i = 0; i < 4; ++i) codes_to_bf16<KV>(x[t][n][i], b[2 * i], b[2 * i + 1]);
-            char* o = dst + t * G::BLKB;
-            // A 16-byte write serves 8 lanes per LDS cycle over 128 bytes of
-            // banks.  Lanes whose chunk pair lies in the upper half of the
-            // code row (and, for 64-byte code rows, lanes of odd rows) write
-            // their odd chunk first, so each write instruction's 8-lane
-            // groups cover 8 distinct chunks modulo 8.
-            const bool odd_first = (c >= L::CH / 2) != (L::CH == 4 && (r & 1));
-            const u32x4_t lo4 = u32x4_t{b[0], b[1], b[2], b[3]}, hi4 = u32x4_t{b[4], b[5], b[6], b[7]};
-            lds_write_b128(o + swz<D>(r, 2 * c + (odd_first ? 1 : 0)), odd_first ? hi4 : lo4);
-            lds_write_b128(o + swz<D>(r, 2 * c + (odd_first ? 0 : 1)), odd_first ? lo4 : hi4);
+    for (int k = 0; k < DQ<D>::KC; ++k) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            uint32_t b[4];
+            codes_to_bf16<KV>(xk[k][2 * h], b[0], b[1]);
+            codes_to_bf16<KV>(xk[k][2 * h + 1], b[2], b[3]);
+            kf[2 * k + h] = __builtin_bit_cast(bf16x8_t, u32x4_t{b[0], b[1], b[2], b[3]});
         }
     }
 }
@@ -339,6 +374,17 @@ __device__ __forceinline__ void block_math(const bf16x8_t (&kf)[Geo<D>::KS], con
                 __builtin_bit_cast(s16x4_t, vf[db]), __builtin_bit_cast(s16x4_t, pl), acc[nb][db], 0, 0, 0);
         }
     }
+}
+
+// V^T operands of one 16-key block stored (swizzled) at vb in LDS, through
+// transposed reads; valid after lds_settle.
+template <int D>
+__device__ __forceinline__ void v_fragments(const char* vb, bf16x4_t (&vf)[Geo<D>::DB], int grp, int col) {
+    using G = Geo<D>;
+    const int r = 4 * grp + (col >> 2);
+    const int q4 = col & 3;
+#pragma unroll
+    for (int db = 0; db < G::DB; ++db) vf[db] = tr_read(vb + swz<D>(r, 2 * db + (q4 >> 1)) + 8 * (q4 & 1));
 }
 
 // Operand fragments of one 16-key block stored (swizzled) at kb / vb in LDS:
@@ -439,7 +485,7 @@ __global__ __launch_bounds__(KV != kKvBf16 ? 64 * kMW8 : kMT) void fd_mfma_parti
         for (int ks = 0; ks < G::KS; ++ks) {
             if (r < nrows) {
                 const uint4 x = *reinterpret_cast<const uint4*>(
-                    static_cast<const uint16_t*>(a.q) + (row0 + r) * D + 8 * grp + 32 * ks);
+                    static_cast<const uint16_t*>(a.q) + (row0 + r) * D + qf_dim<D, C8>(grp, ks));
                 qf[nb][ks] = __builtin_bit_cast(bf16x8_t, x);
             } else {
                 qf[nb][ks] = __builtin_bit_cast(bf16x8_t, make_uint4(0, 0, 0, 0));
@@ -486,7 +532,7 @@ __global__ __launch_bounds__(KV != kKvBf16 ? 64 * kMW8 : kMT) void fd_mfma_parti
 #pragma unroll
     for (int i = 0; i < LG::IPB; ++i) {
         const int r = i * LG::RPI + lane / LG::CH;
-        const int cg = C8 ? lane % LG::CH : (lane % LG::CH) ^ swf<LG::CH>(r);
+        const int cg = C8 ? (lane % LG::CH) ^ cswz8<D>(r) : (lane % LG::CH) ^ swf<LG::CH>(r);
         dma_off[i] = (uint32_t)(r * rsb + cg * 16);
     }
 
@@ -513,17 +559,17 @@ __global__ __launch_bounds__(KV != kKvBf16 ? 64 * kMW8 : kMT) void fd_mfma_parti
         if (j == 0) tl_first = __builtin_amdgcn_s_memrealtime();
 #endif
         const char* kb = ring + (j % NS) * LG::STAGEB;
-        const char* vb = kb + LG::BLKB;
-        if constexpr (C8) {
-            u32x4_t x[2][DQ<D>::NQ];
-            dequant_read<D>(kb, lane, x);
-            dequant_write<D, KV>(x, conv, lane);
-            kb = conv;
-            vb = conv + G::BLKB;
-        }
         bf16x8_t kf[G::KS];
         bf16x4_t vf[G::DB];
-        load_fragments<D>(kb, vb, kf, vf, grp, col);
+        if constexpr (C8) {
+            u32x4_t xv[DQ<D>::NQ], xk[DQ<D>::KC];
+            codes_read<D>(kb, lane, grp, col, xv, xk);
+            codes_settle<D, KV>(xv, xk, conv, lane, kf);
+            v_fragments<D>(conv, vf, grp, col);
+            lds_settle(vf);
+        } else {
+            load_fragments<D>(kb, kb + LG::BLKB, kf, vf, grp, col);
+        }
         const int key0 = lo + (w + j * MW) * kKB;  // first key of the block
         block_math<D, NB>(kf, vf, qf, acc, m, l, mx, key0, key0 + kKB > mask_from, rend, c, grp);
     }
