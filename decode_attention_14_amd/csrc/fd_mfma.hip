@@ -43,7 +43,10 @@
 //                The exact tile max is tracked separately for m_part.
 //
 // The four waves' states are merged through LDS at the end, as in the vector
-// kernel.
+// kernel.  Caches of one-byte codes run eight waves per workgroup over rows
+// of D codes: the K codes are converted into the A operands of the score
+// product in registers, the V codes into a bf16 block for the transposed
+// reads (see codes_read / codes_settle).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -116,8 +119,9 @@ struct Geo {
 
 // Stored-row geometry of the decode kernel's LDS ring: bf16 caches keep
 // 2D-byte rows (the operand layout itself); caches of one-byte codes (C8:
-// FP8 E4M3 or INT8) keep D-byte rows, dequantised per block into a bf16
-// block of the operand layout.
+// FP8 E4M3 or INT8) keep D-byte rows, whose K codes are converted into the
+// score operands in registers and whose V codes are converted per block
+// into a bf16 block of the operand layout (CONVB).
 #ifndef FD_CODE8_STAGES
 #define FD_CODE8_STAGES 2
 #endif
@@ -216,12 +220,11 @@ __device__ __forceinline__ void load_block_at(const PagedKV& pk, int page, const
 // rows at one chunk.  For 128-byte code rows that is the pattern of the K
 // operands of bf16 caches at D = 64, and swf<8> (measured free of bank
 // conflicts for it) serves; 64-byte rows take the row group r / 4 (four rows
-// per 256 bytes of banks).  V goes
-// through LDS: each wave converts its block's V codes into a bf16 block of
-// the operand layout (swz) for the transposed reads, exactly (see
-// codes_to_bf16).  The query rows of such a call are loaded in the same
-// order of dims as the K operands (qf_dims), so each score is the same dot
-// product.
+// per 256 bytes of banks).  V goes through LDS: each wave converts its
+// block's V codes into a bf16 block of the operand layout (swz) for the
+// transposed reads.  Both conversions are exact (see codes_to_bf16).  The
+// query rows of such a call are loaded in the same order of dims as the K
+// operands (qf_dim), so each score is the same dot product.
 template <int D>
 __device__ __forceinline__ int cswz8(int r) {
     constexpr int CH8 = LGeo<D, true>::CH;  // 16-byte chunks per code row
@@ -396,10 +399,7 @@ __device__ __forceinline__ void load_fragments(const char* kb, const char* vb, b
 #pragma unroll
     for (int ks = 0; ks < G::KS; ++ks)
         kf[ks] = *reinterpret_cast<const bf16x8_t*>(kb + swz<D>(col, grp + 4 * ks));
-    const int r = 4 * grp + (col >> 2);
-    const int q4 = col & 3;
-#pragma unroll
-    for (int db = 0; db < G::DB; ++db) vf[db] = tr_read(vb + swz<D>(r, 2 * db + (q4 >> 1)) + 8 * (q4 & 1));
+    v_fragments<D>(vb, vf, grp, col);
     lds_settle(vf);
 }
 
@@ -506,7 +506,7 @@ __global__ __launch_bounds__(KV != kKvBf16 ? 64 * kMW8 : kMT) void fd_mfma_parti
     }
 
     char* ring = smem + w * LG::WAVEB;
-    char* conv = ring + NS * LG::STAGEB;  // codes: this wave's dequantised block
+    char* conv = ring + NS * LG::STAGEB;  // codes: this wave's bf16 V block
     const char* kt;
     const char* vt;
     int rsb;  // bytes from one stored key row of the head to the next
