@@ -219,17 +219,19 @@ __device__ __forceinline__ void load_block_at(const PagedKV& pk, int page, const
 // read as D / 64 16-byte chunks): each 16-byte read covers 16 consecutive
 // rows at one chunk.  For 128-byte code rows that is the pattern of the K
 // operands of bf16 caches at D = 64, and swf<8> (measured free of bank
-// conflicts for it) serves; 64-byte rows take the row group r / 4 (four rows
-// per 256 bytes of banks).  V goes through LDS: each wave converts its
-// block's V codes into a bf16 block of the operand layout (swz) for the
-// transposed reads.  Both conversions are exact (see codes_to_bf16).  The
-// query rows of such a call are loaded in the same order of dims as the K
-// operands (qf_dim), so each score is the same dot product.
+// conflicts for it) serves; 64-byte rows take the row pair r / 2, which of
+// five maps measured left the fewest conflicts (a third fewer than r / 4;
+// what remains at that row size comes from other accesses).  V goes through
+// LDS: each wave converts its block's V codes into a bf16 block of the
+// operand layout (swz) for the transposed reads.  Both conversions are exact
+// (see codes_to_bf16).  The query rows of such a call are loaded in the same
+// order of dims as the K operands (qf_dim), so each score is the same dot
+// product.
 template <int D>
 __device__ __forceinline__ int cswz8(int r) {
     constexpr int CH8 = LGeo<D, true>::CH;  // 16-byte chunks per code row
     if constexpr (CH8 == 8) return swf<8>(r);
-    return (r >> 2) & (CH8 - 1);
+    return (r >> 1) & (CH8 - 1);
 }
 
 // First dim of query fragment ks of lane group grp: the order of the K
