@@ -6,12 +6,15 @@ kernel and the merge kernel (``fd_decode_attention``), on inputs already
 resident in HBM.  The default workload is the 32k-context GQA decode layer
 (batch 1, 32 query heads, 8 KV heads, head_dim 128, bf16, planner splits).
 
-Timing: W untimed eager warm-up steps; then the K steps are captured once in a
-HIP graph (so host launch overhead is not measured), the graph is replayed
-once untimed, and one timed replay of exactly K steps is bracketed by
-synchronisations and events on the stream the kernels run on.  The K/V caches
-rotate over several identical copies (>= 1 GiB in total) so that the 256 MB
-last-level cache cannot hold them and every step reads HBM.
+Timing: W untimed eager warm-up steps; then a HIP graph of G consecutive steps
+is captured (so host launch overhead is not measured) and replayed once
+untimed; the timed region is exactly K steps, K / G replays of that graph,
+bracketed by synchronisations and events on the stream the kernels run on,
+with an event between replays as well.  Each replay gives one sample of the
+time per step (its time / G); the reported time per step is the median of
+those samples (the mean over the whole region is printed beside it).  The K/V
+caches rotate over several identical copies (>= 1 GiB in total) so that the
+256 MB last-level cache cannot hold them and every step reads HBM.
 
 ``--kv-fp8`` / ``--kv-int8`` quantise K and V to FP8 E4M3 or INT8 codes with
 per-tensor scales (bf16 queries and output).  ``--page-size P`` runs the same workload on a paged cache (pages of P keys in
@@ -21,8 +24,11 @@ picks [pages, P, Hkv, D] or [pages, Hkv, P, D]).
 Printed: one JSON line with the metric (algorithmic GB/s per step: the bytes
 any implementation must move -- K, V, q, out, lse -- over the step time), the
 roofline of the dominant kernel (the partial pass, timed per launch over a
-graph of back-to-back launches), and the fp64 CPU oracle's rate on a bounded
-sample of the same workload as a reference point.
+graph of back-to-back launches), the rate of a plain streaming read of the
+same number of bytes (the library's read kernel, best of a few grid sizes:
+the bandwidth this device reaches with no arithmetic at all), and the fp64
+CPU oracle's rate on a bounded sample of the same workload as a reference
+point.
 """
 from __future__ import annotations
 
@@ -66,7 +72,9 @@ def kernel_source_hash(kernel: str) -> str:
 def parse_args():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--graph-steps", type=int, default=10,
+                    help="steps per captured graph; each replay is one timing sample")
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="gqa_32k")
     ap.add_argument("--num-splits", type=int, default=0, help="force a split count (0: planner)")
@@ -83,6 +91,7 @@ def parse_args():
                     help="FP8 E4M3 K/V caches (per-tensor scales) with bf16 queries")
     ap.add_argument("--calibrate-copy", type=int, default=0,
                     help="also run N plain 512 MiB device copies (counter calibration)")
+    ap.add_argument("--no-ceiling", action="store_true", help="skip the streaming-read ceiling")
     return ap.parse_args()
 
 
@@ -114,11 +123,31 @@ def algorithmic_flops(w, lens):
     return 4 * w.head_dim * w.num_q_heads * pairs
 
 
+def host_description():
+    """CPU count and model of the host the oracle runs on."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = os.cpu_count() or 1
+    return {"host_cpus": os.cpu_count(), "usable_cpus": usable, "cpu_model": model}
+
+
 def cpu_baseline(w, q, k, v, cl, alg_bytes, seconds):
     import oracle
     from decode_attention_14_amd.inputs import as_oracle_array
 
-    threads = max(1, min(16, os.cpu_count() or 1))
+    host = host_description()
+    # at most 16 threads: the share of host cores a one-GPU job gets
+    threads = max(1, min(16, host["usable_cpus"]))
     qa, ka, va, la = as_oracle_array(q), as_oracle_array(k), as_oracle_array(v), cl.numpy()
     oracle.load()
     reps, t0 = 0, time.perf_counter()
@@ -133,7 +162,8 @@ def cpu_baseline(w, q, k, v, cl, alg_bytes, seconds):
         "unit": "GB/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": f"{reps} full step(s) of {w.name} in fp64 ({el:.1f} s)",
+        "sample": f"{reps} full step(s) of {w.name} in fp64 ({el:.1f} s) on {threads} threads",
+        **host,
     }
 
 
@@ -249,15 +279,17 @@ def main():
 
     stream = torch.cuda.current_stream(dev)
 
+    def graph_of(fn, n):
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(n):
+                fn(i)
+        return graph
+
     def timed(fn, n):
         """Average ms per call of fn(0..n-1): one untimed pass, then one timed
         pass, as a graph replay unless --no-graph."""
-        graph = None
-        if not args.no_graph:
-            graph = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(graph):
-                for i in range(n):
-                    fn(i)
+        graph = None if args.no_graph else graph_of(fn, n)
         run = graph.replay if graph is not None else (lambda: [fn(i) for i in range(n)])
         run()
         torch.cuda.synchronize()
@@ -268,16 +300,23 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / n
 
-    print(f"[bench] plan {plan.plan} copies={copies} warmup={args.warmup} steps={args.steps} "
-          f"graph={not args.no_graph}", file=sys.stderr, flush=True)
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ms_per_step = timed(step, args.steps)
-    wall = time.perf_counter() - t0
-    print(f"[bench] timed {args.steps} steps: {ms_per_step * 1e3:.2f} us/step (wall incl. capture "
-          f"{wall:.3f} s)", file=sys.stderr, flush=True)
+    def timed_samples(fn, total, per):
+        """Exactly `total` calls of fn, as total / per replays of a graph of
+        `per` calls (eager calls with --no-graph), an event after each
+        replay.  Returns (per-call ms of each replay, mean ms over all)."""
+        reps = max(1, total // per)
+        graph = None if args.no_graph else graph_of(fn, per)
+        run = graph.replay if graph is not None else (lambda: [fn(i) for i in range(per)])
+        run()
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        ev[0].record(stream)
+        for r in range(reps):
+            run()
+            ev[r + 1].record(stream)
+        torch.cuda.synchronize()
+        samples = [ev[r].elapsed_time(ev[r + 1]) / per for r in range(reps)]
+        return samples, ev[0].elapsed_time(ev[reps]) / (reps * per)
 
     # The partial pass alone and the merge alone, back to back in a graph; the
     # average per launch includes the short gap between consecutive kernels.
@@ -298,6 +337,30 @@ def main():
         except (OSError, ValueError):
             traffic = None
 
+    # The streaming-read ceiling: the library's plain read kernel over the
+    # same number of bytes as the partial pass's K/V, in windows rotating
+    # over >= 1 GiB so the last-level cache cannot serve them; best of a few
+    # grid sizes.
+    ceiling = None
+    if not args.no_ceiling:
+        win = (kv_b + 15) // 16 * 16
+        nwin = max(2, math.ceil((1 << 30) / win))
+        cbuf = torch.empty(nwin * win, dtype=torch.uint8, device=dev)
+        cbuf.fill_(1)
+        sink = torch.zeros(1, dtype=torch.int32, device=dev)
+        best = None
+        for wg in (1024, 2048, 4096, 8192):
+            ms = timed(lambda i, wg=wg: fd.stream_read(cbuf, win, wg, sink, offset=(i % nwin) * win), n_k)
+            gbs = win / (ms * 1e-3) / 1e9
+            print(f"[bench] stream read {win} B, {wg} workgroups: {ms * 1e3:.2f} us, {gbs:.0f} GB/s", file=sys.stderr,
+                  flush=True)
+            if best is None or gbs > best[0]:
+                best = (gbs, wg, ms)
+        del cbuf
+        ceiling = {"kernel": "fd_stream_read_kernel", "bytes_per_launch": win, "achieved": round(best[0], 2),
+                   "unit": "GB/s", "us_per_launch": round(best[2] * 1e3, 3), "workgroups": best[1],
+                   "frac_of_peak": round(best[0] / HBM_PEAK_GBS, 4)}
+
     for i in range(args.calibrate_copy):
         a = torch.empty(1 << 29, dtype=torch.uint8, device=dev)
         b = torch.empty_like(a)
@@ -313,6 +376,9 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 6),
         "us_per_step": round(ms_per_step * 1e3, 3),
+        "timing": {"statistic": "median", "samples": len(samples), "steps_per_sample": per,
+                   "us_per_step_mean": round(ms_mean * 1e3, 3), "us_per_step_min": round(srt[0] * 1e3, 3),
+                   "us_per_step_max": round(srt[-1] * 1e3, 3)},
         "pct_of_hbm_peak": round(100 * step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
         "higher_is_better": True,
         "scaling": "weak",
@@ -350,6 +416,10 @@ def main():
             "kernel": partial_kernel_name(w), "flops_per_launch": flops,
             "hbm_achieved_GBs": round(achieved, 2),
         }
+    if ceiling is not None:
+        result["ceiling"] = ceiling
+        if result["roofline"]["bound"] == "hbm":
+            result["roofline"]["frac_of_ceiling"] = round(achieved / ceiling["achieved"], 4)
     if not args.no_cpu_baseline and (coded or paged):
         print("[bench] cpu baseline is timed on the contiguous bf16/fp32 workload only", file=sys.stderr)
     elif not args.no_cpu_baseline:

@@ -26,7 +26,7 @@ FD_PAGES_NHD, FD_PAGES_HND = 0, 1
 EXPORTS = ("fd_plan_splits", "fd_workspace_bytes", "fd_decode_partials", "fd_combine_splits",
            "fd_decode_attention", "fd_decode_attention_paged", "fd_decode_partials_paged",
            "fd_decode_attention_fp8", "fd_decode_partials_fp8", "fd_decode_attention_int8",
-           "fd_decode_partials_int8", "fd_status_string", "fd_last_error", "fd_version")
+           "fd_decode_partials_int8", "fd_stream_read", "fd_status_string", "fd_last_error", "fd_version")
 
 
 class FdDims(ctypes.Structure):
@@ -79,7 +79,7 @@ def load_library(path: str | None = None):
     lib.fd_decode_partials.argtypes = [dims_p, vp, vp, vp, vp, ctypes.c_float, i32, plan_p,
                                        vp, vp, vp, vp]
     lib.fd_decode_partials.restype = i32
-    lib.fd_combine_splits.argtypes = [i32, i32, i32, i32, i32, vp, vp, i32, vp, vp, vp]
+    lib.fd_combine_splits.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, i32, vp, vp, vp]
     lib.fd_combine_splits.restype = i32
     lib.fd_decode_attention.argtypes = [dims_p, vp, vp, vp, vp, ctypes.c_float, i32, plan_p,
                                         vp, u64, vp, vp, vp]
@@ -101,6 +101,8 @@ def load_library(path: str | None = None):
     lib.fd_decode_attention_int8.restype = i32
     lib.fd_decode_partials_int8.argtypes = lib.fd_decode_partials_fp8.argtypes
     lib.fd_decode_partials_int8.restype = i32
+    lib.fd_stream_read.argtypes = [vp, u64, i32, vp, vp]
+    lib.fd_stream_read.restype = i32
     lib.fd_status_string.argtypes = [i32]
     lib.fd_status_string.restype = ctypes.c_char_p
     lib.fd_last_error.argtypes = []
@@ -296,25 +298,47 @@ def decode_partials(q, k_cache, v_cache, cache_lens, scale=None, num_splits: int
     return o_part, m_part, lse_part
 
 
-def combine(o_part, lse_part, out_dtype=torch.float32, out=None, lse=None):
-    """Second pass only: o_part [B,H,T,S,D], lse_part [B,H,T,S] fp32 -> (out, lse)."""
+def combine(o_part, lse_part, out_dtype=torch.float32, out=None, lse=None, splits=None):
+    """Second pass only: o_part [B,H,T,S,D], lse_part [B,H,T,S] fp32 -> (out, lse).
+
+    ``splits``: optional int32 device tensor [B]; the rows of sequence b merge
+    only their first splits[b] slots (None: all S)."""
     lib = load_library()
-    _require_cuda(o_part, lse_part, out, lse)
+    _require_cuda(o_part, lse_part, out, lse, splits)
     if o_part.dim() != 5 or lse_part.shape != o_part.shape[:4]:
         raise FdError(FD_ERR_INVALID, "o_part must be [B,H,T,S,D] and lse_part [B,H,T,S]")
     if o_part.dtype != torch.float32 or lse_part.dtype != torch.float32:
         raise FdError(FD_ERR_INVALID, "partials must be float32")
     B, H, T, S, D = o_part.shape
+    if splits is not None and (splits.dtype != torch.int32 or tuple(splits.shape) != (B,)):
+        raise FdError(FD_ERR_INVALID, "splits must be int32 of shape [B]")
     _check_buffer(out, (B, H, T, D), out.dtype if out is not None else out_dtype, "out")
     _check_buffer(lse, (B, H, T), torch.float32, "lse")
     if out is None:
         out = torch.empty(B, H, T, D, dtype=out_dtype, device=o_part.device)
     if lse is None:
         lse = torch.empty(B, H, T, dtype=torch.float32, device=o_part.device)
-    _check(lib.fd_combine_splits(B, H, T, D, S, _ptr(o_part), _ptr(lse_part),
+    _check(lib.fd_combine_splits(B, H, T, D, S, _ptr(o_part), _ptr(lse_part), _ptr(splits),
                                  _dtype_code(out.dtype), _ptr(out), _ptr(lse),
                                  _stream(o_part.device)))
     return out, lse
+
+
+def stream_read(buf: torch.Tensor, nbytes: int | None = None, workgroups: int = 0, sink=None, offset: int = 0):
+    """Measurement aid: one streaming read of ``nbytes`` bytes of ``buf``
+    from byte ``offset`` on (all of it by default) by the library's read
+    kernel, enqueued on the current stream.  Returns the 4-byte sink tensor."""
+    lib = load_library()
+    _require_cuda(buf, sink)
+    total = buf.numel() * buf.element_size()
+    n = total - offset if nbytes is None else int(nbytes)
+    if offset < 0 or n < 0 or offset + n > total:
+        raise FdError(FD_ERR_INVALID, "read range outside the buffer")
+    if sink is None:
+        sink = torch.zeros(1, dtype=torch.int32, device=buf.device)
+    _check(lib.fd_stream_read(ctypes.c_void_p(buf.data_ptr() + offset), n, int(workgroups), _ptr(sink),
+                              _stream(buf.device)))
+    return sink
 
 
 _LAYOUTS = {"nhd": FD_PAGES_NHD, "hnd": FD_PAGES_HND}

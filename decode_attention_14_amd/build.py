@@ -22,15 +22,7 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
-    """Compile every source into ``libfd.so`` (or ``out``); return its path.
-
-    ``defines``: extra ``NAME=VALUE`` macros (the kernel's tuning constants).
-    """
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = out + ".tmp"
-    cmd = [HIPCC, *FLAGS, *[f"-D{d}" for d in defines], "-I", os.path.join(ROOT, "include"),
-           "-I", CSRC, *srcs, "-o", tmp]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -41,6 +33,30 @@ def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
         raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
     if verbose and msgs:
         print("\n".join(msgs))
+
+
+def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
+    """Compile every source into ``libfd.so`` (or ``out``); return its path.
+
+    Each source is compiled to an object of its own (in parallel, under
+    ``_build/``), then the objects are linked.  ``defines``: extra
+    ``NAME=VALUE`` macros (the kernel's tuning constants).
+    """
+    from concurrent.futures import ThreadPoolExecutor
+
+    tag = os.path.splitext(os.path.basename(out))[0]
+    objdir = os.path.join(PKG, "_build", tag)
+    os.makedirs(objdir, exist_ok=True)
+    common = [HIPCC, *FLAGS, *[f"-D{d}" for d in defines], "-I", os.path.join(ROOT, "include"), "-I", CSRC]
+    objs = [os.path.join(objdir, os.path.splitext(s)[0] + ".o") for s in SOURCES]
+    cmds = [[*common, "-c", "-x", "hip", os.path.join(CSRC, s), "-o", o]
+            for s, o in zip(SOURCES, objs)]
+    for c in cmds:
+        c.remove("-shared")
+    with ThreadPoolExecutor(max_workers=min(len(cmds), os.cpu_count() or 1)) as ex:
+        list(ex.map(lambda c: _run(c, verbose), cmds))
+    tmp = out + ".tmp"
+    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
     os.replace(tmp, out)
     return out
 

@@ -123,6 +123,40 @@ fd_status resolve_rule(int32_t num_splits, const fd_plan* plan, fdk::SplitRule* 
     return FD_OK;
 }
 
+// Bytes of one stored key row of one KV head: bf16 or fp32 elements, or
+// one-byte codes.
+int64_t row_bytes(const fd_dims* d, bool codes) {
+    return (int64_t)d->head_dim * (codes ? 1 : (d->dtype == FD_BF16 ? 2 : 4));
+}
+
+// The most keys one tile of `rule` can hold for a sequence of at most Lmax
+// keys (the tile rule of fdk::tile_of: the last tile takes the rest when the
+// count reaches the slots).
+int64_t max_tile_keys(const fdk::SplitRule& r, int64_t Lmax) {
+    if (Lmax <= 0) return 0;
+    if (r.tile_len > 0) {
+        const int64_t T = r.tile_len;
+        const int64_t S = std::min<int64_t>(ceil_div(Lmax, T), r.slots);
+        return std::max(std::min(T, Lmax), Lmax - (S - 1) * T);
+    }
+    const int64_t T = align_up(ceil_div(Lmax, r.num_splits), r.granule);
+    return std::min(T, Lmax);
+}
+
+// The kernels address a tile's rows with 32-bit byte offsets and buffer
+// ranges; reject a rule under which one tile of one KV head reaches 2^31
+// bytes.
+fd_status check_tile_bytes(const fd_dims* d, const fdk::SplitRule& r, bool codes) {
+    const int64_t keys = max_tile_keys(r, d->max_cache_len);
+    const int64_t bytes = keys * row_bytes(d, codes);
+    if (bytes >= ((int64_t)1 << 31))
+        return fail(FD_ERR_UNSUPPORTED,
+                    "a tile of up to %lld keys spans %lld bytes of one KV head; tiles must stay below 2^31 bytes "
+                    "(use more splits)",
+                    (long long)keys, (long long)bytes);
+    return FD_OK;
+}
+
 fd_status check_tensors(const fd_dims* d, const void* q, const void* k, const void* v,
                         const int32_t* lens) {
     if (!q || !k || !v || !lens) return fail(FD_ERR_INVALID, "q, k_cache, v_cache and cache_lens must be non-NULL");
@@ -200,7 +234,7 @@ const char* fd_status_string(int32_t status) {
 
 const char* fd_last_error(void) { return g_last_error; }
 
-int32_t fd_version(void) { return 300; }
+int32_t fd_version(void) { return 400; }
 
 uint64_t fd_workspace_bytes(const fd_dims* dims, int32_t max_splits) {
     if (max_splits <= 1 || max_splits > FD_MAX_SPLITS) return 0;
@@ -326,6 +360,7 @@ fd_status run_partials(const fd_dims* dims, const void* q, const void* k_cache, 
     if ((st = resolve_rule(num_splits, plan, &rule)) != FD_OK) return st;
     fdk::PagedKV pk{};
     if (pages && (st = resolve_pages(dims, pages, &rule, &pk)) != FD_OK) return st;
+    if ((st = check_tile_bytes(dims, rule, cs != nullptr)) != FD_OK) return st;
     if (dims->batch == 0) return FD_OK;
     if ((st = check_tensors(dims, q, k_cache, v_cache, cache_lens)) != FD_OK) return st;
     if (!o_part || !m_part || !lse_part)
@@ -390,7 +425,8 @@ fd_status fd_decode_partials_int8(const fd_dims* dims, const void* q, const void
 
 fd_status fd_combine_splits(int32_t batch, int32_t num_heads, int32_t q_len, int32_t head_dim,
                             int32_t max_splits, const float* o_part, const float* lse_part,
-                            int32_t out_dtype, void* out, float* lse, void* stream) {
+                            const int32_t* splits_per_seq, int32_t out_dtype, void* out, float* lse,
+                            void* stream) {
     clear_error();
     if (batch < 0 || num_heads < 1 || q_len < 1)
         return fail(FD_ERR_INVALID, "bad sizes (batch=%d, num_heads=%d, q_len=%d)", batch, num_heads, q_len);
@@ -405,11 +441,32 @@ fd_status fd_combine_splits(int32_t batch, int32_t num_heads, int32_t q_len, int
     if (rows == 0) return FD_OK;
     if (!o_part || !lse_part || !out) return fail(FD_ERR_INVALID, "o_part, lse_part and out must be non-NULL");
     if (misaligned(o_part, 16) || misaligned(out, out_dtype == FD_BF16 ? 8 : 16) || misaligned(lse_part, 4) ||
-        (lse && misaligned(lse, 4)))
-        return fail(FD_ERR_INVALID, "misaligned buffer (o_part and out need 16 bytes, bf16 out 8)");
+        (lse && misaligned(lse, 4)) || (splits_per_seq && misaligned(splits_per_seq, 4)))
+        return fail(FD_ERR_INVALID,
+                    "misaligned buffer (o_part and out need 16 bytes, bf16 out 8, lse and splits_per_seq 4)");
     return device_status(fdk::launch_combine(head_dim, out_dtype, rows, max_splits, o_part, lse_part,
-                                             out, lse, static_cast<hipStream_t>(stream)),
+                                             splits_per_seq, (int64_t)num_heads * q_len, out, lse,
+                                             static_cast<hipStream_t>(stream)),
                          "combine kernel launch");
+}
+
+fd_status fd_stream_read(const void* buf, uint64_t bytes, int32_t workgroups, uint32_t* sink, void* stream) {
+    clear_error();
+    if (workgroups < 0) return fail(FD_ERR_INVALID, "workgroups %d < 0", workgroups);
+    if (bytes % 16 != 0) return fail(FD_ERR_INVALID, "bytes %llu is not a multiple of 16", (unsigned long long)bytes);
+    if (bytes == 0) return FD_OK;
+    if (!buf || !sink) return fail(FD_ERR_INVALID, "buf and sink must be non-NULL");
+    if (misaligned(buf, 16) || misaligned(sink, 4))
+        return fail(FD_ERR_INVALID, "buf must be 16-byte aligned and sink 4-byte aligned");
+    if (workgroups == 0) {
+        int dev = 0;
+        hipDeviceProp_t prop;
+        if (hipGetDevice(&dev) != hipSuccess || hipGetDeviceProperties(&prop, dev) != hipSuccess)
+            return fail(FD_ERR_DEVICE, "cannot query the compute-unit count; pass workgroups");
+        workgroups = 8 * prop.multiProcessorCount;
+    }
+    return device_status(fdk::launch_stream_read(buf, bytes, workgroups, sink, static_cast<hipStream_t>(stream)),
+                         "stream read kernel launch");
 }
 
 }  // extern "C"
@@ -471,6 +528,7 @@ fd_status run_attention(const fd_dims* dims, const void* q, const void* k_cache,
     if ((st = resolve_rule(num_splits, plan, &rule)) != FD_OK) return st;
     fdk::PagedKV pk{};
     if (pages && (st = resolve_pages(dims, pages, &rule, &pk)) != FD_OK) return st;
+    if ((st = check_tile_bytes(dims, rule, cs != nullptr)) != FD_OK) return st;
     if (dims->batch == 0) return FD_OK;
     if ((st = check_tensors(dims, q, k_cache, v_cache, cache_lens)) != FD_OK) return st;
     if (!out) return fail(FD_ERR_INVALID, "out is NULL");
@@ -504,7 +562,7 @@ fd_status run_attention(const fd_dims* dims, const void* q, const void* k_cache,
                             "partial kernel launch")) != FD_OK)
         return st;
     return device_status(fdk::launch_combine(dims->head_dim, dims->dtype, total_rows(dims), rule.slots,
-                                             a.o_part, a.lse_part, out, lse, s),
+                                             a.o_part, a.lse_part, nullptr, 0, out, lse, s),
                          "combine kernel launch");
 }
 

@@ -436,15 +436,25 @@ __global__ __launch_bounds__(kPThreads) FD_OCCUPANCY void fd_partial_kernel(Part
 // Merge pass.  WPR waves per query row: up to 32 slots one wave per row (four
 // rows per workgroup); with more, four waves split the row's slots (wave w
 // takes slots w, w + 4, ...) and wave 0 merges their states through LDS.
-// At most four slots go to fd_combine_narrow_kernel below.
+// At most four slots go to fd_combine_narrow_kernel below.  Rows hold
+// `slots` slots each; with a per-sequence count (spl, [rows / rps]) a row
+// merges only the first spl[row / rps] of them.
 
 constexpr int kCThreads = 256;
 constexpr int kCWaves = kCThreads / 64;
 constexpr int kCombineWideSlots = 32;  // above this, four waves per row
 
+// Slots that row `row` merges: all `slots`, or its sequence's count.
+static __device__ __forceinline__ int row_slots(const int32_t* spl, int64_t rps, int64_t row, int slots) {
+    if (!spl) return slots;
+    const int n = spl[row / rps];
+    return n < 0 ? 0 : (n > slots ? slots : n);
+}
+
 template <int D, bool OUT_BF16, int WPR>
 __global__ __launch_bounds__(kCThreads) void fd_combine_kernel(const float* __restrict__ o_part,
                                                                const float* __restrict__ lse_part, int slots,
+                                                               const int32_t* __restrict__ spl, int64_t rps,
                                                                int64_t rows, void* out, float* lse) {
     constexpr int C4 = D / 4;
     constexpr int RPB = kCWaves / WPR;  // rows per workgroup
@@ -452,7 +462,8 @@ __global__ __launch_bounds__(kCThreads) void fd_combine_kernel(const float* __re
     const int lane = threadIdx.x & 63;
     const int64_t row = (int64_t)blockIdx.x * RPB + w / WPR;
     const int64_t r = row < rows ? row : rows - 1;  // spare waves read a valid row, write nothing
-    MergeState st = merge_slots_wave<D>(o_part + r * slots * D, lse_part + r * slots, slots, w % WPR, WPR, lane);
+    const int n = row_slots(spl, rps, r, slots);
+    MergeState st = merge_slots_wave<D>(o_part + r * slots * D, lse_part + r * slots, n, w % WPR, WPR, lane);
     if constexpr (WPR > 1) {
         __shared__ float sm_m[kCWaves], sm_z[kCWaves];
         __shared__ float4 sm_acc[kCWaves][C4];
@@ -488,6 +499,7 @@ constexpr int kCombineRowsPerThread = 4;
 template <int D, bool OUT_BF16, int S>
 __global__ __launch_bounds__(kCThreads) void fd_combine_narrow_kernel(const float* __restrict__ o_part,
                                                                       const float* __restrict__ lse_part,
+                                                                      const int32_t* __restrict__ spl, int64_t rps,
                                                                       int64_t rows, void* out, float* lse) {
     constexpr int C4 = D / 4;                  // float4 columns
     constexpr int RPB = kCThreads / C4;        // rows of the workgroup per round
@@ -500,10 +512,12 @@ __global__ __launch_bounds__(kCThreads) void fd_combine_narrow_kernel(const floa
     for (int i = 0; i < RPT; ++i) {
         const int64_t row = row0 + (int64_t)i * RPB;
         const int64_t r = row < rows ? row : rows - 1;  // spare rows read a valid row, write nothing
+        const int n = row_slots(spl, rps, r, S);
 #pragma unroll
         for (int sl = 0; sl < S; ++sl) {
-            lv[i][sl] = lse_part[r * S + sl];
-            ov[i][sl] = reinterpret_cast<const float4*>(o_part)[(r * S + sl) * C4 + c4];
+            lv[i][sl] = sl < n ? lse_part[r * S + sl] : -INFINITY;
+            ov[i][sl] = sl < n ? reinterpret_cast<const float4*>(o_part)[(r * S + sl) * C4 + c4]
+                               : make_float4(0.f, 0.f, 0.f, 0.f);
         }
     }
 #pragma unroll
@@ -532,34 +546,65 @@ __global__ __launch_bounds__(kCThreads) void fd_combine_narrow_kernel(const floa
 }
 
 template <int D, bool OUT_BF16, int S>
-void launch_combine_narrow(int64_t rows, const float* o_part, const float* lse_part, void* out, float* lse,
-                           hipStream_t stream) {
+void launch_combine_narrow(int64_t rows, const float* o_part, const float* lse_part, const int32_t* spl,
+                           int64_t rps, void* out, float* lse, hipStream_t stream) {
     constexpr int rows_per_block = kCThreads / (D / 4) * kCombineRowsPerThread;
     hipLaunchKernelGGL((fd_combine_narrow_kernel<D, OUT_BF16, S>),
                        dim3((unsigned)((rows + rows_per_block - 1) / rows_per_block)), dim3(kCThreads), 0, stream,
-                       o_part, lse_part, rows, out, lse);
+                       o_part, lse_part, spl, rps, rows, out, lse);
 }
 
 template <int D, bool OUT_BF16>
-void launch_combine_d(int64_t rows, int slots, const float* o_part, const float* lse_part, void* out, float* lse,
-                      hipStream_t stream) {
+void launch_combine_d(int64_t rows, int slots, const float* o_part, const float* lse_part, const int32_t* spl,
+                      int64_t rps, void* out, float* lse, hipStream_t stream) {
     dim3 block(kCThreads);
     if (slots <= kCombineNarrowSlots) {
         switch (slots) {
-            case 1: launch_combine_narrow<D, OUT_BF16, 1>(rows, o_part, lse_part, out, lse, stream); return;
-            case 2: launch_combine_narrow<D, OUT_BF16, 2>(rows, o_part, lse_part, out, lse, stream); return;
-            case 3: launch_combine_narrow<D, OUT_BF16, 3>(rows, o_part, lse_part, out, lse, stream); return;
-            default: launch_combine_narrow<D, OUT_BF16, 4>(rows, o_part, lse_part, out, lse, stream); return;
+            case 1: launch_combine_narrow<D, OUT_BF16, 1>(rows, o_part, lse_part, spl, rps, out, lse, stream); return;
+            case 2: launch_combine_narrow<D, OUT_BF16, 2>(rows, o_part, lse_part, spl, rps, out, lse, stream); return;
+            case 3: launch_combine_narrow<D, OUT_BF16, 3>(rows, o_part, lse_part, spl, rps, out, lse, stream); return;
+            default: launch_combine_narrow<D, OUT_BF16, 4>(rows, o_part, lse_part, spl, rps, out, lse, stream); return;
         }
     }
     if (slots > kCombineWideSlots)
         hipLaunchKernelGGL((fd_combine_kernel<D, OUT_BF16, kCWaves>), dim3((unsigned)rows), block, 0, stream,
-                           o_part, lse_part, slots, rows, out, lse);
+                           o_part, lse_part, slots, spl, rps, rows, out, lse);
     else
         hipLaunchKernelGGL((fd_combine_kernel<D, OUT_BF16, 1>), dim3((unsigned)((rows + kCWaves - 1) / kCWaves)),
-                           block, 0, stream, o_part, lse_part, slots, rows, out, lse);
+                           block, 0, stream, o_part, lse_part, slots, spl, rps, rows, out, lse);
 }
 
+// ---------------------------------------------------------------------------
+// Streaming read (a measurement aid): each thread reads 16-byte pieces
+// kStreamUnroll at a time, all issued before any is used, strided over the
+// grid so that consecutive threads read consecutive pieces, and folds them
+// by XOR.  A wave's fold reaches *sink only if it equals kStreamMagic, which
+// the compiler cannot rule out, so no load can be removed.
+
+constexpr int kStreamThreads = 256;
+constexpr int kStreamUnroll = 8;
+constexpr uint32_t kStreamMagic = 0x6a09e667u;
+
+typedef __attribute__((ext_vector_type(4))) uint32_t stream_u32x4;
+
+__global__ __launch_bounds__(kStreamThreads) void fd_stream_read_kernel(const stream_u32x4* __restrict__ buf,
+                                                                        uint64_t n16, uint32_t* sink) {
+    const uint64_t nthreads = (uint64_t)gridDim.x * kStreamThreads;
+    uint64_t i = (uint64_t)blockIdx.x * kStreamThreads + threadIdx.x;
+    uint32_t acc = 0;
+    for (; i + (kStreamUnroll - 1) * nthreads < n16; i += kStreamUnroll * nthreads) {
+        stream_u32x4 x[kStreamUnroll];
+#pragma unroll
+        for (int u = 0; u < kStreamUnroll; ++u) x[u] = __builtin_nontemporal_load(buf + i + u * nthreads);
+#pragma unroll
+        for (int u = 0; u < kStreamUnroll; ++u) acc ^= x[u].x ^ x[u].y ^ x[u].z ^ x[u].w;
+    }
+    for (; i < n16; i += nthreads) {
+        const stream_u32x4 x = __builtin_nontemporal_load(buf + i);
+        acc ^= x.x ^ x.y ^ x.z ^ x.w;
+    }
+    if (acc == kStreamMagic) *sink = acc;
+}
 
 template <bool BF16, int D, bool CAUSAL, bool PAGED>
 void launch_partials_c(int batch, const PartialArgs& a, hipStream_t stream) {
@@ -607,16 +652,25 @@ hipError_t launch_partials(int dtype, int head_dim, int batch, const PartialArgs
 }
 
 hipError_t launch_combine(int head_dim, int out_dtype, int64_t rows, int slots,
-                          const float* o_part, const float* lse_part, void* out, float* lse,
-                          hipStream_t stream) {
+                          const float* o_part, const float* lse_part, const int32_t* splits_per_seq,
+                          int64_t rows_per_seq, void* out, float* lse, hipStream_t stream) {
     const bool bf16 = out_dtype == 1;
+    const int32_t* spl = splits_per_seq;
+    const int64_t rps = rows_per_seq > 0 ? rows_per_seq : 1;
     if (head_dim == 64) {
-        if (bf16) launch_combine_d<64, true>(rows, slots, o_part, lse_part, out, lse, stream);
-        else launch_combine_d<64, false>(rows, slots, o_part, lse_part, out, lse, stream);
+        if (bf16) launch_combine_d<64, true>(rows, slots, o_part, lse_part, spl, rps, out, lse, stream);
+        else launch_combine_d<64, false>(rows, slots, o_part, lse_part, spl, rps, out, lse, stream);
     } else {
-        if (bf16) launch_combine_d<128, true>(rows, slots, o_part, lse_part, out, lse, stream);
-        else launch_combine_d<128, false>(rows, slots, o_part, lse_part, out, lse, stream);
+        if (bf16) launch_combine_d<128, true>(rows, slots, o_part, lse_part, spl, rps, out, lse, stream);
+        else launch_combine_d<128, false>(rows, slots, o_part, lse_part, spl, rps, out, lse, stream);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_stream_read(const void* buf, uint64_t bytes, int workgroups, uint32_t* sink,
+                              hipStream_t stream) {
+    hipLaunchKernelGGL(fd_stream_read_kernel, dim3((unsigned)workgroups), dim3(kStreamThreads), 0, stream,
+                       static_cast<const stream_u32x4*>(buf), bytes / 16, sink);
     return hipGetLastError();
 }
 

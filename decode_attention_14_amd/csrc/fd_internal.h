@@ -101,8 +101,17 @@ bool vector_kernel_forced();
 hipError_t launch_partials_mfma(int head_dim, int batch, const PartialArgs& a, hipStream_t stream);
 hipError_t launch_chunk_mfma(int head_dim, int batch, const PartialArgs& a, hipStream_t stream);
 
+// Merge pass over rows [rows] of `slots` partial slots each.  With
+// `splits_per_seq` (device [rows / rows_per_seq] int32), row r merges only
+// the first splits_per_seq[r / rows_per_seq] slots (clamped to [0, slots]);
+// nullptr: every row merges all `slots`.
 hipError_t launch_combine(int head_dim, int out_dtype, int64_t rows, int slots,
-                          const float* o_part, const float* lse_part, void* out, float* lse,
-                          hipStream_t stream);
+                          const float* o_part, const float* lse_part, const int32_t* splits_per_seq,
+                          int64_t rows_per_seq, void* out, float* lse, hipStream_t stream);
+
+// Streaming read of [buf, buf + bytes) (bytes a multiple of 16) over
+// `workgroups` workgroups, folded into *sink only on an improbable value.
+hipError_t launch_stream_read(const void* buf, uint64_t bytes, int workgroups, uint32_t* sink,
+                              hipStream_t stream);
 
 }  // namespace fdk

@@ -40,7 +40,10 @@
  *     negative fd_status, records a message for fd_last_error(), and enqueues
  *     nothing.  A device-side launch failure returns FD_ERR_DEVICE.
  *   - Supported: dtype FD_F32 or FD_BF16; D = 64 or 128; any Hq/Hkv ratio;
- *     any q_len >= 1.  Arithmetic is fp32 throughout (scores, softmax,
+ *     any q_len >= 1.  One tile's keys of one KV head must span fewer than
+ *     2^31 bytes of a cache (for bf16 at D = 128, fewer than 8,388,608 keys):
+ *     a call whose split rule allows a larger tile (few splits over a very
+ *     long max_cache_len) returns FD_ERR_UNSUPPORTED; more splits fix it.  Arithmetic is fp32 throughout (scores, softmax,
  *     accumulation); out is rounded to its dtype with round-to-nearest-even.
  *     Caches of one-byte codes (FP8 E4M3, INT8) with bf16 q and out have
  *     calls of their own (fd_decode_attention_fp8, fd_decode_attention_int8),
@@ -147,17 +150,25 @@ fd_status fd_decode_partials(const fd_dims* dims, const void* q, const void* k_c
 /* fd_combine_splits -- the second pass only: merge partials.
  *
  * rows = batch * num_heads * q_len; o_part [rows, max_splits, head_dim] and
- * lse_part [rows, max_splits] fp32 in device memory.  Slots with
+ * lse_part [rows, max_splits] fp32 in device memory.  Row r belongs to
+ * sequence b = r / (num_heads * q_len).  `splits_per_seq` (device [batch]
+ * int32, or NULL) gives the slots S_b that sequence b holds: its rows merge
+ * slots 0 .. S_b - 1 and never read the others (values are clamped into
+ * [0, max_splits]; S_b = 0 gives out = 0, lse = -inf).  NULL means every
+ * sequence holds max_splits slots.  This is the merge of page
+ * "FlashDecoding算法原理与多GPU并行解码实战", multi-GPU section step 3, and of
+ * the per-device local results of page "ChunkedPrefill与FlashDecoding技术解析"
+ * §3.2, where sequences may carry different numbers of partials.  Slots with
  * lse = -inf are empty: their o_part entries do not affect the result and
- * may hold anything, NaN included.  Writes
- * out [rows, head_dim] in out_dtype (FD_F32 or FD_BF16, RNE) and, if
- * non-NULL, lse [rows] fp32.  A row without a finite slot gets out = 0 and
- * lse = -inf.  Errors: FD_ERR_INVALID for negative sizes, max_splits outside
- * [1, FD_MAX_SPLITS], NULL or misaligned buffers; FD_ERR_UNSUPPORTED for
- * other head_dim or out_dtype values. */
+ * may hold anything, NaN included.  Writes out [rows, head_dim] in out_dtype
+ * (FD_F32 or FD_BF16, RNE) and, if non-NULL, lse [rows] fp32.  A row without
+ * a finite slot gets out = 0 and lse = -inf.  Errors: FD_ERR_INVALID for
+ * negative sizes, max_splits outside [1, FD_MAX_SPLITS], NULL or misaligned
+ * buffers; FD_ERR_UNSUPPORTED for other head_dim or out_dtype values. */
 fd_status fd_combine_splits(int32_t batch, int32_t num_heads, int32_t q_len, int32_t head_dim,
                             int32_t max_splits, const float* o_part, const float* lse_part,
-                            int32_t out_dtype, void* out, float* lse, void* stream);
+                            const int32_t* splits_per_seq, int32_t out_dtype, void* out, float* lse,
+                            void* stream);
 
 /* fd_decode_attention -- the whole operation: partials, then merge.
  *
@@ -296,6 +307,19 @@ fd_status fd_decode_partials_int8(const fd_dims* dims, const void* q, const void
  * ("" if none); the pointer stays valid until the next call on the thread. */
 const char* fd_status_string(int32_t status);
 const char* fd_last_error(void);
+
+/* fd_stream_read -- a measurement aid, not part of the operation: reads
+ * `bytes` bytes of device memory from `buf` once, in 16-byte pieces spread
+ * over `workgroups` workgroups of 256 threads (0: eight per compute unit),
+ * and folds them into one word that reaches `*sink` (device memory, 4 bytes)
+ * only if it equals a value no real data is expected to give, so the reads
+ * cannot be optimised away.  Its time over the K/V bytes of a step gives the
+ * bandwidth a plain streaming read reaches on the device, the ceiling against
+ * which the partial kernel's rate is read (page "ChunkedPrefill与FlashDecoding
+ * 技术解析" §4.2 item 2: find where the kernel's time goes before tuning it).
+ * `buf` and `bytes` must be multiples of 16.  Errors: FD_ERR_INVALID for a
+ * NULL or misaligned buffer, a size not a multiple of 16 or workgroups < 0. */
+fd_status fd_stream_read(const void* buf, uint64_t bytes, int32_t workgroups, uint32_t* sink, void* stream);
 
 /* Library version, major * 10000 + minor * 100 + patch. */
 int32_t fd_version(void);

@@ -128,9 +128,9 @@ void validation_paths() {
                               nullptr, nullptr) == FD_ERR_INVALID);
     CHECK(fd_decode_partials(&good, fake(0), fake(1), fake(2), dl, 0.1f, 0, nullptr, (float*)fake(4),
                              (float*)fake(5), (float*)fake(6), nullptr) == FD_ERR_INVALID);
-    CHECK(fd_combine_splits(1, 32, 1, 128, 0, (float*)fake(0), (float*)fake(1), FD_BF16, fake(2), nullptr,
+    CHECK(fd_combine_splits(1, 32, 1, 128, 0, (float*)fake(0), (float*)fake(1), nullptr, FD_BF16, fake(2), nullptr,
                             nullptr) == FD_ERR_INVALID);
-    CHECK(fd_combine_splits(1, 32, 1, 100, 4, (float*)fake(0), (float*)fake(1), FD_BF16, fake(2), nullptr,
+    CHECK(fd_combine_splits(1, 32, 1, 100, 4, (float*)fake(0), (float*)fake(1), nullptr, FD_BF16, fake(2), nullptr,
                             nullptr) == FD_ERR_UNSUPPORTED);
     // paged and fp8 descriptions
     fd_kv_pages pg{(const int32_t*)fake(7), 4, 16, 10, FD_PAGES_NHD};

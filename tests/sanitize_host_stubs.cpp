@@ -9,8 +9,11 @@ hipError_t launch_partials(int, int, int, const PartialArgs&, hipStream_t) { ret
 
 hipError_t launch_partials_mfma(int, int, const PartialArgs&, hipStream_t) { return hipErrorNotSupported; }
 
-hipError_t launch_combine(int, int, int64_t, int, const float*, const float*, void*, float*, hipStream_t) {
+hipError_t launch_combine(int, int, int64_t, int, const float*, const float*, const int32_t*, int64_t, void*,
+                          float*, hipStream_t) {
     return hipErrorNotSupported;
 }
+
+hipError_t launch_stream_read(const void*, uint64_t, int, uint32_t*, hipStream_t) { return hipErrorNotSupported; }
 
 }  // namespace fdk

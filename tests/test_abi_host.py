@@ -242,16 +242,70 @@ def test_partials_and_combine_reject_bad_arguments(lib):
                                   o, m, FAKE[6], None) == fd.FD_ERR_INVALID
     assert lib.fd_decode_partials(ctypes.byref(d), q, k, v, lens, ctypes.c_float(1.0), 4, None,
                                   None, m, FAKE[6], None) == fd.FD_ERR_INVALID
-    assert lib.fd_combine_splits(1, 32, 1, 128, 0, FAKE[0], FAKE[1], fd.FD_BF16, FAKE[2], None,
+    assert lib.fd_combine_splits(1, 32, 1, 128, 0, FAKE[0], FAKE[1], None, fd.FD_BF16, FAKE[2], None,
                                  None) == fd.FD_ERR_INVALID
-    assert lib.fd_combine_splits(1, 32, 1, 128, 257, FAKE[0], FAKE[1], fd.FD_BF16, FAKE[2], None,
+    assert lib.fd_combine_splits(1, 32, 1, 128, 257, FAKE[0], FAKE[1], None, fd.FD_BF16, FAKE[2], None,
                                  None) == fd.FD_ERR_INVALID
-    assert lib.fd_combine_splits(1, 32, 1, 96, 4, FAKE[0], FAKE[1], fd.FD_BF16, FAKE[2], None,
+    assert lib.fd_combine_splits(1, 32, 1, 96, 4, FAKE[0], FAKE[1], None, fd.FD_BF16, FAKE[2], None,
                                  None) == fd.FD_ERR_UNSUPPORTED
-    assert lib.fd_combine_splits(1, 32, 1, 128, 4, None, FAKE[1], fd.FD_BF16, FAKE[2], None,
+    assert lib.fd_combine_splits(1, 32, 1, 128, 4, None, FAKE[1], None, fd.FD_BF16, FAKE[2], None,
                                  None) == fd.FD_ERR_INVALID
-    assert lib.fd_combine_splits(1, 32, 1, 128, 4, FAKE[0], FAKE[1], 5, FAKE[2], None,
+    assert lib.fd_combine_splits(1, 32, 1, 128, 4, FAKE[0], FAKE[1], None, 5, FAKE[2], None,
                                  None) == fd.FD_ERR_UNSUPPORTED
+
+
+def test_combine_rejects_misaligned_splits_per_seq(lib):
+    odd = ctypes.c_void_p(FAKE[3].value + 2)
+    assert lib.fd_combine_splits(1, 32, 1, 128, 4, FAKE[0], FAKE[1], odd, fd.FD_BF16, FAKE[2], None,
+                                 None) == fd.FD_ERR_INVALID
+    assert "splits_per_seq" in lib.fd_last_error().decode()
+
+
+def test_tiles_of_2gib_or_more_are_rejected(lib):
+    """Tiles are addressed with 32-bit byte offsets: a split rule under which
+    one tile of one KV head reaches 2^31 bytes is refused before any launch,
+    for every entry point and cache format."""
+    L = 1 << 23  # bf16 keys at D = 128: 2^23 * 256 B = 2^31 B
+    d = dims(B=1, Hq=32, Hkv=8, D=128, T=1, Lmax=L)
+    # one tile holding every key (no plan): 2^31 bytes
+    assert call_decode(lib, d) == fd.FD_ERR_UNSUPPORTED
+    assert "2^31" in lib.fd_last_error().decode()
+    # two forced splits: 2^30 bytes each -- passes the check, fails later on
+    # the missing workspace
+    assert call_decode(lib, d, num_splits=2) == fd.FD_ERR_WORKSPACE
+    # a plan whose last tile takes the rest of the keys: 2^23 + 2^20 keys in
+    # two slots of 2^20 leave 2^23 keys (2^31 bytes) to the last tile
+    d_long = dims(B=1, Hq=32, Hkv=8, D=128, T=1, Lmax=L + (1 << 20))
+    p = fd.FdPlan(tile_len=1 << 20, max_splits=2)
+    assert call_decode(lib, d_long, plan=p) == fd.FD_ERR_UNSUPPORTED
+    p = fd.FdPlan(tile_len=1 << 20, max_splits=3)  # last tile 2^23 - 2^20 keys
+    assert call_decode(lib, d_long, plan=p) == fd.FD_ERR_WORKSPACE
+    # one-byte codes hold twice the keys per byte: one tile of 2^23 codes at
+    # D = 128 is 2^30 bytes and passes (the misaligned out stops the call
+    # before any launch)
+    odd_out = ctypes.c_void_p(FAKE[4].value + 8)
+    assert lib.fd_decode_attention_fp8(ctypes.byref(d), *FAKE[:3], None, ctypes.c_float(1.0), ctypes.c_float(1.0),
+                                       FAKE[3], ctypes.c_float(1.0), 0, None, None, 0, odd_out, None,
+                                       None) == fd.FD_ERR_INVALID
+    d2 = dims(B=1, Hq=32, Hkv=8, D=128, T=1, Lmax=1 << 24)
+    assert lib.fd_decode_attention_fp8(ctypes.byref(d2), *FAKE[:3], None, ctypes.c_float(1.0), ctypes.c_float(1.0),
+                                       FAKE[3], ctypes.c_float(1.0), 0, None, None, 0, FAKE[4], None,
+                                       None) == fd.FD_ERR_UNSUPPORTED
+    # fp32 rows are twice as long
+    d3 = dims(B=1, Hq=8, Hkv=8, D=128, T=1, Lmax=1 << 22, dt=fd.FD_F32)
+    assert call_decode(lib, d3) == fd.FD_ERR_UNSUPPORTED
+    assert lib.fd_decode_partials(ctypes.byref(d3), *FAKE[:4], ctypes.c_float(1.0), 1, None, FAKE[4], FAKE[5],
+                                  FAKE[6], None) == fd.FD_ERR_UNSUPPORTED
+
+
+def test_stream_read_rejects_bad_arguments(lib):
+    assert lib.fd_stream_read(FAKE[0], 100, 0, FAKE[1], None) == fd.FD_ERR_INVALID
+    assert lib.fd_stream_read(None, 1024, 0, FAKE[1], None) == fd.FD_ERR_INVALID
+    assert lib.fd_stream_read(FAKE[0], 1024, -1, FAKE[1], None) == fd.FD_ERR_INVALID
+    assert lib.fd_stream_read(ctypes.c_void_p(FAKE[0].value + 8), 1024, 8, FAKE[1], None) == fd.FD_ERR_INVALID
+    assert lib.fd_stream_read(FAKE[0], 1024, 8, None, None) == fd.FD_ERR_INVALID
+    # nothing to read: no launch, no pointer touched
+    assert lib.fd_stream_read(None, 0, 0, None, None) == fd.FD_OK
 
 
 def test_empty_batch_is_a_no_op(lib):
@@ -259,7 +313,7 @@ def test_empty_batch_is_a_no_op(lib):
     # nothing to do: OK without touching any pointer
     assert lib.fd_decode_attention(ctypes.byref(d), None, None, None, None, ctypes.c_float(1.0), 0,
                                    None, None, 0, None, None, None) == fd.FD_OK
-    assert lib.fd_combine_splits(0, 4, 1, 64, 2, None, None, fd.FD_F32, None, None, None) == fd.FD_OK
+    assert lib.fd_combine_splits(0, 4, 1, 64, 2, None, None, None, fd.FD_F32, None, None, None) == fd.FD_OK
 
 
 def _up(x):

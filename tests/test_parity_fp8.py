@@ -17,7 +17,7 @@ import oracle
 from decode_attention_14_amd import binding as fd
 from decode_attention_14_amd.inputs import (WORKLOADS, as_oracle_array, fp8_scale_for, make_inputs, paginate,
                                             quantize_fp8, workload_inputs)
-from gpu_cases import TOL, compare, say
+from gpu_cases import TOL, compare, compare_workload, say
 
 pytestmark = [
     pytest.mark.gpu,
@@ -112,8 +112,7 @@ def test_fp8_headline_shape():
     ref_out, ref_lse = oracle.attention_fp8(as_oracle_array(q), kc.numpy(), vc.numpy(), cl.numpy(), w.scale, ks, vs)
     out, lse = fd.decode_attention_fp8(q.cuda(), kc.cuda(), vc.cuda(), cl.cuda(), ks, vs, scale=w.scale, plan=plan)
     torch.cuda.synchronize()
-    err, lerr = compare("fp8 gqa_32k", out, lse, ref_out, ref_lse, TOL["bf16"])
-    say(f"  max abs err out {err:.2e} lse {lerr:.2e}")
+    compare_workload("fp8 gqa_32k", out, lse, ref_out, ref_lse)
 
 
 @pytest.mark.parametrize("D", [128, 64])
@@ -144,5 +143,4 @@ def test_fp8_prefill_workload():
     ref_out, ref_lse = oracle.attention_fp8(as_oracle_array(q), kc.numpy(), vc.numpy(), cl.numpy(), w.scale, ks, vs)
     out, lse = fd.decode_attention_fp8(q.cuda(), kc.cuda(), vc.cuda(), cl.cuda(), ks, vs, scale=w.scale, plan=plan)
     torch.cuda.synchronize()
-    err, lerr = compare("fp8 prefill_chunk_512", out, lse, ref_out, ref_lse, TOL["bf16"])
-    say(f"  max abs err out {err:.2e} lse {lerr:.2e}")
+    compare_workload("fp8 prefill_chunk_512", out, lse, ref_out, ref_lse)

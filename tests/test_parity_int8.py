@@ -19,7 +19,7 @@ import oracle
 from decode_attention_14_amd import binding as fd
 from decode_attention_14_amd.inputs import (WORKLOADS, as_oracle_array, int8_scale_for, make_inputs, paginate,
                                             quantize_int8, workload_inputs)
-from gpu_cases import TOL, compare, say
+from gpu_cases import TOL, compare, compare_workload, say
 
 pytestmark = [
     pytest.mark.gpu,
@@ -119,8 +119,7 @@ def test_int8_headline_shape():
     out, lse = fd.decode_attention_int8(q.cuda(), kc.cuda(), vc.cuda(), cl.cuda(), ks, vs, scale=w.scale,
                                         plan=plan)
     torch.cuda.synchronize()
-    err, lerr = compare("int8 gqa_32k", out, lse, ref_out, ref_lse, TOL["bf16"])
-    say(f"  max abs err out {err:.2e} lse {lerr:.2e}")
+    compare_workload("int8 gqa_32k", out, lse, ref_out, ref_lse)
 
 
 @pytest.mark.parametrize("D", [128, 64])
@@ -149,5 +148,4 @@ def test_int8_prefill_workload():
     out, lse = fd.decode_attention_int8(q.cuda(), kc.cuda(), vc.cuda(), cl.cuda(), ks, vs, scale=w.scale,
                                         plan=plan)
     torch.cuda.synchronize()
-    err, lerr = compare("int8 prefill_chunk_512", out, lse, ref_out, ref_lse, TOL["bf16"])
-    say(f"  max abs err out {err:.2e} lse {lerr:.2e}")
+    compare_workload("int8 prefill_chunk_512", out, lse, ref_out, ref_lse)
