@@ -318,6 +318,24 @@ def main():
         samples = [ev[r].elapsed_time(ev[r + 1]) / per for r in range(reps)]
         return samples, ev[0].elapsed_time(ev[reps]) / (reps * per)
 
+    per = max(1, min(args.graph_steps, args.steps))
+    if args.steps % per:
+        print(f"--steps {args.steps} is not a multiple of --graph-steps {per}", file=sys.stderr)
+        sys.exit(2)
+    print(f"[bench] plan {plan.plan} copies={copies} warmup={args.warmup} steps={args.steps} "
+          f"graph={not args.no_graph} ({per} steps per replay)", file=sys.stderr, flush=True)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    samples, ms_mean = timed_samples(step, args.steps, per)
+    wall = time.perf_counter() - t0
+    srt = sorted(samples)
+    ms_per_step = srt[len(srt) // 2] if len(srt) % 2 else 0.5 * (srt[len(srt) // 2 - 1] + srt[len(srt) // 2])
+    print(f"[bench] timed {args.steps} steps in {len(samples)} samples: median {ms_per_step * 1e3:.2f} us/step, "
+          f"mean {ms_mean * 1e3:.2f}, min {srt[0] * 1e3:.2f}, max {srt[-1] * 1e3:.2f} (wall incl. capture "
+          f"{wall:.3f} s)", file=sys.stderr, flush=True)
+
     # The partial pass alone and the merge alone, back to back in a graph; the
     # average per launch includes the short gap between consecutive kernels.
     n_k = max(20, min(args.steps, 200))
@@ -349,7 +367,7 @@ def main():
         cbuf.fill_(1)
         sink = torch.zeros(1, dtype=torch.int32, device=dev)
         best = None
-        for wg in (1024, 2048, 4096, 8192):
+        for wg in (2048, 8192, 16384, 32768):
             ms = timed(lambda i, wg=wg: fd.stream_read(cbuf, win, wg, sink, offset=(i % nwin) * win), n_k)
             gbs = win / (ms * 1e-3) / 1e9
             print(f"[bench] stream read {win} B, {wg} workgroups: {ms * 1e3:.2f} us, {gbs:.0f} GB/s", file=sys.stderr,

@@ -20,11 +20,12 @@ LIB_PATH = os.environ.get("FD_LIBRARY", os.path.join(_PKG, "libfd.so"))
 FD_OK, FD_ERR_INVALID, FD_ERR_UNSUPPORTED, FD_ERR_WORKSPACE, FD_ERR_DEVICE = 0, -1, -2, -3, -4
 FD_F32, FD_BF16, FD_FP8_E4M3, FD_INT8 = 0, 1, 2, 3
 FD_MAX_SPLITS = 256
+FD_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 FD_PAGES_NHD, FD_PAGES_HND = 0, 1
 
 EXPORTS = ("fd_plan_splits", "fd_workspace_bytes", "fd_decode_partials", "fd_combine_splits",
-           "fd_decode_attention", "fd_decode_attention_paged", "fd_decode_partials_paged",
+           "fd_decode_attention", "fd_decode_attention_noalloc", "fd_decode_attention_paged", "fd_decode_partials_paged",
            "fd_decode_attention_fp8", "fd_decode_partials_fp8", "fd_decode_attention_int8",
            "fd_decode_partials_int8", "fd_stream_read", "fd_status_string", "fd_last_error", "fd_version")
 
@@ -84,6 +85,8 @@ def load_library(path: str | None = None):
     lib.fd_decode_attention.argtypes = [dims_p, vp, vp, vp, vp, ctypes.c_float, i32, plan_p,
                                         vp, u64, vp, vp, vp]
     lib.fd_decode_attention.restype = i32
+    lib.fd_decode_attention_noalloc.argtypes = [dims_p, vp, vp, vp, vp, ctypes.c_float, i32, plan_p, vp, vp, vp]
+    lib.fd_decode_attention_noalloc.restype = i32
     lib.fd_decode_attention_paged.argtypes = [dims_p, vp, vp, vp, ctypes.POINTER(FdKvPages), vp,
                                               ctypes.c_float, i32, plan_p, vp, u64, vp, vp, vp]
     lib.fd_decode_attention_paged.restype = i32
@@ -267,6 +270,29 @@ def decode_attention(q, k_cache, v_cache, cache_lens, scale=None, num_splits: in
                                    int(num_splits), ctypes.byref(fp) if fp is not None else None,
                                    _ptr(workspace), given, _ptr(out), _ptr(lse),
                                    _stream(q.device)))
+    return out, lse
+
+
+def decode_attention_noalloc(q, k_cache, v_cache, cache_lens, scale=None, num_splits: int = 0,
+                             plan: Plan | FdPlan | None = None, out=None, lse=None):
+    """decode_attention through fd_decode_attention_noalloc: the library's
+    static per-GPU scratch holds the partials (no workspace).  Returns
+    (out, lse); out and lse are allocated here when not given."""
+    lib = load_library()
+    _require_cuda(q, k_cache, v_cache, cache_lens, out, lse)
+    dims = dims_of(q, k_cache)
+    _check_inputs(q, k_cache, v_cache, cache_lens)
+    _check_buffer(out, q.shape, q.dtype, "out")
+    _check_buffer(lse, q.shape[:3], torch.float32, "lse")
+    fp = plan.plan if isinstance(plan, Plan) else plan
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    _check(lib.fd_decode_attention_noalloc(ctypes.byref(dims), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                           _ptr(cache_lens), ctypes.c_float(_default_scale(q.shape[-1], scale)),
+                                           int(num_splits), ctypes.byref(fp) if fp is not None else None,
+                                           _ptr(out), _ptr(lse), _stream(q.device)))
     return out, lse
 
 

@@ -8,7 +8,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libfd.so")
-SOURCES = ["fd_api.cpp", "fd_select.cpp", "fd_decode.hip", "fd_mfma.hip", "fd_chunk.hip"]
+SOURCES = ["fd_api.cpp", "fd_select.cpp", "fd_decode.hip", "fd_mfma.hip", "fd_chunk.hip", "fd_scratch.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # Packed fp32 instructions are disabled for every HIP translation unit.

@@ -16,6 +16,8 @@
 
 #include "fd_internal.h"
 
+static_assert(fdk::kNoallocScratchBytes == FD_NOALLOC_SCRATCH_BYTES, "scratch size in fd.h and the library");
+
 namespace {
 
 thread_local char g_last_error[512] = "";
@@ -516,10 +518,13 @@ fd_status resolve_pages(const fd_dims* d, const fd_kv_pages* pages, fdk::SplitRu
 
 // The two passes of the operation over contiguous (pk == nullptr) or paged
 // caches.
+// With noalloc, the workspace is the library's static scratch of the
+// current device (workspace and workspace_bytes are ignored): calls needing
+// more than it holds fail with FD_ERR_WORKSPACE.
 fd_status run_attention(const fd_dims* dims, const void* q, const void* k_cache, const void* v_cache,
                         const fd_kv_pages* pages, const CodeScales* cs, const int32_t* cache_lens, float scale,
                         int32_t num_splits, const fd_plan* plan, void* workspace, uint64_t workspace_bytes,
-                        void* out, float* lse, void* stream) {
+                        void* out, float* lse, void* stream, bool noalloc = false) {
     clear_error();
     fd_status st = check_dims(dims);
     if (st != FD_OK) return st;
@@ -547,6 +552,15 @@ fd_status run_attention(const fd_dims* dims, const void* q, const void* k_cache,
                              "partial kernel launch");
     }
     const Layout lay = workspace_layout(dims, rule.slots);
+    if (noalloc) {
+        if ((uint64_t)lay.bytes > fdk::kNoallocScratchBytes)
+            return fail(FD_ERR_WORKSPACE,
+                        "this call needs %llu bytes of workspace; the static scratch of the no-allocation entry "
+                        "point holds %llu (use fd_decode_attention with a workspace, or fewer splits)",
+                        (unsigned long long)lay.bytes, (unsigned long long)fdk::kNoallocScratchBytes);
+        if ((st = device_status(fdk::noalloc_scratch(&workspace), "static scratch lookup")) != FD_OK) return st;
+        workspace_bytes = fdk::kNoallocScratchBytes;
+    }
     if (!workspace || workspace_bytes < (uint64_t)lay.bytes)
         return fail(FD_ERR_WORKSPACE, "workspace of %llu bytes needed, %llu given%s",
                     (unsigned long long)lay.bytes, (unsigned long long)workspace_bytes,
@@ -576,6 +590,14 @@ fd_status fd_decode_attention(const fd_dims* dims, const void* q, const void* k_
                               uint64_t workspace_bytes, void* out, float* lse, void* stream) {
     return run_attention(dims, q, k_cache, v_cache, nullptr, nullptr, cache_lens, scale, num_splits, plan,
                          workspace, workspace_bytes, out, lse, stream);
+}
+
+fd_status fd_decode_attention_noalloc(const fd_dims* dims, const void* q, const void* k_cache,
+                                      const void* v_cache, const int32_t* cache_lens, float scale,
+                                      int32_t num_splits, const fd_plan* plan, void* out, float* lse,
+                                      void* stream) {
+    return run_attention(dims, q, k_cache, v_cache, nullptr, nullptr, cache_lens, scale, num_splits, plan, nullptr,
+                         0, out, lse, stream, true);
 }
 
 fd_status fd_decode_attention_paged(const fd_dims* dims, const void* q, const void* k_pages,

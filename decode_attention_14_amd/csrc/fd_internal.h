@@ -109,6 +109,13 @@ hipError_t launch_combine(int head_dim, int out_dtype, int64_t rows, int slots,
                           const float* o_part, const float* lse_part, const int32_t* splits_per_seq,
                           int64_t rows_per_seq, void* out, float* lse, hipStream_t stream);
 
+// The statically allocated workspace of fd_decode_attention_noalloc
+// (fd_scratch.hip): kNoallocScratchBytes per device, held until the process
+// ends.  noalloc_scratch returns the current device's copy, looking its
+// address up on the first call on that device.
+constexpr uint64_t kNoallocScratchBytes = 32ull << 20;
+hipError_t noalloc_scratch(void** ptr);
+
 // Streaming read of [buf, buf + bytes) (bytes a multiple of 16) over
 // `workgroups` workgroups, folded into *sink only on an improbable value.
 hipError_t launch_stream_read(const void* buf, uint64_t bytes, int workgroups, uint32_t* sink,

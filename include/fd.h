@@ -185,6 +185,27 @@ fd_status fd_decode_attention(const fd_dims* dims, const void* q, const void* k_
                               int32_t num_splits, const fd_plan* plan, void* workspace,
                               uint64_t workspace_bytes, void* out, float* lse, void* stream);
 
+/* fd_decode_attention_noalloc -- fd_decode_attention for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.
+ *
+ * Same operation, arguments and errors as fd_decode_attention, without the
+ * workspace arguments: the partials live in a statically allocated scratch
+ * area of FD_NOALLOC_SCRATCH_BYTES inside the library, one per GPU, held from
+ * the library's load until the process ends.  A call whose workspace
+ * (fd_workspace_bytes of its dims and slots) exceeds that returns
+ * FD_ERR_WORKSPACE and enqueues nothing.  The call allocates nothing and
+ * calls no allocating routine; the first call on a device looks up that
+ * device's scratch address once.  Every call on one GPU uses the same scratch
+ * and leaves its contents to the next: calls that may overlap on one GPU
+ * (two streams, two threads) race and must be serialised by the caller.
+ * Single-slot calls (one tile per sequence) use no scratch at all. */
+#define FD_NOALLOC_SCRATCH_BYTES (32ull << 20)
+fd_status fd_decode_attention_noalloc(const fd_dims* dims, const void* q, const void* k_cache,
+                                      const void* v_cache, const int32_t* cache_lens, float scale,
+                                      int32_t num_splits, const fd_plan* plan, void* out, float* lse,
+                                      void* stream);
+
 /* Paged K/V caches.
  *
  * Page "FlashDecoding算法原理与多GPU并行解码实战" (deployment engineering

@@ -57,7 +57,19 @@ def compare(name, got_out, got_lse, ref_out, ref_lse, tol):
 # fp32-accurate arithmetic this stays near 1e-4; the fp64 values themselves
 # sit about 2^-9 / sqrt(3) ~ 1.1e-3 (relative rms) from their bf16 roundings,
 # which is why the guard is taken against r and not against the fp64 output.
+#
+# That holds for the decode kernel (up to 32 query rows per KV head), which
+# feeds P to the P.V product as a bf16 head plus a bf16 remainder (about 16
+# significant bits).  The chunk kernel (more rows per KV head) feeds P as one
+# bf16 operand, as matrix-core attention usually does, except in blocks where
+# one key carries more than 1/16 of the running sum: each weight then carries
+# a relative rounding error of rms 2^-9 / sqrt(3) ~ 1.1e-3, which reaches the
+# output at about the same relative rms, comparable to half a bf16 ulp of the
+# output; the rounded result then differs from the rounded oracle by one ulp
+# (2^-8 relative) at roughly E|err| / ulp ~ 23% of the elements, a rel-L2 of
+# about sqrt(0.23) 2^-8 ~ 1.9e-3.  Its guard is REL_L2_GUARD_CHUNK.
 REL_L2_GUARD = 1e-3
+REL_L2_GUARD_CHUNK = 3e-3
 
 
 def rel_l2_rounded(got_out, ref_out):
@@ -68,11 +80,18 @@ def rel_l2_rounded(got_out, ref_out):
     return float(np.linalg.norm(g - r)) / den if den > 0 else float(np.linalg.norm(g))
 
 
-def compare_workload(name, got_out, got_lse, ref_out, ref_lse):
+def rel_l2_guard_for(rows_per_kv_head):
+    """The rel-L2 guard of the kernel that serves a call with this many query
+    rows per KV head (n_rep * q_len): the decode kernel up to 32, else the
+    chunk kernel."""
+    return REL_L2_GUARD if rows_per_kv_head <= 32 else REL_L2_GUARD_CHUNK
+
+
+def compare_workload(name, got_out, got_lse, ref_out, ref_lse, guard=REL_L2_GUARD):
     """Check at a benchmark workload's shape: max abs error <= 2e-3 (bf16) or
     1e-5 (fp32) on out and on lse with no ulp allowance, and rel-L2 of out
-    against the rounded oracle <= REL_L2_GUARD.  Returns (max abs error of
-    out, of lse, rel-L2)."""
+    against the rounded oracle <= guard.  Returns (max abs error of out, of
+    lse, rel-L2)."""
     tol = TOL["bf16"] if got_out.dtype == torch.bfloat16 else TOL["f32"]
     go = got_out.detach().float().cpu().numpy().astype(np.float64)
     assert go.shape == ref_out.shape, (name, go.shape, ref_out.shape)
@@ -88,7 +107,7 @@ def compare_workload(name, got_out, got_lse, ref_out, ref_lse):
     rl2 = rel_l2_rounded(got_out, ref_out)
     say(f"  {name}: max abs err out {err:.2e} lse {lerr:.2e}; rel-L2 vs rounded oracle {rl2:.2e} "
         f"(max |out| {float(np.max(np.abs(ref_out))):.3f})")
-    assert rl2 <= REL_L2_GUARD, f"{name}: rel-L2 {rl2:.3e} above the guard {REL_L2_GUARD:.0e}"
+    assert rl2 <= guard, f"{name}: rel-L2 {rl2:.3e} above the guard {guard:.0e}"
     return err, lerr, rl2
 
 

@@ -14,6 +14,11 @@ hipError_t launch_combine(int, int, int64_t, int, const float*, const float*, co
     return hipErrorNotSupported;
 }
 
+hipError_t noalloc_scratch(void** ptr) {
+    *ptr = nullptr;
+    return hipErrorNotSupported;
+}
+
 hipError_t launch_stream_read(const void*, uint64_t, int, uint32_t*, hipStream_t) { return hipErrorNotSupported; }
 
 }  // namespace fdk

@@ -298,6 +298,21 @@ def test_tiles_of_2gib_or_more_are_rejected(lib):
                                   FAKE[6], None) == fd.FD_ERR_UNSUPPORTED
 
 
+def test_noalloc_rejects_calls_beyond_its_scratch(lib):
+    """fd_decode_attention_noalloc refuses a call whose partials exceed the
+    static scratch before looking it up or launching anything."""
+    d = dims(B=64, Hq=64, Hkv=8, D=128, T=1, Lmax=1024)
+    assert lib.fd_workspace_bytes(ctypes.byref(d), 256) > fd.FD_NOALLOC_SCRATCH_BYTES
+    st = lib.fd_decode_attention_noalloc(ctypes.byref(d), *FAKE[:4], ctypes.c_float(0.1), 256, None, FAKE[4],
+                                         FAKE[5], None)
+    assert st == fd.FD_ERR_WORKSPACE
+    assert "static scratch" in lib.fd_last_error().decode()
+    # the usual validation comes first
+    st = lib.fd_decode_attention_noalloc(ctypes.byref(d), None, *FAKE[1:4], ctypes.c_float(0.1), 256, None,
+                                         FAKE[4], FAKE[5], None)
+    assert st == fd.FD_ERR_INVALID
+
+
 def test_stream_read_rejects_bad_arguments(lib):
     assert lib.fd_stream_read(FAKE[0], 100, 0, FAKE[1], None) == fd.FD_ERR_INVALID
     assert lib.fd_stream_read(None, 1024, 0, FAKE[1], None) == fd.FD_ERR_INVALID
