@@ -6,8 +6,12 @@ launch spends its time: when the workgroups start, when wave 0's first block
 lands, when each wave leaves its block loop, when the workgroups end (100 MHz
 ``s_memrealtime`` clock, shared by all XCDs), and the end times per XCD.
 
-    python -m decode_attention_14_amd.timeline [--workload gqa_32k] [--kv-fp8 | --kv-int8]
+    python -m decode_attention_14_amd.timeline [--workload gqa_32k] [--kv-fp8 | --kv-int8] [--step]
 
+``--step`` times the whole ``fd_decode_attention`` call instead of the partial
+pass alone; where the partial kernel merges in place, each workgroup also
+records when its partial stores had completed and when its arrival count
+returned, and the last workgroup of each (sequence, KV head) is reported.
 Needs a GPU.  The timeline build computes the same results as ``libfd.so``.
 """
 from __future__ import annotations
@@ -24,9 +28,9 @@ from . import binding as fd
 from .build import TIMELINE_LIB
 from .inputs import WORKLOADS, fp8_scale_for, int8_scale_for, quantize_fp8, quantize_int8, workload_inputs
 
-SLOTS = 16           # per workgroup: start, first block, 8 wave loop exits, end, XCD
+SLOTS = 16           # per workgroup: start, first block, 8 wave loop exits, end, XCD, merge stamps
 MAX_WGS = 4096
-T_START, T_FIRST, T_LOOP, T_END, T_XCC = 0, 1, 2, 10, 11
+T_START, T_FIRST, T_LOOP, T_END, T_XCC, T_STORED, T_COUNTED, T_LAST = 0, 1, 2, 10, 11, 12, 13, 14
 TICK_US = 0.01       # s_memrealtime runs at 100 MHz
 
 
@@ -36,6 +40,7 @@ def main(argv=None) -> int:
     ap.add_argument("--kv-fp8", action="store_true")
     ap.add_argument("--kv-int8", action="store_true")
     ap.add_argument("--launches", type=int, default=6, help="launches whose timelines are read")
+    ap.add_argument("--step", action="store_true", help="time the whole fd_decode_attention call")
     args = ap.parse_args(argv)
     if not torch.cuda.is_available():
         print("the timeline needs a GPU", file=sys.stderr)
@@ -69,9 +74,19 @@ def main(argv=None) -> int:
     m_part = torch.empty(*qd.shape[:3], slots, dtype=torch.float32, device=dev)
     l_part = torch.empty_like(m_part)
 
+    ws = fd.new_workspace(fd.workspace_bytes(fd.dims_of(qd, kd0), slots), dev)
+    out = torch.empty_like(qd)
+    lse = torch.empty(qd.shape[:3], dtype=torch.float32, device=dev)
+
     def launch(i):
         kd, vd = kvs[i % copies]
-        if codes:
+        if args.step:
+            if codes:
+                attn = fd.decode_attention_fp8 if codes == "fp8" else fd.decode_attention_int8
+                attn(qd, kd, vd, cld, ks, vs, scale=w.scale, plan=plan.plan, out=out, lse=lse, workspace=ws)
+            else:
+                fd.decode_attention(qd, kd, vd, cld, scale=w.scale, plan=plan.plan, out=out, lse=lse, workspace=ws)
+        elif codes:
             partials(qd, kd, vd, cld, ks, vs, scale=w.scale, plan=plan.plan, o_part=o_part, m_part=m_part,
                      lse_part=l_part)
         else:
@@ -113,6 +128,16 @@ def main(argv=None) -> int:
             "end_us_per_xcd": {int(x): round(float(end[t[:, T_XCC] == x].mean()), 2)
                                for x in np.unique(t[:, T_XCC])},
         }
+        last = t[:, T_LAST] == 1
+        if args.step and last.any():
+            loop_end = start + loops.max(axis=1)
+            stored = (t[:, T_STORED] - t0) * TICK_US
+            counted = (t[:, T_COUNTED] - t0) * TICK_US
+            row["merging_workgroups"] = int(last.sum())
+            row["last_loop_end_us"] = round(float(loop_end.max()), 2)
+            row["merging: loop end -> stores done us"] = round(float((stored - loop_end)[last].mean()), 2)
+            row["merging: stores done -> counted us"] = round(float((counted - stored)[last].mean()), 2)
+            row["merging: counted -> end us"] = round(float((end - counted)[last].mean()), 2)
         summary.append(row)
         print(json.dumps(row), flush=True)
     keys = ("span_us", "start_spread_us", "first_block_us", "end_after_last_wave_us", "end_spread_us")
