@@ -65,25 +65,7 @@ struct PartialArgs {
     PagedKV pages;      // pages.table == nullptr: k/v are [B, Hkv, Lmax, D]
     int32_t kv_codes;   // kKvBf16, or the one-byte code format of k/v (bf16 q/out); k_scale is in qk_scale
     float v_scale;      // codes: value of V = code * v_scale (applied to the output)
-    // Partials mode of the decode kernel only: arrival counters [B * Hkv],
-    // zero on entry and left zero; the last workgroup of each (sequence, KV
-    // head) merges its rows into out/lse (m_part is then not written).
-    // nullptr: partials only, merged by the merge kernel.
-    uint32_t* merge;
 };
-
-// Arrival counters of the merge inside the partial pass: a fixed header at
-// the start of fd_decode_attention's workspace, one 32-bit counter per
-// (sequence, KV head) in a 128-byte line of its own (atomics on one line are
-// serialised, and the groups of a launch arrive at once); calls with more
-// groups merge in a separate kernel.
-constexpr int64_t kMergeHeaderBytes = 256 << 10;
-constexpr int kMergeCounterStride = 32;  // 32-bit words between counters
-constexpr int64_t kMergeCounters = kMergeHeaderBytes / (4 * kMergeCounterStride);
-
-// Whether the partial pass of a call is the decode kernel that can merge in
-// place (bf16 queries, up to 32 rows per KV head, counters for every group).
-bool merge_in_partials(int dtype, int head_dim, int rows, int64_t groups, int32_t kv_codes);
 
 // Packed query rows per workgroup of the matrix-core chunk kernel (row
 // groups of more than 32 rows per KV head).

@@ -63,15 +63,12 @@
 // dispatch order, i < kTimelineWGs) leaves at [i * kTimelineSlots]: its start,
 // the landing of wave 0's first block, each wave's exit from its block loop
 // (up to 8 waves), its end, all in the 100 MHz s_memrealtime clock, and the
-// XCD it ran on; with the merge in the partial pass, also when its partial
-// stores had completed, when its arrival count returned, and whether it was
-// the group's last (1) or not (2).  fd_debug_timeline copies the array to host memory.
+// XCD it ran on.  fd_debug_timeline copies the array to host memory.
 #if FD_WG_TIMELINE
 namespace fdk {
 constexpr int kTimelineWGs = 4096;
 constexpr int kTimelineSlots = 16;
-enum { kTlStart = 0, kTlFirst = 1, kTlLoop = 2, kTlEnd = 10, kTlXcc = 11, kTlStored = 12, kTlCounted = 13,
-       kTlLast = 14 };
+enum { kTlStart = 0, kTlFirst = 1, kTlLoop = 2, kTlEnd = 10, kTlXcc = 11 };
 }  // namespace fdk
 __device__ uint64_t fd_wg_timeline[fdk::kTimelineWGs * fdk::kTimelineSlots];
 extern "C" int fd_debug_timeline(void* host_dst, uint64_t bytes) {
@@ -408,84 +405,7 @@ __device__ __forceinline__ void load_fragments(const char* kb, const char* vb, b
     lds_settle(vf);
 }
 
-// The merge inside the partial pass (fd_decode_attention's split path).
-// Every workgroup of a (sequence b, KV head g) with keys in its tile writes
-// its partials (o_part, lse_part: slot s of each row) with device-scope
-// stores, which go through to the level of the memory system that all
-// compute units and XCDs share; it then counts itself in the group's arrival
-// counter, and the last of the S_b to arrive merges the group's rows over
-// slots 0 .. S_b - 1 in slot order (so the bits do not depend on the arrival
-// order) and writes out and lse -- the merge of page "FlashDecoding算法原理
-// 与多GPU并行解码实战" (multi-GPU step 3), as in fd_combine_kernel.  Before
-// counting, every thread waits until its own stores have completed and the
-// workgroup synchronises; the last workgroup reads the partials with device-
-// scope loads, which fetch from that shared level.  So no cache-wide
-// write-back or invalidation is needed: those stall every workgroup streaming
-// through the XCD's L2.  The last workgroup then sets the counter back to
-// zero, so the counters are zero after every call, as they must be before
-// the first.
-constexpr int kAuxDevice = 16;  // cache policy of a buffer access: sc1, device scope
-
-// Buffer resources over a group's partials: o_part rows [row0, row0 + rows)
-// of `slots` slots, and the matching lse_part entries.
-struct GroupParts {
-    __amdgpu_buffer_rsrc_t o, lse;
-};
-
-__device__ __forceinline__ GroupParts group_parts(const PartialArgs& a, int64_t row0, int D) {
-    const int slots = a.rule.slots;
-    GroupParts gp;
-    gp.o = tile_rsrc(reinterpret_cast<const char*>(a.o_part + row0 * slots * D), (uint32_t)(a.rows * slots * D * 4));
-    gp.lse = tile_rsrc(reinterpret_cast<const char*>(a.lse_part + row0 * slots), (uint32_t)(a.rows * slots * 4));
-    return gp;
-}
-
-template <int D, int MW>
-__device__ __forceinline__ void merge_last(const PartialArgs& a, const GroupParts& gp, int b, int g, int S,
-                                           int64_t row0, int tid) {
-    __shared__ int sm_last;
-    wait_vmcnt_le<0>();  // this thread's partial stores have completed
-    __syncthreads();
-    if (tid == 0) {
-#if FD_WG_TIMELINE
-        const uint64_t tl_stored = __builtin_amdgcn_s_memrealtime();
-#endif
-        uint32_t* cnt = a.merge + ((int64_t)b * a.Hkv + g) * kMergeCounterStride;
-        const uint32_t before = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const bool last = before == (uint32_t)(S - 1);
-        if (last) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        sm_last = last ? 1 : 0;
-#if FD_WG_TIMELINE
-        if (uint64_t* row = timeline_row()) {
-            row[kTlStored] = tl_stored;
-            row[kTlCounted] = __builtin_amdgcn_s_memrealtime();
-            row[kTlLast] = last ? 1 : 2;
-        }
-#endif
-    }
-    __syncthreads();
-    if (!sm_last) return;
-    const int w = tid >> 6, lane = tid & 63;
-    const int slots = a.rule.slots;
-    for (int r = w; r < a.rows; r += MW) {
-        const int rs = r * slots;
-        const MergeState st = merge_slots_wave_by<D>(
-            [&](int sl) {
-                return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(gp.lse, (rs + sl) * 4, 0, kAuxDevice));
-            },
-            [&](int sl, int c4) {
-                return __builtin_bit_cast(
-                    float4, __builtin_amdgcn_raw_buffer_load_b128(gp.o, ((rs + sl) * D + 4 * c4) * 4, 0, kAuxDevice));
-            },
-            S, 0, 1, lane);
-        const int64_t row = row0 + r;
-        if (lane < D / 4)
-            write_merged<true>(st, reinterpret_cast<uint16_t*>(a.out) + row * D, lane, a.lse ? a.lse + row : nullptr);
-    }
-}
-
-// MERGE: partials merged in this kernel (a.merge holds the counters).
-template <int D, int NB, bool CAUSAL, bool PAGED, int KV, bool MERGE>
+template <int D, int NB, bool CAUSAL, bool PAGED, int KV>
 __global__ __launch_bounds__(KV != kKvBf16 ? 64 * kMW8 : kMT) void fd_mfma_partial_kernel(PartialArgs a) {
     constexpr bool C8 = KV != kKvBf16;  // one-byte codes
     using G = Geo<D>;
@@ -528,13 +448,9 @@ __global__ __launch_bounds__(KV != kKvBf16 ? 64 * kMW8 : kMT) void fd_mfma_parti
     const int nrows = a.rows;
     const int64_t row0 = ((int64_t)b * a.Hq + (int64_t)g * a.n_rep) * a.q_len;
     const int slots = a.rule.slots;
-    // Merged in this kernel (see merge_last): a sequence of one tile writes
-    // its output directly, as does tile 0 of an empty one.
-    const bool direct = a.direct || (MERGE && S <= 1);
 
-    if (MERGE && s >= max(S, 1)) return;  // no keys in this slot, nobody reads it
     if (s >= S) {
-        if (direct) {
+        if (a.direct) {
             for (int idx = tid; idx < nrows * D; idx += MT)
                 reinterpret_cast<uint16_t*>(a.out)[row0 * D + idx] = 0;
             if (a.lse && tid < nrows) a.lse[row0 + tid] = -INFINITY;
@@ -702,8 +618,6 @@ __global__ __launch_bounds__(KV != kKvBf16 ? 64 * kMW8 : kMT) void fd_mfma_parti
     // column 0 also writes the row's statistics.  A row with no visible key
     // gets zeros (direct) or no o_part entry.
     constexpr int C4 = D / 4;
-    GroupParts gp{};
-    if (MERGE && !direct) gp = group_parts(a, row0, D);
     for (int idx = tid; idx < nrows * C4; idx += MT) {
         const int r = idx / C4;
         const int c4 = idx - r * C4;
@@ -722,11 +636,8 @@ __global__ __launch_bounds__(KV != kKvBf16 ? 64 * kMW8 : kMT) void fd_mfma_parti
         const int64_t row = row0 + r;
         if (c4 == 0) {
             const float lse_v = empty ? -INFINITY : (M + log2f(den)) * kLn2;
-            if (direct) {
+            if (a.direct) {
                 if (a.lse) a.lse[row] = lse_v;
-            } else if (MERGE) {  // the merge below needs only lse
-                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lse_v), gp.lse, (r * slots + s) * 4, 0,
-                                                      kAuxDevice);
             } else {
                 float X = -INFINITY;
 #pragma unroll
@@ -735,26 +646,22 @@ __global__ __launch_bounds__(KV != kKvBf16 ? 64 * kMW8 : kMT) void fd_mfma_parti
                 a.lse_part[row * slots + s] = lse_v;
             }
         }
-        if (!direct && empty) continue;
+        if (!a.direct && empty) continue;
         // codes: V was dequantised without its scale
         const float inv = empty ? 0.f : (C8 ? a.v_scale : 1.f) * __builtin_amdgcn_rcpf(den);
         f32x4_t o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int x = 0; x < MW; ++x)
             o += (f[x] * inv) * *reinterpret_cast<const f32x4_t*>(sm_acc + (x * NR + r) * RS + 4 * c4);
-        if (direct) {
+        if (a.direct) {
             uint2 pk;
             pk.x = (uint32_t)f32_to_bf16(o[0]) | ((uint32_t)f32_to_bf16(o[1]) << 16);
             pk.y = (uint32_t)f32_to_bf16(o[2]) | ((uint32_t)f32_to_bf16(o[3]) << 16);
             *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.out) + row * D + 4 * c4) = pk;
-        } else if (MERGE) {
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, o), gp.o,
-                                                   ((r * slots + s) * D + 4 * c4) * 4, 0, kAuxDevice);
         } else {
             *reinterpret_cast<f32x4_t*>(a.o_part + (row * slots + s) * D + 4 * c4) = o;
         }
     }
-    if (MERGE && !direct) merge_last<D, MW>(a, gp, b, g, S, row0, tid);
 #if FD_WG_TIMELINE
     if (tid == 0) {
         const uint64_t t = __builtin_amdgcn_s_memrealtime();
@@ -770,30 +677,21 @@ __global__ __launch_bounds__(KV != kKvBf16 ? 64 * kMW8 : kMT) void fd_mfma_parti
 }
 
 
-template <int D, int NB, int KV, bool MERGE>
-void launch_nb_kv_m(int batch, const PartialArgs& a, hipStream_t stream) {
+template <int D, int NB, int KV>
+void launch_nb_kv(int batch, const PartialArgs& a, hipStream_t stream) {
     dim3 grid(a.Hkv, a.rule.slots, batch), block(KV != kKvBf16 ? 64 * kMW8 : kMT);
     const bool paged = a.pages.table != nullptr;
     if (a.q_len > 1) {
         if (paged)
-            hipLaunchKernelGGL((fd_mfma_partial_kernel<D, NB, true, true, KV, MERGE>), grid, block, 0, stream, a);
+            hipLaunchKernelGGL((fd_mfma_partial_kernel<D, NB, true, true, KV>), grid, block, 0, stream, a);
         else
-            hipLaunchKernelGGL((fd_mfma_partial_kernel<D, NB, true, false, KV, MERGE>), grid, block, 0, stream, a);
+            hipLaunchKernelGGL((fd_mfma_partial_kernel<D, NB, true, false, KV>), grid, block, 0, stream, a);
     } else {
         if (paged)
-            hipLaunchKernelGGL((fd_mfma_partial_kernel<D, NB, false, true, KV, MERGE>), grid, block, 0, stream, a);
+            hipLaunchKernelGGL((fd_mfma_partial_kernel<D, NB, false, true, KV>), grid, block, 0, stream, a);
         else
-            hipLaunchKernelGGL((fd_mfma_partial_kernel<D, NB, false, false, KV, MERGE>), grid, block, 0, stream,
-                               a);
+            hipLaunchKernelGGL((fd_mfma_partial_kernel<D, NB, false, false, KV>), grid, block, 0, stream, a);
     }
-}
-
-template <int D, int NB, int KV>
-void launch_nb_kv(int batch, const PartialArgs& a, hipStream_t stream) {
-    if (a.merge && !a.direct)
-        launch_nb_kv_m<D, NB, KV, true>(batch, a, stream);
-    else
-        launch_nb_kv_m<D, NB, KV, false>(batch, a, stream);
 }
 
 template <int D, int NB>

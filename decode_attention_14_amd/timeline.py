@@ -8,10 +8,9 @@ lands, when each wave leaves its block loop, when the workgroups end (100 MHz
 
     python -m decode_attention_14_amd.timeline [--workload gqa_32k] [--kv-fp8 | --kv-int8] [--step]
 
-``--step`` times the whole ``fd_decode_attention`` call instead of the partial
-pass alone; where the partial kernel merges in place, each workgroup also
-records when its partial stores had completed and when its arrival count
-returned, and the last workgroup of each (sequence, KV head) is reported.
+``--step`` times the partial pass inside whole ``fd_decode_attention`` calls
+(partial kernel, then the merge kernel) instead of back-to-back partial
+passes.
 Needs a GPU.  The timeline build computes the same results as ``libfd.so``.
 """
 from __future__ import annotations
@@ -28,9 +27,9 @@ from . import binding as fd
 from .build import TIMELINE_LIB
 from .inputs import WORKLOADS, fp8_scale_for, int8_scale_for, quantize_fp8, quantize_int8, workload_inputs
 
-SLOTS = 16           # per workgroup: start, first block, 8 wave loop exits, end, XCD, merge stamps
+SLOTS = 16           # per workgroup: start, first block, 8 wave loop exits, end, XCD
 MAX_WGS = 4096
-T_START, T_FIRST, T_LOOP, T_END, T_XCC, T_STORED, T_COUNTED, T_LAST = 0, 1, 2, 10, 11, 12, 13, 14
+T_START, T_FIRST, T_LOOP, T_END, T_XCC = 0, 1, 2, 10, 11
 TICK_US = 0.01       # s_memrealtime runs at 100 MHz
 
 
@@ -128,16 +127,6 @@ def main(argv=None) -> int:
             "end_us_per_xcd": {int(x): round(float(end[t[:, T_XCC] == x].mean()), 2)
                                for x in np.unique(t[:, T_XCC])},
         }
-        last = t[:, T_LAST] == 1
-        if args.step and last.any():
-            loop_end = start + loops.max(axis=1)
-            stored = (t[:, T_STORED] - t0) * TICK_US
-            counted = (t[:, T_COUNTED] - t0) * TICK_US
-            row["merging_workgroups"] = int(last.sum())
-            row["last_loop_end_us"] = round(float(loop_end.max()), 2)
-            row["merging: loop end -> stores done us"] = round(float((stored - loop_end)[last].mean()), 2)
-            row["merging: stores done -> counted us"] = round(float((counted - stored)[last].mean()), 2)
-            row["merging: counted -> end us"] = round(float((end - counted)[last].mean()), 2)
         summary.append(row)
         print(json.dumps(row), flush=True)
     keys = ("span_us", "start_spread_us", "first_block_us", "end_after_last_wave_us", "end_spread_us")

@@ -125,11 +125,8 @@ fd_status fd_plan_splits(const fd_dims* dims, const int32_t* cache_lens_host, in
 
 /* fd_workspace_bytes -- bytes of workspace fd_decode_attention needs for
  * `max_splits` partial slots per row (0 when max_splits <= 1 or dims are
- * invalid).  The workspace starts with a header of FD_WORKSPACE_HEADER_BYTES
- * (the arrival counters of the merge inside the partial pass, see
- * fd_decode_attention), followed by o_part, m_part and lse_part as laid out
- * for fd_decode_partials, each starting on a 256-byte boundary. */
-#define FD_WORKSPACE_HEADER_BYTES (256u << 10)
+ * invalid).  The workspace holds o_part, m_part and lse_part as laid out for
+ * fd_decode_partials, each starting on a 256-byte boundary. */
 uint64_t fd_workspace_bytes(const fd_dims* dims, int32_t max_splits);
 
 /* fd_decode_partials -- the first pass only: per-tile partials.
@@ -179,22 +176,10 @@ fd_status fd_combine_splits(int32_t batch, int32_t num_heads, int32_t q_len, int
  * fd_plan_splits); else `plan` (may be NULL: one tile per sequence).  With a
  * single slot the partial kernel writes out and lse directly and no
  * workspace is needed (`workspace` may be NULL).  Otherwise `workspace`
- * (device memory, 256-byte aligned, caller-owned) must hold at least
- * fd_workspace_bytes(dims, slots) bytes, else FD_ERR_WORKSPACE.
- *
- * The merge.  For bf16 queries with up to 32 query rows per KV head
- * (Hq / Hkv * q_len <= 32: decode and short verification chunks, over bf16,
- * FP8, INT8 or paged caches) and at most FD_WORKSPACE_HEADER_BYTES / 128
- * (sequence, KV head) pairs, the partial kernel merges in place: the last of
- * the workgroups of a (sequence, KV head) to finish its tile merges that
- * group's partials in slot order (one launch, bitwise reproducible).  It
- * counts arrivals in the workspace header, which must therefore be all zero
- * before the workspace's first use (allocate it zero-filled); every call
- * leaves the header zero again, so a workspace can be reused without
- * clearing, also under HIP graph replay.  Other calls run a separate merge
- * kernel and do not touch the header.  The rest of the workspace needs no
- * initialisation and is clobbered.  Calls that share a workspace must not run
- * concurrently. */
+ * (device memory, 256-byte aligned, caller-owned, contents irrelevant on
+ * entry and clobbered on return) must hold at least
+ * fd_workspace_bytes(dims, slots) bytes, else FD_ERR_WORKSPACE.  Calls that
+ * share a workspace must not run concurrently. */
 fd_status fd_decode_attention(const fd_dims* dims, const void* q, const void* k_cache,
                               const void* v_cache, const int32_t* cache_lens, float scale,
                               int32_t num_splits, const fd_plan* plan, void* workspace,

@@ -339,13 +339,12 @@ def test_workspace_layout_size():
     d = dims(B=2, Hq=8, Hkv=2, D=64, T=3, Lmax=100, dt=fd.FD_F32)
     rows = 2 * 8 * 3
     S = 5
-    # the header of merge counters, then o_part, m_part, lse_part
-    expect = fd.FD_WORKSPACE_HEADER_BYTES + _up(rows * S * 64 * 4) + 2 * _up(rows * S * 4)
+    expect = _up(rows * S * 64 * 4) + 2 * _up(rows * S * 4)
     assert fd.workspace_bytes(d, S) == expect
     assert fd.workspace_bytes(d, 1) == 0
     d = dims(B=3, Hq=32, Hkv=8, D=128, T=1, Lmax=100, dt=fd.FD_BF16)
     rows = 3 * 32
-    expect = fd.FD_WORKSPACE_HEADER_BYTES + _up(rows * S * 128 * 4) + 2 * _up(rows * S * 4)
+    expect = _up(rows * S * 128 * 4) + 2 * _up(rows * S * 4)
     assert fd.workspace_bytes(d, S) == expect
 
 

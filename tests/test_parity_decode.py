@@ -309,14 +309,8 @@ def test_combine_ragged_splits_per_seq():
 
 
 def test_workspace_reuse_with_garbage_and_changing_shapes():
-    """One workspace reused across shapes, split counts and both merge paths
-    (in the partial kernel and the merge kernel): the documented contract is
-    a zero header of merge counters before the first use (every call leaves
-    it zero) and nothing about the rest, which starts as garbage here.  After
-    the calls the header must be zero again."""
-    say("[case] one workspace (zero header, garbage partial area) reused across shapes and split counts")
+    say("[case] one garbage-filled workspace reused across shapes and split counts")
     ws = torch.full((64 << 20,), 0xFF, dtype=torch.uint8, device="cuda")
-    ws[:fd.FD_WORKSPACE_HEADER_BYTES].zero_()
     cases = [
         (2, 32, 8, 128, 1, 3000, "bf16", [3000, 1234], 7),
         (1, 32, 8, 128, 1, 5000, "bf16", [5000], 40),
@@ -334,7 +328,6 @@ def test_workspace_reuse_with_garbage_and_changing_shapes():
                                            num_splits=S, workspace=ws)
             torch.cuda.synchronize()
             compare(f"reuse case {i} rep {rep}", out, lse, *ref, TOL[dt])
-            assert int(ws[:fd.FD_WORKSPACE_HEADER_BYTES].count_nonzero()) == 0, "merge counters left nonzero"
 
 
 def test_graph_replays_match_eager():
