@@ -30,9 +30,30 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+#include <utility>
+
 #include "fd_device.h"
 #include "fd_internal.h"
 #include "fd_mfma_common.h"
+
+#ifndef FD_WG_TIMELINE
+#define FD_WG_TIMELINE 0
+#endif
+
+// Workgroup timeline of fd_mfma_chunk_kernel (a diagnostic build only,
+// FD_WG_TIMELINE=1, laid out as the decode kernel's): workgroup i of the last
+// launch (dispatch order, i < 4096) leaves at [i * 16] its start, the landing
+// of its first stage, each wave's exit from the stage loop (8 waves), its end
+// and its XCD, in the 100 MHz s_memrealtime clock, and at [12], [13] the
+// shader clock (s_memtime) at the first stage and at wave 0's loop exit.
+#if FD_WG_TIMELINE
+__device__ uint64_t fd_chunk_timeline[4096 * 16];
+extern "C" int fd_debug_chunk_timeline(void* host_dst, uint64_t bytes) {
+    if (bytes > sizeof(fd_chunk_timeline)) bytes = sizeof(fd_chunk_timeline);
+    return (int)hipMemcpyFromSymbol(host_dst, HIP_SYMBOL(fd_chunk_timeline), bytes, 0, hipMemcpyDeviceToHost);
+}
+#endif
 
 namespace fdk {
 namespace {
@@ -100,10 +121,9 @@ __device__ __forceinline__ int cswz(int r, int c) {
 // Start this wave's share of one stage's loads: bytes [off, off + stage) of
 // the K and V tiles, `left` bytes of the tile remaining from off (none if
 // left <= 0; rows past it read as zeros), into the stage buffer at dst.
-template <int D>
+template <class G>
 __device__ __forceinline__ void chunk_load_stage(const char* kt, const char* vt, int left, int off, char* dst,
                                                  const uint32_t* dma_off, const int* lds_off) {
-    using G = CGeo<D>;
     const uint32_t n = left > 0 ? (uint32_t)left : 0u;
     const __amdgpu_buffer_rsrc_t rk = tile_rsrc(kt + off, n);
     const __amdgpu_buffer_rsrc_t rv = tile_rsrc(vt + off, n);
@@ -121,11 +141,10 @@ __device__ __forceinline__ void chunk_load_stage(const char* kt, const char* vt,
 // caches: kt/vt point at the KV head's base and each load instruction looks
 // up the page of its RPI rows (koff[k]: the instruction's first key within
 // the stage).
-template <int D, bool PAGED>
+template <class G, bool PAGED>
 __device__ __forceinline__ void chunk_stage_at(const PagedKV& pk, const int32_t* tbl, const char* kt, const char* vt,
                                                int lo, int kend, int j, int rsb, char* dst, const uint32_t* dma_off,
                                                const int* lds_off, const int* koff) {
-    using G = CGeo<D>;
     if constexpr (PAGED) {
 #pragma unroll
         for (int k = 0; k < G::DPW; ++k) {
@@ -140,7 +159,7 @@ __device__ __forceinline__ void chunk_stage_at(const PagedKV& pk, const int32_t*
         }
     } else {
         const int off = j * G::SKEYS * G::ROWB;
-        chunk_load_stage<D>(kt, vt, (kend - lo) * G::ROWB - off, off, dst, dma_off, lds_off);
+        chunk_load_stage<G>(kt, vt, (kend - lo) * G::ROWB - off, off, dst, dma_off, lds_off);
     }
 }
 
@@ -243,11 +262,14 @@ __device__ __forceinline__ bf16x8_t lds_b128(uint32_t addr) {
 }
 
 // Transposed read (see tr_read) at a lane address plus a compile-time offset.
+// The instruction's offset field holds 16 bits: a larger offset (later
+// stages of a deep ring) moves its high part into the address.
 template <int OFF>
 __device__ __forceinline__ bf16x4_t tr_read_at(uint32_t addr) {
-    static_assert(OFF >= 0 && OFF < 65536, "ds offset field");
+    static_assert(OFF >= 0, "ds offset");
+    constexpr int HI = OFF & ~0x7fff;
     bf16x4_t r;
-    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr + HI), "i"(OFF - HI));
     return r;
 }
 
@@ -415,7 +437,7 @@ __device__ __forceinline__ void chunk_step(bool edge, const uint32_t (&ka)[CGeo<
 }
 
 template <int D, bool PAGED, int KV>
-__global__ __launch_bounds__(kCT) void fd_mfma_chunk_kernel(PartialArgs a) {
+__global__ __launch_bounds__(kCT) void fd_mfma_chunk8_kernel(PartialArgs a) {
     using G = CGeo<D>;
     using G8 = CGeo8<D>;
     constexpr bool C8 = KV != kKvBf16;  // one-byte codes
@@ -598,7 +620,7 @@ __global__ __launch_bounds__(kCT) void fd_mfma_chunk_kernel(PartialArgs a) {
     } else {
 #pragma unroll
         for (int j = 0; j < kCNS - 1; ++j)
-            chunk_stage_at<D, PAGED>(a.pages, tbl, kt, vt, lo, kend, j, rsb, smem + j * G::STGB, dma_off, lds_off,
+            chunk_stage_at<G, PAGED>(a.pages, tbl, kt, vt, lo, kend, j, rsb, smem + j * G::STGB, dma_off, lds_off,
                                      koff);
     }
 
@@ -627,7 +649,7 @@ __global__ __launch_bounds__(kCT) void fd_mfma_chunk_kernel(PartialArgs a) {
             } else {
                 wait_vmcnt_le<(kCNS - 1) * 2 * G::DPW>();  // this wave's loads of stage j
                 __syncthreads();                           // everyone's; stage j - 1 is free
-                chunk_stage_at<D, PAGED>(a.pages, tbl, kt, vt, lo, kend, j + kCNS - 1, rsb,
+                chunk_stage_at<G, PAGED>(a.pages, tbl, kt, vt, lo, kend, j + kCNS - 1, rsb,
                                          smem + ((u + kCNS - 1) % kCNS) * G::STGB, dma_off, lds_off, koff);
             }
             const int key0 = lo + j * G::SKEYS + kh * kCBK;
@@ -715,18 +737,525 @@ __global__ __launch_bounds__(kCT) void fd_mfma_chunk_kernel(PartialArgs a) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// bf16 caches: the software-pipelined chunk kernel (fd_mfma_chunk_kernel).
+//
+// The same work split as fd_mfma_chunk8_kernel -- eight waves, four row
+// groups of 32 rows times two key halves, 64-key stages of which wave (rg,
+// kh) takes block kh, the halves merged through LDS at the end -- but inside
+// a wave the work of consecutive blocks overlaps: block j + 1's score product
+// runs on the matrix core while block j's softmax runs on the vector units
+// (two score tiles in flight), then block j's P.V product follows.  That
+// needs block j + 1's keys before block j's softmax, so the ring has kPNS
+// stages and the loads of stage t + kPNS - 2 start right after the barrier of
+// stage t (the barrier shows every wave done with the slot they refill).  K
+// and V keep separate regions of the ring, so every operand offset fits the
+// LDS instructions' 16-bit offset field.
+
+constexpr int kPT = 512;               // threads per workgroup
+constexpr int kPW = kPT / 64;          // waves
+constexpr int kPRG = 4;                // row groups of 32 rows
+static_assert(kPRG * 32 == kChunkTileRows, "row tile of the chunk kernel");
+#ifndef FD_CHUNK_PIPE_STAGES
+#define FD_CHUNK_PIPE_STAGES 3
+#endif
+constexpr int kPNS = FD_CHUNK_PIPE_STAGES;
+static_assert(kPNS >= 3 && kPNS <= 4, "ring stages of the pipelined chunk kernel");
+// Vector instructions the scheduler places after each score instruction.
+#ifndef FD_PIPE_VALU_PER_MFMA
+#define FD_PIPE_VALU_PER_MFMA 10
+#endif
+
+template <int D>
+struct PGeo {
+    static constexpr int ROWB = 2 * D;
+    static constexpr int CH = ROWB / 16;            // 16-byte chunks per row
+    static constexpr int RPI = 64 / CH;             // rows per 1 KiB load instruction
+    static constexpr int IPB = kCBK / RPI;          // load instructions per block per tensor
+    static constexpr int BLKB = kCBK * ROWB;        // bytes per block per tensor
+    static constexpr int SKB = 2;                   // blocks per stage (key halves)
+    static constexpr int SKEYS = SKB * kCBK;        // keys per stage
+    static constexpr int STGB = SKB * BLKB;         // bytes per stage per tensor
+    static constexpr int VREG = kPNS * STGB;        // V region after the K region
+    static constexpr int NDMA = SKB * IPB;          // load instructions per tensor per stage
+    static constexpr int DPW = NDMA / kPW;          // per wave, per tensor
+    static constexpr int KS = D / 16;               // k-steps of S^T = K Q^T
+    static constexpr int DB = D / 32;               // 32-dim blocks of O^T
+    static_assert(NDMA % kPW == 0 && DPW >= 1, "stage loads split evenly over the waves");
+};
+
+// Stage j of the tile [lo, kend) into ring slot `slot`: K rows into the K
+// region, V rows into the V region (see chunk_stage_at).
+template <int D, bool PAGED>
+__device__ __forceinline__ void pipe_stage(const PagedKV& pk, const int32_t* tbl, const char* kt, const char* vt,
+                                           int lo, int kend, int j, int rsb, char* smem, int slot,
+                                           const uint32_t* dma_off, const int* lds_off, const int* koff) {
+    using G = PGeo<D>;
+    char* dk = smem + slot * G::STGB;
+    char* dv = smem + G::VREG + slot * G::STGB;
+#pragma unroll
+    for (int k = 0; k < G::DPW; ++k) {
+        __amdgpu_buffer_rsrc_t rk, rv;
+        uint32_t off_lane = dma_off[k];
+        if constexpr (PAGED) {
+            int64_t off;
+            const uint32_t n = paged_rows(pk, tbl, lo + j * G::SKEYS + koff[k], G::RPI, kend, rsb, G::ROWB, &off);
+            rk = tile_rsrc(kt + off * 2, n);
+            rv = tile_rsrc(vt + off * 2, n);
+        } else {
+            const int off = j * G::SKEYS * G::ROWB;
+            const int left = (kend - lo) * G::ROWB - off;
+            const uint32_t n = left > 0 ? (uint32_t)left : 0u;
+            rk = tile_rsrc(kt + off, n);
+            rv = tile_rsrc(vt + off, n);
+        }
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t*)(dk + lds_off[k]), 16, off_lane, 0, 0, FD_LOAD_AUX);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)(dv + lds_off[k]), 16, off_lane, 0, 0, FD_LOAD_AUX);
+    }
+}
+
+// max and sum of x over lanes i and i ^ 32 (the two halves of a 32x32 tile
+// hold the same rows); the swap hands every lane the pair (x of the low
+// lane, x of the high lane), so both lanes get the same bits.
+__device__ __forceinline__ float xor32_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// The vector part of one block's online softmax (as chunk_softmax) without
+// branches, so that the scheduler can place it between the matrix
+// instructions of the next block's scores: statistics, the rescale factor
+// alpha, the weights pr, their bf16 head ph and its share of the running
+// sum.  lo says whether the block also needs its remainder (pipe_remainder).
+__device__ __forceinline__ void pipe_softmax(const f32x16_t& st, float c, float& m, float& l, float& mx, float& alpha,
+                                             bool& moved, float (&pr)[16], bf16x8_t (&ph)[2], bool& lo) {
+    float sm = st[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) sm = __builtin_elementwise_maximum(sm, st[r]);
+    const float bm = sm == -INFINITY ? -INFINITY : sm * c;
+    mx = fmaxf(mx, bm);
+    moved = __any(bm > m + kTau);
+    const float bw = xor32_max(bm);
+    const float mn = moved ? fmaxf(m, bw) : m;
+    alpha = m == -INFINITY ? 0.f : fast_exp2(m - mn);
+    m = mn;
+    l *= alpha;
+    const float mref = m == -INFINITY ? 0.f : m;
+    lo = __any(fast_exp2(bm - mref) * 16.f > l);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) pr[r] = fast_exp2(fmaf(st[r], c, -mref));
+    const bf16x2_t ones = {(__bf16)1.f, (__bf16)1.f};
+    bf16x2_t h2[8];
+    float bs = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        h2[i] = __builtin_convertvector(f32x2_t{pr[2 * i], pr[2 * i + 1]}, bf16x2_t);
+        bs = __builtin_amdgcn_fdot2_f32_bf16(h2[i], ones, bs, false);
+    }
+    ph[0] = pack8(h2[0], h2[1], h2[2], h2[3]);
+    ph[1] = pack8(h2[4], h2[5], h2[6], h2[7]);
+    l += bs;
+}
+
+// The bf16 remainder pl = pr - ph of a block's weights, and its share of the
+// running sum (see chunk_softmax for when it is taken).
+__device__ __forceinline__ void pipe_remainder(const float (&pr)[16], const bf16x8_t (&ph)[2], bf16x8_t (&pl)[2],
+                                               float& l) {
+    const bf16x2_t ones = {(__bf16)1.f, (__bf16)1.f};
+    bf16x2_t l2[8];
+    float bs = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const bf16x8_t& h = ph[i / 4];
+        const f32x2_t d = {pr[2 * i] - (float)h[2 * (i % 4)], pr[2 * i + 1] - (float)h[2 * (i % 4) + 1]};
+        l2[i] = __builtin_convertvector(d, bf16x2_t);
+        bs = __builtin_amdgcn_fdot2_f32_bf16(l2[i], ones, bs, false);
+    }
+    pl[0] = pack8(l2[0], l2[1], l2[2], l2[3]);
+    pl[1] = pack8(l2[4], l2[5], l2[6], l2[7]);
+    l += bs;
+}
+
+// Block j of this wave: its scores are in stc (complete); block j + 1's K
+// operands in kf (awaited), block j's V operands in vf (read, awaited here).
+// Computes block j + 1's scores into stn while running block j's softmax,
+// then block j's P.V product.  Keys of block j at or past rend are masked
+// when `edge`.
+template <int D>
+__device__ __forceinline__ void pipe_block(bool edge, f32x16_t& stc, f32x16_t& stn, const bf16x8_t (&kf)[PGeo<D>::KS],
+                                           const bf16x8_t (&qf)[PGeo<D>::KS], bf16x8_t (&vf)[PGeo<D>::DB * 2],
+                                           f32x16_t (&acc)[PGeo<D>::DB], float& m, float& l, float& mx, int key0,
+                                           int rend, float c, int hl) {
+    using G = PGeo<D>;
+    if (edge) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            if (key0 + 8 * (r >> 2) + 4 * hl + (r & 3) >= rend) stc[r] = -INFINITY;
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) stn[r] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < G::KS; ++ks) stn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], stn, 0, 0, 0);
+    float alpha, pr[16];
+    bool moved, lo;
+    bf16x8_t ph[2], pl[2];
+    pipe_softmax(stc, c, m, l, mx, alpha, moved, pr, ph, lo);
+    // block j + 1's score instructions with block j's softmax between them
+#pragma unroll
+    for (int i = 0; i < G::KS; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, FD_PIPE_VALU_PER_MFMA, 0);
+    }
+    // The rare paths read their inputs through register barriers inside the
+    // branch, so the compiler cannot compute them on every block instead.
+    if (lo) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) asm volatile("" : "+v"(pr[r]));
+        pipe_remainder(pr, ph, pl, l);
+    }
+    lds_settle8(vf);
+    if (moved) {
+        float al = alpha;
+        asm volatile("" : "+v"(al));
+#pragma unroll
+        for (int db = 0; db < G::DB; ++db) acc[db] *= al;
+    }
+    chunk_pv<D>(vf, ph, acc);
+    if (lo) chunk_pv<D>(vf, pl, acc);
+}
+
+// K operands of a block at K-region offset OFF (LDS addresses ka).
+template <int D, int OFF>
+__device__ __forceinline__ void pipe_k_reads(const uint32_t (&ka)[PGeo<D>::KS], bf16x8_t (&kf)[PGeo<D>::KS]) {
+#pragma unroll
+    for (int ks = 0; ks < PGeo<D>::KS; ++ks) kf[ks] = lds_b128<OFF>(ka[ks]);
+}
+
+// f(integral_constant<int, 0>), f(.. 1), ..., f(.. N - 1) in order, stopping
+// after the first call that returns false.
+template <class F, int... Us>
+__device__ __forceinline__ void unrolled_seq(F& f, std::integer_sequence<int, Us...>) {
+    (void)(f(std::integral_constant<int, Us>{}) && ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void unrolled(F& f) {
+    unrolled_seq(f, std::make_integer_sequence<int, N>{});
+}
+
+template <int D, bool PAGED>
+__global__ __launch_bounds__(kPT) void fd_mfma_chunk_kernel(PartialArgs a) {
+#if FD_WG_TIMELINE
+    const uint64_t tl_start = __builtin_amdgcn_s_memrealtime();
+    uint64_t tl_first = 0;
+    uint64_t* tl_row = nullptr;
+    {
+        const uint32_t i = blockIdx.y * gridDim.x + blockIdx.x;
+        if (i < 4096u) tl_row = fd_chunk_timeline + (uint64_t)i * 16;
+    }
+#endif
+    using G = PGeo<D>;
+    constexpr int NS = kPNS;
+    constexpr int RS = D + 4;  // padded row stride of the merge area (floats)
+    constexpr int RINGB = 2 * NS * G::STGB;
+    constexpr int MERGEB = kPRG * (32 * RS + 3 * 32) * 4;
+    __shared__ __attribute__((aligned(16))) char smem[RINGB > MERGEB ? RINGB : MERGEB];
+
+    // Grid order as in fd_mfma_chunk8_kernel: the row tiles of one (KV head,
+    // tile) next to each other, one contiguous range of them per XCD.
+    const uint32_t nx = gridDim.x;
+    uint32_t li = blockIdx.x;
+    if ((nx & 7u) == 0) li = (li & 7u) * (nx >> 3) + (li >> 3);
+    const int rt = (int)(li % (uint32_t)a.row_blocks);
+    li /= (uint32_t)a.row_blocks;
+    const int s = (int)(li % (uint32_t)a.rule.slots);
+    const int g = (int)(li / (uint32_t)a.rule.slots);
+    const int b = blockIdx.y;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = (int)uniform((uint32_t)(tid >> 6));
+    const int rg = w % kPRG;   // row group
+    const int kh = w / kPRG;   // key half
+    const int hl = lane >> 5;  // lane half: G of the 32x32 layouts
+    const int col = lane & 31;
+
+    int L = a.cache_lens[b];
+    L = L < 0 ? 0 : (L > a.Lmax ? a.Lmax : L);
+    int lo, hi, S;
+    tile_of(a.rule, L, s, lo, hi, S);
+    lo = (int)uniform((uint32_t)lo);
+    hi = (int)uniform((uint32_t)hi);
+
+    const int R = a.rows;
+    const int n_rep = a.n_rep;
+    const int q_len = a.q_len;
+    const int p0 = rt * kChunkRows;
+    const int64_t rowbase = ((int64_t)b * a.Hq + (int64_t)g * n_rep) * q_len;
+    const int slots = a.rule.slots;
+    const int nrows = min(kChunkRows, R - p0);
+
+    if (s >= S) {
+        for (int idx = tid; idx < nrows; idx += kPT) {
+            const int p = p0 + idx;
+            const int64_t row = rowbase + (int64_t)(p % n_rep) * q_len + p / n_rep;
+            if (a.direct) {
+                uint4* o = reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(a.out) + row * D);
+                for (int k = 0; k < D / 8; ++k) o[k] = make_uint4(0, 0, 0, 0);
+                if (a.lse) a.lse[row] = -INFINITY;
+            } else {
+                a.m_part[row * slots + s] = -INFINITY;
+                a.lse_part[row * slots + s] = -INFINITY;
+            }
+        }
+        return;
+    }
+
+    // Keys the tile's rows can see inside [lo, hi): the last row's limit
+    // bounds them all; masking starts at the first row's limit.
+    const int t_first = p0 / n_rep;
+    const int t_last = (p0 + nrows - 1) / n_rep;
+    const int kend = max(lo, min(hi, L - q_len + t_last + 1));
+    const int mask_from = max(lo, min(hi, L - q_len + t_first + 1));
+
+    // This lane's query row (column of the 32x32 layouts).
+    const int p = p0 + rg * 32 + col;
+    const bool valid = p < R;
+    const int t = p / n_rep;
+    const int64_t mrow = rowbase + (int64_t)(p % n_rep) * q_len + t;
+    const int rend = valid ? max(lo, min(hi, L - q_len + t + 1)) : lo;
+    // Scores are scaled inside the exponent's FMA, which needs c > 0 (see
+    // fd_mfma_chunk8_kernel).
+    const bool neg = a.qk_scale < 0.f;
+    const float c = fmaxf(fabsf(a.qk_scale), 1e-30f);
+    const uint32_t flip = neg ? 0x80008000u : 0u;
+    bf16x8_t qf[G::KS];
+#pragma unroll
+    for (int ks = 0; ks < G::KS; ++ks) {
+        uint4 x = make_uint4(0, 0, 0, 0);
+        if (valid)
+            x = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q) + mrow * D + 16 * ks + 8 * hl);
+        x.x ^= flip; x.y ^= flip; x.z ^= flip; x.w ^= flip;
+        qf[ks] = __builtin_bit_cast(bf16x8_t, x);
+    }
+
+    f32x16_t acc[G::DB];
+#pragma unroll
+    for (int db = 0; db < G::DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
+    float m = -INFINITY, l = 0.f, mx = -INFINITY;
+
+    const char* kt;
+    const char* vt;
+    int rsb;  // bytes from one key row of the head to the next
+    const int32_t* tbl = nullptr;
+    if constexpr (PAGED) {
+        kt = static_cast<const char*>(a.k) + g * a.pages.head_stride * 2;
+        vt = static_cast<const char*>(a.v) + g * a.pages.head_stride * 2;
+        rsb = a.pages.row_stride * 2;
+        tbl = a.pages.table + (int64_t)b * a.pages.max_pages;
+    } else {
+        const int64_t tile_row = ((int64_t)b * a.Hkv + g) * a.Lmax + lo;
+        kt = static_cast<const char*>(a.k) + tile_row * G::ROWB;
+        vt = static_cast<const char*>(a.v) + tile_row * G::ROWB;
+        rsb = G::ROWB;
+    }
+    const int nst = (kend - lo + G::SKEYS - 1) / G::SKEYS;
+
+    // Load instruction k of this wave fills RPI rows of block bb of a stage;
+    // lane l takes row l / CH, global chunk (l % CH) ^ swizzle.
+    uint32_t dma_off[G::DPW];
+    int lds_off[G::DPW];
+    int koff[G::DPW];
+#pragma unroll
+    for (int k = 0; k < G::DPW; ++k) {
+        const int n = w + k * kPW;
+        const int bb = n / G::IPB;
+        const int i = n - bb * G::IPB;
+        const int r = i * G::RPI + lane / G::CH;
+        const int cg = (lane % G::CH) ^ cswf<G::CH>(r);
+        koff[k] = bb * kCBK + i * G::RPI;
+        dma_off[k] = (uint32_t)((PAGED ? lane / G::CH : koff[k] + lane / G::CH) * rsb + cg * 16);
+        lds_off[k] = bb * G::BLKB + i * 1024;
+    }
+    auto stage = [&](int j, int slot) {
+        pipe_stage<D, PAGED>(a.pages, tbl, kt, vt, lo, kend, j, rsb, smem, slot, dma_off, lds_off, koff);
+    };
+
+    // Lane-constant LDS addresses of this wave's K and V operands in ring
+    // slot 0 (block kh); other slots add compile-time offsets.
+    uint32_t ka[G::KS];
+    uint32_t va[G::DB][2];
+    {
+        const uint32_t kbase = lds_addr(smem) + kh * G::BLKB;
+#pragma unroll
+        for (int ks = 0; ks < G::KS; ++ks) ka[ks] = kbase + cswz<D>(col, 2 * ks + hl);
+        const int g16 = lane >> 4;
+        const int i16 = lane & 15;
+        const int q4 = i16 & 3;
+#pragma unroll
+        for (int db = 0; db < G::DB; ++db)
+#pragma unroll
+            for (int t2 = 0; t2 < 2; ++t2)
+                va[db][t2] = kbase + G::VREG +
+                             cswz<D>(8 * t2 + 4 * hl + (i16 >> 2), (32 * db + 16 * (g16 & 1)) / 8 + (q4 >> 1)) +
+                             8 * (q4 & 1);
+    }
+
+    // Stages 0 .. NS - 3 in flight; after the barrier of stage t the loads of
+    // stage t + NS - 2 start (into the slot of stage t - 2, which every wave
+    // is done with).  This wave's block of stage t is at ring slot t % NS.
+#pragma unroll
+    for (int j = 0; j < NS - 2; ++j) stage(j, j);
+    wait_vmcnt_le<(NS - 3) * 2 * G::DPW>();
+    __syncthreads();
+#if FD_WG_TIMELINE
+    tl_first = __builtin_amdgcn_s_memrealtime();
+    const uint64_t tl_clk0 = __builtin_amdgcn_s_memtime();
+#endif
+    stage(NS - 2, NS - 2);
+    f32x16_t st[2];
+    bf16x8_t kf[G::KS], vf[G::DB * 2];
+    pipe_k_reads<D, 0>(ka, kf);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) st[0][r] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < G::KS; ++ks) st[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], st[0], 0, 0, 0);
+    chunk_v_reads<D, 0>(va, vf);
+
+    // Unrolled by NS stages, so that ring slots and the score buffer are
+    // compile-time constants (U: the stage's place in the unrolled run).
+    for (int j0 = 0; j0 < nst; j0 += 2 * NS) {
+        const auto step = [&](auto UC) -> bool {
+            constexpr int U = decltype(UC)::value;
+            const int j = j0 + U;
+            if (j >= nst) return false;
+            // Stage j + 1: landed for everyone after the barrier, which also
+            // frees the slot of stage j - 1 for stage j + NS - 1.
+            if (j + 1 < nst) {
+                wait_vmcnt_le<(NS - 3) * 2 * G::DPW>();
+                __syncthreads();
+                stage(j + NS - 1, (U + NS - 1) % NS);
+            }
+            pipe_k_reads<D, ((U + 1) % NS) * G::STGB>(ka, kf);
+            const int key0 = lo + j * G::SKEYS + kh * kCBK;
+            const bool edge = key0 + kCBK > mask_from;
+            pipe_block<D>(edge, st[U % 2], st[1 - U % 2], kf, qf, vf, acc, m, l, mx, key0, rend, c, hl);
+            chunk_v_reads<D, ((U + 1) % NS) * G::STGB>(va, vf);
+            return true;
+        };
+        unrolled<2 * NS>(step);
+    }
+    wait_vmcnt_le<0>();
+    lds_settle8(vf);
+#if FD_WG_TIMELINE
+    {
+        const uint64_t t = __builtin_amdgcn_s_memrealtime();
+        const uint64_t clk = __builtin_amdgcn_s_memtime();
+        if (tl_row && lane == 0) tl_row[2 + w] = t;
+        if (tl_row && tid == 0) {
+            tl_row[12] = tl_clk0;
+            tl_row[13] = clk;
+        }
+    }
+#endif
+
+    // Per-row totals over the two lane halves; then merge the key halves.
+    l = xor32_sum(l);
+    mx = xor32_max(mx);
+    __syncthreads();  // the ring is free
+    float* sm_acc = reinterpret_cast<float*>(smem);  // [kPRG][32][RS]
+    float* sm_m = sm_acc + kPRG * 32 * RS;           // [kPRG][32]
+    float* sm_l = sm_m + kPRG * 32;
+    float* sm_x = sm_l + kPRG * 32;
+    if (kh == 1) {
+        float* o = sm_acc + (rg * 32 + col) * RS;
+#pragma unroll
+        for (int db = 0; db < G::DB; ++db)
+#pragma unroll
+            for (int a4 = 0; a4 < 4; ++a4)
+                *reinterpret_cast<f32x4_t*>(o + 32 * db + 8 * a4 + 4 * hl) =
+                    f32x4_t{acc[db][4 * a4], acc[db][4 * a4 + 1], acc[db][4 * a4 + 2], acc[db][4 * a4 + 3]};
+        if (hl == 0) {
+            sm_m[rg * 32 + col] = m;
+            sm_l[rg * 32 + col] = l;
+            sm_x[rg * 32 + col] = mx;
+        }
+    }
+    __syncthreads();
+    if (kh == 1 || !valid) return;
+    const float m2 = sm_m[rg * 32 + col];
+    const float M = fmaxf(m, m2);
+    const float f1 = m == -INFINITY ? 0.f : fast_exp2(m - M);
+    const float f2 = m2 == -INFINITY ? 0.f : fast_exp2(m2 - M);
+    const float den = l * f1 + sm_l[rg * 32 + col] * f2;
+    const float X = fmaxf(mx, sm_x[rg * 32 + col]);
+    const bool empty = M == -INFINITY;
+    const float inv = empty ? 0.f : 1.f / den;
+    const float lse_v = empty ? -INFINITY : (M + log2f(den)) * kLn2;
+    const float* o2 = sm_acc + (rg * 32 + col) * RS;
+    if (a.direct) {
+        uint16_t* o = reinterpret_cast<uint16_t*>(a.out) + mrow * D;
+#pragma unroll
+        for (int db = 0; db < G::DB; ++db)
+#pragma unroll
+            for (int a4 = 0; a4 < 4; ++a4) {
+                const int d = 32 * db + 8 * a4 + 4 * hl;
+                const f32x4_t y = *reinterpret_cast<const f32x4_t*>(o2 + d);
+                float v[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = (acc[db][4 * a4 + e] * f1 + y[e] * f2) * inv;
+                uint2 packed;
+                packed.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+                packed.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+                *reinterpret_cast<uint2*>(o + d) = packed;
+            }
+        if (hl == 0 && a.lse) a.lse[mrow] = lse_v;
+    } else {
+        if (!empty) {
+            float* o = a.o_part + (mrow * slots + s) * D;
+#pragma unroll
+            for (int db = 0; db < G::DB; ++db)
+#pragma unroll
+                for (int a4 = 0; a4 < 4; ++a4) {
+                    const int d = 32 * db + 8 * a4 + 4 * hl;
+                    const f32x4_t y = *reinterpret_cast<const f32x4_t*>(o2 + d);
+                    f32x4_t v;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[e] = (acc[db][4 * a4 + e] * f1 + y[e] * f2) * inv;
+                    *reinterpret_cast<f32x4_t*>(o + d) = v;
+                }
+        }
+        if (hl == 0) {
+            a.m_part[mrow * slots + s] = empty ? -INFINITY : X * kLn2;
+            a.lse_part[mrow * slots + s] = lse_v;
+        }
+    }
+#if FD_WG_TIMELINE
+    if (tid == 0 && tl_row) {
+        tl_row[0] = tl_start;
+        tl_row[1] = tl_first;
+        tl_row[10] = __builtin_amdgcn_s_memrealtime();
+        tl_row[11] = __builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20);  // HW_REG_XCC_ID bits 3:0
+    }
+#endif
+}
+
 template <int D, bool PAGED>
 void launch_chunk_p(int batch, const PartialArgs& a, hipStream_t stream) {
-    dim3 grid((uint32_t)a.rule.slots * a.Hkv * a.row_blocks, batch), block(kCT);
+    const uint32_t x = (uint32_t)a.rule.slots * a.Hkv * a.row_blocks;
     switch (a.kv_codes) {
         case kKvE4M3:
-            hipLaunchKernelGGL((fd_mfma_chunk_kernel<D, PAGED, kKvE4M3>), grid, block, 0, stream, a);
+            hipLaunchKernelGGL((fd_mfma_chunk8_kernel<D, PAGED, kKvE4M3>), dim3(x, batch), dim3(kCT), 0, stream, a);
             break;
         case kKvInt8:
-            hipLaunchKernelGGL((fd_mfma_chunk_kernel<D, PAGED, kKvInt8>), grid, block, 0, stream, a);
+            hipLaunchKernelGGL((fd_mfma_chunk8_kernel<D, PAGED, kKvInt8>), dim3(x, batch), dim3(kCT), 0, stream, a);
             break;
         default:
-            hipLaunchKernelGGL((fd_mfma_chunk_kernel<D, PAGED, kKvBf16>), grid, block, 0, stream, a);
+            hipLaunchKernelGGL((fd_mfma_chunk_kernel<D, PAGED>), dim3(x, batch), dim3(kPT), 0, stream, a);
             break;
     }
 }

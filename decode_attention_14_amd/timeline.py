@@ -1,4 +1,4 @@
-"""Workgroup timeline of the matrix-core decode kernel (diagnostic).
+"""Workgroup timeline of the matrix-core decode and chunk kernels (diagnostic).
 
 Runs a workload's partial pass through ``libfd_timeline.so`` (the library
 built with FD_WG_TIMELINE=1; ``build.build_timeline()``) and prints where a
@@ -28,8 +28,10 @@ from .build import TIMELINE_LIB
 from .inputs import WORKLOADS, fp8_scale_for, int8_scale_for, quantize_fp8, quantize_int8, workload_inputs
 
 SLOTS = 16           # per workgroup: start, first block, 8 wave loop exits, end, XCD
+CHUNK_ROW_TILE = 128  # packed query rows per workgroup of the chunk kernel
 MAX_WGS = 4096
 T_START, T_FIRST, T_LOOP, T_END, T_XCC = 0, 1, 2, 10, 11
+T_CLK0, T_CLK1 = 12, 13  # chunk kernel: shader clock at the first stage and at wave 0's loop exit
 TICK_US = 0.01       # s_memrealtime runs at 100 MHz
 
 
@@ -45,19 +47,22 @@ def main(argv=None) -> int:
         print("the timeline needs a GPU", file=sys.stderr)
         return 1
     lib = fd.use_library(TIMELINE_LIB)
-    lib.fd_debug_timeline.argtypes = [ctypes.c_void_p, ctypes.c_uint64]
-    lib.fd_debug_timeline.restype = ctypes.c_int
+    for name in ("fd_debug_timeline", "fd_debug_chunk_timeline"):
+        getattr(lib, name).argtypes = [ctypes.c_void_p, ctypes.c_uint64]
+        getattr(lib, name).restype = ctypes.c_int
 
     w = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     q, k, v, cl = workload_inputs(w)
     plan = fd.plan_for(q, k, cl)
     rows = w.num_q_heads // w.num_kv_heads * w.q_len
-    if w.dtype != "bf16" or rows > 32:
-        print("the timeline covers the matrix-core decode kernel (bf16 queries, up to 32 rows per KV head)",
-              file=sys.stderr)
-        return 2
     codes = "fp8" if args.kv_fp8 else "int8" if args.kv_int8 else None
+    chunk = rows > 32
+    if w.dtype != "bf16" or (chunk and codes):
+        print("the timeline covers the matrix-core decode kernel (bf16 queries, up to 32 rows per KV head) and "
+              "the pipelined chunk kernel (bf16 queries and caches, more rows)", file=sys.stderr)
+        return 2
+    read_timeline = lib.fd_debug_chunk_timeline if chunk else lib.fd_debug_timeline
     if codes:
         scale_for, quantize = (fp8_scale_for, quantize_fp8) if codes == "fp8" else (int8_scale_for, quantize_int8)
         ks, vs = scale_for(k), scale_for(v)
@@ -92,11 +97,12 @@ def main(argv=None) -> int:
             fd.decode_partials(qd, kd, vd, cld, scale=w.scale, plan=plan.plan, o_part=o_part, m_part=m_part,
                                lse_part=l_part)
 
-    nwg = w.num_kv_heads * slots * w.batch
+    row_tiles = -(-rows // CHUNK_ROW_TILE) if chunk else 1
+    nwg = w.num_kv_heads * slots * row_tiles * w.batch
     if nwg > MAX_WGS:
         print(f"{nwg} workgroups; the timeline keeps the first {MAX_WGS}", file=sys.stderr)
         nwg = MAX_WGS
-    waves = 8 if codes else 4
+    waves = 8 if codes or chunk else 4
     for i in range(20):
         launch(i)
     torch.cuda.synchronize()
@@ -108,8 +114,8 @@ def main(argv=None) -> int:
         launch(2 * rep)          # the launch before keeps the clocks up
         launch(2 * rep + 1)
         torch.cuda.synchronize()
-        if lib.fd_debug_timeline(buf.ctypes.data, buf.nbytes) != 0:
-            raise RuntimeError("fd_debug_timeline failed")
+        if read_timeline(buf.ctypes.data, buf.nbytes) != 0:
+            raise RuntimeError("reading the workgroup timeline failed")
         t = buf.reshape(nwg, SLOTS).astype(np.int64)
         t0 = t[:, T_START].min()
         start = (t[:, T_START] - t0) * TICK_US
@@ -121,15 +127,21 @@ def main(argv=None) -> int:
             "span_us": round(float(end.max()), 2),
             "start_spread_us": round(float(start.max()), 2),
             "first_block_us": round(float(first.mean()), 2),
+            "loop_us": round(float((loops.max(axis=1) - first).mean()), 2),
+            "loop_us_max": round(float((loops.max(axis=1) - first).max()), 2),
             "wave_loop_end_us": [round(float(x), 2) for x in loops.mean(axis=0)],
             "end_after_last_wave_us": round(float(after_last.mean()), 2),
+            **({"loop_clock_mhz": round(float(np.median((t[:, T_CLK1] - t[:, T_CLK0]) /
+                                                          np.maximum(1, t[:, T_LOOP] - t[:, T_FIRST]) / TICK_US)), 1)}
+               if chunk else {}),
             "end_spread_us": round(float(end.max() - end.min()), 2),
             "end_us_per_xcd": {int(x): round(float(end[t[:, T_XCC] == x].mean()), 2)
                                for x in np.unique(t[:, T_XCC])},
         }
         summary.append(row)
         print(json.dumps(row), flush=True)
-    keys = ("span_us", "start_spread_us", "first_block_us", "end_after_last_wave_us", "end_spread_us")
+    keys = ("span_us", "start_spread_us", "first_block_us", "loop_us", "loop_us_max", "end_after_last_wave_us",
+            "end_spread_us") + (("loop_clock_mhz",) if chunk else ())
     print("median over launches:", json.dumps({k: float(np.median([r[k] for r in summary])) for k in keys}),
           flush=True)
     return 0

@@ -42,13 +42,15 @@ def test_exports_every_declared_symbol(lib):
 
 def test_timeline_diagnostic_only_in_its_own_build(lib):
     """The workgroup-timeline diagnostic (FD_WG_TIMELINE=1) is a separate
-    build with the same ABI plus fd_debug_timeline; libfd.so has none of it."""
+    build with the same ABI plus fd_debug_timeline and fd_debug_chunk_timeline;
+    libfd.so has none of it."""
     assert not hasattr(lib, "fd_debug_timeline")
+    assert not hasattr(lib, "fd_debug_chunk_timeline")
     from decode_attention_14_amd.build import TIMELINE_LIB
     if not os.path.exists(TIMELINE_LIB):
         pytest.skip("the timeline build is made by __graft_entry__.build()")
     tl = ctypes.CDLL(TIMELINE_LIB)
-    for name in fd.EXPORTS + ("fd_debug_timeline",):
+    for name in fd.EXPORTS + ("fd_debug_timeline", "fd_debug_chunk_timeline"):
         assert hasattr(tl, name), name
 
 
