@@ -211,7 +211,7 @@ __device__ __forceinline__ void chunk_stage8_at(const PagedKV& pk, const int32_t
 
 // Dequantise a landed code stage (src, format KV) into the bf16 stage layout
 // (dst), exactly (see codes_to_bf16):
-// thread t converts 16-byte chunks t, t + kCT, ... through lds_read_b128 /
+// thread t converts 16-byte chunks t, t + kCT, ... through lds_load_b128 /
 // lds_write_b128, so the stage loads still in flight are not waited for.
 template <int D, int KV>
 __device__ __forceinline__ void chunk_dequant_stage(const char* src, char* dst, int tid) {
@@ -220,10 +220,7 @@ __device__ __forceinline__ void chunk_dequant_stage(const char* src, char* dst, 
     constexpr int QPT = G8::TENB / 16;  // chunks per tensor
     u32x4_t x[G8::NQ];
 #pragma unroll
-    for (int n = 0; n < G8::NQ; ++n) x[n] = lds_read_b128(src + (n * kCT + tid) * 16);
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-#pragma unroll
-    for (int n = 0; n < G8::NQ; ++n) asm volatile("" : "+v"(x[n]));
+    for (int n = 0; n < G8::NQ; ++n) x[n] = lds_load_b128(lds_addr(src + (n * kCT + tid) * 16));
 #pragma unroll
     for (int n = 0; n < G8::NQ; ++n) {
         const int q = n * kCT + tid;
@@ -295,6 +292,29 @@ __device__ __forceinline__ void chunk_scores(const uint32_t (&ka)[CGeo<D>::KS], 
     // All K reads first, so the products wait on LDS once.
     __builtin_amdgcn_sched_group_barrier(0x100, G::KS, 0);
     __builtin_amdgcn_sched_group_barrier(0x008, G::KS, 0);
+}
+
+// A block's V operands (stage buffer at offset OFF from the lane addresses
+// va) through transposed reads, waited for.
+template <int D, int OFF>
+__device__ __forceinline__ void chunk_v_reads_wait(const uint32_t (&va)[CGeo<D>::DB][2],
+                                                   bf16x8_t (&vf)[CGeo<D>::DB * 2]) {
+    using G = CGeo<D>;
+    constexpr int K2 = 16 * G::ROWB;  // 16 rows further down the block
+    uint32_t a[2 * G::DB];
+#pragma unroll
+    for (int db = 0; db < G::DB; ++db) {
+        a[2 * db] = va[db][0];
+        a[2 * db + 1] = va[db][1];
+    }
+    bf16x4_t x[2 * G::DB], y[2 * G::DB];
+    tr_read_wait<OFF>(a, x);
+    tr_read_wait<OFF + K2>(a, y);
+#pragma unroll
+    for (int db = 0; db < G::DB; ++db) {
+        vf[db * 2] = __builtin_shufflevector(x[2 * db], x[2 * db + 1], 0, 1, 2, 3, 4, 5, 6, 7);
+        vf[db * 2 + 1] = __builtin_shufflevector(y[2 * db], y[2 * db + 1], 0, 1, 2, 3, 4, 5, 6, 7);
+    }
 }
 
 // Start the transposed reads of a block's V operands; valid after lds_settle8.
@@ -420,7 +440,6 @@ __device__ __forceinline__ void chunk_step(bool edge, const uint32_t (&ka)[CGeo<
     bool moved, lo;
     bf16x8_t pl[2];
     chunk_softmax(st, c, m, l, mx, alpha, moved, ph, pl, lo);
-    chunk_v_reads<D, OFF>(va, vf);
     // P.V products of the previous block with the softmax's vector work
     // between them.
 #pragma unroll
@@ -428,7 +447,9 @@ __device__ __forceinline__ void chunk_step(bool edge, const uint32_t (&ka)[CGeo<
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x002, FD_CHUNK_VALU_PER_MFMA, 0);
     }
-    lds_settle8(vf);
+    __builtin_amdgcn_sched_barrier(0);
+    // This block's V operands (the products above have taken the previous ones).
+    chunk_v_reads_wait<D, OFF>(va, vf);
     if (moved) {
 #pragma unroll
         for (int db = 0; db < G::DB; ++db) acc[db] *= alpha;
@@ -747,10 +768,15 @@ __global__ __launch_bounds__(kCT) void fd_mfma_chunk8_kernel(PartialArgs a) {
 // runs on the matrix core while block j's softmax runs on the vector units
 // (two score tiles in flight), then block j's P.V product follows.  That
 // needs block j + 1's keys before block j's softmax, so the ring has kPNS
-// stages and the loads of stage t + kPNS - 2 start right after the barrier of
-// stage t (the barrier shows every wave done with the slot they refill).  K
-// and V keep separate regions of the ring, so every operand offset fits the
-// LDS instructions' 16-bit offset field.
+// stages and the loads of stage t + kPNS - 1 start right after the barrier of
+// step t (the barrier shows every wave done with the slot they refill; each
+// wave waits before it for its own loads of stage t + 1 only, and with four
+// stages the next stage's loads stay in flight across it).  The barrier is a
+// bare s_barrier between compiler memory barriers: a workgroup fence would
+// also wait for every load in flight.  K stages share one LDS array, read
+// with plain 16-byte loads; each V stage has an array of its own, read with
+// the transposing-load builtin, so that the compiler sees which buffer-to-LDS
+// loads a read depends on and waits for exactly those.
 
 constexpr int kPT = 512;               // threads per workgroup
 constexpr int kPW = kPT / 64;          // waves
@@ -776,23 +802,21 @@ struct PGeo {
     static constexpr int SKB = 2;                   // blocks per stage (key halves)
     static constexpr int SKEYS = SKB * kCBK;        // keys per stage
     static constexpr int STGB = SKB * BLKB;         // bytes per stage per tensor
-    static constexpr int VREG = kPNS * STGB;        // V region after the K region
     static constexpr int NDMA = SKB * IPB;          // load instructions per tensor per stage
     static constexpr int DPW = NDMA / kPW;          // per wave, per tensor
+    static constexpr int PER = 2 * DPW;             // loads per wave per stage
     static constexpr int KS = D / 16;               // k-steps of S^T = K Q^T
     static constexpr int DB = D / 32;               // 32-dim blocks of O^T
     static_assert(NDMA % kPW == 0 && DPW >= 1, "stage loads split evenly over the waves");
 };
 
-// Stage j of the tile [lo, kend) into ring slot `slot`: K rows into the K
-// region, V rows into the V region (see chunk_stage_at).
+// Start this wave's loads of stage j of the tile [lo, kend): K rows into dk,
+// V rows into dv (the stage's slots of the two rings; see chunk_stage_at).
 template <int D, bool PAGED>
 __device__ __forceinline__ void pipe_stage(const PagedKV& pk, const int32_t* tbl, const char* kt, const char* vt,
-                                           int lo, int kend, int j, int rsb, char* smem, int slot,
+                                           int lo, int kend, int j, int rsb, char* dk, char* dv,
                                            const uint32_t* dma_off, const int* lds_off, const int* koff) {
     using G = PGeo<D>;
-    char* dk = smem + slot * G::STGB;
-    char* dv = smem + G::VREG + slot * G::STGB;
 #pragma unroll
     for (int k = 0; k < G::DPW; ++k) {
         __amdgpu_buffer_rsrc_t rk, rv;
@@ -814,6 +838,24 @@ __device__ __forceinline__ void pipe_stage(const PagedKV& pk, const int32_t* tbl
     }
 }
 
+// Workgroup barrier without a memory fence: the compiler keeps memory
+// accesses on their side of it; the waits for loads are the caller's.
+__device__ __forceinline__ void bare_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// Wait until at most n (0 or 1, wave-uniform) stages' loads of this wave are
+// in flight, PER loads each.
+template <int PER>
+__device__ __forceinline__ void wait_stages(int n) {
+    if (n >= 1)
+        wait_vmcnt_le<PER>();
+    else
+        wait_vmcnt_le<0>();
+}
+
 // max and sum of x over lanes i and i ^ 32 (the two halves of a 32x32 tile
 // hold the same rows); the swap hands every lane the pair (x of the low
 // lane, x of the high lane), so both lanes get the same bits.
@@ -830,7 +872,9 @@ __device__ __forceinline__ float xor32_sum(float x) {
 // branches, so that the scheduler can place it between the matrix
 // instructions of the next block's scores: statistics, the rescale factor
 // alpha, the weights pr, their bf16 head ph and its share of the running
-// sum.  lo says whether the block also needs its remainder (pipe_remainder).
+// sum.  lo says whether the block also needs its remainder (pipe_remainder):
+// whether some row's largest weight in the block passes 1/16 of the row's
+// running sum, this block's heads included (both lane halves of the row).
 __device__ __forceinline__ void pipe_softmax(const f32x16_t& st, float c, float& m, float& l, float& mx, float& alpha,
                                              bool& moved, float (&pr)[16], bf16x8_t (&ph)[2], bool& lo) {
     float sm = st[0];
@@ -845,7 +889,7 @@ __device__ __forceinline__ void pipe_softmax(const f32x16_t& st, float c, float&
     m = mn;
     l *= alpha;
     const float mref = m == -INFINITY ? 0.f : m;
-    lo = __any(fast_exp2(bm - mref) * 16.f > l);
+    const float pm = fast_exp2(bm - mref);
 #pragma unroll
     for (int r = 0; r < 16; ++r) pr[r] = fast_exp2(fmaf(st[r], c, -mref));
     const bf16x2_t ones = {(__bf16)1.f, (__bf16)1.f};
@@ -859,6 +903,7 @@ __device__ __forceinline__ void pipe_softmax(const f32x16_t& st, float c, float&
     ph[0] = pack8(h2[0], h2[1], h2[2], h2[3]);
     ph[1] = pack8(h2[4], h2[5], h2[6], h2[7]);
     l += bs;
+    lo = __any(pm * 16.f > xor32_sum(l));
 }
 
 // The bf16 remainder pl = pr - ph of a block's weights, and its share of the
@@ -880,8 +925,32 @@ __device__ __forceinline__ void pipe_remainder(const float (&pr)[16], const bf16
     l += bs;
 }
 
+// Transposed LDS read (ds_read_b64_tr_b16, lane layout as tr_read_wait) at
+// byte offset off of the V stage array sv.
+__device__ __forceinline__ bf16x4_t v_tr_read(const char* sv, uint32_t off) {
+    const s16x4_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)(sv + off));
+    return __builtin_bit_cast(bf16x4_t, r);
+}
+
+// A block's V operands from the V stage array sv (lane offsets va, which
+// include the wave's block).
+template <int D>
+__device__ __forceinline__ void pipe_v_reads(const char* sv, const uint32_t (&va)[PGeo<D>::DB][2],
+                                             bf16x8_t (&vf)[PGeo<D>::DB * 2]) {
+    constexpr int K2 = 16 * PGeo<D>::ROWB;  // 16 rows further down the block
+#pragma unroll
+    for (int db = 0; db < PGeo<D>::DB; ++db) {
+        const bf16x4_t a0 = v_tr_read(sv, va[db][0]);
+        const bf16x4_t a1 = v_tr_read(sv, va[db][1]);
+        const bf16x4_t b0 = v_tr_read(sv, va[db][0] + K2);
+        const bf16x4_t b1 = v_tr_read(sv, va[db][1] + K2);
+        vf[db * 2] = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
+        vf[db * 2 + 1] = __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+}
+
 // Block j of this wave: its scores are in stc (complete); block j + 1's K
-// operands in kf (awaited), block j's V operands in vf (read, awaited here).
+// operands in kf, block j's V operands in vf (read in the previous step).
 // Computes block j + 1's scores into stn while running block j's softmax,
 // then block j's P.V product.  Keys of block j at or past rend are masked
 // when `edge`.
@@ -917,7 +986,6 @@ __device__ __forceinline__ void pipe_block(bool edge, f32x16_t& stc, f32x16_t& s
         for (int r = 0; r < 16; ++r) asm volatile("" : "+v"(pr[r]));
         pipe_remainder(pr, ph, pl, l);
     }
-    lds_settle8(vf);
     if (moved) {
         float al = alpha;
         asm volatile("" : "+v"(al));
@@ -946,6 +1014,14 @@ __device__ __forceinline__ void unrolled(F& f) {
     unrolled_seq(f, std::make_integer_sequence<int, N>{});
 }
 
+// Float offset of dims d .. d + 3 (d a multiple of 4) of row r in a row
+// group's merge block [32][D]: 16-byte chunks XOR-swizzled by r & 15, so that
+// 16 consecutive rows at one chunk fall in distinct banks.
+template <int D>
+__device__ __forceinline__ int merge_at(int r, int d) {
+    return r * D + (((d >> 2) ^ (r & 15)) << 2);
+}
+
 template <int D, bool PAGED>
 __global__ __launch_bounds__(kPT) void fd_mfma_chunk_kernel(PartialArgs a) {
 #if FD_WG_TIMELINE
@@ -959,10 +1035,19 @@ __global__ __launch_bounds__(kPT) void fd_mfma_chunk_kernel(PartialArgs a) {
 #endif
     using G = PGeo<D>;
     constexpr int NS = kPNS;
-    constexpr int RS = D + 4;  // padded row stride of the merge area (floats)
-    constexpr int RINGB = 2 * NS * G::STGB;
-    constexpr int MERGEB = kPRG * (32 * RS + 3 * 32) * 4;
-    __shared__ __attribute__((aligned(16))) char smem[RINGB > MERGEB ? RINGB : MERGEB];
+    // One array per V stage (more strictly aligned, so that they come first
+    // and the V reads' LDS addresses fit the instructions' offset field), then
+    // the K ring.  The merge at the end reuses them: the statistics at the
+    // start of the K ring, a row group's accumulators in V stage rg (the last
+    // group in the K ring after the statistics when there are three stages).
+    __shared__ __attribute__((aligned(1024))) char sv0[G::STGB];
+    __shared__ __attribute__((aligned(1024))) char sv1[G::STGB];
+    __shared__ __attribute__((aligned(1024))) char sv2[G::STGB];
+    __shared__ __attribute__((aligned(1024))) char sv3[NS > 3 ? G::STGB : 16];
+    __shared__ __attribute__((aligned(16))) char sk[NS * G::STGB];
+    char* const svs[4] = {sv0, sv1, sv2, sv3};
+    static_assert(32 * D * 4 == G::STGB, "a row group's merge block fills one V stage");
+    static_assert(2048 + G::STGB <= NS * G::STGB, "statistics and a merge block fit the K ring");
 
     // Grid order as in fd_mfma_chunk8_kernel: the row tiles of one (KV head,
     // tile) next to each other, one contiguous range of them per XCD.
@@ -1081,16 +1166,18 @@ __global__ __launch_bounds__(kPT) void fd_mfma_chunk_kernel(PartialArgs a) {
         dma_off[k] = (uint32_t)((PAGED ? lane / G::CH : koff[k] + lane / G::CH) * rsb + cg * 16);
         lds_off[k] = bb * G::BLKB + i * 1024;
     }
-    auto stage = [&](int j, int slot) {
-        pipe_stage<D, PAGED>(a.pages, tbl, kt, vt, lo, kend, j, rsb, smem, slot, dma_off, lds_off, koff);
+    auto stage = [&](int j, auto SLOT) {
+        constexpr int SL = decltype(SLOT)::value;
+        pipe_stage<D, PAGED>(a.pages, tbl, kt, vt, lo, kend, j, rsb, sk + SL * G::STGB, svs[SL], dma_off, lds_off,
+                             koff);
     };
 
-    // Lane-constant LDS addresses of this wave's K and V operands in ring
-    // slot 0 (block kh); other slots add compile-time offsets.
+    // Lane addresses of this wave's operands (block kh): K absolute in ring
+    // slot 0 (other slots add compile-time offsets), V relative to a V stage.
     uint32_t ka[G::KS];
     uint32_t va[G::DB][2];
     {
-        const uint32_t kbase = lds_addr(smem) + kh * G::BLKB;
+        const uint32_t kbase = lds_addr(sk) + kh * G::BLKB;
 #pragma unroll
         for (int ks = 0; ks < G::KS; ++ks) ka[ks] = kbase + cswz<D>(col, 2 * ks + hl);
         const int g16 = lane >> 4;
@@ -1100,23 +1187,30 @@ __global__ __launch_bounds__(kPT) void fd_mfma_chunk_kernel(PartialArgs a) {
         for (int db = 0; db < G::DB; ++db)
 #pragma unroll
             for (int t2 = 0; t2 < 2; ++t2)
-                va[db][t2] = kbase + G::VREG +
+                va[db][t2] = kh * G::BLKB +
                              cswz<D>(8 * t2 + 4 * hl + (i16 >> 2), (32 * db + 16 * (g16 & 1)) / 8 + (q4 >> 1)) +
                              8 * (q4 & 1);
     }
 
-    // Stages 0 .. NS - 3 in flight; after the barrier of stage t the loads of
-    // stage t + NS - 2 start (into the slot of stage t - 2, which every wave
-    // is done with).  This wave's block of stage t is at ring slot t % NS.
-#pragma unroll
-    for (int j = 0; j < NS - 2; ++j) stage(j, j);
-    wait_vmcnt_le<(NS - 3) * 2 * G::DPW>();
-    __syncthreads();
+    // Stages 0 .. NS - 3 in flight and stage 0 awaited; after the barrier of
+    // step t the loads of stage t + NS - 1 start (into the slot of stage
+    // t - 1, which every wave is done with).  Stage t is at ring slot t % NS;
+    // stages past the last one are never loaded (their slots are read but
+    // the results never used).
+    {
+        const auto issue = [&](auto UC) -> bool {
+            if (decltype(UC)::value < nst) stage(decltype(UC)::value, UC);
+            return true;
+        };
+        unrolled<NS - 2>(issue);
+    }
+    wait_stages<G::PER>(min(nst, NS - 2) - 1);
+    bare_barrier();
 #if FD_WG_TIMELINE
     tl_first = __builtin_amdgcn_s_memrealtime();
     const uint64_t tl_clk0 = __builtin_amdgcn_s_memtime();
 #endif
-    stage(NS - 2, NS - 2);
+    if (NS - 2 < nst) stage(NS - 2, std::integral_constant<int, NS - 2>{});
     f32x16_t st[2];
     bf16x8_t kf[G::KS], vf[G::DB * 2];
     pipe_k_reads<D, 0>(ka, kf);
@@ -1124,7 +1218,7 @@ __global__ __launch_bounds__(kPT) void fd_mfma_chunk_kernel(PartialArgs a) {
     for (int r = 0; r < 16; ++r) st[0][r] = 0.f;
 #pragma unroll
     for (int ks = 0; ks < G::KS; ++ks) st[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], st[0], 0, 0, 0);
-    chunk_v_reads<D, 0>(va, vf);
+    pipe_v_reads<D>(svs[0], va, vf);
 
     // Unrolled by NS stages, so that ring slots and the score buffer are
     // compile-time constants (U: the stage's place in the unrolled run).
@@ -1133,24 +1227,24 @@ __global__ __launch_bounds__(kPT) void fd_mfma_chunk_kernel(PartialArgs a) {
             constexpr int U = decltype(UC)::value;
             const int j = j0 + U;
             if (j >= nst) return false;
-            // Stage j + 1: landed for everyone after the barrier, which also
-            // frees the slot of stage j - 1 for stage j + NS - 1.
+            // Stage j + 1: landed for everyone after the barrier (a later
+            // stage may stay in flight), which also frees the slot of stage
+            // j - 1 for stage j + NS - 1.
             if (j + 1 < nst) {
-                wait_vmcnt_le<(NS - 3) * 2 * G::DPW>();
-                __syncthreads();
-                stage(j + NS - 1, (U + NS - 1) % NS);
+                wait_stages<G::PER>(min(nst - 1, j + NS - 2) - (j + 1));
+                bare_barrier();
+                if (j + NS - 1 < nst) stage(j + NS - 1, std::integral_constant<int, (U + NS - 1) % NS>{});
             }
             pipe_k_reads<D, ((U + 1) % NS) * G::STGB>(ka, kf);
             const int key0 = lo + j * G::SKEYS + kh * kCBK;
             const bool edge = key0 + kCBK > mask_from;
             pipe_block<D>(edge, st[U % 2], st[1 - U % 2], kf, qf, vf, acc, m, l, mx, key0, rend, c, hl);
-            chunk_v_reads<D, ((U + 1) % NS) * G::STGB>(va, vf);
+            pipe_v_reads<D>(svs[(U + 1) % NS], va, vf);
             return true;
         };
         unrolled<2 * NS>(step);
     }
     wait_vmcnt_le<0>();
-    lds_settle8(vf);
 #if FD_WG_TIMELINE
     {
         const uint64_t t = __builtin_amdgcn_s_memrealtime();
@@ -1166,18 +1260,18 @@ __global__ __launch_bounds__(kPT) void fd_mfma_chunk_kernel(PartialArgs a) {
     // Per-row totals over the two lane halves; then merge the key halves.
     l = xor32_sum(l);
     mx = xor32_max(mx);
-    __syncthreads();  // the ring is free
-    float* sm_acc = reinterpret_cast<float*>(smem);  // [kPRG][32][RS]
-    float* sm_m = sm_acc + kPRG * 32 * RS;           // [kPRG][32]
+    __syncthreads();  // the rings are free
+    float* sm_m = reinterpret_cast<float*>(sk);  // [kPRG][32]
     float* sm_l = sm_m + kPRG * 32;
     float* sm_x = sm_l + kPRG * 32;
+    char* const mblk = rg == 0 ? sv0 : rg == 1 ? sv1 : rg == 2 ? sv2 : NS > 3 ? sv3 : sk + 2048;
+    float* sm_acc = reinterpret_cast<float*>(mblk);  // [32][D], swizzled
     if (kh == 1) {
-        float* o = sm_acc + (rg * 32 + col) * RS;
 #pragma unroll
         for (int db = 0; db < G::DB; ++db)
 #pragma unroll
             for (int a4 = 0; a4 < 4; ++a4)
-                *reinterpret_cast<f32x4_t*>(o + 32 * db + 8 * a4 + 4 * hl) =
+                *reinterpret_cast<f32x4_t*>(sm_acc + merge_at<D>(col, 32 * db + 8 * a4 + 4 * hl)) =
                     f32x4_t{acc[db][4 * a4], acc[db][4 * a4 + 1], acc[db][4 * a4 + 2], acc[db][4 * a4 + 3]};
         if (hl == 0) {
             sm_m[rg * 32 + col] = m;
@@ -1196,7 +1290,6 @@ __global__ __launch_bounds__(kPT) void fd_mfma_chunk_kernel(PartialArgs a) {
     const bool empty = M == -INFINITY;
     const float inv = empty ? 0.f : 1.f / den;
     const float lse_v = empty ? -INFINITY : (M + log2f(den)) * kLn2;
-    const float* o2 = sm_acc + (rg * 32 + col) * RS;
     if (a.direct) {
         uint16_t* o = reinterpret_cast<uint16_t*>(a.out) + mrow * D;
 #pragma unroll
@@ -1204,7 +1297,7 @@ __global__ __launch_bounds__(kPT) void fd_mfma_chunk_kernel(PartialArgs a) {
 #pragma unroll
             for (int a4 = 0; a4 < 4; ++a4) {
                 const int d = 32 * db + 8 * a4 + 4 * hl;
-                const f32x4_t y = *reinterpret_cast<const f32x4_t*>(o2 + d);
+                const f32x4_t y = *reinterpret_cast<const f32x4_t*>(sm_acc + merge_at<D>(col, d));
                 float v[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) v[e] = (acc[db][4 * a4 + e] * f1 + y[e] * f2) * inv;
@@ -1222,7 +1315,7 @@ __global__ __launch_bounds__(kPT) void fd_mfma_chunk_kernel(PartialArgs a) {
 #pragma unroll
                 for (int a4 = 0; a4 < 4; ++a4) {
                     const int d = 32 * db + 8 * a4 + 4 * hl;
-                    const f32x4_t y = *reinterpret_cast<const f32x4_t*>(o2 + d);
+                    const f32x4_t y = *reinterpret_cast<const f32x4_t*>(sm_acc + merge_at<D>(col, d));
                     f32x4_t v;
 #pragma unroll
                     for (int e = 0; e < 4; ++e) v[e] = (acc[db][4 * a4 + e] * f1 + y[e] * f2) * inv;

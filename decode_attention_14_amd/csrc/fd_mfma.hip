@@ -162,15 +162,6 @@ __device__ __forceinline__ int swz(int r, int c) {
     return r * Geo<D>::ROWB + ((c ^ swf<Geo<D>::CH>(r)) << 4);
 }
 
-// Wait for every LDS read of this wave, then make the transposed reads'
-// registers visible to the compiler as defined here.
-template <int N>
-__device__ __forceinline__ void lds_settle(bf16x4_t (&v)[N]) {
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-#pragma unroll
-    for (int i = 0; i < N; ++i) asm volatile("" : "+v"(v[i]));
-}
-
 // Start the loads of one block (16 rows of K and of V, `left` bytes of the
 // tile from kp/vp on; none if left <= 0) into LDS at dst: K rows first, then
 // V rows.  Lane l of load instruction i reads its row's global chunk
@@ -258,8 +249,8 @@ __device__ __forceinline__ void dq_row_chunk(int n, int lane, int& r, int& p) {
     p = q % CH8;
 }
 
-// Start the LDS reads of one landed code block (at src): the lane's V
-// chunks (xv) and its K operand chunks (xk); valid after codes_settle.
+// LDS reads of one landed code block (at src): the lane's V chunks (xv) and
+// its K operand chunks (xk), as plain loads the compiler waits for.
 template <int D>
 __device__ __forceinline__ void codes_read(const char* src, int lane, int grp, int col,
                                            u32x4_t (&xv)[DQ<D>::NQ], u32x4_t (&xk)[DQ<D>::KC]) {
@@ -268,27 +259,22 @@ __device__ __forceinline__ void codes_read(const char* src, int lane, int grp, i
     for (int n = 0; n < DQ<D>::NQ; ++n) {
         int r, p;
         dq_row_chunk<D>(n, lane, r, p);
-        xv[n] = lds_read_b128(src + L::BLKB + r * L::ROWB + p * 16);
+        xv[n] = lds_load_b128(lds_addr(src + L::BLKB + r * L::ROWB + p * 16));
     }
 #pragma unroll
     for (int k = 0; k < DQ<D>::KC; ++k) {
         const int c = grp * DQ<D>::KC + k;  // chunk of dims 16 c .. 16 c + 15
-        xk[k] = lds_read_b128(src + col * L::ROWB + ((c ^ cswz8<D>(col)) << 4));
+        xk[k] = lds_load_b128(lds_addr(src + col * L::ROWB + ((c ^ cswz8<D>(col)) << 4)));
     }
 }
 
-// Wait for codes_read, write the bf16 V block at dst and turn the K chunks
-// into the score product's A operands.
+// Write the bf16 V block at dst from codes_read's V chunks and turn its K
+// chunks into the score product's A operands.
 template <int D, int KV>
 __device__ __forceinline__ void codes_settle(u32x4_t (&xv)[DQ<D>::NQ], u32x4_t (&xk)[DQ<D>::KC], char* dst,
                                              int lane, bf16x8_t (&kf)[Geo<D>::KS]) {
     using L = LGeo<D, true>;
     constexpr int NQ = DQ<D>::NQ;
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-#pragma unroll
-    for (int n = 0; n < NQ; ++n) asm volatile("" : "+v"(xv[n]));
-#pragma unroll
-    for (int k = 0; k < DQ<D>::KC; ++k) asm volatile("" : "+v"(xk[k]));
 #pragma unroll
     for (int n = 0; n < NQ; ++n) {
         int r, p;
@@ -382,14 +368,16 @@ __device__ __forceinline__ void block_math(const bf16x8_t (&kf)[Geo<D>::KS], con
 }
 
 // V^T operands of one 16-key block stored (swizzled) at vb in LDS, through
-// transposed reads; valid after lds_settle.
+// transposed reads (waited for).
 template <int D>
 __device__ __forceinline__ void v_fragments(const char* vb, bf16x4_t (&vf)[Geo<D>::DB], int grp, int col) {
     using G = Geo<D>;
     const int r = 4 * grp + (col >> 2);
     const int q4 = col & 3;
+    uint32_t a[G::DB];
 #pragma unroll
-    for (int db = 0; db < G::DB; ++db) vf[db] = tr_read(vb + swz<D>(r, 2 * db + (q4 >> 1)) + 8 * (q4 & 1));
+    for (int db = 0; db < G::DB; ++db) a[db] = lds_addr(vb + swz<D>(r, 2 * db + (q4 >> 1)) + 8 * (q4 & 1));
+    tr_read_wait<0>(a, vf);
 }
 
 // Operand fragments of one 16-key block stored (swizzled) at kb / vb in LDS:
@@ -402,7 +390,6 @@ __device__ __forceinline__ void load_fragments(const char* kb, const char* vb, b
     for (int ks = 0; ks < G::KS; ++ks)
         kf[ks] = *reinterpret_cast<const bf16x8_t*>(kb + swz<D>(col, grp + 4 * ks));
     v_fragments<D>(vb, vf, grp, col);
-    lds_settle(vf);
 }
 
 template <int D, int NB, bool CAUSAL, bool PAGED, int KV>
@@ -568,7 +555,6 @@ __global__ __launch_bounds__(KV != kKvBf16 ? 64 * kMW8 : kMT) void fd_mfma_parti
             codes_read<D>(kb, lane, grp, col, xv, xk);
             codes_settle<D, KV>(xv, xk, conv, lane, kf);
             v_fragments<D>(conv, vf, grp, col);
-            lds_settle(vf);
         } else {
             load_fragments<D>(kb, kb + LG::BLKB, kf, vf, grp, col);
         }

@@ -42,30 +42,61 @@ static __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char*)p));
 }
 
-// Transposing LDS read, ds_read_b64_tr_b16: in each 16-lane group, lane
-// 4j + q names 4 consecutive bf16 of a row; lane i receives element i % 4 of
-// lane 4j + i / 4 for j = 0..3.  Issued as inline assembly because the
-// compiler treats the builtin as possibly aliasing the LDS loads in flight and
-// would wait for all of them; the result is only valid after an explicit
-// s_waitcnt lgkmcnt(0).
-static __device__ __forceinline__ bf16x4_t tr_read(const char* p) {
-    bf16x4_t r;
-    asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(lds_addr(p)));
-    return r;
+// LDS loads.  A load result must never be in flight outside the compiler's
+// view: either the compiler issues the load and counts it (plain loads,
+// builtins), or one inline-asm statement issues the loads and waits for them.
+//
+// 16-byte load as a plain load through the integer LDS address: the compiler
+// counts it and waits for it before its first use, and with the pointer
+// rebuilt from an integer it does not hold it back for the buffer-to-LDS
+// loads in flight.  The caller makes sure the bytes have landed.
+static __device__ __forceinline__ u32x4_t lds_load_b128(uint32_t addr) {
+    return *(const __attribute__((address_space(3))) u32x4_t*)(uintptr_t)addr;
 }
 
-// 16-byte LDS read and write as inline assembly.  As plain loads and stores
-// the compiler would treat them as possibly aliasing the buffer-to-LDS loads
-// in flight and wait for all of those first, which serialises a load ring.
-// The caller makes sure that what it reads has landed and that what it
-// writes is read only after its own later waits; LDS executes one wave's
-// accesses in order.  A read's result is valid after s_waitcnt lgkmcnt(0).
-static __device__ __forceinline__ u32x4_t lds_read_b128(const char* p) {
-    u32x4_t r;
-    asm volatile("ds_read_b128 %0, %1" : "=v"(r) : "v"(lds_addr(p)));
-    return r;
+// N (4 or 8) transposing reads, ds_read_b64_tr_b16 (in each 16-lane group,
+// lane 4j + q names 4 consecutive bf16 of a row; lane i receives element i % 4
+// of lane 4j + i / 4 for j = 0..3), at lane addresses a[i] + OFF, and the wait
+// for all of this wave's LDS accesses, in one asm statement.  The outputs are
+// early-clobber, so no result lands on an address still to be read.  (The
+// builtin would make the compiler wait for every buffer-to-LDS load in flight
+// into the same LDS array.)
+template <int OFF>
+static __device__ __forceinline__ void tr_read_wait(const uint32_t (&a)[4], bf16x4_t (&v)[4]) {
+    static_assert(OFF >= 0 && OFF < 65536, "ds offset");
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %4 offset:%8\n\t"
+        "ds_read_b64_tr_b16 %1, %5 offset:%8\n\t"
+        "ds_read_b64_tr_b16 %2, %6 offset:%8\n\t"
+        "ds_read_b64_tr_b16 %3, %7 offset:%8\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "i"(OFF)
+        : "memory");
+}
+template <int OFF>
+static __device__ __forceinline__ void tr_read_wait(const uint32_t (&a)[8], bf16x4_t (&v)[8]) {
+    static_assert(OFF >= 0 && OFF < 65536, "ds offset");
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %8 offset:%16\n\t"
+        "ds_read_b64_tr_b16 %1, %9 offset:%16\n\t"
+        "ds_read_b64_tr_b16 %2, %10 offset:%16\n\t"
+        "ds_read_b64_tr_b16 %3, %11 offset:%16\n\t"
+        "ds_read_b64_tr_b16 %4, %12 offset:%16\n\t"
+        "ds_read_b64_tr_b16 %5, %13 offset:%16\n\t"
+        "ds_read_b64_tr_b16 %6, %14 offset:%16\n\t"
+        "ds_read_b64_tr_b16 %7, %15 offset:%16\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]), "=&v"(v[7])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]), "i"(OFF)
+        : "memory");
 }
 
+// 16-byte LDS write as inline assembly (no result register).  As a plain
+// store the compiler would treat it as possibly aliasing the buffer-to-LDS
+// loads in flight and wait for all of those first; the caller makes sure the
+// bytes it overwrites are no longer read and that what it writes is read only
+// after its own later waits (LDS executes one wave's accesses in order).
 static __device__ __forceinline__ void lds_write_b128(char* p, u32x4_t x) {
     asm volatile("ds_write_b128 %0, %1" : : "v"(lds_addr(p)), "v"(x) : "memory");
 }

@@ -48,6 +48,18 @@ SWF = load_swizzle("fd_mfma.hip", "swf")
 CSWF = load_swizzle("fd_chunk.hip", "cswf")
 
 
+def load_merge_at():
+    """merge_at(r, d) of fd_chunk.hip (float offset of dims d .. d + 3 of row
+    r in a row group's merge block) as a Python function of (r, d, D)."""
+    src = open(os.path.join(CSRC, "fd_chunk.hip")).read()
+    m = re.search(r"int merge_at\(int r, int d\) \{\n\s*return (.*?);\n\}", src, re.S)
+    assert m, "merge_at not found in fd_chunk.hip"
+    return eval("lambda r, d, D: " + m.group(1))
+
+
+MERGE_AT = load_merge_at()
+
+
 def conflict_free(addrs, nbytes, window):
     banks = {}
     for a in addrs:
@@ -126,6 +138,23 @@ def test_chunk_v_reads_conflict_free(D):
                             + step * 16 * rowb)
 
                 assert not tr_read(v_addr), (D, db, t, step)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_chunk_merge_block_layout(D):
+    # Each row's 16-byte chunks are permuted within the row (the block holds
+    # 32 rows x D floats exactly), and the key-half merge's float4 writes --
+    # lane (hl, col) writes dims 32 db + 8 a4 + 4 hl of row col -- are
+    # conflict-free.
+    for r in range(32):
+        offs = sorted(MERGE_AT(r, d, D) for d in range(0, D, 4))
+        assert offs == list(range(r * D, (r + 1) * D, 4)), (D, r)
+    for db in range(D // 32):
+        for a4 in range(4):
+            def addr(l, db=db, a4=a4):
+                hl, col = l >> 5, l & 31
+                return 4 * MERGE_AT(col, 32 * db + 8 * a4 + 4 * hl, D)
+            assert not write_b128(addr), (D, db, a4)
 
 
 def dequant_chunks(D, odd_first_rule):
