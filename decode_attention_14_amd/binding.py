@@ -104,7 +104,7 @@ def load_library(path: str | None = None):
     lib.fd_decode_attention_int8.restype = i32
     lib.fd_decode_partials_int8.argtypes = lib.fd_decode_partials_fp8.argtypes
     lib.fd_decode_partials_int8.restype = i32
-    lib.fd_stream_read.argtypes = [vp, u64, i32, vp, vp]
+    lib.fd_stream_read.argtypes = [vp, u64, i32, i32, vp, vp]
     lib.fd_stream_read.restype = i32
     lib.fd_status_string.argtypes = [i32]
     lib.fd_status_string.restype = ctypes.c_char_p
@@ -350,10 +350,13 @@ def combine(o_part, lse_part, out_dtype=torch.float32, out=None, lse=None, split
     return out, lse
 
 
-def stream_read(buf: torch.Tensor, nbytes: int | None = None, workgroups: int = 0, sink=None, offset: int = 0):
+def stream_read(buf: torch.Tensor, nbytes: int | None = None, workgroups: int = 0, sink=None, offset: int = 0,
+                pattern: int = 0):
     """Measurement aid: one streaming read of ``nbytes`` bytes of ``buf``
     from byte ``offset`` on (all of it by default) by the library's read
-    kernel, enqueued on the current stream.  Returns the 4-byte sink tensor."""
+    kernel, enqueued on the current stream; ``pattern`` 0 strides over the
+    grid, 1 gives each workgroup a contiguous range.  Returns the 4-byte
+    sink tensor."""
     lib = load_library()
     _require_cuda(buf, sink)
     total = buf.numel() * buf.element_size()
@@ -362,7 +365,7 @@ def stream_read(buf: torch.Tensor, nbytes: int | None = None, workgroups: int = 
         raise FdError(FD_ERR_INVALID, "read range outside the buffer")
     if sink is None:
         sink = torch.zeros(1, dtype=torch.int32, device=buf.device)
-    _check(lib.fd_stream_read(ctypes.c_void_p(buf.data_ptr() + offset), n, int(workgroups), _ptr(sink),
+    _check(lib.fd_stream_read(ctypes.c_void_p(buf.data_ptr() + offset), n, int(workgroups), int(pattern), _ptr(sink),
                               _stream(buf.device)))
     return sink
 

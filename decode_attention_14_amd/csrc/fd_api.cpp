@@ -236,7 +236,7 @@ const char* fd_status_string(int32_t status) {
 
 const char* fd_last_error(void) { return g_last_error; }
 
-int32_t fd_version(void) { return 400; }
+int32_t fd_version(void) { return 500; }
 
 uint64_t fd_workspace_bytes(const fd_dims* dims, int32_t max_splits) {
     if (max_splits <= 1 || max_splits > FD_MAX_SPLITS) return 0;
@@ -452,9 +452,11 @@ fd_status fd_combine_splits(int32_t batch, int32_t num_heads, int32_t q_len, int
                          "combine kernel launch");
 }
 
-fd_status fd_stream_read(const void* buf, uint64_t bytes, int32_t workgroups, uint32_t* sink, void* stream) {
+fd_status fd_stream_read(const void* buf, uint64_t bytes, int32_t workgroups, int32_t pattern, uint32_t* sink,
+                         void* stream) {
     clear_error();
     if (workgroups < 0) return fail(FD_ERR_INVALID, "workgroups %d < 0", workgroups);
+    if (pattern != 0 && pattern != 1) return fail(FD_ERR_INVALID, "pattern %d is neither 0 nor 1", pattern);
     if (bytes % 16 != 0) return fail(FD_ERR_INVALID, "bytes %llu is not a multiple of 16", (unsigned long long)bytes);
     if (bytes == 0) return FD_OK;
     if (!buf || !sink) return fail(FD_ERR_INVALID, "buf and sink must be non-NULL");
@@ -467,7 +469,8 @@ fd_status fd_stream_read(const void* buf, uint64_t bytes, int32_t workgroups, ui
             return fail(FD_ERR_DEVICE, "cannot query the compute-unit count; pass workgroups");
         workgroups = 8 * prop.multiProcessorCount;
     }
-    return device_status(fdk::launch_stream_read(buf, bytes, workgroups, sink, static_cast<hipStream_t>(stream)),
+    return device_status(fdk::launch_stream_read(buf, bytes, workgroups, pattern, sink,
+                                                 static_cast<hipStream_t>(stream)),
                          "stream read kernel launch");
 }
 

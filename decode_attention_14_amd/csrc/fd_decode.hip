@@ -576,10 +576,12 @@ void launch_combine_d(int64_t rows, int slots, const float* o_part, const float*
 
 // ---------------------------------------------------------------------------
 // Streaming read (a measurement aid): each thread reads 16-byte pieces
-// kStreamUnroll at a time, all issued before any is used, strided over the
-// grid so that consecutive threads read consecutive pieces, and folds them
-// by XOR.  A wave's fold reaches *sink only if it equals kStreamMagic, which
-// the compiler cannot rule out, so no load can be removed.
+// kStreamUnroll at a time, all issued before any is used, and folds them by
+// XOR.  Two patterns: strided over the whole grid (consecutive threads read
+// consecutive pieces, the grid sweeps the buffer together), or one
+// contiguous range per workgroup (as the partial kernels read their tiles).
+// A thread's fold reaches *sink only if it equals kStreamMagic, which the
+// compiler cannot rule out, so no load can be removed.
 
 constexpr int kStreamThreads = 256;
 constexpr int kStreamUnroll = 8;
@@ -600,6 +602,29 @@ __global__ __launch_bounds__(kStreamThreads) void fd_stream_read_kernel(const st
         for (int u = 0; u < kStreamUnroll; ++u) acc ^= x[u].x ^ x[u].y ^ x[u].z ^ x[u].w;
     }
     for (; i < n16; i += nthreads) {
+        const stream_u32x4 x = __builtin_nontemporal_load(buf + i);
+        acc ^= x.x ^ x.y ^ x.z ^ x.w;
+    }
+    if (acc == kStreamMagic) *sink = acc;
+}
+
+// Workgroup w reads pieces [w * per, (w + 1) * per) (per a multiple of
+// kStreamThreads), kStreamUnroll rows of kStreamThreads pieces at a time.
+__global__ __launch_bounds__(kStreamThreads) void fd_stream_read_chunk_kernel(const stream_u32x4* __restrict__ buf,
+                                                                              uint64_t n16, uint64_t per,
+                                                                              uint32_t* sink) {
+    const uint64_t beg = (uint64_t)blockIdx.x * per;
+    const uint64_t end = beg + per < n16 ? beg + per : n16;
+    uint64_t i = beg + threadIdx.x;
+    uint32_t acc = 0;
+    for (; i + (kStreamUnroll - 1) * kStreamThreads < end; i += kStreamUnroll * kStreamThreads) {
+        stream_u32x4 x[kStreamUnroll];
+#pragma unroll
+        for (int u = 0; u < kStreamUnroll; ++u) x[u] = __builtin_nontemporal_load(buf + i + u * kStreamThreads);
+#pragma unroll
+        for (int u = 0; u < kStreamUnroll; ++u) acc ^= x[u].x ^ x[u].y ^ x[u].z ^ x[u].w;
+    }
+    for (; i < end; i += kStreamThreads) {
         const stream_u32x4 x = __builtin_nontemporal_load(buf + i);
         acc ^= x.x ^ x.y ^ x.z ^ x.w;
     }
@@ -667,10 +692,18 @@ hipError_t launch_combine(int head_dim, int out_dtype, int64_t rows, int slots,
     return hipGetLastError();
 }
 
-hipError_t launch_stream_read(const void* buf, uint64_t bytes, int workgroups, uint32_t* sink,
+hipError_t launch_stream_read(const void* buf, uint64_t bytes, int workgroups, int pattern, uint32_t* sink,
                               hipStream_t stream) {
-    hipLaunchKernelGGL(fd_stream_read_kernel, dim3((unsigned)workgroups), dim3(kStreamThreads), 0, stream,
-                       static_cast<const stream_u32x4*>(buf), bytes / 16, sink);
+    const uint64_t n16 = bytes / 16;
+    if (pattern == 0) {
+        hipLaunchKernelGGL(fd_stream_read_kernel, dim3((unsigned)workgroups), dim3(kStreamThreads), 0, stream,
+                           static_cast<const stream_u32x4*>(buf), n16, sink);
+    } else {
+        uint64_t per = (n16 + (uint64_t)workgroups - 1) / (uint64_t)workgroups;
+        per = (per + kStreamThreads - 1) / kStreamThreads * kStreamThreads;
+        hipLaunchKernelGGL(fd_stream_read_chunk_kernel, dim3((unsigned)workgroups), dim3(kStreamThreads), 0, stream,
+                           static_cast<const stream_u32x4*>(buf), n16, per, sink);
+    }
     return hipGetLastError();
 }
 

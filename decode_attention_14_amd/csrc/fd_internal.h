@@ -117,8 +117,10 @@ constexpr uint64_t kNoallocScratchBytes = 32ull << 20;
 hipError_t noalloc_scratch(void** ptr);
 
 // Streaming read of [buf, buf + bytes) (bytes a multiple of 16) over
-// `workgroups` workgroups, folded into *sink only on an improbable value.
-hipError_t launch_stream_read(const void* buf, uint64_t bytes, int workgroups, uint32_t* sink,
+// `workgroups` workgroups, strided over the grid (pattern 0) or one
+// contiguous range per workgroup (1), folded into *sink only on an
+// improbable value.
+hipError_t launch_stream_read(const void* buf, uint64_t bytes, int workgroups, int pattern, uint32_t* sink,
                               hipStream_t stream);
 
 }  // namespace fdk

@@ -332,15 +332,19 @@ const char* fd_last_error(void);
 /* fd_stream_read -- a measurement aid, not part of the operation: reads
  * `bytes` bytes of device memory from `buf` once, in 16-byte pieces spread
  * over `workgroups` workgroups of 256 threads (0: eight per compute unit),
- * and folds them into one word that reaches `*sink` (device memory, 4 bytes)
- * only if it equals a value no real data is expected to give, so the reads
- * cannot be optimised away.  Its time over the K/V bytes of a step gives the
+ * either strided over the whole grid (`pattern` 0: consecutive threads read
+ * consecutive pieces) or one contiguous range per workgroup (`pattern` 1, as
+ * the partial kernels read their tiles), and folds them into one word that
+ * reaches `*sink` (device memory, 4 bytes) only if it equals a value no real
+ * data is expected to give, so the reads cannot be optimised away.  Its time over the K/V bytes of a step gives the
  * bandwidth a plain streaming read reaches on the device, the ceiling against
  * which the partial kernel's rate is read (page "ChunkedPrefill与FlashDecoding
  * 技术解析" §4.2 item 2: find where the kernel's time goes before tuning it).
  * `buf` and `bytes` must be multiples of 16.  Errors: FD_ERR_INVALID for a
- * NULL or misaligned buffer, a size not a multiple of 16 or workgroups < 0. */
-fd_status fd_stream_read(const void* buf, uint64_t bytes, int32_t workgroups, uint32_t* sink, void* stream);
+ * NULL or misaligned buffer, a size not a multiple of 16, workgroups < 0 or
+ * a pattern other than 0 and 1. */
+fd_status fd_stream_read(const void* buf, uint64_t bytes, int32_t workgroups, int32_t pattern, uint32_t* sink,
+                         void* stream);
 
 /* Library version, major * 10000 + minor * 100 + patch. */
 int32_t fd_version(void);

@@ -19,6 +19,6 @@ hipError_t noalloc_scratch(void** ptr) {
     return hipErrorNotSupported;
 }
 
-hipError_t launch_stream_read(const void*, uint64_t, int, uint32_t*, hipStream_t) { return hipErrorNotSupported; }
+hipError_t launch_stream_read(const void*, uint64_t, int, int, uint32_t*, hipStream_t) { return hipErrorNotSupported; }
 
 }  // namespace fdk

@@ -316,13 +316,15 @@ def test_noalloc_rejects_calls_beyond_its_scratch(lib):
 
 
 def test_stream_read_rejects_bad_arguments(lib):
-    assert lib.fd_stream_read(FAKE[0], 100, 0, FAKE[1], None) == fd.FD_ERR_INVALID
-    assert lib.fd_stream_read(None, 1024, 0, FAKE[1], None) == fd.FD_ERR_INVALID
-    assert lib.fd_stream_read(FAKE[0], 1024, -1, FAKE[1], None) == fd.FD_ERR_INVALID
-    assert lib.fd_stream_read(ctypes.c_void_p(FAKE[0].value + 8), 1024, 8, FAKE[1], None) == fd.FD_ERR_INVALID
-    assert lib.fd_stream_read(FAKE[0], 1024, 8, None, None) == fd.FD_ERR_INVALID
+    assert lib.fd_stream_read(FAKE[0], 100, 0, 0, FAKE[1], None) == fd.FD_ERR_INVALID
+    assert lib.fd_stream_read(None, 1024, 0, 0, FAKE[1], None) == fd.FD_ERR_INVALID
+    assert lib.fd_stream_read(FAKE[0], 1024, -1, 0, FAKE[1], None) == fd.FD_ERR_INVALID
+    assert lib.fd_stream_read(FAKE[0], 1024, 8, 2, FAKE[1], None) == fd.FD_ERR_INVALID
+    assert lib.fd_stream_read(FAKE[0], 1024, 8, -1, FAKE[1], None) == fd.FD_ERR_INVALID
+    assert lib.fd_stream_read(ctypes.c_void_p(FAKE[0].value + 8), 1024, 8, 0, FAKE[1], None) == fd.FD_ERR_INVALID
+    assert lib.fd_stream_read(FAKE[0], 1024, 8, 0, None, None) == fd.FD_ERR_INVALID
     # nothing to read: no launch, no pointer touched
-    assert lib.fd_stream_read(None, 0, 0, None, None) == fd.FD_OK
+    assert lib.fd_stream_read(None, 0, 0, 0, None, None) == fd.FD_OK
 
 
 def test_empty_batch_is_a_no_op(lib):
