@@ -106,9 +106,9 @@ def algorithmic_bytes(w, lens, kv_codes=False):
 def partial_kernel_name(w) -> str:
     """The partial-pass kernel the library dispatches to for this workload:
     matrix cores for bf16 (decode rows, or chunk tiles above 32 rows), vector
-    ALUs for fp32."""
+    ALUs for fp32 or when FD_DECODE_KERNEL=vector forces them."""
     rows = w.num_q_heads // w.num_kv_heads * w.q_len
-    if w.dtype != "bf16":
+    if w.dtype != "bf16" or os.environ.get("FD_DECODE_KERNEL") == "vector":
         return "fd_partial_kernel"
     return "fd_mfma_partial_kernel" if rows <= 32 else "fd_mfma_chunk_kernel"
 
