@@ -810,10 +810,26 @@ struct PGeo {
     static_assert(NDMA % kPW == 0 && DPW >= 1, "stage loads split evenly over the waves");
 };
 
+// Page ids of this wave's loads of stage j (wave-uniform scalar loads), or
+// -1 past kend.  They are read at the end of the step before the stage's
+// loads: a scalar load in flight makes the compiler wait for every LDS read
+// at the next LDS wait, so it is issued after the step's K-operand waits and
+// consumed after the next barrier, when nothing else is left in flight.
+template <int D, bool PAGED>
+__device__ __forceinline__ void pipe_pages(const PagedKV& pk, const int32_t* tbl, int lo, int kend, int j,
+                                           const int* koff, int* pg) {
+    if constexpr (PAGED) {
+#pragma unroll
+        for (int k = 0; k < PGeo<D>::DPW; ++k) pg[k] = page_at(pk, tbl, lo + j * PGeo<D>::SKEYS + koff[k], kend);
+    }
+}
+
 // Start this wave's loads of stage j of the tile [lo, kend): K rows into dk,
 // V rows into dv (the stage's slots of the two rings; see chunk_stage_at).
+// A paged cache's page ids of this wave's loads come in pg (read a step
+// ahead, pipe_pages).
 template <int D, bool PAGED>
-__device__ __forceinline__ void pipe_stage(const PagedKV& pk, const int32_t* tbl, const char* kt, const char* vt,
+__device__ __forceinline__ void pipe_stage(const PagedKV& pk, const int* pg, const char* kt, const char* vt,
                                            int lo, int kend, int j, int rsb, char* dk, char* dv,
                                            const uint32_t* dma_off, const int* lds_off, const int* koff) {
     using G = PGeo<D>;
@@ -823,7 +839,8 @@ __device__ __forceinline__ void pipe_stage(const PagedKV& pk, const int32_t* tbl
         uint32_t off_lane = dma_off[k];
         if constexpr (PAGED) {
             int64_t off;
-            const uint32_t n = paged_rows(pk, tbl, lo + j * G::SKEYS + koff[k], G::RPI, kend, rsb, G::ROWB, &off);
+            const uint32_t n = paged_rows_in(pk, pg[k], lo + j * G::SKEYS + koff[k], G::RPI, kend, rsb, G::ROWB,
+                                             &off);
             rk = tile_rsrc(kt + off * 2, n);
             rv = tile_rsrc(vt + off * 2, n);
         } else {
@@ -1166,9 +1183,12 @@ __global__ __launch_bounds__(kPT) void fd_mfma_chunk_kernel(PartialArgs a) {
         dma_off[k] = (uint32_t)((PAGED ? lane / G::CH : koff[k] + lane / G::CH) * rsb + cg * 16);
         lds_off[k] = bb * G::BLKB + i * 1024;
     }
+    // Page ids of the next stage to load (paged caches).
+    int pg[G::DPW];
+    auto pages = [&](int j) { pipe_pages<D, PAGED>(a.pages, tbl, lo, kend, j, koff, pg); };
     auto stage = [&](int j, auto SLOT) {
         constexpr int SL = decltype(SLOT)::value;
-        pipe_stage<D, PAGED>(a.pages, tbl, kt, vt, lo, kend, j, rsb, sk + SL * G::STGB, svs[SL], dma_off, lds_off,
+        pipe_stage<D, PAGED>(a.pages, pg, kt, vt, lo, kend, j, rsb, sk + SL * G::STGB, svs[SL], dma_off, lds_off,
                              koff);
     };
 
@@ -1199,11 +1219,15 @@ __global__ __launch_bounds__(kPT) void fd_mfma_chunk_kernel(PartialArgs a) {
     // the results never used).
     {
         const auto issue = [&](auto UC) -> bool {
-            if (decltype(UC)::value < nst) stage(decltype(UC)::value, UC);
+            if (decltype(UC)::value < nst) {
+                pages(decltype(UC)::value);
+                stage(decltype(UC)::value, UC);
+            }
             return true;
         };
         unrolled<NS - 2>(issue);
     }
+    pages(NS - 2);
     wait_stages<G::PER>(min(nst, NS - 2) - 1);
     bare_barrier();
 #if FD_WG_TIMELINE
@@ -1211,6 +1235,7 @@ __global__ __launch_bounds__(kPT) void fd_mfma_chunk_kernel(PartialArgs a) {
     const uint64_t tl_clk0 = __builtin_amdgcn_s_memtime();
 #endif
     if (NS - 2 < nst) stage(NS - 2, std::integral_constant<int, NS - 2>{});
+    pages(NS - 1);
     f32x16_t st[2];
     bf16x8_t kf[G::KS], vf[G::DB * 2];
     pipe_k_reads<D, 0>(ka, kf);
@@ -1239,6 +1264,7 @@ __global__ __launch_bounds__(kPT) void fd_mfma_chunk_kernel(PartialArgs a) {
             const int key0 = lo + j * G::SKEYS + kh * kCBK;
             const bool edge = key0 + kCBK > mask_from;
             pipe_block<D>(edge, st[U % 2], st[1 - U % 2], kf, qf, vf, acc, m, l, mx, key0, rend, c, hl);
+            if (j + NS < nst) pages(j + NS);
             pipe_v_reads<D>(svs[(U + 1) % NS], va, vf);
             return true;
         };
