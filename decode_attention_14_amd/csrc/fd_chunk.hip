@@ -885,33 +885,26 @@ __device__ __forceinline__ float xor32_sum(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// The vector part of one block's online softmax (as chunk_softmax) without
-// branches, so that the scheduler can place it between the matrix
-// instructions of the next block's scores: statistics, the rescale factor
-// alpha, the weights pr, their bf16 head ph and its share of the running
-// sum.  lo says whether the block also needs its remainder (pipe_remainder):
-// whether some row's largest weight in the block passes 1/16 of the row's
-// running sum, this block's heads included (both lane halves of the row).
-__device__ __forceinline__ void pipe_softmax(const f32x16_t& st, float c, float& m, float& l, float& mx, float& alpha,
-                                             bool& moved, float (&pr)[16], bf16x8_t (&ph)[2], bool& lo) {
-    float sm = st[0];
-#pragma unroll
-    for (int r = 1; r < 16; ++r) sm = __builtin_elementwise_maximum(sm, st[r]);
-    const float bm = sm == -INFINITY ? -INFINITY : sm * c;
-    mx = fmaxf(mx, bm);
-    moved = __any(bm > m + kTau);
-    const float bw = xor32_max(bm);
-    const float mn = moved ? fmaxf(m, bw) : m;
-    alpha = m == -INFINITY ? 0.f : fast_exp2(m - mn);
-    m = mn;
-    l *= alpha;
-    const float mref = m == -INFINITY ? 0.f : m;
-    const float pm = fast_exp2(bm - mref);
+// Running statistics of one lane's query row in the pipelined kernel: the
+// reference max m (scaled scores, log2 units; -inf before the row's first
+// visible key), the exponent offset mref (m, or 0 while m is -inf), thr, the
+// raw score above which a key moves the reference (m + kTau in raw units,
+// -inf while m is -inf), the running sum l of the weights the products use
+// (this lane's keys), and the running max xr of this lane's raw scores.
+struct RowStat {
+    float m, mref, thr, l, xr;
+};
+
+// Weights of a block against the offset mref: pr = 2^(c s - mref), their
+// bf16 heads ph, and l = l0 plus the heads (bf16 dot products against ones:
+// exact products, fp32 sums).
+__device__ __forceinline__ void pipe_weights(const f32x16_t& st, float c, float mref, float l0, float (&pr)[16],
+                                             bf16x8_t (&ph)[2], float& l) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) pr[r] = fast_exp2(fmaf(st[r], c, -mref));
     const bf16x2_t ones = {(__bf16)1.f, (__bf16)1.f};
     bf16x2_t h2[8];
-    float bs = 0.f;
+    float bs = l0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         h2[i] = __builtin_convertvector(f32x2_t{pr[2 * i], pr[2 * i + 1]}, bf16x2_t);
@@ -919,8 +912,54 @@ __device__ __forceinline__ void pipe_softmax(const f32x16_t& st, float c, float&
     }
     ph[0] = pack8(h2[0], h2[1], h2[2], h2[3]);
     ph[1] = pack8(h2[4], h2[5], h2[6], h2[7]);
-    l += bs;
-    lo = __any(pm * 16.f > xor32_sum(l));
+    l = bs;
+}
+
+// Whether the block also needs its remainder (pipe_remainder): whether some
+// row's largest weight in the block, 2^(c sm - mref), passes 1/16 of the
+// row's running sum, this block's heads included (both lane halves).
+__device__ __forceinline__ bool pipe_needs_remainder(float sm, float c, const RowStat& rs) {
+    const float pm = fast_exp2(fmaf(sm, c, -rs.mref));
+    return __any(pm * 16.f > xor32_sum(rs.l));
+}
+
+// The common path of one block's online softmax, without branches, so that
+// the scheduler can place it between the matrix instructions of the next
+// block's scores: the block's raw max sm (also folded into xr), whether it
+// moves the reference (some row's max passes thr), the weights against the
+// current reference and the remainder test.  When the reference moves, the
+// caller recomputes the weights (pipe_move); l0 keeps the sum before the
+// block for that.
+__device__ __forceinline__ void pipe_softmax(const f32x16_t& st, float c, RowStat& rs, float& sm, float& l0,
+                                             bool& moved, float (&pr)[16], bf16x8_t (&ph)[2], bool& lo) {
+    // IEEE maximum (v_maximum3_f32): no quieting of the matrix results.
+    sm = st[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) sm = __builtin_elementwise_maximum(sm, st[r]);
+    rs.xr = __builtin_elementwise_maximum(rs.xr, sm);
+    moved = __any(sm > rs.thr);
+    l0 = rs.l;
+    pipe_weights(st, c, rs.mref, l0, pr, ph, rs.l);
+    lo = pipe_needs_remainder(sm, c, rs);
+}
+
+// The rare path of a block whose max moved the reference: the new reference
+// is the larger of the old one and the row's block max (both lane halves);
+// alpha is the factor the sum and the accumulators owe (0 after -inf).  The
+// weights, the sum and the remainder test are redone against it from the
+// block's scores st (recomputed by the caller: the common path's weights may
+// have overflowed, and keeping the scores alive would cost registers).
+__device__ __forceinline__ float pipe_move(const f32x16_t& st, float c, float cinv, float sm, float l0, RowStat& rs,
+                                           float (&pr)[16], bf16x8_t (&ph)[2], bool& lo) {
+    const float bw = xor32_max(sm * c);
+    const float mn = fmaxf(rs.m, bw);
+    const float alpha = rs.m == -INFINITY ? 0.f : fast_exp2(rs.m - mn);
+    rs.m = mn;
+    rs.mref = mn == -INFINITY ? 0.f : mn;
+    rs.thr = mn == -INFINITY ? -INFINITY : (mn + kTau) * cinv;
+    pipe_weights(st, c, rs.mref, l0 * alpha, pr, ph, rs.l);
+    lo = pipe_needs_remainder(sm, c, rs);
+    return alpha;
 }
 
 // The bf16 remainder pl = pr - ph of a block's weights, and its share of the
@@ -966,30 +1005,47 @@ __device__ __forceinline__ void pipe_v_reads(const char* sv, const uint32_t (&va
     }
 }
 
-// Block j of this wave: its scores are in stc (complete); block j + 1's K
-// operands in kf, block j's V operands in vf (read in the previous step).
-// Computes block j + 1's scores into stn while running block j's softmax,
-// then block j's P.V product.  Keys of block j at or past rend are masked
-// when `edge`.
+// K operands of a block at K-region offset OFF (LDS addresses ka).
+template <int D, int OFF>
+__device__ __forceinline__ void pipe_k_reads(const uint32_t (&ka)[PGeo<D>::KS], bf16x8_t (&kf)[PGeo<D>::KS]) {
+#pragma unroll
+    for (int ks = 0; ks < PGeo<D>::KS; ++ks) kf[ks] = lds_b128<OFF>(ka[ks]);
+}
+
+// Scores of a block, S^T = K Q^T, from K operands kf.
 template <int D>
-__device__ __forceinline__ void pipe_block(bool edge, f32x16_t& stc, f32x16_t& stn, const bf16x8_t (&kf)[PGeo<D>::KS],
-                                           const bf16x8_t (&qf)[PGeo<D>::KS], bf16x8_t (&vf)[PGeo<D>::DB * 2],
-                                           f32x16_t (&acc)[PGeo<D>::DB], float& m, float& l, float& mx, int key0,
-                                           int rend, float c, int hl) {
+__device__ __forceinline__ void pipe_scores(const bf16x8_t (&kf)[PGeo<D>::KS], const bf16x8_t (&qf)[PGeo<D>::KS],
+                                            f32x16_t& st) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) st[r] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < PGeo<D>::KS; ++ks) st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], st, 0, 0, 0);
+}
+
+// Keys of a block at or past rend (this lane's row) get score -inf.
+__device__ __forceinline__ void pipe_mask(f32x16_t& st, int key0, int rend, int hl) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+        if (key0 + 8 * (r >> 2) + 4 * hl + (r & 3) >= rend) st[r] = -INFINITY;
+}
+
+// Block j of this wave: its scores are in stc (complete); block j + 1's K
+// operands in kf, block j's V operands in vf (read in the previous step);
+// block j's K operands are at K-ring offset KOFF.  Computes block j + 1's
+// scores into stn while running block j's softmax, then block j's P.V
+// product.  Keys of block j at or past rend are masked when `edge`.
+template <int D, int KOFF>
+__device__ __forceinline__ void pipe_block(bool edge, f32x16_t& stc, f32x16_t& stn, const uint32_t (&ka)[PGeo<D>::KS],
+                                           const bf16x8_t (&kf)[PGeo<D>::KS], const bf16x8_t (&qf)[PGeo<D>::KS],
+                                           bf16x8_t (&vf)[PGeo<D>::DB * 2], f32x16_t (&acc)[PGeo<D>::DB],
+                                           RowStat& rs, int key0, int rend, float c, float cinv, int hl) {
     using G = PGeo<D>;
-    if (edge) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-            if (key0 + 8 * (r >> 2) + 4 * hl + (r & 3) >= rend) stc[r] = -INFINITY;
-    }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) stn[r] = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < G::KS; ++ks) stn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], stn, 0, 0, 0);
-    float alpha, pr[16];
+    if (edge) pipe_mask(stc, key0, rend, hl);
+    pipe_scores<D>(kf, qf, stn);
+    float pr[16], sm, l0;
     bool moved, lo;
-    bf16x8_t ph[2], pl[2];
-    pipe_softmax(stc, c, m, l, mx, alpha, moved, pr, ph, lo);
+    bf16x8_t ph[2];
+    pipe_softmax(stc, c, rs, sm, l0, moved, pr, ph, lo);
     // block j + 1's score instructions with block j's softmax between them
 #pragma unroll
     for (int i = 0; i < G::KS; ++i) {
@@ -998,27 +1054,36 @@ __device__ __forceinline__ void pipe_block(bool edge, f32x16_t& stc, f32x16_t& s
     }
     // The rare paths read their inputs through register barriers inside the
     // branch, so the compiler cannot compute them on every block instead.
+    if (moved) {
+        // The block's scores again, bit for bit: same operands (its K stage
+        // stays in the ring until the next barrier), same instructions.
+        uint32_t kar[G::KS];
+#pragma unroll
+        for (int ks = 0; ks < G::KS; ++ks) {
+            kar[ks] = ka[ks];
+            asm volatile("" : "+v"(kar[ks]));
+        }
+        bf16x8_t kr[G::KS];
+        pipe_k_reads<D, KOFF>(kar, kr);
+        f32x16_t sc;
+        pipe_scores<D>(kr, qf, sc);
+        if (edge) pipe_mask(sc, key0, rend, hl);
+        float smv = sm, l0v = l0;
+        asm volatile("" : "+v"(smv), "+v"(l0v));
+        const float al = pipe_move(sc, c, cinv, smv, l0v, rs, pr, ph, lo);
+#pragma unroll
+        for (int db = 0; db < G::DB; ++db) acc[db] *= al;
+    }
+    bf16x8_t pl[2];
     if (lo) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) asm volatile("" : "+v"(pr[r]));
-        pipe_remainder(pr, ph, pl, l);
-    }
-    if (moved) {
-        float al = alpha;
-        asm volatile("" : "+v"(al));
-#pragma unroll
-        for (int db = 0; db < G::DB; ++db) acc[db] *= al;
+        pipe_remainder(pr, ph, pl, rs.l);
     }
     chunk_pv<D>(vf, ph, acc);
     if (lo) chunk_pv<D>(vf, pl, acc);
 }
 
-// K operands of a block at K-region offset OFF (LDS addresses ka).
-template <int D, int OFF>
-__device__ __forceinline__ void pipe_k_reads(const uint32_t (&ka)[PGeo<D>::KS], bf16x8_t (&kf)[PGeo<D>::KS]) {
-#pragma unroll
-    for (int ks = 0; ks < PGeo<D>::KS; ++ks) kf[ks] = lds_b128<OFF>(ka[ks]);
-}
 
 // f(integral_constant<int, 0>), f(.. 1), ..., f(.. N - 1) in order, stopping
 // after the first call that returns false.
@@ -1148,7 +1213,8 @@ __global__ __launch_bounds__(kPT) void fd_mfma_chunk_kernel(PartialArgs a) {
     for (int db = 0; db < G::DB; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
-    float m = -INFINITY, l = 0.f, mx = -INFINITY;
+    RowStat rs = {-INFINITY, 0.f, -INFINITY, 0.f, -INFINITY};
+    const float cinv = 1.f / c;
 
     const char* kt;
     const char* vt;
@@ -1263,7 +1329,8 @@ __global__ __launch_bounds__(kPT) void fd_mfma_chunk_kernel(PartialArgs a) {
             pipe_k_reads<D, ((U + 1) % NS) * G::STGB>(ka, kf);
             const int key0 = lo + j * G::SKEYS + kh * kCBK;
             const bool edge = key0 + kCBK > mask_from;
-            pipe_block<D>(edge, st[U % 2], st[1 - U % 2], kf, qf, vf, acc, m, l, mx, key0, rend, c, hl);
+            pipe_block<D, (U % NS) * G::STGB>(edge, st[U % 2], st[1 - U % 2], ka, kf, qf, vf, acc, rs, key0, rend, c,
+                                                cinv, hl);
             if (j + NS < nst) pages(j + NS);
             pipe_v_reads<D>(svs[(U + 1) % NS], va, vf);
             return true;
@@ -1284,8 +1351,9 @@ __global__ __launch_bounds__(kPT) void fd_mfma_chunk_kernel(PartialArgs a) {
 #endif
 
     // Per-row totals over the two lane halves; then merge the key halves.
-    l = xor32_sum(l);
-    mx = xor32_max(mx);
+    const float m = rs.m;
+    const float l = xor32_sum(rs.l);
+    const float mx = xor32_max(rs.xr) * c;
     __syncthreads();  // the rings are free
     float* sm_m = reinterpret_cast<float*>(sk);  // [kPRG][32]
     float* sm_l = sm_m + kPRG * 32;
