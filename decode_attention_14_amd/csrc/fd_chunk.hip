@@ -764,32 +764,32 @@ __global__ __launch_bounds__(kCT) void fd_mfma_chunk8_kernel(PartialArgs a) {
 // The same work split as fd_mfma_chunk8_kernel -- eight waves, four row
 // groups of 32 rows times two key halves, 64-key stages of which wave (rg,
 // kh) takes block kh, the halves merged through LDS at the end -- but inside
-// a wave the work of consecutive blocks overlaps: block j + 1's score product
-// runs on the matrix core while block j's softmax runs on the vector units
-// (two score tiles in flight), then block j's P.V product follows.  That
-// needs block j + 1's keys before block j's softmax, so the ring has kPNS
-// stages and the loads of stage t + kPNS - 1 start right after the barrier of
-// step t (the barrier shows every wave done with the slot they refill; each
-// wave waits before it for its own loads of stage t + 1 only, and with four
-// stages the next stage's loads stay in flight across it).  The barrier is a
-// bare s_barrier between compiler memory barriers: a workgroup fence would
-// also wait for every load in flight.  K stages share one LDS array, read
-// with plain 16-byte loads; each V stage has an array of its own, read with
-// the transposing-load builtin, so that the compiler sees which buffer-to-LDS
-// loads a read depends on and waits for exactly those.
+// a wave the work of consecutive blocks overlaps.  Step j of a wave issues
+// block j + 1's score product beside the second half of block j's softmax,
+// then block j's P.V product beside the first half of block j + 1's softmax,
+// so that vector work sits between both groups of matrix instructions (two
+// score tiles in flight).  K operands are read a step ahead of their
+// product and V operands a step ahead of theirs; the ring has four stages,
+// and after the barrier of step t, which shows stage t + 2 landed for every
+// wave (each waits for its own loads before it) and every wave done with
+// step t - 1, the loads of stage t + 3 start into the slot of stage t - 1.
+// The barrier is a bare s_barrier between compiler memory barriers: a
+// workgroup fence would also wait for every load in flight.  K stages share
+// one LDS array, read with plain 16-byte loads; each V stage has an array of
+// its own, read with the transposing-load builtin, so that the compiler
+// sees which buffer-to-LDS loads a read depends on and waits for exactly
+// those.
 
 constexpr int kPT = 512;               // threads per workgroup
 constexpr int kPW = kPT / 64;          // waves
 constexpr int kPRG = 4;                // row groups of 32 rows
 static_assert(kPRG * 32 == kChunkTileRows, "row tile of the chunk kernel");
-#ifndef FD_CHUNK_PIPE_STAGES
-#define FD_CHUNK_PIPE_STAGES 3
-#endif
-constexpr int kPNS = FD_CHUNK_PIPE_STAGES;
-static_assert(kPNS >= 3 && kPNS <= 4, "ring stages of the pipelined chunk kernel");
-// Vector instructions the scheduler places after each score instruction.
+constexpr int kPNS = 4;  // ring stages
+// Vector instructions the scheduler places after each matrix instruction (a
+// probe kernel hides about four 4-cycle vector instructions under each
+// 32x32x16 matrix instruction of a SIMD).
 #ifndef FD_PIPE_VALU_PER_MFMA
-#define FD_PIPE_VALU_PER_MFMA 10
+#define FD_PIPE_VALU_PER_MFMA 4
 #endif
 
 template <int D>
@@ -895,11 +895,12 @@ struct RowStat {
     float m, mref, thr, l, xr;
 };
 
-// Weights of a block against the offset mref: pr = 2^(c s - mref), their
-// bf16 heads ph, and l = l0 plus the heads (bf16 dot products against ones:
-// exact products, fp32 sums).
-__device__ __forceinline__ void pipe_weights(const f32x16_t& st, float c, float mref, float l0, float (&pr)[16],
-                                             bf16x8_t (&ph)[2], float& l) {
+// Weights of a block against the offset mref, in place: the scores st become
+// 2^(c s - mref); their bf16 heads ph, and l = l0 plus the heads (bf16 dot
+// products against ones: exact products, fp32 sums).
+__device__ __forceinline__ void pipe_weights(f32x16_t& st, float c, float mref, float l0, bf16x8_t (&ph)[2],
+                                             float& l) {
+    f32x16_t& pr = st;
 #pragma unroll
     for (int r = 0; r < 16; ++r) pr[r] = fast_exp2(fmaf(st[r], c, -mref));
     const bf16x2_t ones = {(__bf16)1.f, (__bf16)1.f};
@@ -923,23 +924,48 @@ __device__ __forceinline__ bool pipe_needs_remainder(float sm, float c, const Ro
     return __any(pm * 16.f > xor32_sum(rs.l));
 }
 
-// The common path of one block's online softmax, without branches, so that
-// the scheduler can place it between the matrix instructions of the next
-// block's scores: the block's raw max sm (also folded into xr), whether it
-// moves the reference (some row's max passes thr), the weights against the
-// current reference and the remainder test.  When the reference moves, the
-// caller recomputes the weights (pipe_move); l0 keeps the sum before the
-// block for that.
-__device__ __forceinline__ void pipe_softmax(const f32x16_t& st, float c, RowStat& rs, float& sm, float& l0,
-                                             bool& moved, float (&pr)[16], bf16x8_t (&ph)[2], bool& lo) {
+// The common path of one block's online softmax comes in two halves without
+// branches, so that the scheduler can place each between matrix
+// instructions: the first beside the previous block's P.V product, the
+// second beside the next block's score product.
+//
+// First half, in place on the block's (masked) scores st: the block's raw
+// max sm (also folded into xr), whether it moves the reference (some row's
+// max passes thr), the exponents c s - mref, and the weights of the first
+// eight of them.
+__device__ __forceinline__ void pipe_softmax1(f32x16_t& st, float c, RowStat& rs, float& sm, bool& moved) {
     // IEEE maximum (v_maximum3_f32): no quieting of the matrix results.
     sm = st[0];
 #pragma unroll
     for (int r = 1; r < 16; ++r) sm = __builtin_elementwise_maximum(sm, st[r]);
     rs.xr = __builtin_elementwise_maximum(rs.xr, sm);
     moved = __any(sm > rs.thr);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) st[r] = fmaf(st[r], c, -rs.mref);
+#pragma unroll
+    for (int r = 0; r < 8; ++r) st[r] = fast_exp2(st[r]);
+}
+
+// Second half: the other eight weights (st then holds all sixteen), their
+// bf16 heads ph, the running sum (l0 keeps it from before the block, for a
+// reference move) and the remainder test.  When the reference moves, the
+// caller recomputes the weights (pipe_move).
+__device__ __forceinline__ void pipe_softmax2(f32x16_t& st, float c, RowStat& rs, float sm, float& l0,
+                                              bf16x8_t (&ph)[2], bool& lo) {
+#pragma unroll
+    for (int r = 8; r < 16; ++r) st[r] = fast_exp2(st[r]);
+    const bf16x2_t ones = {(__bf16)1.f, (__bf16)1.f};
+    bf16x2_t h2[8];
     l0 = rs.l;
-    pipe_weights(st, c, rs.mref, l0, pr, ph, rs.l);
+    float bs = l0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        h2[i] = __builtin_convertvector(f32x2_t{st[2 * i], st[2 * i + 1]}, bf16x2_t);
+        bs = __builtin_amdgcn_fdot2_f32_bf16(h2[i], ones, bs, false);
+    }
+    ph[0] = pack8(h2[0], h2[1], h2[2], h2[3]);
+    ph[1] = pack8(h2[4], h2[5], h2[6], h2[7]);
+    rs.l = bs;
     lo = pipe_needs_remainder(sm, c, rs);
 }
 
@@ -947,24 +973,25 @@ __device__ __forceinline__ void pipe_softmax(const f32x16_t& st, float c, RowSta
 // is the larger of the old one and the row's block max (both lane halves);
 // alpha is the factor the sum and the accumulators owe (0 after -inf).  The
 // weights, the sum and the remainder test are redone against it from the
-// block's scores st (recomputed by the caller: the common path's weights may
-// have overflowed, and keeping the scores alive would cost registers).
-__device__ __forceinline__ float pipe_move(const f32x16_t& st, float c, float cinv, float sm, float l0, RowStat& rs,
-                                           float (&pr)[16], bf16x8_t (&ph)[2], bool& lo) {
+// block's scores st, in place (recomputed by the caller: the common path's
+// weights may have overflowed, and keeping the scores alive would cost
+// registers).
+__device__ __forceinline__ float pipe_move(f32x16_t& st, float c, float cinv, float sm, float l0, RowStat& rs,
+                                           bf16x8_t (&ph)[2], bool& lo) {
     const float bw = xor32_max(sm * c);
     const float mn = fmaxf(rs.m, bw);
     const float alpha = rs.m == -INFINITY ? 0.f : fast_exp2(rs.m - mn);
     rs.m = mn;
     rs.mref = mn == -INFINITY ? 0.f : mn;
     rs.thr = mn == -INFINITY ? -INFINITY : (mn + kTau) * cinv;
-    pipe_weights(st, c, rs.mref, l0 * alpha, pr, ph, rs.l);
+    pipe_weights(st, c, rs.mref, l0 * alpha, ph, rs.l);
     lo = pipe_needs_remainder(sm, c, rs);
     return alpha;
 }
 
 // The bf16 remainder pl = pr - ph of a block's weights, and its share of the
 // running sum (see chunk_softmax for when it is taken).
-__device__ __forceinline__ void pipe_remainder(const float (&pr)[16], const bf16x8_t (&ph)[2], bf16x8_t (&pl)[2],
+__device__ __forceinline__ void pipe_remainder(const f32x16_t& pr, const bf16x8_t (&ph)[2], bf16x8_t (&pl)[2],
                                                float& l) {
     const bf16x2_t ones = {(__bf16)1.f, (__bf16)1.f};
     bf16x2_t l2[8];
@@ -1029,60 +1056,90 @@ __device__ __forceinline__ void pipe_mask(f32x16_t& st, int key0, int rend, int 
         if (key0 + 8 * (r >> 2) + 4 * hl + (r & 3) >= rend) st[r] = -INFINITY;
 }
 
-// Block j of this wave: its scores are in stc (complete); block j + 1's K
-// operands in kf, block j's V operands in vf (read in the previous step);
-// block j's K operands are at K-ring offset KOFF.  Computes block j + 1's
-// scores into stn while running block j's softmax, then block j's P.V
-// product.  Keys of block j at or past rend are masked when `edge`.
-template <int D, int KOFF>
-__device__ __forceinline__ void pipe_block(bool edge, f32x16_t& stc, f32x16_t& stn, const uint32_t (&ka)[PGeo<D>::KS],
-                                           const bf16x8_t (&kf)[PGeo<D>::KS], const bf16x8_t (&qf)[PGeo<D>::KS],
-                                           bf16x8_t (&vf)[PGeo<D>::DB * 2], f32x16_t (&acc)[PGeo<D>::DB],
-                                           RowStat& rs, int key0, int rend, float c, float cinv, int hl) {
+// Step j of this wave.  On entry stc holds block j's softmax after its
+// first half (pipe_softmax1; sm, moved: its max and move test), kf block j +
+// 1's K operands, vf block j's V operands.  Computes block j + 1's scores
+// into stn beside the second half of block j's softmax (reading block j +
+// 2's K operands at K-ring offset KNEXT into kf as the score instructions
+// issue), takes the rare paths (a reference move recomputes block j's
+// scores from its K stage at offset KOFF), then block j's P.V product
+// beside the first half of block j + 1's softmax (its keys masked from
+// rend when edge1), which leaves its max and move test in sm and moved.
+template <int D, int KOFF, int KNEXT>
+__device__ __forceinline__ void pipe_block(bool edge, bool edge1, f32x16_t& stc, f32x16_t& stn,
+                                           const uint32_t (&ka)[PGeo<D>::KS], bf16x8_t (&kf)[PGeo<D>::KS],
+                                           const bf16x8_t (&qf)[PGeo<D>::KS], bf16x8_t (&vf)[PGeo<D>::DB * 2],
+                                           f32x16_t (&acc)[PGeo<D>::DB], RowStat& rs, float& sm, bool& moved,
+                                           const char* svn, const uint32_t (&va)[PGeo<D>::DB][2], int key0,
+                                           int rend, float c, float cinv, int hl) {
     using G = PGeo<D>;
-    if (edge) pipe_mask(stc, key0, rend, hl);
-    pipe_scores<D>(kf, qf, stn);
-    float pr[16], sm, l0;
-    bool moved, lo;
+    // Block j + 1's scores; each K operand is replaced by block j + 2's once
+    // its instruction has issued.
+#pragma unroll
+    for (int r = 0; r < 16; ++r) stn[r] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < G::KS; ++ks) {
+        stn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], stn, 0, 0, 0);
+        kf[ks] = lds_b128<KNEXT>(ka[ks]);
+    }
+    float l0;
+    bool lo;
     bf16x8_t ph[2];
-    pipe_softmax(stc, c, rs, sm, l0, moved, pr, ph, lo);
-    // block j + 1's score instructions with block j's softmax between them
+    pipe_softmax2(stc, c, rs, sm, l0, ph, lo);
 #pragma unroll
     for (int i = 0; i < G::KS; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x002, FD_PIPE_VALU_PER_MFMA, 0);
     }
-    // The rare paths read their inputs through register barriers inside the
-    // branch, so the compiler cannot compute them on every block instead.
+    // stc now holds block j's weights.  The rare paths read their inputs
+    // through register barriers inside the branch, so the compiler cannot
+    // compute them on every block instead.
     if (moved) {
-        // The block's scores again, bit for bit: same operands (its K stage
-        // stays in the ring until the next barrier), same instructions.
-        uint32_t kar[G::KS];
+        // The block's scores again, bit for bit (same operands: its K stage
+        // stays in the ring through this step; same instructions), in place
+        // of the weights.
+#pragma unroll
+        for (int r = 0; r < 16; ++r) stc[r] = 0.f;
 #pragma unroll
         for (int ks = 0; ks < G::KS; ++ks) {
-            kar[ks] = ka[ks];
-            asm volatile("" : "+v"(kar[ks]));
+            // one K operand at a time: block j + 2's are live here
+            stc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128<KOFF>(ka[ks]), qf[ks], stc, 0, 0, 0);
+            asm volatile("" ::: "memory");
         }
-        bf16x8_t kr[G::KS];
-        pipe_k_reads<D, KOFF>(kar, kr);
-        f32x16_t sc;
-        pipe_scores<D>(kr, qf, sc);
-        if (edge) pipe_mask(sc, key0, rend, hl);
+        if (edge) pipe_mask(stc, key0, rend, hl);
         float smv = sm, l0v = l0;
         asm volatile("" : "+v"(smv), "+v"(l0v));
-        const float al = pipe_move(sc, c, cinv, smv, l0v, rs, pr, ph, lo);
+        const float al = pipe_move(stc, c, cinv, smv, l0v, rs, ph, lo);
 #pragma unroll
         for (int db = 0; db < G::DB; ++db) acc[db] *= al;
     }
-    bf16x8_t pl[2];
     if (lo) {
+        f32x16_t pr = stc;
 #pragma unroll
         for (int r = 0; r < 16; ++r) asm volatile("" : "+v"(pr[r]));
+        bf16x8_t pl[2];
         pipe_remainder(pr, ph, pl, rs.l);
+        chunk_pv<D>(vf, pl, acc);
     }
+    // Block j's P.V product beside the first half of block j + 1's softmax,
+    // then block j + 1's V operands (from the V stage array svn) into vf.
+    if (edge1) pipe_mask(stn, key0 + G::SKEYS, rend, hl);
     chunk_pv<D>(vf, ph, acc);
-    if (lo) chunk_pv<D>(vf, pl, acc);
+    pipe_softmax1(stn, c, rs, sm, moved);
+    pipe_v_reads<D>(svn, va, vf);
+#pragma unroll
+    for (int i = 0; i < G::KS; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+        __builtin_amdgcn_sched_group_barrier(0x002, FD_PIPE_VALU_PER_MFMA, 1);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 4 * G::DB, 1);
+    // computed here, not where they are used
+#pragma unroll
+    for (int r = 0; r < 16; ++r) asm volatile("" : "+v"(stn[r]));
+    asm volatile("" : "+v"(sm));
 }
+
 
 
 // f(integral_constant<int, 0>), f(.. 1), ..., f(.. N - 1) in order, stopping
@@ -1120,16 +1177,15 @@ __global__ __launch_bounds__(kPT) void fd_mfma_chunk_kernel(PartialArgs a) {
     // One array per V stage (more strictly aligned, so that they come first
     // and the V reads' LDS addresses fit the instructions' offset field), then
     // the K ring.  The merge at the end reuses them: the statistics at the
-    // start of the K ring, a row group's accumulators in V stage rg (the last
-    // group in the K ring after the statistics when there are three stages).
+    // start of the K ring, a row group's accumulators in V stage rg.
     __shared__ __attribute__((aligned(1024))) char sv0[G::STGB];
     __shared__ __attribute__((aligned(1024))) char sv1[G::STGB];
     __shared__ __attribute__((aligned(1024))) char sv2[G::STGB];
-    __shared__ __attribute__((aligned(1024))) char sv3[NS > 3 ? G::STGB : 16];
+    __shared__ __attribute__((aligned(1024))) char sv3[G::STGB];
     __shared__ __attribute__((aligned(16))) char sk[NS * G::STGB];
     char* const svs[4] = {sv0, sv1, sv2, sv3};
     static_assert(32 * D * 4 == G::STGB, "a row group's merge block fills one V stage");
-    static_assert(2048 + G::STGB <= NS * G::STGB, "statistics and a merge block fit the K ring");
+    static_assert(2048 <= NS * G::STGB, "the statistics fit the K ring");
 
     // Grid order as in fd_mfma_chunk8_kernel: the row tiles of one (KV head,
     // tile) next to each other, one contiguous range of them per XCD.
@@ -1214,7 +1270,7 @@ __global__ __launch_bounds__(kPT) void fd_mfma_chunk_kernel(PartialArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
     RowStat rs = {-INFINITY, 0.f, -INFINITY, 0.f, -INFINITY};
-    const float cinv = 1.f / c;
+    const float cinv = __uint_as_float(uniform(__float_as_uint(1.f / c)));
 
     const char* kt;
     const char* vt;
@@ -1231,6 +1287,8 @@ __global__ __launch_bounds__(kPT) void fd_mfma_chunk_kernel(PartialArgs a) {
         vt = static_cast<const char*>(a.v) + tile_row * G::ROWB;
         rsb = G::ROWB;
     }
+    kt = uniform(kt);  // scalar registers for the whole loop
+    vt = uniform(vt);
     const int nst = (kend - lo + G::SKEYS - 1) / G::SKEYS;
 
     // Load instruction k of this wave fills RPI rows of block bb of a stage;
@@ -1278,11 +1336,15 @@ __global__ __launch_bounds__(kPT) void fd_mfma_chunk_kernel(PartialArgs a) {
                              8 * (q4 & 1);
     }
 
-    // Stages 0 .. NS - 3 in flight and stage 0 awaited; after the barrier of
-    // step t the loads of stage t + NS - 1 start (into the slot of stage
-    // t - 1, which every wave is done with).  Stage t is at ring slot t % NS;
-    // stages past the last one are never loaded (their slots are read but
-    // the results never used).
+    // Stage t is at ring slot t % NS.  Step t uses block t's scores, block t +
+    // 1's K operands and block t's V operands (all read in step t - 1), and
+    // reads block t + 2's K operands and block t + 1's V operands; block t's
+    // K stays readable through step t (the rare reference move recomputes
+    // its scores).  So after the barrier of step t, which shows stage t + 2
+    // landed for every wave (each waits for its own loads before it) and
+    // every wave done with step t - 1, the loads of stage t + 3 start into
+    // the slot of stage t - 1.  Stages past the last one are never loaded
+    // (their slots are read but the results never used).
     {
         const auto issue = [&](auto UC) -> bool {
             if (decltype(UC)::value < nst) {
@@ -1291,51 +1353,53 @@ __global__ __launch_bounds__(kPT) void fd_mfma_chunk_kernel(PartialArgs a) {
             }
             return true;
         };
-        unrolled<NS - 2>(issue);
+        unrolled<NS - 1>(issue);
     }
-    pages(NS - 2);
-    wait_stages<G::PER>(min(nst, NS - 2) - 1);
+    pages(NS - 1);
+    wait_stages<G::PER>(min(nst, NS - 1) - 2);  // stages 0 and 1
     bare_barrier();
 #if FD_WG_TIMELINE
     tl_first = __builtin_amdgcn_s_memrealtime();
     const uint64_t tl_clk0 = __builtin_amdgcn_s_memtime();
 #endif
-    if (NS - 2 < nst) stage(NS - 2, std::integral_constant<int, NS - 2>{});
-    pages(NS - 1);
     f32x16_t st[2];
     bf16x8_t kf[G::KS], vf[G::DB * 2];
     pipe_k_reads<D, 0>(ka, kf);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) st[0][r] = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < G::KS; ++ks) st[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], st[0], 0, 0, 0);
+    pipe_scores<D>(kf, qf, st[0]);
+    pipe_k_reads<D, G::STGB>(ka, kf);
     pipe_v_reads<D>(svs[0], va, vf);
+    float sm;
+    bool moved;
+    {
+        const int key00 = lo + kh * kCBK;
+        if (key00 + kCBK > mask_from) pipe_mask(st[0], key00, rend, hl);
+        pipe_softmax1(st[0], c, rs, sm, moved);
+    }
 
     // Unrolled by NS stages, so that ring slots and the score buffer are
     // compile-time constants (U: the stage's place in the unrolled run).
-    for (int j0 = 0; j0 < nst; j0 += 2 * NS) {
+    static_assert(NS % 2 == 0, "score buffers alternate within the unrolled run");
+    for (int j0 = 0; j0 < nst; j0 += NS) {
         const auto step = [&](auto UC) -> bool {
             constexpr int U = decltype(UC)::value;
             const int j = j0 + U;
             if (j >= nst) return false;
-            // Stage j + 1: landed for everyone after the barrier (a later
-            // stage may stay in flight), which also frees the slot of stage
-            // j - 1 for stage j + NS - 1.
-            if (j + 1 < nst) {
-                wait_stages<G::PER>(min(nst - 1, j + NS - 2) - (j + 1));
+            if (j + 2 < nst) {
+                wait_vmcnt_le<0>();  // this wave's loads of stage j + 2
                 bare_barrier();
-                if (j + NS - 1 < nst) stage(j + NS - 1, std::integral_constant<int, (U + NS - 1) % NS>{});
+                if (j + 3 < nst) stage(j + 3, std::integral_constant<int, (U + 3) % NS>{});
             }
-            pipe_k_reads<D, ((U + 1) % NS) * G::STGB>(ka, kf);
             const int key0 = lo + j * G::SKEYS + kh * kCBK;
             const bool edge = key0 + kCBK > mask_from;
-            pipe_block<D, (U % NS) * G::STGB>(edge, st[U % 2], st[1 - U % 2], ka, kf, qf, vf, acc, rs, key0, rend, c,
-                                                cinv, hl);
+            const bool edge1 = key0 + G::SKEYS + kCBK > mask_from;
+            pipe_block<D, (U % NS) * G::STGB, ((U + 2) % NS) * G::STGB>(edge, edge1, st[U % 2], st[1 - U % 2], ka, kf,
+                                                                         qf, vf, acc, rs, sm, moved,
+                                                                         svs[(U + 1) % NS], va, key0, rend, c, cinv,
+                                                                         hl);
             if (j + NS < nst) pages(j + NS);
-            pipe_v_reads<D>(svs[(U + 1) % NS], va, vf);
             return true;
         };
-        unrolled<2 * NS>(step);
+        unrolled<NS>(step);
     }
     wait_vmcnt_le<0>();
 #if FD_WG_TIMELINE
@@ -1350,6 +1414,16 @@ __global__ __launch_bounds__(kPT) void fd_mfma_chunk_kernel(PartialArgs a) {
     }
 #endif
 
+    // This lane's row again, from an opaque lane id: recomputed here rather
+    // than kept live (in registers the loop needs) through the loop.
+    uint32_t lane_e;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane_e));
+    const int col_e = (int)(lane_e & 31u);
+    const int hl_e = (int)(lane_e >> 5);
+    const int p_e = p0 + rg * 32 + col_e;
+    const bool valid_e = p_e < R;
+    const int64_t mrow_e = rowbase + (int64_t)(p_e % n_rep) * q_len + p_e / n_rep;
+
     // Per-row totals over the two lane halves; then merge the key halves.
     const float m = rs.m;
     const float l = xor32_sum(rs.l);
@@ -1358,40 +1432,40 @@ __global__ __launch_bounds__(kPT) void fd_mfma_chunk_kernel(PartialArgs a) {
     float* sm_m = reinterpret_cast<float*>(sk);  // [kPRG][32]
     float* sm_l = sm_m + kPRG * 32;
     float* sm_x = sm_l + kPRG * 32;
-    char* const mblk = rg == 0 ? sv0 : rg == 1 ? sv1 : rg == 2 ? sv2 : NS > 3 ? sv3 : sk + 2048;
+    char* const mblk = rg == 0 ? sv0 : rg == 1 ? sv1 : rg == 2 ? sv2 : sv3;
     float* sm_acc = reinterpret_cast<float*>(mblk);  // [32][D], swizzled
     if (kh == 1) {
 #pragma unroll
         for (int db = 0; db < G::DB; ++db)
 #pragma unroll
             for (int a4 = 0; a4 < 4; ++a4)
-                *reinterpret_cast<f32x4_t*>(sm_acc + merge_at<D>(col, 32 * db + 8 * a4 + 4 * hl)) =
+                *reinterpret_cast<f32x4_t*>(sm_acc + merge_at<D>(col_e, 32 * db + 8 * a4 + 4 * hl_e)) =
                     f32x4_t{acc[db][4 * a4], acc[db][4 * a4 + 1], acc[db][4 * a4 + 2], acc[db][4 * a4 + 3]};
-        if (hl == 0) {
-            sm_m[rg * 32 + col] = m;
-            sm_l[rg * 32 + col] = l;
-            sm_x[rg * 32 + col] = mx;
+        if (hl_e == 0) {
+            sm_m[rg * 32 + col_e] = m;
+            sm_l[rg * 32 + col_e] = l;
+            sm_x[rg * 32 + col_e] = mx;
         }
     }
     __syncthreads();
-    if (kh == 1 || !valid) return;
-    const float m2 = sm_m[rg * 32 + col];
+    if (kh == 1 || !valid_e) return;
+    const float m2 = sm_m[rg * 32 + col_e];
     const float M = fmaxf(m, m2);
     const float f1 = m == -INFINITY ? 0.f : fast_exp2(m - M);
     const float f2 = m2 == -INFINITY ? 0.f : fast_exp2(m2 - M);
-    const float den = l * f1 + sm_l[rg * 32 + col] * f2;
-    const float X = fmaxf(mx, sm_x[rg * 32 + col]);
+    const float den = l * f1 + sm_l[rg * 32 + col_e] * f2;
+    const float X = fmaxf(mx, sm_x[rg * 32 + col_e]);
     const bool empty = M == -INFINITY;
     const float inv = empty ? 0.f : 1.f / den;
     const float lse_v = empty ? -INFINITY : (M + log2f(den)) * kLn2;
     if (a.direct) {
-        uint16_t* o = reinterpret_cast<uint16_t*>(a.out) + mrow * D;
+        uint16_t* o = reinterpret_cast<uint16_t*>(a.out) + mrow_e * D;
 #pragma unroll
         for (int db = 0; db < G::DB; ++db)
 #pragma unroll
             for (int a4 = 0; a4 < 4; ++a4) {
-                const int d = 32 * db + 8 * a4 + 4 * hl;
-                const f32x4_t y = *reinterpret_cast<const f32x4_t*>(sm_acc + merge_at<D>(col, d));
+                const int d = 32 * db + 8 * a4 + 4 * hl_e;
+                const f32x4_t y = *reinterpret_cast<const f32x4_t*>(sm_acc + merge_at<D>(col_e, d));
                 float v[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) v[e] = (acc[db][4 * a4 + e] * f1 + y[e] * f2) * inv;
@@ -1400,25 +1474,25 @@ __global__ __launch_bounds__(kPT) void fd_mfma_chunk_kernel(PartialArgs a) {
                 packed.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
                 *reinterpret_cast<uint2*>(o + d) = packed;
             }
-        if (hl == 0 && a.lse) a.lse[mrow] = lse_v;
+        if (hl_e == 0 && a.lse) a.lse[mrow_e] = lse_v;
     } else {
         if (!empty) {
-            float* o = a.o_part + (mrow * slots + s) * D;
+            float* o = a.o_part + (mrow_e * slots + s) * D;
 #pragma unroll
             for (int db = 0; db < G::DB; ++db)
 #pragma unroll
                 for (int a4 = 0; a4 < 4; ++a4) {
-                    const int d = 32 * db + 8 * a4 + 4 * hl;
-                    const f32x4_t y = *reinterpret_cast<const f32x4_t*>(sm_acc + merge_at<D>(col, d));
+                    const int d = 32 * db + 8 * a4 + 4 * hl_e;
+                    const f32x4_t y = *reinterpret_cast<const f32x4_t*>(sm_acc + merge_at<D>(col_e, d));
                     f32x4_t v;
 #pragma unroll
                     for (int e = 0; e < 4; ++e) v[e] = (acc[db][4 * a4 + e] * f1 + y[e] * f2) * inv;
                     *reinterpret_cast<f32x4_t*>(o + d) = v;
                 }
         }
-        if (hl == 0) {
-            a.m_part[mrow * slots + s] = empty ? -INFINITY : X * kLn2;
-            a.lse_part[mrow * slots + s] = lse_v;
+        if (hl_e == 0) {
+            a.m_part[mrow_e * slots + s] = empty ? -INFINITY : X * kLn2;
+            a.lse_part[mrow_e * slots + s] = lse_v;
         }
     }
 #if FD_WG_TIMELINE
