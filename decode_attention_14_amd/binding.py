@@ -199,13 +199,9 @@ def workspace_bytes(dims: FdDims, max_splits: int) -> int:
     return int(load_library().fd_workspace_bytes(ctypes.byref(dims), int(max_splits)))
 
 
-FD_WORKSPACE_HEADER_BYTES = 256 << 10
-
-
 def new_workspace(nbytes: int, device) -> torch.Tensor:
-    """Device memory for a decode_attention workspace, zero-filled (its
-    header of merge counters must start at zero; calls leave it zero)."""
-    return torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+    """Device memory for a decode_attention workspace (contents irrelevant)."""
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
 
 
 def _ptr(t):

@@ -17,7 +17,6 @@
 #include "fd_internal.h"
 
 static_assert(fdk::kNoallocScratchBytes == FD_NOALLOC_SCRATCH_BYTES, "scratch size in fd.h and the library");
-static_assert(fdk::kMergeHeaderBytes == FD_WORKSPACE_HEADER_BYTES, "workspace header in fd.h and the library");
 
 namespace {
 
@@ -95,15 +94,11 @@ struct Layout {
     int64_t o_off, m_off, lse_off, bytes;
 };
 
-// fd_decode_attention's workspace: a fixed header of merge counters (see
-// fd_decode_attention: at the same place for every call, so that no call's
-// partials ever land on another call's counters), then o_part, m_part and
-// lse_part as fd_decode_partials lays them out, each on a 256-byte boundary.
 Layout workspace_layout(const fd_dims* d, int slots) {
     const int64_t rows = total_rows(d);
     Layout l;
-    l.o_off = fdk::kMergeHeaderBytes;
-    l.m_off = l.o_off + align_up(rows * slots * d->head_dim * 4, kAlign);
+    l.o_off = 0;
+    l.m_off = align_up(rows * slots * d->head_dim * 4, kAlign);
     l.lse_off = l.m_off + align_up(rows * slots * 4, kAlign);
     l.bytes = l.lse_off + align_up(rows * slots * 4, kAlign);
     return l;
@@ -216,9 +211,7 @@ void trace_launch(const char* entry, const fd_dims* d, const fdk::PartialArgs& a
                  a.kv_codes == fdk::kKvE4M3 ? " fp8-kv" : a.kv_codes == fdk::kKvInt8 ? " int8-kv" : "",
                  a.rule.tile_len,
                  a.rule.num_splits, a.rule.slots, a.rule.granule, a.rows, a.row_blocks, kernel,
-                 a.direct || a.rule.slots <= 1 ? "direct output"
-                 : a.merge                     ? "partials merged in the chunk kernel"
-                                               : "partials + merge kernel");
+                 a.rule.slots > 1 && !a.direct ? "partials + merge" : "direct output");
 }
 
 fd_status device_status(hipError_t e, const char* what) {
@@ -581,25 +574,6 @@ fd_status run_attention(const fd_dims* dims, const void* q, const void* k_cache,
     a.m_part = reinterpret_cast<float*>(ws + lay.m_off);
     a.lse_part = reinterpret_cast<float*>(ws + lay.lse_off);
     a.direct = 0;
-    // The bf16 chunk kernel merges in place (one launch): the last workgroup
-    // of each (sequence, KV head, row block) to finish merges its rows,
-    // counted in the workspace header, with the merge kernel's arithmetic.
-    // Only for calls of 2 to 4 slots (a long chunk cut into a few tiles;
-    // more slots take more trips to memory than the merge kernel's wide
-    // form), and not for the no-allocation entry point (its scratch keeps no
-    // state between calls), for more groups than the header holds, nor where
-    // a group's partials pass 4 GiB (buffer offsets).
-    const int64_t groups = (int64_t)dims->batch * dims->num_kv_heads * a.row_blocks;
-    if (!noalloc && fdk::merge_in_chunk(dims->dtype, dims->head_dim, a.rows, a.kv_codes) &&
-        groups <= fdk::kMergeCounters && rule.slots <= fdk::kCombineNarrowSlots &&
-        (int64_t)a.rows * rule.slots * dims->head_dim * 4 < (int64_t(1) << 32)) {
-        a.merge = reinterpret_cast<uint32_t*>(ws);
-        a.out = out;
-        a.lse = lse;
-        trace_launch("attention", dims, a);
-        return device_status(fdk::launch_partials(dims->dtype, dims->head_dim, dims->batch, a, s),
-                             "partial kernel launch");
-    }
     trace_launch("attention", dims, a);
     if ((st = device_status(fdk::launch_partials(dims->dtype, dims->head_dim, dims->batch, a, s),
                             "partial kernel launch")) != FD_OK)

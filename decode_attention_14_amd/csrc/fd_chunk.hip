@@ -1161,121 +1161,6 @@ __device__ __forceinline__ int merge_at(int r, int d) {
     return r * D + (((d >> 2) ^ (r & 15)) << 2);
 }
 
-// The merge inside the chunk kernel (fd_decode_attention over bf16 caches).
-// Every workgroup of a (sequence b, KV head g, row block) group with keys in
-// its tile writes its partials (o_part, lse_part: slot s of each row) with
-// device-scope stores, which go through to the level of the memory system
-// all XCDs share; it then counts itself in the group's arrival counter, and
-// the last of the S_b to arrive merges the group's rows over slots 0 ..
-// S_b - 1 in slot order (so the bits do not depend on the arrival order) and
-// writes out and lse -- the merge of page "FlashDecoding算法原理与多GPU并行
-// 解码实战" (multi-GPU step 3), as in the merge kernels.  Before counting,
-// every thread waits until its own stores have completed and the workgroup
-// synchronises; the last workgroup reads the partials with device-scope
-// loads, which fetch from that shared level, so no cache-wide write-back or
-// invalidation is needed (those would stall every workgroup streaming
-// through the XCD's L2).  The last workgroup sets the counter back to zero:
-// the counters are zero after every call, as they must be before the first.
-constexpr int kAuxDevice = 16;  // cache policy of a buffer access: sc1, device scope
-
-// Buffer resources over the partials of the (sequence, KV head) whose rows
-// start at rowbase: its a.rows rows of `slots` slots in o_part, and the
-// matching lse_part entries (the caller keeps them under 4 GiB).
-struct GroupParts {
-    __amdgpu_buffer_rsrc_t o, lse;
-};
-
-__device__ __forceinline__ GroupParts group_parts(const PartialArgs& a, int64_t rowbase, int D) {
-    const int slots = a.rule.slots;
-    GroupParts gp;
-    gp.o = tile_rsrc(reinterpret_cast<const char*>(a.o_part + rowbase * slots * D),
-                     (uint32_t)((int64_t)a.rows * slots * D * 4));
-    gp.lse = tile_rsrc(reinterpret_cast<const char*>(a.lse_part + rowbase * slots),
-                       (uint32_t)((int64_t)a.rows * slots * 4));
-    return gp;
-}
-
-// The merge of a group's rows over NS slots (2 to 4), with the arithmetic of
-// fd_combine_narrow_kernel: thread tid takes (row, float4 column) items tid,
-// tid + kPT, ..., and issues all their loads before any arithmetic (the
-// device-scope loads take a trip to the shared level each).
-template <int D, int NS>
-__device__ __forceinline__ void chunk_merge_narrow(const PartialArgs& a, const GroupParts& gp, int p0, int nrows,
-                                                   int64_t rowbase, int tid) {
-    constexpr int C4 = D / 4;
-    constexpr int IPT = kChunkRows * C4 / kPT;  // items per thread
-    const int slots = a.rule.slots;
-    float lv[IPT][NS];
-    float4 ov[IPT][NS];
-    int64_t rr[IPT];
-#pragma unroll
-    for (int it = 0; it < IPT; ++it) {
-        const int idx = tid + it * kPT;
-        const int i = idx / C4;
-        const int c4 = idx - i * C4;
-        const int p = p0 + (i < nrows ? i : 0);  // spare items read a valid row, write nothing
-        rr[it] = (int64_t)(p % a.n_rep) * a.q_len + p / a.n_rep;
-        const uint32_t rs = (uint32_t)(rr[it] * slots);
-#pragma unroll
-        for (int sl = 0; sl < NS; ++sl) {
-            lv[it][sl] = __uint_as_float(
-                __builtin_amdgcn_raw_buffer_load_b32(gp.lse, (int)((rs + (uint32_t)sl) * 4u), 0, kAuxDevice));
-            ov[it][sl] = __builtin_bit_cast(
-                float4, __builtin_amdgcn_raw_buffer_load_b128(
-                            gp.o, (int)(((rs + (uint32_t)sl) * D + 4u * (uint32_t)c4) * 4u), 0, kAuxDevice));
-        }
-    }
-#pragma unroll
-    for (int it = 0; it < IPT; ++it) {
-        const int idx = tid + it * kPT;
-        const int i = idx / C4;
-        if (i >= nrows) continue;
-        const int c4 = idx - i * C4;
-        MergeState st{-INFINITY, 0.f, make_float4(0.f, 0.f, 0.f, 0.f)};
-#pragma unroll
-        for (int sl = 0; sl < NS; ++sl) st.m = fmaxf(st.m, lv[it][sl]);
-        if (st.m != -INFINITY) {
-#pragma unroll
-            for (int sl = 0; sl < NS; ++sl) {
-                if (lv[it][sl] == -INFINITY) continue;  // empty slot: its o entry never enters
-                const float wgt = __expf(lv[it][sl] - st.m);
-                st.z += wgt;
-                st.acc.x = fmaf(wgt, ov[it][sl].x, st.acc.x);
-                st.acc.y = fmaf(wgt, ov[it][sl].y, st.acc.y);
-                st.acc.z = fmaf(wgt, ov[it][sl].z, st.acc.z);
-                st.acc.w = fmaf(wgt, ov[it][sl].w, st.acc.w);
-            }
-        }
-        write_merged<true>(st, reinterpret_cast<uint16_t*>(a.out) + (rowbase + rr[it]) * D, c4,
-                           a.lse ? a.lse + rowbase + rr[it] : nullptr);
-    }
-}
-
-// Count this workgroup in counter `group`; the last of the S (2 to 4) to
-// arrive merges packed rows p0 .. p0 + nrows - 1 with the arithmetic of the
-// merge kernel for calls of at most kCombineNarrowSlots slots.
-template <int D>
-__device__ __forceinline__ void chunk_merge_last(const PartialArgs& a, const GroupParts& gp, int64_t group, int S,
-                                                 int p0, int nrows, int64_t rowbase, int tid) {
-    __shared__ int sm_last;
-    wait_vmcnt_le<0>();  // this thread's partial stores have completed
-    __syncthreads();
-    if (tid == 0) {
-        uint32_t* cnt = a.merge + group * kMergeCounterStride;
-        const uint32_t before = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const bool last = before == (uint32_t)(S - 1);
-        if (last) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        sm_last = last ? 1 : 0;
-    }
-    __syncthreads();
-    if (!sm_last) return;
-    // as fd_combine_narrow_kernel: one thread per (row, float4 column); all
-    // of a thread's loads issued before any arithmetic
-    if (S == 2) chunk_merge_narrow<D, 2>(a, gp, p0, nrows, rowbase, tid);
-    else if (S == 3) chunk_merge_narrow<D, 3>(a, gp, p0, nrows, rowbase, tid);
-    else chunk_merge_narrow<D, 4>(a, gp, p0, nrows, rowbase, tid);
-}
-
 template <int D, bool PAGED>
 __global__ __launch_bounds__(kPT) void fd_mfma_chunk_kernel(PartialArgs a) {
 #if FD_WG_TIMELINE
@@ -1334,17 +1219,12 @@ __global__ __launch_bounds__(kPT) void fd_mfma_chunk_kernel(PartialArgs a) {
     const int64_t rowbase = ((int64_t)b * a.Hq + (int64_t)g * n_rep) * q_len;
     const int slots = a.rule.slots;
     const int nrows = min(kChunkRows, R - p0);
-    // Merged in this kernel (chunk_merge_last): a sequence of one tile writes
-    // its output directly, as does tile 0 of an empty one.
-    const bool merge = a.merge != nullptr;
-    const bool direct = a.direct || (merge && S <= 1);
 
-    if (merge && s >= max(S, 1)) return;  // no keys in this slot, nobody reads it
     if (s >= S) {
         for (int idx = tid; idx < nrows; idx += kPT) {
             const int p = p0 + idx;
             const int64_t row = rowbase + (int64_t)(p % n_rep) * q_len + p / n_rep;
-            if (direct) {
+            if (a.direct) {
                 uint4* o = reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(a.out) + row * D);
                 for (int k = 0; k < D / 8; ++k) o[k] = make_uint4(0, 0, 0, 0);
                 if (a.lse) a.lse[row] = -INFINITY;
@@ -1543,7 +1423,6 @@ __global__ __launch_bounds__(kPT) void fd_mfma_chunk_kernel(PartialArgs a) {
     const int p_e = p0 + rg * 32 + col_e;
     const bool valid_e = p_e < R;
     const int64_t mrow_e = rowbase + (int64_t)(p_e % n_rep) * q_len + p_e / n_rep;
-    const int tid_e = w * 64 + (int)lane_e;
 
     // Per-row totals over the two lane halves; then merge the key halves.
     const float m = rs.m;
@@ -1569,82 +1448,55 @@ __global__ __launch_bounds__(kPT) void fd_mfma_chunk_kernel(PartialArgs a) {
         }
     }
     __syncthreads();
-    // The group's buffers of partials (merged here) and this row's place in
-    // them; then the key-half merge of the rows of waves kh = 0.
-    GroupParts gp{};
-    if (merge && !direct) gp = group_parts(a, rowbase, D);
-    const int64_t rr_e = mrow_e - rowbase;
-    if (kh == 0 && valid_e) {
-        const float m2 = sm_m[rg * 32 + col_e];
-        const float M = fmaxf(m, m2);
-        const float f1 = m == -INFINITY ? 0.f : fast_exp2(m - M);
-        const float f2 = m2 == -INFINITY ? 0.f : fast_exp2(m2 - M);
-        const float den = l * f1 + sm_l[rg * 32 + col_e] * f2;
-        const float X = fmaxf(mx, sm_x[rg * 32 + col_e]);
-        const bool empty = M == -INFINITY;
-        const float inv = empty ? 0.f : 1.f / den;
-        const float lse_v = empty ? -INFINITY : (M + log2f(den)) * kLn2;
-        if (direct) {
-            uint16_t* o = reinterpret_cast<uint16_t*>(a.out) + mrow_e * D;
+    if (kh == 1 || !valid_e) return;
+    const float m2 = sm_m[rg * 32 + col_e];
+    const float M = fmaxf(m, m2);
+    const float f1 = m == -INFINITY ? 0.f : fast_exp2(m - M);
+    const float f2 = m2 == -INFINITY ? 0.f : fast_exp2(m2 - M);
+    const float den = l * f1 + sm_l[rg * 32 + col_e] * f2;
+    const float X = fmaxf(mx, sm_x[rg * 32 + col_e]);
+    const bool empty = M == -INFINITY;
+    const float inv = empty ? 0.f : 1.f / den;
+    const float lse_v = empty ? -INFINITY : (M + log2f(den)) * kLn2;
+    if (a.direct) {
+        uint16_t* o = reinterpret_cast<uint16_t*>(a.out) + mrow_e * D;
+#pragma unroll
+        for (int db = 0; db < G::DB; ++db)
+#pragma unroll
+            for (int a4 = 0; a4 < 4; ++a4) {
+                const int d = 32 * db + 8 * a4 + 4 * hl_e;
+                const f32x4_t y = *reinterpret_cast<const f32x4_t*>(sm_acc + merge_at<D>(col_e, d));
+                float v[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = (acc[db][4 * a4 + e] * f1 + y[e] * f2) * inv;
+                uint2 packed;
+                packed.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+                packed.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+                *reinterpret_cast<uint2*>(o + d) = packed;
+            }
+        if (hl_e == 0 && a.lse) a.lse[mrow_e] = lse_v;
+    } else {
+        if (!empty) {
+            float* o = a.o_part + (mrow_e * slots + s) * D;
 #pragma unroll
             for (int db = 0; db < G::DB; ++db)
 #pragma unroll
                 for (int a4 = 0; a4 < 4; ++a4) {
                     const int d = 32 * db + 8 * a4 + 4 * hl_e;
                     const f32x4_t y = *reinterpret_cast<const f32x4_t*>(sm_acc + merge_at<D>(col_e, d));
-                    float v[4];
+                    f32x4_t v;
 #pragma unroll
                     for (int e = 0; e < 4; ++e) v[e] = (acc[db][4 * a4 + e] * f1 + y[e] * f2) * inv;
-                    uint2 packed;
-                    packed.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
-                    packed.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
-                    *reinterpret_cast<uint2*>(o + d) = packed;
+                    *reinterpret_cast<f32x4_t*>(o + d) = v;
                 }
-            if (hl_e == 0 && a.lse) a.lse[mrow_e] = lse_v;
-        } else if (merge) {  // device-scope stores; the merge needs only lse
-            if (!empty) {
-#pragma unroll
-                for (int db = 0; db < G::DB; ++db)
-#pragma unroll
-                    for (int a4 = 0; a4 < 4; ++a4) {
-                        const int d = 32 * db + 8 * a4 + 4 * hl_e;
-                        const f32x4_t y = *reinterpret_cast<const f32x4_t*>(sm_acc + merge_at<D>(col_e, d));
-                        f32x4_t v;
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) v[e] = (acc[db][4 * a4 + e] * f1 + y[e] * f2) * inv;
-                        __builtin_amdgcn_raw_buffer_store_b128(
-                            __builtin_bit_cast(u32x4_t, v), gp.o,
-                            (int)((((uint32_t)rr_e * slots + s) * D + d) * 4u), 0, kAuxDevice);
-                    }
-            }
-            if (hl_e == 0)
-                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lse_v), gp.lse,
-                                                      (int)(((uint32_t)rr_e * slots + s) * 4u), 0, kAuxDevice);
-        } else {
-            if (!empty) {
-                float* o = a.o_part + (mrow_e * slots + s) * D;
-#pragma unroll
-                for (int db = 0; db < G::DB; ++db)
-#pragma unroll
-                    for (int a4 = 0; a4 < 4; ++a4) {
-                        const int d = 32 * db + 8 * a4 + 4 * hl_e;
-                        const f32x4_t y = *reinterpret_cast<const f32x4_t*>(sm_acc + merge_at<D>(col_e, d));
-                        f32x4_t v;
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) v[e] = (acc[db][4 * a4 + e] * f1 + y[e] * f2) * inv;
-                        *reinterpret_cast<f32x4_t*>(o + d) = v;
-                    }
-            }
-            if (hl_e == 0) {
-                a.m_part[mrow_e * slots + s] = empty ? -INFINITY : X * kLn2;
-                a.lse_part[mrow_e * slots + s] = lse_v;
-            }
+        }
+        if (hl_e == 0) {
+            a.m_part[mrow_e * slots + s] = empty ? -INFINITY : X * kLn2;
+            a.lse_part[mrow_e * slots + s] = lse_v;
         }
     }
-    if (merge && !direct)
-        chunk_merge_last<D>(a, gp, ((int64_t)b * a.Hkv + g) * a.row_blocks + rt, S, p0, nrows, rowbase, tid_e);
 #if FD_WG_TIMELINE
-    if (tid_e == 0 && tl_row) {
+    if (tid == 0 && tl_row) {
         tl_row[0] = tl_start;
         tl_row[1] = tl_first;
         tl_row[10] = __builtin_amdgcn_s_memrealtime();

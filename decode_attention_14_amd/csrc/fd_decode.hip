@@ -442,6 +442,7 @@ __global__ __launch_bounds__(kPThreads) FD_OCCUPANCY void fd_partial_kernel(Part
 
 constexpr int kCThreads = 256;
 constexpr int kCWaves = kCThreads / 64;
+constexpr int kCombineWideSlots = 32;  // above this, four waves per row
 
 // Slots that row `row` merges: all `slots`, or its sequence's count.
 static __device__ __forceinline__ int row_slots(const int32_t* spl, int64_t rps, int64_t row, int slots) {
@@ -492,6 +493,7 @@ __global__ __launch_bounds__(kCThreads) void fd_combine_kernel(const float* __re
 // float4 column), kCombineRowsPerThread rows per thread whose loads are all
 // issued before any arithmetic, so each thread keeps several 16-byte loads
 // in flight instead of one per wave-row.
+constexpr int kCombineNarrowSlots = 4;
 constexpr int kCombineRowsPerThread = 4;
 
 template <int D, bool OUT_BF16, int S>

@@ -143,19 +143,19 @@ static __device__ __forceinline__ void merge_into(MergeState& a, const MergeStat
 }
 
 // One wave accumulates the slots first, first + stride, first + 2 stride, ...
-// (< slots) of one row: lse_at(s) gives slot s's lse and o_at(s, c4) float4
-// column c4 of its o.  Lane (slot group sg, float4 column c4) takes every
-// SG-th of those slots, 32 slots of the wave per batch of loads; the slot
-// groups are merged with shuffles, so lanes c4 < D/4 return the wave's state
-// for column c4.
-template <int D, class LseAt, class OAt>
-static __device__ __forceinline__ MergeState merge_slots_wave_by(LseAt lse_at, OAt o_at, int slots, int first,
-                                                                int stride, int lane) {
+// (< slots) of one row: o_row [slots][D], lse_row [slots] fp32.  Lane (slot
+// group sg, float4 column c4) takes every SG-th of those slots, 32 slots of
+// the wave per batch of loads; the slot groups are merged with shuffles, so
+// lanes c4 < D/4 return the wave's state for column c4.
+template <int D>
+static __device__ __forceinline__ MergeState merge_slots_wave(const float* o_row, const float* lse_row, int slots,
+                                                             int first, int stride, int lane) {
     constexpr int C4 = D / 4;     // float4 columns
     constexpr int SG = 64 / C4;   // slot groups (2 for D = 128, 4 for D = 64)
     constexpr int CH = 32 / SG;   // slots per lane per batch
     const int sg = lane / C4;
     const int c4 = lane - sg * C4;
+    const float4* op = reinterpret_cast<const float4*>(o_row) + c4;
     MergeState st{-INFINITY, 0.f, make_float4(0.f, 0.f, 0.f, 0.f)};
     for (int base = first + sg * stride; base < slots; base += SG * CH * stride) {
         float lv[CH];
@@ -163,8 +163,8 @@ static __device__ __forceinline__ MergeState merge_slots_wave_by(LseAt lse_at, O
 #pragma unroll
         for (int k = 0; k < CH; ++k) {
             const int s = base + k * SG * stride;
-            lv[k] = s < slots ? lse_at(s) : -INFINITY;
-            ov[k] = s < slots ? o_at(s, c4) : make_float4(0.f, 0.f, 0.f, 0.f);
+            lv[k] = s < slots ? lse_row[s] : -INFINITY;
+            ov[k] = s < slots ? op[(int64_t)s * C4] : make_float4(0.f, 0.f, 0.f, 0.f);
         }
         float bm = st.m;
 #pragma unroll
@@ -197,16 +197,6 @@ static __device__ __forceinline__ MergeState merge_slots_wave_by(LseAt lse_at, O
         merge_into(st, o);
     }
     return st;
-}
-
-// The same over a row in ordinary memory: o_row [slots][D], lse_row [slots].
-template <int D>
-static __device__ __forceinline__ MergeState merge_slots_wave(const float* o_row, const float* lse_row, int slots,
-                                                             int first, int stride, int lane) {
-    const float4* op = reinterpret_cast<const float4*>(o_row);
-    return merge_slots_wave_by<D>([&](int s) { return lse_row[s]; },
-                                  [&](int s, int c4) { return op[(int64_t)s * (D / 4) + c4]; }, slots, first, stride,
-                                  lane);
 }
 
 // Final output of a merged row for column c4: out (bf16 or fp32) and lse.

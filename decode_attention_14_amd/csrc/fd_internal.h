@@ -65,29 +65,7 @@ struct PartialArgs {
     PagedKV pages;      // pages.table == nullptr: k/v are [B, Hkv, Lmax, D]
     int32_t kv_codes;   // kKvBf16, or the one-byte code format of k/v (bf16 q/out); k_scale is in qk_scale
     float v_scale;      // codes: value of V = code * v_scale (applied to the output)
-    // Partials mode of the bf16 chunk kernel only: arrival counters, one per
-    // (sequence, KV head, row block) kMergeCounterStride words apart, zero on
-    // entry and left zero; the last workgroup of each group to finish merges
-    // the group's rows into out/lse (m_part is then not written).  nullptr:
-    // partials only, merged by the merge kernel.
-    uint32_t* merge;
 };
-
-// Arrival counters of the merge inside the chunk kernel: a fixed header at
-// the start of fd_decode_attention's workspace, one 32-bit counter per
-// (sequence, KV head, row block) in a 128-byte line of its own (atomics on
-// one line are serialised); calls with more groups merge in the merge kernel.
-constexpr int64_t kMergeHeaderBytes = 256 << 10;
-constexpr int kMergeCounterStride = 32;  // 32-bit words between counters
-constexpr int64_t kMergeCounters = kMergeHeaderBytes / (4 * kMergeCounterStride);
-
-// Slot counts of the merge kernels' three forms: one thread per (row,
-// float4 column) up to kCombineNarrowSlots slots, one wave per row up to
-// kCombineWideSlots, four waves per row above.  The merge inside the chunk
-// kernel repeats the first form's arithmetic (so both paths give the same
-// bits) and serves calls of up to kCombineNarrowSlots slots only.
-constexpr int kCombineNarrowSlots = 4;
-constexpr int kCombineWideSlots = 32;
 
 // Packed query rows per workgroup of the matrix-core chunk kernel (row
 // groups of more than 32 rows per KV head).
@@ -117,9 +95,6 @@ int vector_block_rows(int rows);
 // bf16 caches; read once per process).
 bool use_mfma_partials(int dtype, int head_dim, int rows);
 bool vector_kernel_forced();
-// Whether a (dtype, head_dim, rows) call with caches of format kv_codes runs
-// the bf16 chunk kernel, which can merge in place.
-bool merge_in_chunk(int dtype, int head_dim, int rows, int32_t kv_codes);
 
 // Matrix-core launches: row groups of up to 32 rows (fd_mfma.hip), which
 // hands larger ones to the chunk kernel (fd_chunk.hip).

@@ -38,10 +38,6 @@ bool use_mfma_partials(int dtype, int head_dim, int rows) {
     return mfma_partials_supported(dtype, head_dim, rows) && !vector_kernel_forced();
 }
 
-bool merge_in_chunk(int dtype, int head_dim, int rows, int32_t kv_codes) {
-    return kv_codes == kKvBf16 && use_mfma_partials(dtype, head_dim, rows) && rows > 32;
-}
-
 int partial_block_rows(int dtype, int head_dim, int rows) {
     return use_mfma_partials(dtype, head_dim, rows) ? mfma_block_rows(rows) : vector_block_rows(rows);
 }

@@ -125,11 +125,8 @@ fd_status fd_plan_splits(const fd_dims* dims, const int32_t* cache_lens_host, in
 
 /* fd_workspace_bytes -- bytes of workspace fd_decode_attention needs for
  * `max_splits` partial slots per row (0 when max_splits <= 1 or dims are
- * invalid).  The workspace starts with a header of FD_WORKSPACE_HEADER_BYTES
- * (the arrival counters of the merge inside the chunk kernel, see
- * fd_decode_attention), followed by o_part, m_part and lse_part as laid out
- * for fd_decode_partials, each starting on a 256-byte boundary. */
-#define FD_WORKSPACE_HEADER_BYTES (256u << 10)
+ * invalid).  The workspace holds o_part, m_part and lse_part as laid out for
+ * fd_decode_partials, each starting on a 256-byte boundary. */
 uint64_t fd_workspace_bytes(const fd_dims* dims, int32_t max_splits);
 
 /* fd_decode_partials -- the first pass only: per-tile partials.
@@ -179,22 +176,10 @@ fd_status fd_combine_splits(int32_t batch, int32_t num_heads, int32_t q_len, int
  * fd_plan_splits); else `plan` (may be NULL: one tile per sequence).  With a
  * single slot the partial kernel writes out and lse directly and no
  * workspace is needed (`workspace` may be NULL).  Otherwise `workspace`
- * (device memory, 256-byte aligned, caller-owned) must hold at least
- * fd_workspace_bytes(dims, slots) bytes, else FD_ERR_WORKSPACE.
- *
- * The merge.  Calls served by the bf16 chunk kernel (bf16 queries and
- * caches, contiguous or paged, more than 32 query rows per KV head:
- * Hq / Hkv * q_len > 32) with at most FD_WORKSPACE_HEADER_BYTES / 128
- * (sequence, KV head, 128-row block) groups merge inside that kernel: the
- * last of a group's workgroups to finish its tile merges the group's
- * partials in slot order (one launch, bitwise reproducible).  It counts
- * arrivals in the workspace header, which must therefore be all zero before
- * the workspace's first use (allocate it zero-filled); every call leaves the
- * header zero again, so a workspace can be reused without clearing, also
- * under HIP graph replay.  Other calls run a separate merge kernel and do
- * not touch the header.  The rest of the workspace needs no initialisation
- * and is clobbered.  Calls that share a workspace must not run
- * concurrently. */
+ * (device memory, 256-byte aligned, caller-owned, contents irrelevant on
+ * entry and clobbered on return) must hold at least
+ * fd_workspace_bytes(dims, slots) bytes, else FD_ERR_WORKSPACE.  Calls that
+ * share a workspace must not run concurrently. */
 fd_status fd_decode_attention(const fd_dims* dims, const void* q, const void* k_cache,
                               const void* v_cache, const int32_t* cache_lens, float scale,
                               int32_t num_splits, const fd_plan* plan, void* workspace,
@@ -214,9 +199,7 @@ fd_status fd_decode_attention(const fd_dims* dims, const void* q, const void* k_
  * device's scratch address once.  Every call on one GPU uses the same scratch
  * and leaves its contents to the next: calls that may overlap on one GPU
  * (two streams, two threads) race and must be serialised by the caller.
- * Single-slot calls (one tile per sequence) use no scratch at all; calls
- * of the chunk kernel merge in the separate merge kernel here (the scratch
- * keeps no counters between calls). */
+ * Single-slot calls (one tile per sequence) use no scratch at all. */
 #define FD_NOALLOC_SCRATCH_BYTES (32ull << 20)
 fd_status fd_decode_attention_noalloc(const fd_dims* dims, const void* q, const void* k_cache,
                                       const void* v_cache, const int32_t* cache_lens, float scale,
