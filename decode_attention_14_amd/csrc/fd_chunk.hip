@@ -25,7 +25,7 @@
 //                for the two 16-key steps, so P stays in place; V^T comes
 //                from transposed LDS reads.  P enters as bf16, plus its
 //                bf16 remainder while single keys still carry a visible
-//                share of a row's weight (see chunk_softmax).
+//                share of a row's weight (see pipe_needs_remainder).
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -354,12 +354,9 @@ __device__ __forceinline__ bf16x8_t pack8(bf16x2_t a, bf16x2_t b, bf16x2_t c, bf
     return __builtin_shufflevector(ab, cd, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-// Online-softmax statistics and weights of one block (no access to the
-// accumulators, so it can overlap the matrix work of the previous block):
-// tracks the exact max mx, moves the lazy reference m when the block's max
-// passes it by more than kTau (alpha is then the factor that the
-// accumulators still owe, else 1), and writes P as bf16 head ph and, if lo,
-// remainder pl.
+// Online softmax of a block, in base 2 with a lazily moved reference max m
+// (moved when a key passes it by more than kTau, so the accumulators are
+// rescaled rarely), the exact running max tracked apart for the partial's m.
 //
 // The running sum l adds the weights that the products actually use: the
 // bf16 heads, plus the remainders where they are used.  With weights rounded
@@ -369,32 +366,40 @@ __device__ __forceinline__ bf16x8_t pack8(bf16x2_t a, bf16x2_t b, bf16x2_t c, bf
 // row's running sum takes the remainder product as well, which bounds that
 // sum's spread by 2^-9 * sqrt(1/16 / 3) * rms(v - o) = 2.8e-4 rms(v - o), and
 // keeps few dominant keys (short rows, peaked scores) exact to 2^-17.  c > 0.
-__device__ __forceinline__ void chunk_softmax(const f32x16_t& st, float c, float& m, float& l, float& mx, float& alpha,
-                                              bool& moved, bf16x8_t (&ph)[2], bf16x8_t (&pl)[2], bool& lo) {
-    // IEEE maximum (v_maximum3_f32): unlike fmaxf it needs no quieting of
-    // the matrix results first; a NaN score propagates either way.
-    float sm = st[0];
-#pragma unroll
-    for (int r = 1; r < 16; ++r) sm = __builtin_elementwise_maximum(sm, st[r]);
-    const float bm = sm == -INFINITY ? -INFINITY : sm * c;
-    mx = fmaxf(mx, bm);
-    moved = __any(bm > m + kTau);
-    const float bw = fmaxf(bm, __shfl_xor(bm, 32));
-    const float mn = moved ? fmaxf(m, bw) : m;
-    alpha = m == -INFINITY ? 0.f : fast_exp2(m - mn);
-    m = mn;
-    l *= alpha;
-    const float mref = m == -INFINITY ? 0.f : m;
-    lo = __any(fast_exp2(bm - mref) * 16.f > l);
-    // P rounded to bf16 two values per instruction; the block's share of
-    // the running sum accumulates the rounded values with bf16 dot products
-    // against ones (exact products, fp32 sums).
-    float pr[16];
+
+// max and sum of x over lanes i and i ^ 32 (the two halves of a 32x32 tile
+// hold the same rows); the swap hands every lane the pair (x of the low
+// lane, x of the high lane), so both lanes get the same bits.
+__device__ __forceinline__ float xor32_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Running statistics of one lane's query row in the pipelined kernel: the
+// reference max m (scaled scores, log2 units; -inf before the row's first
+// visible key), the exponent offset mref (m, or 0 while m is -inf), thr, the
+// raw score above which a key moves the reference (m + kTau in raw units,
+// -inf while m is -inf), the running sum l of the weights the products use
+// (this lane's keys), and the running max xr of this lane's raw scores.
+struct RowStat {
+    float m, mref, thr, l, xr;
+};
+
+// Weights of a block against the offset mref, in place: the scores st become
+// 2^(c s - mref); their bf16 heads ph, and l = l0 plus the heads (bf16 dot
+// products against ones: exact products, fp32 sums).
+__device__ __forceinline__ void pipe_weights(f32x16_t& st, float c, float mref, float l0, bf16x8_t (&ph)[2],
+                                             float& l) {
+    f32x16_t& pr = st;
 #pragma unroll
     for (int r = 0; r < 16; ++r) pr[r] = fast_exp2(fmaf(st[r], c, -mref));
     const bf16x2_t ones = {(__bf16)1.f, (__bf16)1.f};
     bf16x2_t h2[8];
-    float bs = 0.f;
+    float bs = l0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         h2[i] = __builtin_convertvector(f32x2_t{pr[2 * i], pr[2 * i + 1]}, bf16x2_t);
@@ -402,17 +407,98 @@ __device__ __forceinline__ void chunk_softmax(const f32x16_t& st, float c, float
     }
     ph[0] = pack8(h2[0], h2[1], h2[2], h2[3]);
     ph[1] = pack8(h2[4], h2[5], h2[6], h2[7]);
-    if (lo) {
-        bf16x2_t l2[8];
+    l = bs;
+}
+
+// Whether the block also needs its remainder (pipe_remainder): whether some
+// row's largest weight in the block, 2^(c sm - mref), passes 1/16 of the
+// row's running sum, this block's heads included (both lane halves).
+__device__ __forceinline__ bool pipe_needs_remainder(float sm, float c, const RowStat& rs) {
+    const float pm = fast_exp2(fmaf(sm, c, -rs.mref));
+    return __any(pm * 16.f > xor32_sum(rs.l));
+}
+
+// The common path of one block's online softmax comes in two halves without
+// branches, so that the scheduler can place each between matrix
+// instructions: the first beside the previous block's P.V product, the
+// second beside the next block's score product.
+//
+// First half, in place on the block's (masked) scores st: the block's raw
+// max sm (also folded into xr), whether it moves the reference (some row's
+// max passes thr), the exponents c s - mref, and the weights of the first
+// eight of them.
+__device__ __forceinline__ void pipe_softmax1(f32x16_t& st, float c, RowStat& rs, float& sm, bool& moved) {
+    // IEEE maximum (v_maximum3_f32): no quieting of the matrix results.
+    sm = st[0];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const f32x2_t d = {pr[2 * i] - (float)h2[i][0], pr[2 * i + 1] - (float)h2[i][1]};
-            l2[i] = __builtin_convertvector(d, bf16x2_t);
-            bs = __builtin_amdgcn_fdot2_f32_bf16(l2[i], ones, bs, false);
-        }
-        pl[0] = pack8(l2[0], l2[1], l2[2], l2[3]);
-        pl[1] = pack8(l2[4], l2[5], l2[6], l2[7]);
+    for (int r = 1; r < 16; ++r) sm = __builtin_elementwise_maximum(sm, st[r]);
+    rs.xr = __builtin_elementwise_maximum(rs.xr, sm);
+    moved = __any(sm > rs.thr);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) st[r] = fmaf(st[r], c, -rs.mref);
+#pragma unroll
+    for (int r = 0; r < 8; ++r) st[r] = fast_exp2(st[r]);
+}
+
+// Second half: the other eight weights (st then holds all sixteen), their
+// bf16 heads ph, the running sum (l0 keeps it from before the block, for a
+// reference move) and the remainder test.  When the reference moves, the
+// caller recomputes the weights (pipe_move).
+__device__ __forceinline__ void pipe_softmax2(f32x16_t& st, float c, RowStat& rs, float sm, float& l0,
+                                              bf16x8_t (&ph)[2], bool& lo) {
+#pragma unroll
+    for (int r = 8; r < 16; ++r) st[r] = fast_exp2(st[r]);
+    const bf16x2_t ones = {(__bf16)1.f, (__bf16)1.f};
+    bf16x2_t h2[8];
+    l0 = rs.l;
+    float bs = l0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        h2[i] = __builtin_convertvector(f32x2_t{st[2 * i], st[2 * i + 1]}, bf16x2_t);
+        bs = __builtin_amdgcn_fdot2_f32_bf16(h2[i], ones, bs, false);
     }
+    ph[0] = pack8(h2[0], h2[1], h2[2], h2[3]);
+    ph[1] = pack8(h2[4], h2[5], h2[6], h2[7]);
+    rs.l = bs;
+    lo = pipe_needs_remainder(sm, c, rs);
+}
+
+// The rare path of a block whose max moved the reference: the new reference
+// is the larger of the old one and the row's block max (both lane halves);
+// alpha is the factor the sum and the accumulators owe (0 after -inf).  The
+// weights, the sum and the remainder test are redone against it from the
+// block's scores st, in place (recomputed by the caller: the common path's
+// weights may have overflowed, and keeping the scores alive would cost
+// registers).
+__device__ __forceinline__ float pipe_move(f32x16_t& st, float c, float cinv, float sm, float l0, RowStat& rs,
+                                           bf16x8_t (&ph)[2], bool& lo) {
+    const float bw = xor32_max(sm * c);
+    const float mn = fmaxf(rs.m, bw);
+    const float alpha = rs.m == -INFINITY ? 0.f : fast_exp2(rs.m - mn);
+    rs.m = mn;
+    rs.mref = mn == -INFINITY ? 0.f : mn;
+    rs.thr = mn == -INFINITY ? -INFINITY : (mn + kTau) * cinv;
+    pipe_weights(st, c, rs.mref, l0 * alpha, ph, rs.l);
+    lo = pipe_needs_remainder(sm, c, rs);
+    return alpha;
+}
+
+// The bf16 remainder pl = pr - ph of a block's weights, and its share of the
+// running sum (taken when pipe_needs_remainder says so).
+__device__ __forceinline__ void pipe_remainder(const f32x16_t& pr, const bf16x8_t (&ph)[2], bf16x8_t (&pl)[2],
+                                               float& l) {
+    const bf16x2_t ones = {(__bf16)1.f, (__bf16)1.f};
+    bf16x2_t l2[8];
+    float bs = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const bf16x8_t& h = ph[i / 4];
+        const f32x2_t d = {pr[2 * i] - (float)h[2 * (i % 4)], pr[2 * i + 1] - (float)h[2 * (i % 4) + 1]};
+        l2[i] = __builtin_convertvector(d, bf16x2_t);
+        bs = __builtin_amdgcn_fdot2_f32_bf16(l2[i], ones, bs, false);
+    }
+    pl[0] = pack8(l2[0], l2[1], l2[2], l2[3]);
+    pl[1] = pack8(l2[4], l2[5], l2[6], l2[7]);
     l += bs;
 }
 
@@ -425,8 +511,8 @@ template <int D, int OFF>
 __device__ __forceinline__ void chunk_step(bool edge, const uint32_t (&ka)[CGeo<D>::KS],
                                            const uint32_t (&va)[CGeo<D>::DB][2], const bf16x8_t (&qf)[CGeo<D>::KS],
                                            f32x16_t (&acc)[CGeo<D>::DB], bf16x8_t (&vf)[CGeo<D>::DB * 2],
-                                           bf16x8_t (&ph)[2], float& m, float& l, float& mx, int key0, int rend,
-                                           float c, int hl) {
+                                           bf16x8_t (&ph)[2], RowStat& rs, int key0, int rend, float c, float cinv,
+                                           int hl) {
     using G = CGeo<D>;
     f32x16_t st;
     chunk_scores<D, OFF>(ka, qf, st);
@@ -436,10 +522,20 @@ __device__ __forceinline__ void chunk_step(bool edge, const uint32_t (&ka)[CGeo<
             if (key0 + 8 * (r >> 2) + 4 * hl + (r & 3) >= rend) st[r] = -INFINITY;
     }
     chunk_pv<D>(vf, ph, acc);
-    float alpha;
-    bool moved, lo;
-    bf16x8_t pl[2];
-    chunk_softmax(st, c, m, l, mx, alpha, moved, ph, pl, lo);
+    // The common path of this block's softmax (as the pipelined kernel's:
+    // the block max, the move test, the weights against the current
+    // reference, the sum and the remainder test); the scores stay for a
+    // reference move.  IEEE maximum (v_maximum3_f32): no quieting of the
+    // matrix results.
+    float sm = st[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) sm = __builtin_elementwise_maximum(sm, st[r]);
+    rs.xr = __builtin_elementwise_maximum(rs.xr, sm);
+    const bool moved = __any(sm > rs.thr);
+    f32x16_t pr = st;
+    const float l0 = rs.l;
+    pipe_weights(pr, c, rs.mref, l0, ph, rs.l);
+    bool lo = pipe_needs_remainder(sm, c, rs);
     // P.V products of the previous block with the softmax's vector work
     // between them.
 #pragma unroll
@@ -448,12 +544,25 @@ __device__ __forceinline__ void chunk_step(bool edge, const uint32_t (&ka)[CGeo<
         __builtin_amdgcn_sched_group_barrier(0x002, FD_CHUNK_VALU_PER_MFMA, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
+    // The rare paths read their inputs through register barriers inside the
+    // branch, so the compiler cannot compute them on every block instead.
+    if (moved) {
+        f32x16_t sc = st;
+        float smv = sm, l0v = l0;
+        asm volatile("" : "+v"(sc), "+v"(smv), "+v"(l0v));
+        const float al = pipe_move(sc, c, cinv, smv, l0v, rs, ph, lo);
+        pr = sc;
+#pragma unroll
+        for (int db = 0; db < G::DB; ++db) acc[db] *= al;
+    }
+    bf16x8_t pl[2];
+    if (lo) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) asm volatile("" : "+v"(pr[r]));
+        pipe_remainder(pr, ph, pl, rs.l);
+    }
     // This block's V operands (the products above have taken the previous ones).
     chunk_v_reads_wait<D, OFF>(va, vf);
-    if (moved) {
-#pragma unroll
-        for (int db = 0; db < G::DB; ++db) acc[db] *= alpha;
-    }
     if (lo) chunk_pv<D>(vf, pl, acc);
 }
 
@@ -557,7 +666,8 @@ __global__ __launch_bounds__(kCT) void fd_mfma_chunk8_kernel(PartialArgs a) {
     for (int db = 0; db < G::DB; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
-    float m = -INFINITY, l = 0.f, mx = -INFINITY;
+    RowStat rs = {-INFINITY, 0.f, -INFINITY, 0.f, -INFINITY};
+    const float cinv = __uint_as_float(uniform(__float_as_uint(1.f / c)));
 
     const char* kt;
     const char* vt;
@@ -675,18 +785,19 @@ __global__ __launch_bounds__(kCT) void fd_mfma_chunk8_kernel(PartialArgs a) {
             }
             const int key0 = lo + j * G::SKEYS + kh * kCBK;
             const bool edge = key0 + kCBK > mask_from;
-            if (u == 0) chunk_step<D, 0>(edge, ka, va, qf, acc, vf, ph, m, l, mx, key0, rend, c, hl);
-            if (u == 1) chunk_step<D, G::STGB>(edge, ka, va, qf, acc, vf, ph, m, l, mx, key0, rend, c, hl);
+            if (u == 0) chunk_step<D, 0>(edge, ka, va, qf, acc, vf, ph, rs, key0, rend, c, cinv, hl);
+            if (u == 1) chunk_step<D, G::STGB>(edge, ka, va, qf, acc, vf, ph, rs, key0, rend, c, cinv, hl);
             if constexpr (kCNS > 2)
-                if (u == 2) chunk_step<D, 2 * G::STGB>(edge, ka, va, qf, acc, vf, ph, m, l, mx, key0, rend, c, hl);
+                if (u == 2) chunk_step<D, 2 * G::STGB>(edge, ka, va, qf, acc, vf, ph, rs, key0, rend, c, cinv, hl);
         }
     }
     chunk_pv<D>(vf, ph, acc);
     wait_vmcnt_le<0>();
 
     // Per-row totals over the two lane halves; then merge the key halves.
-    l += __shfl_xor(l, 32);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m = rs.m;
+    const float l = xor32_sum(rs.l);
+    const float mx = xor32_max(rs.xr) * c;
     __syncthreads();  // the ring is free
     float* sm_acc = reinterpret_cast<float*>(smem);  // [kCRG][32][RS]
     float* sm_m = sm_acc + kCRG * 32 * RS;           // [kCRG][32]
@@ -873,140 +984,6 @@ __device__ __forceinline__ void wait_stages(int n) {
         wait_vmcnt_le<0>();
 }
 
-// max and sum of x over lanes i and i ^ 32 (the two halves of a 32x32 tile
-// hold the same rows); the swap hands every lane the pair (x of the low
-// lane, x of the high lane), so both lanes get the same bits.
-__device__ __forceinline__ float xor32_max(float x) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float xor32_sum(float x) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-// Running statistics of one lane's query row in the pipelined kernel: the
-// reference max m (scaled scores, log2 units; -inf before the row's first
-// visible key), the exponent offset mref (m, or 0 while m is -inf), thr, the
-// raw score above which a key moves the reference (m + kTau in raw units,
-// -inf while m is -inf), the running sum l of the weights the products use
-// (this lane's keys), and the running max xr of this lane's raw scores.
-struct RowStat {
-    float m, mref, thr, l, xr;
-};
-
-// Weights of a block against the offset mref, in place: the scores st become
-// 2^(c s - mref); their bf16 heads ph, and l = l0 plus the heads (bf16 dot
-// products against ones: exact products, fp32 sums).
-__device__ __forceinline__ void pipe_weights(f32x16_t& st, float c, float mref, float l0, bf16x8_t (&ph)[2],
-                                             float& l) {
-    f32x16_t& pr = st;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) pr[r] = fast_exp2(fmaf(st[r], c, -mref));
-    const bf16x2_t ones = {(__bf16)1.f, (__bf16)1.f};
-    bf16x2_t h2[8];
-    float bs = l0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        h2[i] = __builtin_convertvector(f32x2_t{pr[2 * i], pr[2 * i + 1]}, bf16x2_t);
-        bs = __builtin_amdgcn_fdot2_f32_bf16(h2[i], ones, bs, false);
-    }
-    ph[0] = pack8(h2[0], h2[1], h2[2], h2[3]);
-    ph[1] = pack8(h2[4], h2[5], h2[6], h2[7]);
-    l = bs;
-}
-
-// Whether the block also needs its remainder (pipe_remainder): whether some
-// row's largest weight in the block, 2^(c sm - mref), passes 1/16 of the
-// row's running sum, this block's heads included (both lane halves).
-__device__ __forceinline__ bool pipe_needs_remainder(float sm, float c, const RowStat& rs) {
-    const float pm = fast_exp2(fmaf(sm, c, -rs.mref));
-    return __any(pm * 16.f > xor32_sum(rs.l));
-}
-
-// The common path of one block's online softmax comes in two halves without
-// branches, so that the scheduler can place each between matrix
-// instructions: the first beside the previous block's P.V product, the
-// second beside the next block's score product.
-//
-// First half, in place on the block's (masked) scores st: the block's raw
-// max sm (also folded into xr), whether it moves the reference (some row's
-// max passes thr), the exponents c s - mref, and the weights of the first
-// eight of them.
-__device__ __forceinline__ void pipe_softmax1(f32x16_t& st, float c, RowStat& rs, float& sm, bool& moved) {
-    // IEEE maximum (v_maximum3_f32): no quieting of the matrix results.
-    sm = st[0];
-#pragma unroll
-    for (int r = 1; r < 16; ++r) sm = __builtin_elementwise_maximum(sm, st[r]);
-    rs.xr = __builtin_elementwise_maximum(rs.xr, sm);
-    moved = __any(sm > rs.thr);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) st[r] = fmaf(st[r], c, -rs.mref);
-#pragma unroll
-    for (int r = 0; r < 8; ++r) st[r] = fast_exp2(st[r]);
-}
-
-// Second half: the other eight weights (st then holds all sixteen), their
-// bf16 heads ph, the running sum (l0 keeps it from before the block, for a
-// reference move) and the remainder test.  When the reference moves, the
-// caller recomputes the weights (pipe_move).
-__device__ __forceinline__ void pipe_softmax2(f32x16_t& st, float c, RowStat& rs, float sm, float& l0,
-                                              bf16x8_t (&ph)[2], bool& lo) {
-#pragma unroll
-    for (int r = 8; r < 16; ++r) st[r] = fast_exp2(st[r]);
-    const bf16x2_t ones = {(__bf16)1.f, (__bf16)1.f};
-    bf16x2_t h2[8];
-    l0 = rs.l;
-    float bs = l0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        h2[i] = __builtin_convertvector(f32x2_t{st[2 * i], st[2 * i + 1]}, bf16x2_t);
-        bs = __builtin_amdgcn_fdot2_f32_bf16(h2[i], ones, bs, false);
-    }
-    ph[0] = pack8(h2[0], h2[1], h2[2], h2[3]);
-    ph[1] = pack8(h2[4], h2[5], h2[6], h2[7]);
-    rs.l = bs;
-    lo = pipe_needs_remainder(sm, c, rs);
-}
-
-// The rare path of a block whose max moved the reference: the new reference
-// is the larger of the old one and the row's block max (both lane halves);
-// alpha is the factor the sum and the accumulators owe (0 after -inf).  The
-// weights, the sum and the remainder test are redone against it from the
-// block's scores st, in place (recomputed by the caller: the common path's
-// weights may have overflowed, and keeping the scores alive would cost
-// registers).
-__device__ __forceinline__ float pipe_move(f32x16_t& st, float c, float cinv, float sm, float l0, RowStat& rs,
-                                           bf16x8_t (&ph)[2], bool& lo) {
-    const float bw = xor32_max(sm * c);
-    const float mn = fmaxf(rs.m, bw);
-    const float alpha = rs.m == -INFINITY ? 0.f : fast_exp2(rs.m - mn);
-    rs.m = mn;
-    rs.mref = mn == -INFINITY ? 0.f : mn;
-    rs.thr = mn == -INFINITY ? -INFINITY : (mn + kTau) * cinv;
-    pipe_weights(st, c, rs.mref, l0 * alpha, ph, rs.l);
-    lo = pipe_needs_remainder(sm, c, rs);
-    return alpha;
-}
-
-// The bf16 remainder pl = pr - ph of a block's weights, and its share of the
-// running sum (see chunk_softmax for when it is taken).
-__device__ __forceinline__ void pipe_remainder(const f32x16_t& pr, const bf16x8_t (&ph)[2], bf16x8_t (&pl)[2],
-                                               float& l) {
-    const bf16x2_t ones = {(__bf16)1.f, (__bf16)1.f};
-    bf16x2_t l2[8];
-    float bs = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const bf16x8_t& h = ph[i / 4];
-        const f32x2_t d = {pr[2 * i] - (float)h[2 * (i % 4)], pr[2 * i + 1] - (float)h[2 * (i % 4) + 1]};
-        l2[i] = __builtin_convertvector(d, bf16x2_t);
-        bs = __builtin_amdgcn_fdot2_f32_bf16(l2[i], ones, bs, false);
-    }
-    pl[0] = pack8(l2[0], l2[1], l2[2], l2[3]);
-    pl[1] = pack8(l2[4], l2[5], l2[6], l2[7]);
-    l += bs;
-}
 
 // Transposed LDS read (ds_read_b64_tr_b16, lane layout as tr_read_wait) at
 // byte offset off of the V stage array sv.
