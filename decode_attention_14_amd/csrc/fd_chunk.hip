@@ -177,8 +177,7 @@ struct CGeo8 {
     static constexpr int PW = 2 * NDMA / kCW;         // instructions per wave per stage (K and V)
     static constexpr int TENB = CGeo<D>::SKEYS * ROWB;
     static constexpr int STGB = 2 * TENB;             // K rows, then V rows
-    static constexpr int NQ = STGB / 16 / kCT;        // 16-byte chunks each thread dequantises
-    static_assert((2 * NDMA) % kCW == 0 && PW >= 1 && STGB % (16 * kCT) == 0, "even split");
+    static_assert((2 * NDMA) % kCW == 0 && PW >= 1 && STGB % (8 * kCT) == 0, "even split");
 };
 
 // Start this wave's loads of code stage j into dst (see chunk_stage_at).
@@ -210,36 +209,34 @@ __device__ __forceinline__ void chunk_stage8_at(const PagedKV& pk, const int32_t
 }
 
 // Dequantise a landed code stage (src, format KV) into the bf16 stage layout
-// (dst), exactly (see codes_to_bf16):
-// thread t converts 16-byte chunks t, t + kCT, ... through lds_load_b128 /
-// lds_write_b128, so the stage loads still in flight are not waited for.
+// (dst), exactly (see codes_to_bf16): thread t converts the 8-byte code units
+// t, t + kCT, ... (8 codes each, one 16-byte bf16 chunk) through lds_load_b64
+// / lds_write_b128, so the stage loads still in flight are not waited for.
+// The 8 lanes of a write cycle (8 lanes over 128 bytes of banks) convert 8
+// consecutive units of one code row, one aligned group of 8 bf16 chunks, which
+// cswz keeps on 8 distinct chunks modulo 8.
 template <int D, int KV>
 __device__ __forceinline__ void chunk_dequant_stage(const char* src, char* dst, int tid) {
     using G = CGeo<D>;
     using G8 = CGeo8<D>;
-    constexpr int QPT = G8::TENB / 16;  // chunks per tensor
-    u32x4_t x[G8::NQ];
+    constexpr int NU = G8::STGB / 8 / kCT;  // units per thread
+    constexpr int UPT = G8::TENB / 8;       // units per tensor
+    constexpr int UPR = G8::ROWB / 8;       // units per code row
+    u32x2_t x[NU];
 #pragma unroll
-    for (int n = 0; n < G8::NQ; ++n) x[n] = lds_load_b128(lds_addr(src + (n * kCT + tid) * 16));
+    for (int n = 0; n < NU; ++n) x[n] = lds_load_b64(lds_addr(src + (n * kCT + tid) * 8));
 #pragma unroll
-    for (int n = 0; n < G8::NQ; ++n) {
+    for (int n = 0; n < NU; ++n) {
         const int q = n * kCT + tid;
-        const int tsr = q / QPT;  // 0: K, 1: V
-        const int rem = q - tsr * QPT;
-        const int r = rem / G8::CH;
-        const int c8 = rem - r * G8::CH;  // codes of dims 16 c8 .. 16 c8 + 15
-        uint32_t bw[8];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) codes_to_bf16<KV>(x[n][i], bw[2 * i], bw[2 * i + 1]);
+        const int tsr = q / UPT;  // 0: K, 1: V
+        const int rem = q - tsr * UPT;
+        const int r = rem / UPR;
+        const int c = rem - r * UPR;  // codes of dims 8 c .. 8 c + 7
+        uint32_t bw[4];
+        codes_to_bf16<KV>(x[n][0], bw[0], bw[1]);
+        codes_to_bf16<KV>(x[n][1], bw[2], bw[3]);
         char* o = dst + tsr * G::SKB * G::BLKB + (r / kCBK) * G::BLKB;
-        // 8 lanes per LDS write cycle over 128 bytes of banks: lanes in the
-        // upper half of a code row (and, for 64-byte code rows, lanes of odd
-        // rows) write their odd chunk first, so each 8-lane group covers 8
-        // distinct chunks modulo 8.
-        const bool odd_first = (c8 >= G8::CH / 2) != (G8::CH == 4 && (r & 1));
-        const u32x4_t lo4 = u32x4_t{bw[0], bw[1], bw[2], bw[3]}, hi4 = u32x4_t{bw[4], bw[5], bw[6], bw[7]};
-        lds_write_b128(o + cswz<D>(r % kCBK, 2 * c8 + (odd_first ? 1 : 0)), odd_first ? hi4 : lo4);
-        lds_write_b128(o + cswz<D>(r % kCBK, 2 * c8 + (odd_first ? 0 : 1)), odd_first ? lo4 : hi4);
+        lds_write_b128(o + cswz<D>(r % kCBK, c), u32x4_t{bw[0], bw[1], bw[2], bw[3]});
     }
 }
 

@@ -234,33 +234,19 @@ __device__ __forceinline__ int qf_dim(int grp, int ks) {
 
 template <int D>
 struct DQ {
-    static constexpr int NQ = LGeo<D, true>::BLKB / 16 / 64;  // 16-byte V chunks per lane
-    static constexpr int KC = D / 64;                          // 16-byte K chunks per lane
+    static constexpr int NU = LGeo<D, true>::BLKB / 8 / 64;  // 8-byte V code units per lane
+    static constexpr int KC = D / 64;                         // 16-byte K chunks per lane
 };
 
-// The code chunk (row r, physical chunk p) that lane `lane` reads in its
-// n-th round of the V conversion: consecutive lanes take consecutive 16-byte
-// chunks of the block, so the reads cover the LDS banks in order.
-template <int D>
-__device__ __forceinline__ void dq_row_chunk(int n, int lane, int& r, int& p) {
-    constexpr int CH8 = LGeo<D, true>::CH;
-    const int q = n * 64 + lane;
-    r = q / CH8;
-    p = q % CH8;
-}
-
-// LDS reads of one landed code block (at src): the lane's V chunks (xv) and
-// its K operand chunks (xk), as plain loads the compiler waits for.
+// LDS reads of one landed code block (at src): the lane's V code units (xv:
+// unit n * 64 + lane of the block, so each read covers consecutive bytes)
+// and its K operand chunks (xk), as plain loads the compiler waits for.
 template <int D>
 __device__ __forceinline__ void codes_read(const char* src, int lane, int grp, int col,
-                                           u32x4_t (&xv)[DQ<D>::NQ], u32x4_t (&xk)[DQ<D>::KC]) {
+                                           u32x2_t (&xv)[DQ<D>::NU], u32x4_t (&xk)[DQ<D>::KC]) {
     using L = LGeo<D, true>;
 #pragma unroll
-    for (int n = 0; n < DQ<D>::NQ; ++n) {
-        int r, p;
-        dq_row_chunk<D>(n, lane, r, p);
-        xv[n] = lds_load_b128(lds_addr(src + L::BLKB + r * L::ROWB + p * 16));
-    }
+    for (int n = 0; n < DQ<D>::NU; ++n) xv[n] = lds_load_b64(lds_addr(src + L::BLKB + (n * 64 + lane) * 8));
 #pragma unroll
     for (int k = 0; k < DQ<D>::KC; ++k) {
         const int c = grp * DQ<D>::KC + k;  // chunk of dims 16 c .. 16 c + 15
@@ -268,31 +254,27 @@ __device__ __forceinline__ void codes_read(const char* src, int lane, int grp, i
     }
 }
 
-// Write the bf16 V block at dst from codes_read's V chunks and turn its K
-// chunks into the score product's A operands.
+// Write the bf16 V block at dst from codes_read's V units and turn its K
+// chunks into the score product's A operands.  A V unit (8 codes of row r,
+// physical code chunk pu / 2, half pu % 2) becomes one 16-byte bf16 chunk.
+// A 16-byte write serves 8 lanes per LDS cycle over 128 bytes of banks; the 8
+// lanes of a group hold 8 consecutive units of one code row, whose bf16
+// chunks form one aligned group of 8 (cswz8 XORs whole code chunks, bf16
+// chunk pairs, so an aligned group stays one), and swz keeps them on 8
+// distinct chunks modulo 8: the writes are conflict-free in lane order.
 template <int D, int KV>
-__device__ __forceinline__ void codes_settle(u32x4_t (&xv)[DQ<D>::NQ], u32x4_t (&xk)[DQ<D>::KC], char* dst,
+__device__ __forceinline__ void codes_settle(u32x2_t (&xv)[DQ<D>::NU], u32x4_t (&xk)[DQ<D>::KC], char* dst,
                                              int lane, bf16x8_t (&kf)[Geo<D>::KS]) {
-    using L = LGeo<D, true>;
-    constexpr int NQ = DQ<D>::NQ;
+    constexpr int UPR = LGeo<D, true>::ROWB / 8;  // 8-byte units per code row
 #pragma unroll
-    for (int n = 0; n < NQ; ++n) {
-        int r, p;
-        dq_row_chunk<D>(n, lane, r, p);
-        const int c = p ^ cswz8<D>(r);  // 16 codes of row r = dims 16c .. 16c + 15
-        uint32_t b[8];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) codes_to_bf16<KV>(xv[n][i], b[2 * i], b[2 * i + 1]);
-        // A 16-byte write serves 8 lanes per LDS cycle over 128 bytes of
-        // banks.  Lanes whose chunk pair lies in the upper half of the code
-        // row (and, for 64-byte code rows, lanes of odd rows) write their odd
-        // chunk first, so each write instruction's 8-lane groups cover 8
-        // distinct chunks modulo 8 (the swizzle only reorders the chunks of a
-        // row among its lanes).
-        const bool odd_first = (c >= L::CH / 2) != (L::CH == 4 && (r & 1));
-        const u32x4_t lo4 = u32x4_t{b[0], b[1], b[2], b[3]}, hi4 = u32x4_t{b[4], b[5], b[6], b[7]};
-        lds_write_b128(dst + swz<D>(r, 2 * c + (odd_first ? 1 : 0)), odd_first ? hi4 : lo4);
-        lds_write_b128(dst + swz<D>(r, 2 * c + (odd_first ? 0 : 1)), odd_first ? lo4 : hi4);
+    for (int n = 0; n < DQ<D>::NU; ++n) {
+        const int u = n * 64 + lane;
+        const int r = u / UPR, pu = u % UPR;
+        const int c = (((pu >> 1) ^ cswz8<D>(r)) << 1) | (pu & 1);  // 8 codes of row r = dims 8c .. 8c + 7
+        uint32_t b[4];
+        codes_to_bf16<KV>(xv[n][0], b[0], b[1]);
+        codes_to_bf16<KV>(xv[n][1], b[2], b[3]);
+        lds_write_b128(dst + swz<D>(r, c), u32x4_t{b[0], b[1], b[2], b[3]});
     }
     // K: 16 codes per chunk, 8 per operand (ks = 2 k + half).
 #pragma unroll
@@ -551,7 +533,8 @@ __global__ __launch_bounds__(KV != kKvBf16 ? 64 * kMW8 : kMT) void fd_mfma_parti
         bf16x8_t kf[G::KS];
         bf16x4_t vf[G::DB];
         if constexpr (C8) {
-            u32x4_t xv[DQ<D>::NQ], xk[DQ<D>::KC];
+            u32x2_t xv[DQ<D>::NU];
+            u32x4_t xk[DQ<D>::KC];
             codes_read<D>(kb, lane, grp, col, xv, xk);
             codes_settle<D, KV>(xv, xk, conv, lane, kf);
             v_fragments<D>(conv, vf, grp, col);

@@ -21,6 +21,7 @@ typedef __attribute__((ext_vector_type(4))) short s16x4_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 typedef __attribute__((ext_vector_type(2))) float f32x2_t;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
 typedef __attribute__((address_space(3))) void lds_void_t;
 
 // Lazy rescale threshold of the online softmax, in log2 units: a running
@@ -52,6 +53,10 @@ static __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // loads in flight.  The caller makes sure the bytes have landed.
 static __device__ __forceinline__ u32x4_t lds_load_b128(uint32_t addr) {
     return *(const __attribute__((address_space(3))) u32x4_t*)(uintptr_t)addr;
+}
+// The same for 8 bytes (the compiler may pair two into one ds_read2_b64).
+static __device__ __forceinline__ u32x2_t lds_load_b64(uint32_t addr) {
+    return *(const __attribute__((address_space(3))) u32x2_t*)(uintptr_t)addr;
 }
 
 // N (4 or 8) transposing reads, ds_read_b64_tr_b16 (in each 16-lane group,

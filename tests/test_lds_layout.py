@@ -14,8 +14,8 @@ different addresses.  ``ds_read_b128`` follows no such simple pass model; the
 K-operand maps were chosen by measuring the kernels themselves.
 The lane -> (row, chunk) maps below restate the address arithmetic of the
 kernels (decode: 16x16 layouts, lane = 16 grp + col; chunk kernel: 32x32
-layouts, lane = 32 hl + col; dequantisation: lane l converts 16-byte code
-chunk n * lanes + l).
+layouts, lane = 32 hl + col; dequantisation: lane l converts 8-byte code
+unit n * lanes + l into one 16-byte bf16 chunk).
 """
 import os
 import re
@@ -157,37 +157,40 @@ def test_chunk_merge_block_layout(D):
             assert not write_b128(addr), (D, db, a4)
 
 
-def dequant_chunks(D, odd_first_rule):
-    """(row, first bf16 chunk, second bf16 chunk) of each 16-byte code chunk
-    q in lane order: code rows of D bytes (CH8 chunks), bf16 rows of 2D."""
-    ch8 = D // 16
+def dequant_units(D, code_swz):
+    """(row, bf16 chunk) written for each 8-byte code unit u in lane order:
+    code rows of D bytes whose 16-byte chunks are XOR-swizzled by
+    code_swz(row) (the decode kernel's ring; 0 for the chunk kernel's plain
+    code stage), bf16 rows of 2D bytes (16-byte chunk c = dims 8c .. 8c + 7)."""
+    upr = D // 8
     out = []
-    for q in range(16 * ch8):
-        r, c = q // ch8, q % ch8
-        odd_first = odd_first_rule(r, c, ch8)
-        out.append((r, 2 * c + (1 if odd_first else 0), 2 * c + (0 if odd_first else 1)))
+    for u in range(16 * upr):
+        r, pu = u // upr, u % upr
+        out.append((r, (((pu >> 1) ^ code_swz(r)) << 1) | (pu & 1)))
     return out
-
-
-KERNEL_RULE = lambda r, c, ch8: (c >= ch8 // 2) != (ch8 == 4 and (r & 1) == 1)  # noqa: E731
 
 
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("sw,name", [(SWF, "decode"), (CSWF, "chunk")])
 def test_dequant_writes_conflict_free(D, sw, name):
-    ch = 2 * D // 16
-    chunks = dequant_chunks(D, KERNEL_RULE)
-    for which in (1, 2):
-        for n in range(len(chunks) // 64):
-            def addr(l, n=n, which=which):
-                r, a, b = chunks[n * 64 + l]
-                return r * 2 * D + (((a if which == 1 else b) ^ sw(r, ch)) << 4)
-            assert not write_b128(addr), (name, D, which, n)
+    # Any code swizzle that XORs a row's chunk index with a value below its
+    # chunk count keeps each write cycle conflict-free: the decode kernel's
+    # cswz8 is one of these, the chunk kernel's plain code stage is k = 0.
+    ch, ch8 = 2 * D // 16, D // 16
+    for k in range(ch8):
+        units = dequant_units(D, lambda r, k=k: (5 * r + k) % ch8)
+        for n in range(len(units) // 64):
+            def addr(l, n=n):
+                r, c = units[n * 64 + l]
+                return r * 2 * D + ((c ^ sw(r, ch)) << 4)
+            assert not write_b128(addr), (name, D, k, n)
 
 
 def test_models_see_the_plain_conflicts():
     # The checks can fail: unswizzled transposed reads of 256-byte rows at
-    # one chunk pair, and dequantisation writes in plain even/odd order.
+    # one chunk pair, and dequantisation writes of 16-byte code chunks in even/odd
+    # order.
     assert tr_read(lambda l: ((l >> 2) & 7) * 256 + 8 * (l & 3))
-    plain = dequant_chunks(128, lambda r, c, ch8: False)
-    assert write_b128(lambda l: plain[l][0] * 256 + (plain[l][1] << 4))
+    # (Lane l converting 16-byte code chunk l and writing its even bf16 chunk
+    # first: the 8 lanes of a cycle hit only 4 chunks modulo 8.)
+    assert write_b128(lambda l: (l // 8) * 256 + ((2 * (l % 8)) << 4))
