@@ -40,11 +40,11 @@ class FdDims(ctypes.Structure):
 class FdPlan(ctypes.Structure):
     _fields_ = [("tile_len", ctypes.c_int32), ("max_splits", ctypes.c_int32),
                 ("workspace_bytes", ctypes.c_uint64), ("work_units", ctypes.c_int32),
-                ("reserved", ctypes.c_int32)]
+                ("spans", ctypes.c_int32)]
 
     def __repr__(self):
         return (f"FdPlan(tile_len={self.tile_len}, max_splits={self.max_splits}, "
-                f"workspace_bytes={self.workspace_bytes}, work_units={self.work_units})")
+                f"workspace_bytes={self.workspace_bytes}, work_units={self.work_units}, spans={self.spans})")
 
 
 class FdKvPages(ctypes.Structure):
@@ -174,6 +174,10 @@ class Plan:
     @property
     def workspace_bytes(self):
         return self.plan.workspace_bytes
+
+    @property
+    def spans(self):
+        return self.plan.spans
 
 
 def plan_splits(dims: FdDims, cache_lens_host, num_splits: int = 0, num_cus: int = 0) -> Plan:

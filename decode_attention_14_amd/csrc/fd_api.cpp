@@ -55,6 +55,14 @@ constexpr int kMinTile = 256;
 constexpr int kTileGranule = 64;
 constexpr int kUnitsPerCUEqual = 1;
 constexpr int kUnitsPerCUMixed = 4;
+// Mixed lengths on the matrix-core decode kernel (up to 32 rows per KV head):
+// the plan asks for balanced spans (fdk::SplitRule::spans), sized for up to
+// kSpanWGsPerCU workgroups per compute unit.  Every span workgroup scans the
+// batch's lengths, so batches above kSpanMaxBatch keep tiles.
+constexpr int kSpanWGsPerCU = 2;
+constexpr int kSpanMaxBatch = 256;
+constexpr int kSpanBlockKeys = 16;
+constexpr int kSpanMax = 1 << 20;
 
 int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -121,7 +129,9 @@ fd_status resolve_rule(int32_t num_splits, const fd_plan* plan, fdk::SplitRule* 
     if (plan->tile_len < 1)
         return fail(FD_ERR_INVALID, "plan tile_len %d < 1 (a forced-count plan needs num_splits)",
                     plan->tile_len);
-    *rule = {plan->tile_len, 1, plan->max_splits, 1};
+    if (plan->spans < 0 || plan->spans > kSpanMax)
+        return fail(FD_ERR_INVALID, "plan spans %d outside [0, %d]", plan->spans, kSpanMax);
+    *rule = {plan->tile_len, 1, plan->max_splits, 1, plan->max_splits >= 2 ? plan->spans : 0};
     return FD_OK;
 }
 
@@ -176,6 +186,7 @@ fdk::PartialArgs make_args(const fd_dims* d, const void* q, const void* k, const
     a.k = k;
     a.v = v;
     a.cache_lens = lens;
+    a.batch = d->batch;
     a.Hq = d->num_q_heads;
     a.Hkv = d->num_kv_heads;
     a.q_len = d->q_len;
@@ -205,12 +216,12 @@ void trace_launch(const char* entry, const fd_dims* d, const fdk::PartialArgs& a
                          : a.rows > 32 ? "fd_mfma_chunk_kernel" : "fd_mfma_partial_kernel";
     std::fprintf(stderr,
                  "[fd] %s: B=%d Hq=%d Hkv=%d D=%d q_len=%d Lmax=%d dtype=%d%s%s | tile_len=%d num_splits=%d "
-                 "slots=%d granule=%d | rows/KV head=%d row_blocks=%d | %s, %s\n",
+                 "slots=%d granule=%d spans=%d | rows/KV head=%d row_blocks=%d | %s, %s\n",
                  entry, d->batch, d->num_q_heads, d->num_kv_heads, d->head_dim, d->q_len, d->max_cache_len,
                  d->dtype, a.pages.table ? " paged" : "",
                  a.kv_codes == fdk::kKvE4M3 ? " fp8-kv" : a.kv_codes == fdk::kKvInt8 ? " int8-kv" : "",
                  a.rule.tile_len,
-                 a.rule.num_splits, a.rule.slots, a.rule.granule, a.rows, a.row_blocks, kernel,
+                 a.rule.num_splits, a.rule.slots, a.rule.granule, a.rule.spans, a.rows, a.row_blocks, kernel,
                  a.rule.slots > 1 && !a.direct ? "partials + merge" : "direct output");
 }
 
@@ -311,6 +322,22 @@ fd_status fd_plan_splits(const fd_dims* dims, const int32_t* cache_lens_host, in
         p.tile_len = (int32_t)T;
         p.max_splits = (int32_t)smax;
         p.work_units = (int32_t)std::min<int64_t>(units, INT32_MAX);
+        if (min_len != max_len && rows <= 32 && fdk::use_mfma_partials(dims->dtype, dims->head_dim, rows) &&
+            dims->batch <= kSpanMaxBatch && units > (int64_t)num_cus * kSpanWGsPerCU) {
+            // More tiles than one round of workgroups: equal spans instead,
+            // two per CU, none shorter than kMinTile keys, and enough slots
+            // that a pair of the longest sequence spans ceil(blocks / span) + 1
+            // of them.
+            int64_t blocks = 0;
+            for (int b = 0; b < dims->batch; ++b) blocks += ceil_div(cache_lens_host[b], kSpanBlockKeys);
+            const int64_t nspans = std::min<int64_t>(
+                {(int64_t)num_cus * kSpanWGsPerCU, ceil_div(blocks * dims->num_kv_heads, kMinTile / kSpanBlockKeys),
+                 (int64_t)kSpanMax});
+            const int64_t span = std::max<int64_t>(1, ceil_div(blocks * dims->num_kv_heads, nspans));
+            const int64_t need = ceil_div(ceil_div(max_len, kSpanBlockKeys), span) + 1;
+            p.max_splits = (int32_t)std::min<int64_t>(FD_MAX_SPLITS, std::max<int64_t>(smax, need));
+            p.spans = p.max_splits >= 2 ? (int32_t)nspans : 0;
+        }
     }
     p.workspace_bytes = p.max_splits > 1 ? (uint64_t)workspace_layout(dims, p.max_splits).bytes : 0;
     *plan = p;

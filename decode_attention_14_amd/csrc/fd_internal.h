@@ -19,6 +19,7 @@ struct SplitRule {
     int32_t num_splits;
     int32_t slots;
     int32_t granule;
+    int32_t spans;  // > 0: the decode kernel cuts the batch's key blocks into this many equal spans (slots >= 2)
 };
 
 // Where the K/V rows of a paged cache live.  Key j of sequence b, KV head g
@@ -56,7 +57,7 @@ struct PartialArgs {
     float* lse_part; // [rows_total, slots]
     void* out;       // [rows_total, D]             (direct mode)
     float* lse;      // [rows_total] or nullptr
-    int32_t Hq, Hkv, q_len, Lmax, n_rep;
+    int32_t batch, Hq, Hkv, q_len, Lmax, n_rep;
     int32_t rows;       // query rows per (sequence, KV head): n_rep * q_len
     int32_t row_blocks; // workgroups per (sequence, KV head, tile) along rows
     SplitRule rule;

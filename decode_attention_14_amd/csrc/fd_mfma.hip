@@ -50,6 +50,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <cstdio>
+#include <cstdlib>
+
 #include "fd_device.h"
 #include "fd_internal.h"
 #include "fd_mfma_common.h"
@@ -102,6 +105,12 @@ constexpr int kMW = kMT / 64;     // waves per workgroup
 constexpr int kMW8 = FD_CODE8_WAVES;  // waves per workgroup over one-byte caches
 constexpr int kKB = 16;           // keys per block
 constexpr int kNS = FD_MFMA_STAGES;
+// Span mode: line positions in front of each (sequence, KV head) pair, the
+// fixed cost of one piece (its first loads and its merge) in 16-key blocks:
+// a span holding more pieces gets fewer blocks.  Measured on the 32-sequence
+// variable-length batch: FP8 caches 58.7 against 60.4 us at 16 (57.7-58.0 at
+// 32), bf16 caches 101.9 against 102.0 us (103.1 at 32).
+constexpr int kSpanPieceBlocks = 16;
 
 template <int D>
 struct Geo {
@@ -374,63 +383,49 @@ __device__ __forceinline__ void load_fragments(const char* kb, const char* vb, b
     v_fragments<D>(vb, vf, grp, col);
 }
 
+// Launch geometry and LDS bytes of the decode kernel.
+template <int D, int NB, int KV>
+struct DecodeGeo {
+    static constexpr bool C8 = KV != kKvBf16;  // one-byte codes
+    static constexpr int MW = C8 ? kMW8 : kMW;  // waves per workgroup
+    static constexpr int MT = 64 * MW;
+    static constexpr int NR = 16 * NB;          // query rows per workgroup
+    static constexpr int RS = D + 4;            // padded row stride of the merge area (floats)
+    static constexpr int MERGEB = MW * (NR * RS + 3 * NR) * 4;
+    static constexpr int RINGB = MW * LGeo<D, C8>::WAVEB;
+    static constexpr int SMEMB = RINGB > MERGEB ? RINGB : MERGEB;
+};
+
+// One work unit of the decode kernel: KV head g of sequence b (L visible
+// keys), keys [lo, hi) (lo < hi), partial slot s.  Slots [pad_from, slots)
+// of the unit's rows get the empty state (m_part = lse_part = -inf, o_part
+// untouched); pad_from = slots pads nothing.  smem: the kernel's LDS block;
+// on return every wave is past its last LDS access of the unit only after a
+// barrier, which the caller places before reusing it.
 template <int D, int NB, bool CAUSAL, bool PAGED, int KV>
-__global__ __launch_bounds__(KV != kKvBf16 ? 64 * kMW8 : kMT) void fd_mfma_partial_kernel(PartialArgs a) {
-    constexpr bool C8 = KV != kKvBf16;  // one-byte codes
+__device__ __forceinline__ void partial_unit(const PartialArgs& a, char* smem, int g, int b, int s, int L, int lo,
+                                             int hi, int pad_from, uint64_t& tl_first) {
+    using DG = DecodeGeo<D, NB, KV>;
+    constexpr bool C8 = DG::C8;
     using G = Geo<D>;
     using LG = LGeo<D, C8>;
-    constexpr int MW = C8 ? kMW8 : kMW;  // waves per workgroup
-    constexpr int MT = 64 * MW;
+    constexpr int MW = DG::MW;
+    constexpr int MT = DG::MT;
     constexpr int NS = LG::NS;
     constexpr int ESZ = C8 ? 1 : 2;  // bytes per stored K/V element
-    constexpr int NR = 16 * NB;  // query rows per workgroup
-    constexpr int RS = D + 4;    // padded row stride of the merge area (floats)
-    constexpr int MERGEB = MW * (NR * RS + 3 * NR) * 4;
-    constexpr int SMEMB = MW * LG::WAVEB > MERGEB ? MW * LG::WAVEB : MERGEB;
-    __shared__ __attribute__((aligned(16))) char smem[SMEMB];
+    constexpr int NR = DG::NR;
+    constexpr int RS = DG::RS;
+    (void)tl_first;
 
-    // KV head fastest: workgroups are dealt to the eight XCDs round-robin in
-    // launch order, so consecutive ids take the heads of one (tile, sequence)
-    // and every XCD gets the same mix of tiles (all heads of a sequence have
-    // the same length).  With the tile fastest instead, a tile index would
-    // pin to a subset of XCDs and short sequences would leave some idle.
-    const int g = blockIdx.x;
-    const int s = blockIdx.y;
-    const int b = blockIdx.z;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int w = (int)uniform((uint32_t)(tid >> 6));
     const int grp = lane >> 4;
     const int col = lane & 15;
-#if FD_WG_TIMELINE
-    const uint64_t tl_start = __builtin_amdgcn_s_memrealtime();
-    uint64_t tl_first = 0;
-#endif
-
-    int L = a.cache_lens[b];
-    L = L < 0 ? 0 : (L > a.Lmax ? a.Lmax : L);
-    int lo, hi, S;
-    tile_of(a.rule, L, s, lo, hi, S);
-    lo = (int)uniform((uint32_t)lo);
-    hi = (int)uniform((uint32_t)hi);
 
     const int nrows = a.rows;
     const int64_t row0 = ((int64_t)b * a.Hq + (int64_t)g * a.n_rep) * a.q_len;
     const int slots = a.rule.slots;
-
-    if (s >= S) {
-        if (a.direct) {
-            for (int idx = tid; idx < nrows * D; idx += MT)
-                reinterpret_cast<uint16_t*>(a.out)[row0 * D + idx] = 0;
-            if (a.lse && tid < nrows) a.lse[row0 + tid] = -INFINITY;
-            return;
-        }
-        if (tid < nrows) {
-            a.m_part[(row0 + tid) * slots + s] = -INFINITY;
-            a.lse_part[(row0 + tid) * slots + s] = -INFINITY;
-        }
-        return;
-    }
 
     // Visible-key end of this lane's query row in each N block.  Causal rows
     // t of a chunk see keys < L - q_len + t + 1; the smallest end (t = 0)
@@ -631,8 +626,165 @@ __global__ __launch_bounds__(KV != kKvBf16 ? 64 * kMW8 : kMT) void fd_mfma_parti
             *reinterpret_cast<f32x4_t*>(a.o_part + (row * slots + s) * D + 4 * c4) = o;
         }
     }
+    // Slots past this unit's (span mode: the last segment of its KV head).
+    const int npad = slots - pad_from;
+    if (npad > 0) {
+        for (int idx = tid; idx < nrows * npad; idx += MT) {
+            const int r = idx / npad;
+            const int sl = pad_from + (idx - r * npad);
+            a.m_part[(row0 + r) * slots + sl] = -INFINITY;
+            a.lse_part[(row0 + r) * slots + sl] = -INFINITY;
+        }
+    }
+}
+
+// Span mode (equal shares of a ragged batch's keys per workgroup, as page
+// "FlashDecoding算法原理与多GPU并行解码实战", variable-length section, fills
+// equal token bins per device): the (sequence, KV head) pairs' 16-key blocks
+// laid end to end (sequence-major, then KV head, each pair's blocks in key
+// order, each pair preceded by kSpanPieceBlocks positions that stand for the
+// fixed cost of a piece: its first loads and its merge), cut into
+// rule.spans equal contiguous spans; workgroup w runs spans w, w + grid, ...
+// (the launch makes grid = spans, so one each)
+// A span runs one unit per pair it touches; the pair's units take slots 0,
+// 1, ... in span order (slot = span - the span of the pair's first block),
+// and the span holding a pair's last block pads the pair's remaining slots.
+// The span length is at least ceil(line length / spans) and at least
+// ceil(max blocks of a pair / (slots - 1)), so no pair needs more than
+// `slots` units whatever the lengths are.  Sequences without keys are padded
+// whole by workgroup b % grid.  Every workgroup computes the totals from
+// cache_lens itself (wave-uniform scalar loop over the batch).
+template <int D, int NB, bool CAUSAL, bool PAGED, int KV, bool SPANS>
+__global__ __launch_bounds__(KV != kKvBf16 ? 64 * kMW8 : kMT) void fd_mfma_partial_kernel(PartialArgs a) {
+    using DG = DecodeGeo<D, NB, KV>;
+    __shared__ __attribute__((aligned(16))) char smem[DG::SMEMB];
+    uint64_t tl_first = 0;
 #if FD_WG_TIMELINE
-    if (tid == 0) {
+    const uint64_t tl_start = __builtin_amdgcn_s_memrealtime();
+#endif
+    const int slots = a.rule.slots;
+    if constexpr (!SPANS) {
+        // Tile mode.  KV head fastest: workgroups are dealt to the eight XCDs
+        // round-robin in launch order, so consecutive ids take the heads of
+        // one (tile, sequence) and every XCD gets the same mix of tiles (all
+        // heads of a sequence have the same length).  With the tile fastest
+        // instead, a tile index would pin to a subset of XCDs and short
+        // sequences would leave some idle.
+        const int g = blockIdx.x;
+        const int s = blockIdx.y;
+        const int b = blockIdx.z;
+        int L = a.cache_lens[b];
+        L = L < 0 ? 0 : (L > a.Lmax ? a.Lmax : L);
+        int lo, hi, S;
+        tile_of(a.rule, L, s, lo, hi, S);
+        lo = (int)uniform((uint32_t)lo);
+        hi = (int)uniform((uint32_t)hi);
+        if (s >= S) {
+            const int tid = threadIdx.x;
+            const int64_t row0 = ((int64_t)b * a.Hq + (int64_t)g * a.n_rep) * a.q_len;
+            if (a.direct) {
+                for (int idx = tid; idx < a.rows * D; idx += DG::MT)
+                    reinterpret_cast<uint16_t*>(a.out)[row0 * D + idx] = 0;
+                if (a.lse && tid < a.rows) a.lse[row0 + tid] = -INFINITY;
+                return;
+            }
+            if (tid < a.rows) {
+                a.m_part[(row0 + tid) * slots + s] = -INFINITY;
+                a.lse_part[(row0 + tid) * slots + s] = -INFINITY;
+            }
+            return;
+        }
+        partial_unit<D, NB, CAUSAL, PAGED, KV>(a, smem, g, b, s, L, lo, hi, slots, tl_first);
+    } else {
+        // Span state: span sp of nsp, [R0, R1) of per blocks; the current
+        // pair (sb, sg) of sb's snb blocks and sL keys, sC the first block of
+        // sequence sb's pairs.
+        const int nsp = a.rule.spans;
+        int sp = blockIdx.x;
+        int sb = 0, sg = 0, snb = 0, sL = 0;
+        int64_t sC = 0, per = 1, R0 = 0, R1 = 0, N = 0;
+        bool more = false;
+        auto clamp_len = [&](int b) {
+            const int L = a.cache_lens[b];
+            return L < 0 ? 0 : (L > a.Lmax ? a.Lmax : L);
+        };
+        // Start span sp: more = it holds blocks; then (sb, sg) is the pair
+        // holding block R0.
+        auto begin_span = [&]() {
+            R0 = (int64_t)sp * per;
+            R1 = R0 + per < N ? R0 + per : N;
+            more = R0 < R1;
+            if (!more) return;
+            sC = 0;
+            for (sb = 0; sb < a.batch; ++sb) {
+                sL = clamp_len(sb);
+                snb = (sL + kKB - 1) / kKB;
+                const int64_t wseq = snb > 0 ? (int64_t)a.Hkv * (kSpanPieceBlocks + snb) : 0;
+                if (snb > 0 && sC + wseq > R0) break;
+                sC += wseq;
+            }
+            sg = R0 > sC ? (int)((R0 - sC) / (kSpanPieceBlocks + snb)) : 0;
+        };
+        int nbmax = 0;
+        for (int b = 0; b < a.batch; ++b) {
+            const int nb = (clamp_len(b) + kKB - 1) / kKB;
+            N += nb > 0 ? (int64_t)a.Hkv * (kSpanPieceBlocks + nb) : 0;
+            nbmax = nb > nbmax ? nb : nbmax;
+        }
+        per = (N + nsp - 1) / nsp;
+        const int64_t per_min = (nbmax + slots - 2) / (slots - 1);
+        per = per > per_min ? per : per_min;
+        per = per > 1 ? per : 1;
+        // Sequences without keys: every slot of every row empty.
+        for (int b = blockIdx.x; b < a.batch; b += gridDim.x) {
+            if (clamp_len(b) > 0) continue;
+            const int64_t r0 = (int64_t)b * a.Hq * a.q_len;
+            const int64_t n = (int64_t)a.Hq * a.q_len * slots;
+            for (int64_t idx = threadIdx.x; idx < n; idx += DG::MT) {
+                a.m_part[r0 * slots + idx] = -INFINITY;
+                a.lse_part[r0 * slots + idx] = -INFINITY;
+            }
+        }
+        begin_span();
+        for (int it = 0;; ++it) {
+            // The next piece: in this span, else in this workgroup's next span.
+            bool done = false;
+            for (;;) {
+                if (more && sC + (int64_t)sg * (kSpanPieceBlocks + snb) + kSpanPieceBlocks < R1) break;
+                sp += gridDim.x;
+                if (sp >= nsp) {
+                    done = true;
+                    break;
+                }
+                begin_span();
+            }
+            if (done) break;
+            const int64_t st = sC + (int64_t)sg * (kSpanPieceBlocks + snb) + kSpanPieceBlocks;  // first block
+            const int64_t en = st + snb;
+            const int blo = (int)((R0 > st ? R0 : st) - st);
+            const int bhi = (int)((R1 < en ? R1 : en) - st);
+            const int g = sg, b = sb, L = sL;
+            const int s = sp - (int)(st / per);
+            const int lo = (int)uniform((uint32_t)(blo * kKB));
+            const int hi = (int)uniform((uint32_t)(bhi * kKB < L ? bhi * kKB : L));
+            const int pad_from = en <= R1 ? s + 1 : slots;
+            // Next pair: the next KV head, else the next sequence with keys.
+            if (++sg == a.Hkv) {
+                sg = 0;
+                sC += (int64_t)a.Hkv * (kSpanPieceBlocks + snb);
+                snb = 0;
+                while (snb == 0 && ++sb < a.batch) {
+                    sL = clamp_len(sb);
+                    snb = (sL + kKB - 1) / kKB;
+                }
+                more = sb < a.batch;
+            }
+            if (it > 0) __syncthreads();  // the previous unit's LDS reads are done
+            partial_unit<D, NB, CAUSAL, PAGED, KV>(a, smem, g, b, s, L, lo, hi, pad_from, tl_first);
+        }
+    }
+#if FD_WG_TIMELINE
+    if (threadIdx.x == 0) {
         const uint64_t t = __builtin_amdgcn_s_memrealtime();
         uint64_t* row = timeline_row();
         if (row) {
@@ -645,22 +797,73 @@ __global__ __launch_bounds__(KV != kKvBf16 ? 64 * kMW8 : kMT) void fd_mfma_parti
 #endif
 }
 
+// FD_TRACE=1 in the environment: print each span launch's grid on stderr.
+bool span_trace() {
+    static const bool on = [] {
+        const char* e = std::getenv("FD_TRACE");
+        return e != nullptr && e[0] != '\0' && e[0] != '0';
+    }();
+    return on;
+}
 
-template <int D, int NB, int KV>
-void launch_nb_kv(int batch, const PartialArgs& a, hipStream_t stream) {
-    dim3 grid(a.Hkv, a.rule.slots, batch), block(KV != kKvBf16 ? 64 * kMW8 : kMT);
+// Workgroups of kernel K resident at once on the current device, as many per
+// compute unit as its registers and LDS allow (cached per device).
+template <auto K>
+int span_workgroups(int threads) {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+    if (dev >= 0 && dev < 64 && cached[dev] > 0) return cached[dev];
+    int cus = 0, occ = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 1;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, K, threads, 0) != hipSuccess || occ < 1) occ = 1;
+    const int n = cus * occ;
+    if (dev >= 0 && dev < 64) cached[dev] = n;
+    return n;
+}
+
+// A span-mode launch cuts the batch into min(plan spans, resident workgroups)
+// spans, one workgroup each: more spans than can run at once would only add
+// per-span fills and merges (measured: 512 spans on the 256 resident
+// workgroups of the one-byte kernel took 64 against 60 us on the
+// variable-length batch).
+template <auto K>
+void launch_decode(dim3 grid, dim3 block, const PartialArgs& a, hipStream_t stream) {
+    if (a.rule.spans > 0) {
+        const int n = span_workgroups<K>((int)block.x);
+        PartialArgs as = a;
+        as.rule.spans = a.rule.spans < n ? a.rule.spans : n;
+        if (span_trace())
+            std::fprintf(stderr, "[fd] span launch: %d spans asked, %d resident workgroups\n", a.rule.spans, n);
+        hipLaunchKernelGGL(K, dim3((unsigned)as.rule.spans), block, 0, stream, as);
+        return;
+    }
+    hipLaunchKernelGGL(K, grid, block, 0, stream, a);
+}
+
+template <int D, int NB, int KV, bool SPANS>
+void launch_nb_kv_s(int batch, const PartialArgs& a, hipStream_t stream) {
+    const dim3 grid(a.Hkv, a.rule.slots, batch), block(KV != kKvBf16 ? 64 * kMW8 : kMT);
     const bool paged = a.pages.table != nullptr;
     if (a.q_len > 1) {
         if (paged)
-            hipLaunchKernelGGL((fd_mfma_partial_kernel<D, NB, true, true, KV>), grid, block, 0, stream, a);
+            launch_decode<fd_mfma_partial_kernel<D, NB, true, true, KV, SPANS>>(grid, block, a, stream);
         else
-            hipLaunchKernelGGL((fd_mfma_partial_kernel<D, NB, true, false, KV>), grid, block, 0, stream, a);
+            launch_decode<fd_mfma_partial_kernel<D, NB, true, false, KV, SPANS>>(grid, block, a, stream);
     } else {
         if (paged)
-            hipLaunchKernelGGL((fd_mfma_partial_kernel<D, NB, false, true, KV>), grid, block, 0, stream, a);
+            launch_decode<fd_mfma_partial_kernel<D, NB, false, true, KV, SPANS>>(grid, block, a, stream);
         else
-            hipLaunchKernelGGL((fd_mfma_partial_kernel<D, NB, false, false, KV>), grid, block, 0, stream, a);
+            launch_decode<fd_mfma_partial_kernel<D, NB, false, false, KV, SPANS>>(grid, block, a, stream);
     }
+}
+
+template <int D, int NB, int KV>
+void launch_nb_kv(int batch, const PartialArgs& a, hipStream_t stream) {
+    if (a.rule.spans > 0)
+        launch_nb_kv_s<D, NB, KV, true>(batch, a, stream);
+    else
+        launch_nb_kv_s<D, NB, KV, false>(batch, a, stream);
 }
 
 template <int D, int NB>

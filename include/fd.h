@@ -90,15 +90,34 @@ typedef struct fd_dims {
 
 /* A split plan.  Sequence b is cut into tiles of `tile_len` keys,
  * S_b = min(ceil(L_b / tile_len), max_splits) of them; when the ceiling
- * exceeds max_splits the last tile also takes the remaining keys.  Callers
- * may fill a plan by hand (tile_len >= 1, 1 <= max_splits <= FD_MAX_SPLITS)
- * or get one from fd_plan_splits. */
+ * exceeds max_splits the last tile also takes the remaining keys.
+ *
+ * With spans > 0 (and max_splits >= 2) the matrix-core decode kernel
+ * (bf16 queries, up to 32 query rows per KV head, any cache format or
+ * layout) balances the batch instead.  A launch uses n = min(spans, the
+ * workgroups of the kernel that runs resident at once on the device) spans,
+ * one workgroup each.  The 16-key blocks of all (sequence, KV head) pairs
+ * with keys are laid on one line, sequence by sequence and head by head,
+ * each pair's blocks preceded by 16 positions that stand for the fixed cost
+ * of a piece; the line is cut into n equal contiguous spans of
+ * max(ceil(line length / n), ceil(longest sequence's blocks / (max_splits -
+ * 1))) positions, and the blocks of a pair inside one span are one split.  The pieces of a pair fill its slots 0, 1, ... in key order
+ * (slot = span index - index of the span holding the pair's first block)
+ * and its remaining slots are empty (m_part = lse_part = -inf, o_part
+ * untouched), as are all slots of a sequence without keys.  The merged
+ * result is the same attention; which keys share a split differs from the
+ * tile rule.  Other kernels (fp32 queries, longer query chunks) keep the
+ * tile rule.
+ *
+ * Callers may fill a plan by hand (tile_len >= 1, 1 <= max_splits <=
+ * FD_MAX_SPLITS, 0 <= spans <= 2^20; zero-initialise it) or get one from
+ * fd_plan_splits. */
 typedef struct fd_plan {
     int32_t tile_len;         /* keys per tile */
     int32_t max_splits;       /* partial slots per row */
     uint64_t workspace_bytes; /* bytes fd_decode_attention needs (0 if max_splits == 1) */
     int32_t work_units;       /* (sequence, KV head, row block, tile) units holding keys */
-    int32_t reserved;
+    int32_t spans;            /* > 0: this many balanced spans on the matrix-core decode kernel, 0: tiles */
 } fd_plan;
 
 /* fd_plan_splits -- choose tile length and split counts from host lengths.
@@ -115,7 +134,13 @@ typedef struct fd_plan {
  * and four per compute unit otherwise, at least 256 keys (below
  * about 256 keys per chunk launch overhead eats the gain, page
  * "FlashDecoding算法原理..." benchmark section), at most the longest sequence,
- * raised if needed so no sequence needs more than FD_MAX_SPLITS.
+ * raised if needed so no sequence needs more than FD_MAX_SPLITS.  When the
+ * lengths differ, the batch has at most 256 sequences, the call goes to the
+ * matrix-core decode kernel and the tiles outnumber two per compute unit,
+ * the plan also asks for two spans per compute unit (spans of at least 256
+ * keys) and raises max_splits to what they need
+ * (equal shares of the batch's keys, as page "FlashDecoding算法原理..."
+ * variable-length section allots them to devices).  splits_per_seq reports the tile rule's counts.
  * `num_cus` is the compute-unit count to plan for; 0 queries the current
  * HIP device (the only device call this function may make).
  * Errors: FD_ERR_INVALID for bad dims, negative lengths, lengths above

@@ -48,6 +48,9 @@ def _declare(lib):
     lib.orc_attention_split.restype = i32
     lib.orc_attention_sequential.argtypes = [i32] * 7 + [vp, vp, vp, vp, dbl, i32, vp, vp, i32]
     lib.orc_attention_sequential.restype = i32
+    lib.orc_attention_ranges.argtypes = ([i32] * 7 + [vp, vp, vp, vp, dbl, i32, vp, vp]
+                                         + [vp] * 5 + [i32])
+    lib.orc_attention_ranges.restype = i32
     lib.orc_merge_lse.argtypes = [ctypes.c_long, i32, i32, vp, vp, vp, vp]
     lib.orc_merge_lse.restype = i32
     return lib
@@ -139,6 +142,77 @@ def attention_split(q, k, v, cache_lens, scale, num_splits: int = 0, tile_len: i
                                  int(slots), _ptr(o_part), _ptr(m_part), _ptr(lse_part),
                                  _ptr(out), _ptr(lse), nthreads)
     _check(rc, "attention_split")
+    return out, lse, o_part, m_part, lse_part
+
+
+def span_ranges(cache_lens, num_kv_heads: int, spans: int, slots: int, piece_blocks: int = 16,
+                block: int = 16):
+    """Key ranges of the balanced-span split (the equal token bins of page
+    "FlashDecoding算法原理与多GPU并行解码实战", variable-length section, with
+    one bin per span instead of per device).
+
+    Each (sequence b, KV head g) pair holds nb_b = ceil(L_b / block) blocks of
+    ``block`` keys.  Lay the pairs with keys end to end on a line (sequence
+    0's heads 0, 1, ..., then sequence 1's, ...), each taking
+    ``piece_blocks`` positions for the fixed cost of a piece followed by its
+    nb_b blocks, and cut the line every ``per`` positions, per =
+    max(ceil(line length / spans), ceil(max nb_b / (slots - 1)), 1).  The
+    blocks of one pair inside one cut are one piece; its pieces, in key
+    order, are its slots 0, 1, ...: slot i of the pair is cut k0 + i, where
+    k0 is the cut holding the pair's first block.  Returns (lo, hi, per):
+    int32 arrays [B, Hkv, slots] of key ranges (lo == hi == 0: an empty
+    slot) and the cut length in positions.
+    """
+    lens = [max(0, int(x)) for x in np.asarray(cache_lens).reshape(-1)]
+    if slots < 2 or spans < 1:
+        raise ValueError("spans need at least 2 slots and 1 span")
+    nb = [-(-L // block) for L in lens]
+    line = sum(num_kv_heads * (piece_blocks + n) for n in nb if n > 0)
+    per = max(-(-line // spans), -(-max(nb + [0]) // (slots - 1)), 1)
+    lo = np.zeros((len(lens), num_kv_heads, slots), np.int32)
+    hi = np.zeros_like(lo)
+    pos = 0  # line position of the current pair
+    for b, L in enumerate(lens):
+        if nb[b] == 0:
+            continue
+        for g in range(num_kv_heads):
+            first = pos + piece_blocks  # line position of the pair's block 0
+            first_cut = first // per
+            for cut in range(first_cut, (first + nb[b] - 1) // per + 1):
+                a = max(cut * per, first) - first
+                e = min((cut + 1) * per, first + nb[b]) - first
+                i = cut - first_cut
+                if i >= slots:
+                    raise AssertionError("a pair needs more slots than the rule allows")
+                lo[b, g, i] = a * block
+                hi[b, g, i] = min(e * block, L)
+            pos = first + nb[b]
+    return lo, hi, per
+
+
+def attention_ranges(q, k, v, cache_lens, scale, lo, hi, nthreads: int = 0, lib=None):
+    """Split form over explicit key ranges ``lo``/``hi`` [B, Hkv, S] per
+    (sequence, KV head) and slot.  Returns (out, lse, o_part, m_part,
+    lse_part); a slot whose range holds no visible key of a row has m = lse =
+    -inf and o = 0 there."""
+    lib = lib or load()
+    q, k, v, lens, dims = _prep(q, k, v, cache_lens)
+    B, Hq, Hkv, D, q_len, Lmax, code = dims
+    lo = np.ascontiguousarray(lo, dtype=np.int32)
+    hi = np.ascontiguousarray(hi, dtype=np.int32)
+    if lo.shape != hi.shape or lo.ndim != 3 or lo.shape[:2] != (B, Hkv):
+        raise ValueError("lo and hi must be [B, Hkv, S]")
+    S = lo.shape[2]
+    out = np.empty((B, Hq, q_len, D), np.float64)
+    lse = np.empty((B, Hq, q_len), np.float64)
+    o_part = np.empty((B, Hq, q_len, S, D), np.float64)
+    m_part = np.empty((B, Hq, q_len, S), np.float64)
+    lse_part = np.empty((B, Hq, q_len, S), np.float64)
+    rc = lib.orc_attention_ranges(*dims, _ptr(q), _ptr(k), _ptr(v), _ptr(lens),
+                                  float(np.float32(scale)), int(S), _ptr(lo), _ptr(hi),
+                                  _ptr(o_part), _ptr(m_part), _ptr(lse_part), _ptr(out), _ptr(lse),
+                                  nthreads)
+    _check(rc, "attention_ranges")
     return out, lse, o_part, m_part, lse_part
 
 

@@ -315,6 +315,88 @@ int orc_attention_split(int B, int Hq, int Hkv, int D, int q_len, int Lmax, int 
 }
 
 /* ---------------------------------------------------------------------- */
+/* Split form over explicit key ranges: slot i of the rows of (b, g) covers  */
+/* keys [lo, hi) of range arrays [B][Hkv][S] (lo >= hi: an empty slot).      */
+/* Each slot's partial is the definition over its visible keys; the output */
+/* is their merge.  Any disjoint ranges covering each row's visible keys    */
+/* give the attention itself.                                               */
+
+typedef struct {
+    const orc_problem *p;
+    int S;
+    const int32_t *lo, *hi;
+    double *o_part, *m_part, *lse_part, *out, *lse;
+} range_ctx;
+
+static void range_row_fn(void *vctx, long row, double *s) {
+    range_ctx *c = (range_ctx *)vctx;
+    const orc_problem *p = c->p;
+    int b, h, t;
+    split_row(p, row, &b, &h, &t);
+    const int g = h / (p->Hq / p->Hkv);
+    const int n = visible_keys(p, b, t);
+    const size_t pair = ((size_t)b * p->Hkv + g) * c->S;
+    double *mp = c->m_part + (size_t)row * c->S;
+    double *lp = c->lse_part + (size_t)row * c->S;
+    double *op = c->o_part + (size_t)row * c->S * p->D;
+    double *o = c->out + (size_t)row * p->D;
+    for (int d = 0; d < p->D; ++d) o[d] = 0.0;
+    double M = -INFINITY;
+    for (int i = 0; i < c->S; ++i) {
+        int lo = c->lo[pair + i], hi = c->hi[pair + i];
+        if (hi > n) hi = n;
+        mp[i] = -INFINITY;
+        lp[i] = -INFINITY;
+        for (int d = 0; d < p->D; ++d) op[(size_t)i * p->D + d] = 0.0;
+        if (lo < 0) lo = 0;
+        if (hi <= lo) continue;
+        double m = -INFINITY;
+        for (int j = lo; j < hi; ++j) {
+            s[j - lo] = score(p, b, h, t, g, j);
+            m = s[j - lo] > m ? s[j - lo] : m;
+        }
+        double z = 0.0;
+        for (int j = lo; j < hi; ++j) z += exp(s[j - lo] - m);
+        for (int j = lo; j < hi; ++j) {
+            const double w = exp(s[j - lo] - m) / z;
+            for (int d = 0; d < p->D; ++d)
+                op[(size_t)i * p->D + d] += w * load_elem(p->v, p->dtype, kv_index(p, b, g, j, d));
+        }
+        mp[i] = m;
+        lp[i] = m + log(z);
+        M = lp[i] > M ? lp[i] : M;
+    }
+    if (M == -INFINITY) {
+        c->lse[row] = -INFINITY;
+        return;
+    }
+    /* exp(LSE) = sum_i exp(lse_i); out = sum_i exp(lse_i - LSE) o_i. */
+    double z = 0.0;
+    for (int i = 0; i < c->S; ++i)
+        if (lp[i] != -INFINITY) z += exp(lp[i] - M);
+    for (int i = 0; i < c->S; ++i) {
+        if (lp[i] == -INFINITY) continue;
+        const double w = exp(lp[i] - M) / z;
+        for (int d = 0; d < p->D; ++d) o[d] += w * op[(size_t)i * p->D + d];
+    }
+    c->lse[row] = M + log(z);
+}
+
+int orc_attention_ranges(int B, int Hq, int Hkv, int D, int q_len, int Lmax, int dtype,
+                         const void *q, const void *k, const void *v, const int32_t *cache_lens,
+                         double scale, int S, const int32_t *lo, const int32_t *hi,
+                         double *o_part, double *m_part, double *lse_part,
+                         double *out, double *lse, int nthreads) {
+    orc_problem p = {B, Hq, Hkv, D, q_len, Lmax, dtype, q, k, v, cache_lens, scale};
+    if (check_problem(&p)) return -1;
+    if (S < 1 || !lo || !hi) return -1;
+    for (size_t i = 0; i < (size_t)B * Hkv * S; ++i)
+        if (lo[i] < hi[i] && (lo[i] < 0 || hi[i] > Lmax)) return -1;
+    range_ctx c = {&p, S, lo, hi, o_part, m_part, lse_part, out, lse};
+    return run_rows(range_row_fn, &c, (long)B * Hq * q_len, (size_t)Lmax, nthreads);
+}
+
+/* ---------------------------------------------------------------------- */
 /* Sequential form: running max, running sum and running output, rescaled  */
 /* block by block.                                                         */
 
