@@ -350,7 +350,7 @@ def main():
                                                   (f"/paged{args.page_size}{args.page_layout}" if paged else ""))
             if (t and t.get("kernel") == partial_kernel_name(w)
                     and t.get("kernel_hash") == kernel_source_hash(t["kernel"])
-                    and t.get("tile_len") == plan.tile_len):
+                    and t.get("tile_len") == plan.tile_len and t.get("spans", 0) == plan.spans):
                 traffic = t.get("bytes_per_launch")
         except (OSError, ValueError):
             traffic = None
@@ -412,7 +412,7 @@ def main():
             "kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "q_len": w.q_len,
             "cache_lens": "fixed %d" % lens[0] if len(set(lens)) == 1 else "U%s sum %d" % (
                 list(w.len_range), sum(lens)),
-            "tile_len": plan.tile_len, "splits": slots, "kv_copies": copies,
+            "tile_len": plan.tile_len, "splits": slots, "spans": plan.spans, "kv_copies": copies,
             "kv_cache": (f"paged, {args.page_size}-key pages, {args.page_layout}" if paged else "contiguous") +
                         ({"fp8": ", fp8 e4m3 (per-tensor scales)", "int8": ", int8 (symmetric per-tensor scales)",
                           None: ""}[codes]),

@@ -89,6 +89,7 @@ def traffic_entry(key: str, fetch_dir: str, write_dir: str, bench_line: dict) ->
         "kernel": kernel,
         "kernel_hash": kernel_source_hash(kernel),
         "tile_len": bench_line["config"]["tile_len"],
+        "spans": bench_line["config"].get("spans", 0),
         "fetch_kib_raw": round(fk, 2),
         "fetch_scale": round(fs, 4),
         "write_kib_raw": round(wk, 2),
