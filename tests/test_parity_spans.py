@@ -104,6 +104,24 @@ def test_span_count_above_resident_workgroups():
     compare("span 5000 asked", out, lse, *run_oracle(q, k, v, cl, _scale(128)), TOL["bf16"])
 
 
+def test_span_large_ragged_batch_and_empty_batch():
+    """200 short sequences (every workgroup scans the whole batch), then a
+    batch whose sequences all have no keys (every slot padded)."""
+    rng = np.random.Generator(np.random.PCG64(4260))
+    lens = rng.integers(0, 300, size=200).tolist()
+    say(f"[case] span 200 sequences, sum {sum(lens)}")
+    q, k, v, cl = inputs(200, 8, 2, 64, 1, 300, "bf16", 4261, lens, poison=True)
+    plan = _span_plan(64, 4)
+    out, lse = fd.decode_attention(q.cuda(), k.cuda(), v.cuda(), cl.cuda(), scale=_scale(64), plan=plan)
+    torch.cuda.synchronize()
+    compare("span 200 sequences", out, lse, *run_oracle(q, k, v, cl, _scale(64)), TOL["bf16"])
+    say("[case] span batch without keys")
+    q, k, v, cl = inputs(3, 8, 2, 64, 1, 64, "bf16", 4262, [0, 0, 0])
+    out, lse = fd.decode_attention(q.cuda(), k.cuda(), v.cuda(), cl.cuda(), scale=_scale(64), plan=_span_plan(16, 3))
+    torch.cuda.synchronize()
+    assert torch.all(out.float() == 0) and torch.all(torch.isneginf(lse))
+
+
 @pytest.mark.parametrize("codes", ["fp8", "int8"])
 def test_span_one_byte_caches(codes):
     lens = [3000, 100, 0, 1777, 16]

@@ -40,11 +40,13 @@ def _noalloc_c(qd, kd, vd, cld, sc, num_splits, plan, out, lse):
 
 
 CASES = [
-    # name, (B, Hq, Hkv, D, q_len, Lmax, dtype), lens, num_splits (0: planner)
+    # name, (B, Hq, Hkv, D, q_len, Lmax, dtype), lens, num_splits (0: planner; -n: planner for n compute
+    # units, which gives these ragged batches a balanced-span plan)
     ("gqa 8k planned", (2, 32, 8, 128, 1, 8192, "bf16"), [8192, 5000], 0),
     ("smaller: mha D64 forced 5", (1, 8, 2, 64, 1, 700, "bf16"), [700], 5),
     ("chunk q_len 40 forced 3", (2, 8, 2, 128, 40, 1500, "bf16"), [1500, 300], 3),
     ("f32 forced 7", (2, 8, 2, 128, 1, 900, "f32"), [900, 31], 7),
+    ("ragged, balanced spans", (5, 32, 8, 128, 1, 2000, "bf16"), [2000, 77, 0, 1500, 640], -4),
 ]
 
 
@@ -54,7 +56,10 @@ def test_noalloc_matches_workspace_entry_point():
         q, k, v, cl = inputs(B, Hq, Hkv, D, T, Lmax, dt, 7000 + i, lens)
         qd, kd, vd, cld = q.cuda(), k.cuda(), v.cuda(), cl.cuda()
         sc = _scale(D)
-        plan = fd.plan_for(q, k, cl) if S == 0 else None
+        plan = fd.plan_for(q, k, cl, num_cus=-S) if S < 0 else fd.plan_for(q, k, cl) if S == 0 else None
+        if S < 0:
+            assert plan.spans > 0
+            S = 0
         ref_out, ref_lse = fd.decode_attention(qd, kd, vd, cld, scale=sc, num_splits=S, plan=plan)
         out = torch.full_like(qd, float("nan"))
         lse = torch.full(qd.shape[:3], float("nan"), dtype=torch.float32, device="cuda")
