@@ -234,6 +234,32 @@ def test_decode_rejects_bad_split_arguments(lib):
     assert call_decode(lib, d, plan=bad) == fd.FD_ERR_INVALID
     bad = fd.FdPlan(tile_len=256, max_splits=300)
     assert call_decode(lib, d, plan=bad) == fd.FD_ERR_INVALID
+    bad = fd.FdPlan(tile_len=256, max_splits=4, spans=-1)
+    assert call_decode(lib, d, plan=bad) == fd.FD_ERR_INVALID
+    bad = fd.FdPlan(tile_len=256, max_splits=4, spans=(1 << 20) + 1)
+    assert call_decode(lib, d, plan=bad) == fd.FD_ERR_INVALID
+
+
+def test_planner_asks_for_spans_only_past_one_round_of_tiles():
+    """Mixed lengths with more tiles than two per compute unit get balanced
+    spans (two per unit) and enough slots for them; equal lengths, small
+    batches, fp32 and long chunks keep tiles."""
+    rng = np.random.Generator(np.random.PCG64(3))
+    lens = rng.integers(512, 8193, size=32).tolist()
+    d = fd.make_dims(32, 64, 8, 128, 1, 8192, fd.FD_BF16)
+    p = fd.plan_splits(d, lens, num_cus=256)
+    assert p.spans == 512 and p.plan.work_units > 512
+    # a pair of the longest sequence fits its slots at the shortest span
+    blocks = sum(-(-L // 16) for L in lens) * 8
+    span = -(-blocks // 512)
+    assert p.max_splits >= -(-(-(-max(lens) // 16)) // span) + 1
+    assert fd.plan_splits(d, [8192] * 32, num_cus=256).spans == 0          # equal lengths
+    assert fd.plan_splits(d, lens, num_cus=4096).spans == 0                # one round of tiles
+    d32 = fd.make_dims(32, 64, 8, 128, 1, 8192, fd.FD_F32)
+    assert fd.plan_splits(d32, lens, num_cus=256).spans == 0               # vector kernel
+    dq = fd.make_dims(32, 64, 8, 128, 8, 8192, fd.FD_BF16)
+    assert fd.plan_splits(dq, lens, num_cus=256).spans == 0                # 64-row chunks: chunk kernel
+    assert fd.plan_splits(d, lens, num_splits=4, num_cus=256).spans == 0   # forced count
 
 
 def test_partials_and_combine_reject_bad_arguments(lib):
