@@ -10,7 +10,7 @@
   requires.  ``--update`` writes the entry into profiles/traffic.json under
   KEY (the workload name, ``/fp8`` or ``/int8`` for one-byte caches).
 
-    python -m decode_attention_14_amd.profiling trace gpurun_out/prof/trace_32k
+    python -m decode_attention_14_amd.profiling trace prof/trace_32k
     python -m decode_attention_14_amd.profiling traffic gqa_32k DIR_F DIR_W bench.json --update
 """
 from __future__ import annotations
