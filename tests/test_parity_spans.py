@@ -122,6 +122,20 @@ def test_span_large_ragged_batch_and_empty_batch():
     assert torch.all(out.float() == 0) and torch.all(torch.isneginf(lse))
 
 
+@pytest.mark.parametrize("dt,T", [("f32", 1), ("bf16", 40)])
+def test_span_plans_on_tile_kernels(dt, T):
+    """A span plan handed to a call that the decode kernel does not serve
+    (fp32 caches: the vector kernel; 320 rows per KV head: the chunk kernel)
+    runs the plan's tiles."""
+    lens = [1000, 77, 0, 640]
+    say(f"[case] span plan on the {'vector' if dt == 'f32' else 'chunk'} kernel")
+    q, k, v, cl = inputs(4, 16, 2, 128, T, 1000, dt, 4270 + T, lens)
+    plan = _span_plan(9, 4)
+    out, lse = fd.decode_attention(q.cuda(), k.cuda(), v.cuda(), cl.cuda(), scale=_scale(128), plan=plan)
+    torch.cuda.synchronize()
+    compare(f"span plan, {dt} q_len {T}", out, lse, *run_oracle(q, k, v, cl, _scale(128)), TOL[dt])
+
+
 @pytest.mark.parametrize("codes", ["fp8", "int8"])
 def test_span_one_byte_caches(codes):
     lens = [3000, 100, 0, 1777, 16]
