@@ -173,3 +173,45 @@ def test_span_paged_equals_contiguous(layout):
     fin = torch.isfinite(l_p)
     assert torch.equal(o_p[fin], co[fin])
     compare(f"span paged {layout}", out, lse, *run_oracle(q, k, v, cl, sc), TOL["bf16"])
+
+
+COMBO_CASES = [
+    # codes, page (size, layout) or None, q_len, D, Hq, Hkv
+    ("fp8", (16, "nhd"), 3, 64, 16, 4),
+    ("int8", (32, "hnd"), 1, 128, 32, 8),
+    (None, (16, "hnd"), 2, 64, 16, 2),
+    ("fp8", None, 4, 128, 64, 8),
+]
+
+
+@pytest.mark.parametrize("case", COMBO_CASES, ids=lambda c: f"{c[0]}-{c[1]}-q{c[2]}-D{c[3]}")
+def test_span_combinations(case):
+    """Spans with one-byte codes, pages, causal chunks, both head dims and
+    up to 32 rows per KV head, whole calls against the oracle."""
+    codes, page, T, D, Hq, Hkv = case
+    lens = [1500, 3, 0, 700, 129, 2048]
+    lens = [max(L, T) if L else 0 for L in lens]
+    say(f"[case] span combination {case}")
+    q, k, v, cl = inputs(len(lens), Hq, Hkv, D, T, 2048, "bf16", 4300 + D + T, lens)
+    sc = _scale(D)
+    plan = _span_plan(23, 5)
+    if codes:
+        scale_for, quantize = (fp8_scale_for, quantize_fp8) if codes == "fp8" else (int8_scale_for, quantize_int8)
+        ks, vs = scale_for(k), scale_for(v)
+        kc, vc = quantize(k, ks), quantize(v, vs)
+        ref_fn = oracle.attention_fp8 if codes == "fp8" else oracle.attention_int8
+        ref = ref_fn(as_oracle_array(q), kc.numpy(), vc.numpy(), cl.numpy(), sc, ks, vs)
+        table, layout = None, "nhd"
+        if page is not None:
+            pc = paginate(kc, vc, cl, page[0], page[1], seed=4390)
+            kc, vc, table, layout = pc.k_pages, pc.v_pages, pc.block_table.cuda(), page[1]
+        attn = fd.decode_attention_fp8 if codes == "fp8" else fd.decode_attention_int8
+        out, lse = attn(q.cuda(), kc.cuda(), vc.cuda(), cl.cuda(), ks, vs, block_table=table, layout=layout,
+                        scale=sc, plan=plan)
+    else:
+        ref = run_oracle(q, k, v, cl, sc)
+        pc = paginate(k, v, cl, page[0], page[1], seed=4391)
+        out, lse = fd.decode_attention_paged(q.cuda(), pc.k_pages.cuda(), pc.v_pages.cuda(), pc.block_table.cuda(),
+                                             cl.cuda(), layout=page[1], scale=sc, plan=plan)
+    torch.cuda.synchronize()
+    compare(f"span {case}", out, lse, *ref, TOL["bf16"])
