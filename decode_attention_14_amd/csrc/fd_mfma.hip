@@ -103,6 +103,19 @@ constexpr int kMW = kMT / 64;     // waves per workgroup
 #define FD_CODE8_WAVES 8
 #endif
 constexpr int kMW8 = FD_CODE8_WAVES;  // waves per workgroup over one-byte caches
+#ifndef FD_CODE8_SPAN_WAVES
+#define FD_CODE8_SPAN_WAVES 4
+#endif
+// ... in span mode: three four-wave workgroups fit a compute unit's LDS, and
+// while one merges a piece or waits for a piece's first loads the others
+// stream (FP8 caches, 32-sequence variable-length batch: 56.7-56.8 against
+// 57.7 us with eight waves).
+constexpr int kMW8S = FD_CODE8_SPAN_WAVES;
+
+// Waves per workgroup of the decode kernel for a cache format and mode.
+__host__ __device__ constexpr int decode_waves(int kv, bool spans) {
+    return kv == kKvBf16 ? kMW : (spans ? kMW8S : kMW8);
+}
 constexpr int kKB = 16;           // keys per block
 constexpr int kNS = FD_MFMA_STAGES;
 // Span mode: line positions in front of each (sequence, KV head) pair, the
@@ -384,10 +397,10 @@ __device__ __forceinline__ void load_fragments(const char* kb, const char* vb, b
 }
 
 // Launch geometry and LDS bytes of the decode kernel.
-template <int D, int NB, int KV>
+template <int D, int NB, int KV, bool SPANS>
 struct DecodeGeo {
     static constexpr bool C8 = KV != kKvBf16;  // one-byte codes
-    static constexpr int MW = C8 ? kMW8 : kMW;  // waves per workgroup
+    static constexpr int MW = decode_waves(KV, SPANS);  // waves per workgroup
     static constexpr int MT = 64 * MW;
     static constexpr int NR = 16 * NB;          // query rows per workgroup
     static constexpr int RS = D + 4;            // padded row stride of the merge area (floats)
@@ -402,10 +415,10 @@ struct DecodeGeo {
 // untouched); pad_from = slots pads nothing.  smem: the kernel's LDS block;
 // on return every wave is past its last LDS access of the unit only after a
 // barrier, which the caller places before reusing it.
-template <int D, int NB, bool CAUSAL, bool PAGED, int KV>
+template <int D, int NB, bool CAUSAL, bool PAGED, int KV, bool SPANS>
 __device__ __forceinline__ void partial_unit(const PartialArgs& a, char* smem, int g, int b, int s, int L, int lo,
                                              int hi, int pad_from, uint64_t& tl_first) {
-    using DG = DecodeGeo<D, NB, KV>;
+    using DG = DecodeGeo<D, NB, KV, SPANS>;
     constexpr bool C8 = DG::C8;
     using G = Geo<D>;
     using LG = LGeo<D, C8>;
@@ -655,8 +668,8 @@ __device__ __forceinline__ void partial_unit(const PartialArgs& a, char* smem, i
 // whole by workgroup b % grid.  Every workgroup computes the totals from
 // cache_lens itself (wave-uniform scalar loop over the batch).
 template <int D, int NB, bool CAUSAL, bool PAGED, int KV, bool SPANS>
-__global__ __launch_bounds__(KV != kKvBf16 ? 64 * kMW8 : kMT) void fd_mfma_partial_kernel(PartialArgs a) {
-    using DG = DecodeGeo<D, NB, KV>;
+__global__ __launch_bounds__(64 * decode_waves(KV, SPANS)) void fd_mfma_partial_kernel(PartialArgs a) {
+    using DG = DecodeGeo<D, NB, KV, SPANS>;
     __shared__ __attribute__((aligned(16))) char smem[DG::SMEMB];
     uint64_t tl_first = 0;
 #if FD_WG_TIMELINE
@@ -694,7 +707,7 @@ __global__ __launch_bounds__(KV != kKvBf16 ? 64 * kMW8 : kMT) void fd_mfma_parti
             }
             return;
         }
-        partial_unit<D, NB, CAUSAL, PAGED, KV>(a, smem, g, b, s, L, lo, hi, slots, tl_first);
+        partial_unit<D, NB, CAUSAL, PAGED, KV, SPANS>(a, smem, g, b, s, L, lo, hi, slots, tl_first);
     } else {
         // Span state: span sp of nsp, [R0, R1) of per blocks; the current
         // pair (sb, sg) of sb's snb blocks and sL keys, sC the first block of
@@ -780,7 +793,7 @@ __global__ __launch_bounds__(KV != kKvBf16 ? 64 * kMW8 : kMT) void fd_mfma_parti
                 more = sb < a.batch;
             }
             if (it > 0) __syncthreads();  // the previous unit's LDS reads are done
-            partial_unit<D, NB, CAUSAL, PAGED, KV>(a, smem, g, b, s, L, lo, hi, pad_from, tl_first);
+            partial_unit<D, NB, CAUSAL, PAGED, KV, SPANS>(a, smem, g, b, s, L, lo, hi, pad_from, tl_first);
         }
     }
 #if FD_WG_TIMELINE
@@ -843,7 +856,7 @@ void launch_decode(dim3 grid, dim3 block, const PartialArgs& a, hipStream_t stre
 
 template <int D, int NB, int KV, bool SPANS>
 void launch_nb_kv_s(int batch, const PartialArgs& a, hipStream_t stream) {
-    const dim3 grid(a.Hkv, a.rule.slots, batch), block(KV != kKvBf16 ? 64 * kMW8 : kMT);
+    const dim3 grid(a.Hkv, a.rule.slots, batch), block(64 * decode_waves(KV, SPANS));
     const bool paged = a.pages.table != nullptr;
     if (a.q_len > 1) {
         if (paged)
