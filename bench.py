@@ -79,6 +79,8 @@ def parse_args():
     ap.add_argument("--workload", default="gqa_32k")
     ap.add_argument("--num-splits", type=int, default=0, help="force a split count (0: planner)")
     ap.add_argument("--tile-len", type=int, default=0, help="override the planner's tile length")
+    ap.add_argument("--spans", type=int, default=-1,
+                    help="force N balanced spans (0: tiles; -1: the planner's choice)")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of a graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target oracle time")
@@ -212,6 +214,18 @@ def main():
                                        w.max_cache_len, q.dtype), cl, num_splits=args.num_splits)
     if args.tile_len:
         plan = fd.Plan(fd.FdPlan(args.tile_len, max(1, -(-max(lens) // args.tile_len))), [])
+    if args.spans >= 0:
+        if args.num_splits:
+            raise SystemExit("bench.py: --spans and --num-splits do not combine")
+        slots = plan.max_splits
+        if args.spans:
+            # the slots a pair needs when the line of 16-key blocks (each pair
+            # with keys preceded by 16 positions) is cut into args.spans spans
+            nb = [-(-max(0, min(L, w.max_cache_len)) // 16) for L in lens]
+            line = sum(w.num_kv_heads * (16 + n) for n in nb if n)
+            per = max(1, -(-line // args.spans))
+            slots = min(fd.FD_MAX_SPLITS, max(slots, -(-max(nb) // per) + 1))
+        plan = fd.Plan(fd.FdPlan(tile_len=plan.tile_len, max_splits=slots, spans=args.spans), plan.splits_per_seq)
     num_splits = args.num_splits
     slots = num_splits if num_splits else plan.max_splits
 
