@@ -1,11 +1,12 @@
 """GPU parity of the one-byte and paged cache paths at the benchmark
 workloads' shapes, in the launch configuration the benchmark times (the
-planner's tiles), every output row against the fp64 oracle at the flat
+planner's plan), every output row against the fp64 oracle at the flat
 tolerance (2e-3 on out and lse) with the rel-L2 guard.
 
-Shapes: the 32-sequence variable-length batch (lengths U[512, 8192], 1280-key
-tiles, several units per compute unit) and the 4 x 128k batch (16384-key
-tiles, which give each wave of the one-byte decode kernel 128 blocks); FP8
+Shapes: the 32-sequence variable-length batch (lengths U[512, 8192]; on a
+256-CU device the planner cuts it into balanced spans, one per resident
+workgroup) and the 4 x 128k batch (16384-key tiles, which give each wave of
+the one-byte decode kernel 128 blocks); FP8
 E4M3 and INT8 caches (per-tensor scales) and 16-key pages in both layouts.
 Page "ChunkedPrefill与FlashDecoding技术解析" §4.2 item 1 asks for exactly this
 check: the tiled result against the full one on the same seeded inputs.
