@@ -143,9 +143,12 @@ int64_t row_bytes(const fd_dims* d, bool codes) {
 
 // The most keys one tile of `rule` can hold for a sequence of at most Lmax
 // keys (the tile rule of fdk::tile_of: the last tile takes the rest when the
-// count reaches the slots).
+// count reaches the slots).  Under balanced spans a piece is bounded only by
+// its (sequence, KV head) pair, since few resident workgroups make long
+// spans: all Lmax keys.
 int64_t max_tile_keys(const fdk::SplitRule& r, int64_t Lmax) {
     if (Lmax <= 0) return 0;
+    if (r.spans > 0) return Lmax;
     if (r.tile_len > 0) {
         const int64_t T = r.tile_len;
         const int64_t S = std::min<int64_t>(ceil_div(Lmax, T), r.slots);
@@ -322,8 +325,11 @@ fd_status fd_plan_splits(const fd_dims* dims, const int32_t* cache_lens_host, in
         p.tile_len = (int32_t)T;
         p.max_splits = (int32_t)smax;
         p.work_units = (int32_t)std::min<int64_t>(units, INT32_MAX);
+        // Spans only where a whole pair of bf16 rows stays below 2^31 bytes
+        // (the bound the launch checks a span rule against).
+        const bool span_bytes_ok = (int64_t)dims->max_cache_len * dims->head_dim * 2 < ((int64_t)1 << 31);
         if (min_len != max_len && rows <= 32 && fdk::use_mfma_partials(dims->dtype, dims->head_dim, rows) &&
-            dims->batch <= kSpanMaxBatch && units > (int64_t)num_cus * kSpanWGsPerCU) {
+            dims->batch <= kSpanMaxBatch && units > (int64_t)num_cus * kSpanWGsPerCU && span_bytes_ok) {
             // More tiles than one round of workgroups: equal spans instead,
             // two per CU, none shorter than kMinTile keys, and enough slots
             // that a pair of the longest sequence spans ceil(blocks / span) + 1

@@ -43,7 +43,10 @@
  *     any q_len >= 1.  One tile's keys of one KV head must span fewer than
  *     2^31 bytes of a cache (for bf16 at D = 128, fewer than 8,388,608 keys):
  *     a call whose split rule allows a larger tile (few splits over a very
- *     long max_cache_len) returns FD_ERR_UNSUPPORTED; more splits fix it.  Arithmetic is fp32 throughout (scores, softmax,
+ *     long max_cache_len) returns FD_ERR_UNSUPPORTED; more splits fix it.
+ *     Under balanced spans (fd_plan.spans > 0) a piece can hold a whole
+ *     (sequence, KV head) pair, so max_cache_len itself must stay below
+ *     that bound; the planner asks for spans only then.  Arithmetic is fp32 throughout (scores, softmax,
  *     accumulation); out is rounded to its dtype with round-to-nearest-even.
  *     Caches of one-byte codes (FP8 E4M3, INT8) with bf16 q and out have
  *     calls of their own (fd_decode_attention_fp8, fd_decode_attention_int8),

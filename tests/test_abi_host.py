@@ -260,6 +260,10 @@ def test_planner_asks_for_spans_only_past_one_round_of_tiles():
     dq = fd.make_dims(32, 64, 8, 128, 8, 8192, fd.FD_BF16)
     assert fd.plan_splits(dq, lens, num_cus=256).spans == 0                # 64-row chunks: chunk kernel
     assert fd.plan_splits(d, lens, num_splits=4, num_cus=256).spans == 0   # forced count
+    # a pair of 2^23 bf16 rows at D = 128 would reach 2^31 bytes in one piece
+    big = [1 << 22, 1000, 5000, 300]
+    assert fd.plan_splits(fd.make_dims(4, 64, 8, 128, 1, (1 << 23) - 16, fd.FD_BF16), big, num_cus=4).spans > 0
+    assert fd.plan_splits(fd.make_dims(4, 64, 8, 128, 1, 1 << 23, fd.FD_BF16), big, num_cus=4).spans == 0
 
 
 def test_partials_and_combine_reject_bad_arguments(lib):
@@ -308,6 +312,14 @@ def test_tiles_of_2gib_or_more_are_rejected(lib):
     assert call_decode(lib, d_long, plan=p) == fd.FD_ERR_UNSUPPORTED
     p = fd.FdPlan(tile_len=1 << 20, max_splits=3)  # last tile 2^23 - 2^20 keys
     assert call_decode(lib, d_long, plan=p) == fd.FD_ERR_WORKSPACE
+    # the same plan with balanced spans: a piece may hold a whole pair
+    # (2^23 + 2^20 keys) when few workgroups are resident, so it is refused;
+    # below 2^23 keys the span plan passes
+    p = fd.FdPlan(tile_len=1 << 20, max_splits=3, spans=64)
+    assert call_decode(lib, d_long, plan=p) == fd.FD_ERR_UNSUPPORTED
+    assert "2^31" in lib.fd_last_error().decode()
+    d_short = dims(B=1, Hq=32, Hkv=8, D=128, T=1, Lmax=L - 16)
+    assert call_decode(lib, d_short, plan=p) == fd.FD_ERR_WORKSPACE
     # one-byte codes hold twice the keys per byte: one tile of 2^23 codes at
     # D = 128 is 2^30 bytes and passes (the misaligned out stops the call
     # before any launch)
