@@ -13,7 +13,7 @@ import oracle
 from decode_attention_14_amd import binding as fd
 from decode_attention_14_amd.inputs import (as_oracle_array, fp8_scale_for, int8_scale_for, paginate, quantize_fp8,
                                             quantize_int8)
-from gpu_cases import TOL, compare, inputs, run_oracle, say
+from gpu_cases import TOL, compare, compare_workload, inputs, run_oracle, say
 
 pytestmark = [
     pytest.mark.gpu,
@@ -215,3 +215,25 @@ def test_span_combinations(case):
                                              cl.cuda(), layout=page[1], scale=sc, plan=plan)
     torch.cuda.synchronize()
     compare(f"span {case}", out, lse, *ref, TOL["bf16"])
+
+
+@pytest.mark.parametrize("codes", ["bf16", "fp8"])
+def test_span_plan_forced_on_the_32k_layer(codes):
+    """Spans forced on the equal-length 32k layer (B1, Hq32, Hkv8, D128, 32768
+    keys), as ``bench.py --spans 512`` times it (512 spans, 64 slots): every
+    output row against the fp64 oracle at the flat workload tolerance."""
+    from decode_attention_14_amd.inputs import WORKLOADS, workload_inputs
+    w = WORKLOADS["gqa_32k"]
+    say(f"[case] {codes} caches, workload {w.name}, 512 forced spans over 64 slots")
+    q, k, v, cl = workload_inputs(w)
+    plan = fd.FdPlan(tile_len=1024, max_splits=64, spans=512)
+    if codes == "fp8":
+        ks, vs = fp8_scale_for(k), fp8_scale_for(v)
+        kc, vc = quantize_fp8(k, ks), quantize_fp8(v, vs)
+        ref = oracle.attention_fp8(as_oracle_array(q), kc.numpy(), vc.numpy(), cl.numpy(), w.scale, ks, vs)
+        out, lse = fd.decode_attention_fp8(q.cuda(), kc.cuda(), vc.cuda(), cl.cuda(), ks, vs, scale=w.scale, plan=plan)
+    else:
+        ref = run_oracle(q, k, v, cl, w.scale)
+        out, lse = fd.decode_attention(q.cuda(), k.cuda(), v.cuda(), cl.cuda(), scale=w.scale, plan=plan)
+    torch.cuda.synchronize()
+    compare_workload(f"{codes} {w.name} 512 spans", out, lse, *ref)
